@@ -1,0 +1,446 @@
+"""Pins that tie the fp64 oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and returns a list of failure
+messages (empty = pass).  ``test_oracle_pins.py`` runs them against the real
+oracle; ``test_oracle_mutants.py`` runs them against deliberately broken builds
+of the oracle and requires every broken build to fail at least one pin.
+
+None of these re-types the oracle's own formula: each compares against a value
+printed on a page, a closed form, a brute-force selection, an invariant, or a
+reduction of one case to another.
+"""
+from __future__ import annotations
+
+import json
+import math
+import pathlib
+
+import numpy as np
+
+import oracle as oracle_mod
+
+GOLDEN = json.loads((pathlib.Path(__file__).parent / "golden" / "worked_example.json").read_text())
+CAUSAL = oracle_mod.MASK_CAUSAL
+NONE = oracle_mod.MASK_NONE
+
+
+def _close(fails, what, got, want, tol):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    if got.shape != want.shape:
+        fails.append(f"{what}: shape {got.shape} != {want.shape}")
+        return
+    if not np.all(np.isfinite(got)):
+        fails.append(f"{what}: non-finite values")
+        return
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    if not err <= tol:
+        fails.append(f"{what}: max err {err:.3g} > {tol:.3g}")
+
+
+def _same(fails, what, got, want):
+    if not np.array_equal(np.asarray(got), np.asarray(want)):
+        fails.append(f"{what}: not bit-identical")
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# --------------------------------------------------------------------------
+# Values printed on the pages.
+
+def pin_worked_example(orc):
+    """aicomputerinstitute.com chapter, 'Worked example: attention weights and outputs
+    by hand' and 'Active recall' answers 2 and 3: weights, outputs and scaled scores
+    printed to 6 decimals for the 3-token example (Q = K = V = X, d_k = 2)."""
+    fails = []
+    tol = GOLDEN["tolerance"]
+    toks = GOLDEN["tokens"]
+    for case in GOLDEN["cases"]:
+        x = np.array(case["X"], np.float64)[None, None]
+        out, w = orc.attention(x, x, x, scale=case["scale"], return_weights=True, nthreads=1)
+        s = orc.scores(x, x, scale=case["scale"])
+        for tok, vals in case["weights"].items():
+            _close(fails, f"{case['name']} weights[{tok}]", w[0, 0, toks.index(tok)], vals, tol)
+        for tok, vals in case["outputs"].items():
+            _close(fails, f"{case['name']} out[{tok}]", out[0, 0, toks.index(tok)], vals, tol)
+        for tok, vals in case.get("scaled_scores", {}).items():
+            _close(fails, f"{case['name']} scores[{tok}]", s[0, 0, toks.index(tok)], vals, tol)
+    return fails
+
+
+def _case(name):
+    return next(c for c in GOLDEN["cases"] if c["name"] == name)
+
+
+def _printed_outputs(case):
+    toks = GOLDEN["tokens"]
+    return np.array([case["outputs"][t] for t in toks], np.float64)
+
+
+def pin_worked_example_projection(orc):
+    """The same example through the projection path.  The page uses identity
+    projections, so with H = 1 and W_Q = W_K = W_V = W_O = I the printed outputs
+    must come back.  With H = 2 and the two printed variants side by side in the
+    two heads' feature blocks, head h's outputs land in column block h of the
+    concatenation ([TP] "Multi-Head Attention"); a W_O that swaps the two blocks
+    swaps them in the output ([TP] "The Output Projection W^O")."""
+    fails = []
+    tol = GOLDEN["tolerance"]
+    base, dbl = _case("scaled"), _case("was_doubled")
+    xb = np.array(base["X"], np.float64)
+    xd = np.array(dbl["X"], np.float64)
+    eye2 = np.eye(2)
+    out = orc.mha_proj(xb[None], None, eye2, eye2, eye2, eye2, H=1, scale=base["scale"], nthreads=1)
+    _close(fails, "H=1 identity projections", out[0], _printed_outputs(base), tol)
+
+    x2 = np.concatenate([xb, xd], axis=1)[None]          # [1, 3, 4]
+    eye4 = np.eye(4)
+    out = orc.mha_proj(x2, None, eye4, eye4, eye4, eye4, H=2, scale=base["scale"], nthreads=1)
+    _close(fails, "H=2 head 0 block", out[0, :, 0:2], _printed_outputs(base), tol)
+    _close(fails, "H=2 head 1 block", out[0, :, 2:4], _printed_outputs(dbl), tol)
+    swap = np.zeros((4, 4))
+    for r in range(4):
+        swap[r, (r + 2) % 4] = 1.0
+    out = orc.mha_proj(x2, None, eye4, eye4, eye4, swap, H=2, scale=base["scale"], nthreads=1)
+    _close(fails, "H=2 swapped W_O block 0", out[0, :, 0:2], _printed_outputs(dbl), tol)
+    _close(fails, "H=2 swapped W_O block 1", out[0, :, 2:4], _printed_outputs(base), tol)
+    return fails
+
+
+# --------------------------------------------------------------------------
+# Closed forms and invariants.
+
+def _random_case(seed, B=3, H=2, Nq=21, Nk=21, dk=16, dv=12, lo=1):
+    g = _rng(seed)
+    q = g.standard_normal((B, H, Nq, dk))
+    k = g.standard_normal((B, H, Nk, dk))
+    v = g.standard_normal((B, H, Nk, dv))
+    lens = g.integers(lo, Nk + 1, size=B).astype(np.int32)
+    return q, k, v, lens
+
+
+def pin_row_sums_and_zero_weights(orc):
+    """Every softmax row sums to 1 ([TP] step 3; [AD] 'The attention mechanism');
+    masked keys get weight exactly 0 and visible keys a positive weight ([TP] 'Why
+    Masking Is Required': exp(-inf) = 0)."""
+    fails = []
+    for mask in (NONE, CAUSAL):
+        q, k, v, lens = _random_case(11 + mask)
+        lens[0] = q.shape[2]
+        _, w = orc.attention(q, k, v, mask_kind=mask, key_lens=lens, return_weights=True, nthreads=2)
+        B, H, Nq, Nk = w.shape
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nk)[None, :]
+        for b in range(B):
+            vis = j < lens[b]
+            if mask == CAUSAL:
+                vis = vis & (j <= i)
+            vis = np.broadcast_to(vis, (H, Nq, Nk))
+            wb = w[b]
+            if np.any(wb[~vis] != 0.0):
+                fails.append(f"mask={mask} b={b}: masked weight not exactly 0")
+            if np.any(wb[vis] <= 0.0):
+                fails.append(f"mask={mask} b={b}: visible weight not positive")
+            _close(fails, f"mask={mask} b={b} row sums", wb.sum(-1), np.ones((H, Nq)), 1e-14)
+    return fails
+
+
+def pin_zero_query_gives_mean(orc):
+    """With Q = 0 every visible score is equal, so the weights are uniform and each
+    output row is the mean of the visible V rows ([TP] steps 3-4)."""
+    fails = []
+    for mask, Nq, Nk in ((NONE, 13, 29), (CAUSAL, 17, 17)):
+        q, k, v, lens = _random_case(21 + mask, Nq=Nq, Nk=Nk)
+        q[:] = 0.0
+        out = orc.attention(q, k, v, mask_kind=mask, key_lens=lens, nthreads=2)
+        want = np.zeros_like(out)
+        for b in range(q.shape[0]):
+            for i in range(Nq):
+                n = min(lens[b], i + 1) if mask == CAUSAL else lens[b]
+                want[b, :, i] = v[b, :, :n].mean(axis=1)
+        _close(fails, f"Q=0 mean (mask={mask})", out, want, 1e-13)
+    return fails
+
+
+def pin_causal_first_row(orc):
+    """Under the causal mask query 0 sees only key 0, whose weight is then exactly
+    1, so output row 0 equals V row 0 ([AD] 'Masked Multi-Head Attention')."""
+    fails = []
+    q, k, v, lens = _random_case(31)
+    out = orc.attention(q, k, v, mask_kind=CAUSAL, key_lens=lens, nthreads=2)
+    _same(fails, "causal row 0 == V row 0", out[:, :, 0], v[:, :, 0])
+    return fails
+
+
+def pin_one_hot_selection(orc):
+    """One-hot keys k_j = c e_pi(j) and one-hot queries q_i = e_pi(t_i): the only
+    large score in row i is at key t_i (scaled score 40 against 0), so the output is
+    V row t_i up to e^-40 -- a brute-force selection, for cross-attention shapes
+    (Nq != Nk, padded source) and for causal self-attention."""
+    fails = []
+    g = _rng(41)
+    d = 64
+    scale = 1.0 / math.sqrt(d)
+    c = 40.0 / scale
+    for mask, B, Nq, Nk in ((NONE, 3, 37, 50), (CAUSAL, 2, 45, 45)):
+        H = 2
+        q = np.zeros((B, H, Nq, d))
+        k = np.zeros((B, H, Nk, d))
+        v = g.standard_normal((B, H, Nk, 24))
+        lens = g.integers(1, Nk + 1, size=B).astype(np.int32)
+        want = np.zeros((B, H, Nq, 24))
+        for b in range(B):
+            for h in range(H):
+                pi = g.permutation(d)[:Nk]
+                k[b, h, np.arange(Nk), pi] = c
+                for i in range(Nq):
+                    hi = min(lens[b], i + 1) if mask == CAUSAL else lens[b]
+                    t = int(g.integers(0, hi))
+                    q[b, h, i, pi[t]] = 1.0
+                    want[b, h, i] = v[b, h, t]
+        out = orc.attention(q, k, v, mask_kind=mask, key_lens=lens, scale=scale, nthreads=2)
+        _close(fails, f"one-hot selection (mask={mask})", out, want, 1e-12)
+    return fails
+
+
+def pin_large_logits(orc):
+    """Scaled logits of about 1000 (far beyond exp's range) must still give the
+    selected V row: softmax is shift-invariant, so a correct implementation never
+    forms exp of a large positive number."""
+    fails = []
+    B, H, Nq, Nk, d = 1, 1, 5, 7, 8
+    q = np.zeros((B, H, Nq, d))
+    k = np.zeros((B, H, Nk, d))
+    v = _rng(43).standard_normal((B, H, Nk, 3))
+    for j in range(Nk):
+        k[0, 0, j, j] = 1000.0 + j
+    for i in range(Nq):
+        q[0, 0, i, (3 * i + 1) % Nk] = 1.0
+    out = orc.attention(q, k, v, scale=1.0, nthreads=1)
+    want = v[0, 0, [(3 * i + 1) % Nk for i in range(Nq)]][None, None]
+    _close(fails, "selection with logits ~1e3", out, want, 1e-12)
+    return fails
+
+
+def pin_two_key_logistic(orc):
+    """With two visible keys the softmax is the logistic function of the score gap:
+    w0 = 1 / (1 + exp(s1 - s0)).  q = (1, 2), k0 = (3, 0), k1 = (0, 1) give raw
+    scores 3 and 2, so at scale 1/2 the gap is 1/2."""
+    fails = []
+    q = np.array([1.0, 2.0])[None, None, None]
+    k = np.array([[3.0, 0.0], [0.0, 1.0]])[None, None]
+    v = np.array([[1.0, -2.0, 5.0], [-4.0, 0.5, 7.0]])[None, None]
+    out, w = orc.attention(q, k, v, scale=0.5, return_weights=True, nthreads=1)
+    w0 = 1.0 / (1.0 + math.exp(-0.5))
+    _close(fails, "two-key weights", w[0, 0, 0], [w0, 1.0 - w0], 1e-15)
+    _close(fails, "two-key output", out[0, 0, 0], w0 * v[0, 0, 0] + (1.0 - w0) * v[0, 0, 1], 1e-14)
+    return fails
+
+
+def pin_sqrt_dk_statistics(orc):
+    """For N(0,1) query and key components q.k has variance d_k, so over 4,000
+    independent pairs std(q.k) is near sqrt(d_k) and near 1 after the 1/sqrt(d_k)
+    scale ([TP] 'Why the sqrt(d_k) Scaling Exists'; [AC] 'Why the dot product is
+    divided by the square root of d_k', which reports 1.99 / 7.89 / 22.54)."""
+    fails = []
+    g = _rng(51)
+    for dk in (4, 64, 512):
+        q = g.standard_normal((4000, 1, 1, dk))
+        k = g.standard_normal((4000, 1, 1, dk))
+        raw = orc.scores(q, k, scale=1.0).ravel()
+        scaled = orc.scores(q, k, scale=1.0 / math.sqrt(dk)).ravel()
+        r = raw.std() / math.sqrt(dk)
+        if abs(r - 1.0) > 0.05:
+            fails.append(f"d_k={dk}: std(q.k)/sqrt(d_k) = {r:.3f}")
+        if abs(scaled.std() - 1.0) > 0.05:
+            fails.append(f"d_k={dk}: std(scaled) = {scaled.std():.3f}")
+    return fails
+
+
+def pin_permutation_equivariance(orc):
+    """Without a mask, permuting the query rows permutes the output rows, and
+    permuting the key and value rows together leaves the output unchanged
+    ([ACI] 'The problem attention creates...'; [ZS] 'Telling the positions apart')."""
+    fails = []
+    q, k, v, _ = _random_case(61, Nq=19, Nk=26)
+    g = _rng(62)
+    out = orc.attention(q, k, v, nthreads=2)
+    pq = g.permutation(q.shape[2])
+    _same(fails, "query permutation", orc.attention(q[:, :, pq], k, v, nthreads=2), out[:, :, pq])
+    pk = g.permutation(k.shape[2])
+    _close(fails, "joint key/value permutation",
+           orc.attention(q, k[:, :, pk], v[:, :, pk], nthreads=2), out, 1e-13)
+    return fails
+
+
+def pin_future_tokens(orc):
+    """Changing a future token never changes an earlier output under the causal
+    mask ([AC] 'Pitfalls when reproducing the paper')."""
+    fails = []
+    q, k, v, lens = _random_case(71, Nq=24, Nk=24)
+    lens[:] = 24
+    out = orc.attention(q, k, v, mask_kind=CAUSAL, key_lens=lens, nthreads=2)
+    g = _rng(72)
+    for i0 in (0, 7, 22):
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        for t in (q2, k2, v2):
+            t[:, :, i0 + 1:] = g.standard_normal(t[:, :, i0 + 1:].shape) * 100.0
+        out2 = orc.attention(q2, k2, v2, mask_kind=CAUSAL, key_lens=lens, nthreads=2)
+        _same(fails, f"rows <= {i0} after changing later tokens", out2[:, :, :i0 + 1],
+              out[:, :, :i0 + 1])
+        if np.array_equal(out2[:, :, i0 + 1:], out[:, :, i0 + 1:]):
+            fails.append(f"rows > {i0} did not react to changed tokens")
+    return fails
+
+
+def pin_padding_is_on_keys(orc):
+    """Padding hides keys, not queries ([AC] 'Pitfalls'; [AD] 'Two masks, not one'):
+    the result for a sequence of length L equals attention over its first L keys and
+    values alone; padded query rows are ordinary rows; whatever sits in padded key
+    and value slots (even inf or NaN) never reaches the output."""
+    fails = []
+    for mask in (NONE, CAUSAL):
+        q, k, v, lens = _random_case(81 + mask, B=4, Nq=20, Nk=20)
+        lens[:] = [20, 13, 1, 7]
+        out = orc.attention(q, k, v, mask_kind=mask, key_lens=lens, nthreads=2)
+        for b in range(4):
+            L = int(lens[b])
+            if mask == NONE:
+                ref = orc.attention(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], nthreads=1)
+                _same(fails, f"mask={mask} b={b} truncated keys", out[b:b + 1], ref)
+            else:
+                ref = orc.attention(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L],
+                                    mask_kind=CAUSAL, nthreads=1)
+                _same(fails, f"mask={mask} b={b} truncated rows < L", out[b:b + 1, :, :L], ref)
+                # rows i >= L see exactly the L visible keys, like an unmasked query
+                tail = orc.attention(q[b:b + 1, :, L:], k[b:b + 1, :, :L], v[b:b + 1, :, :L],
+                                     nthreads=1)
+                _same(fails, f"mask={mask} b={b} padded query rows", out[b:b + 1, :, L:], tail)
+        for poison in (np.inf, np.nan, 1e300):
+            k2, v2 = k.copy(), v.copy()
+            for b in range(4):
+                k2[b, :, lens[b]:] = poison
+                v2[b, :, lens[b]:] = -poison
+            out2 = orc.attention(q, k2, v2, mask_kind=mask, key_lens=lens, nthreads=2)
+            _same(fails, f"mask={mask} poison {poison} in padded slots", out2, out)
+    return fails
+
+
+def pin_empty_rows(orc):
+    """A row with no visible key (key length 0) returns 0 -- the reading taken for
+    the NaN case of [AC] 'Pitfalls' -- and has all-zero weights."""
+    fails = []
+    q, k, v, lens = _random_case(91, B=2)
+    lens[:] = [0, 5]
+    out, w = orc.attention(q, k, v, key_lens=lens, return_weights=True, nthreads=1)
+    _same(fails, "empty row output", out[0], np.zeros_like(out[0]))
+    _same(fails, "empty row weights", w[0], np.zeros_like(w[0]))
+    if not np.all(np.abs(out[1]) > 0):
+        fails.append("non-empty rows returned zeros")
+    return fails
+
+
+def pin_projection_uniform_closed_form(orc):
+    """W_Q = W_K = 0 makes every score equal (b_Q . b_K times the scale), so each
+    head averages its visible value rows: out = mean_{j<L}(x_kv_j W_V^T + b_V) W_O^T
+    + b_O, a closed form checked here for cross-attention with padding."""
+    fails = []
+    g = _rng(101)
+    B, Nq, Nk, D, H, dk, dv = 3, 6, 9, 12, 3, 4, 5
+    x_q = g.standard_normal((B, Nq, D))
+    x_kv = g.standard_normal((B, Nk, D))
+    W_Q = np.zeros((H * dk, D))
+    W_K = np.zeros((H * dk, D))
+    W_V = g.standard_normal((H * dv, D))
+    W_O = g.standard_normal((D, H * dv))
+    b_Q, b_K = g.standard_normal(H * dk), g.standard_normal(H * dk)
+    b_V, b_O = g.standard_normal(H * dv), g.standard_normal(D)
+    lens = np.array([9, 4, 1], np.int32)
+    out = orc.mha_proj(x_q, x_kv, W_Q, W_K, W_V, W_O, H=H, b_Q=b_Q, b_K=b_K, b_V=b_V, b_O=b_O,
+                       key_lens=lens, nthreads=2)
+    want = np.zeros_like(out)
+    for b in range(B):
+        mean_v = (x_kv[b, :lens[b]] @ W_V.T + b_V).mean(axis=0)
+        want[b] = (mean_v @ W_O.T + b_O)[None, :]
+    _close(fails, "uniform-attention closed form", out, want, 1e-12)
+    return fails
+
+
+def pin_projection_one_hot_cross(orc):
+    """Cross-attention through the projection path: the decoder side x_q carries a
+    one-hot query in its second feature half, the encoder side x_kv a one-hot key in
+    its first half and a payload in its second half.  W_Q reads x_q's second half,
+    W_K x_kv's first half, W_V x_kv's second half and W_O copies the head output to
+    the first D/2 output features, so out[i] = payload of the key query i points
+    at ([AD] 'Multi-Head Attention (middle) - cross-attention')."""
+    fails = []
+    g = _rng(111)
+    B, Nq, Nk, m = 2, 7, 11, 16
+    D = 2 * m
+    scale = 0.25
+    c = 40.0 / scale
+    x_q = np.zeros((B, Nq, D))
+    x_kv = np.zeros((B, Nk, D))
+    x_kv[:, :, m:] = g.standard_normal((B, Nk, m))
+    lens = np.array([11, 6], np.int32)
+    want = np.zeros((B, Nq, D))
+    for b in range(B):
+        pi = g.permutation(m)[:Nk]
+        x_kv[b, np.arange(Nk), pi] = c
+        for i in range(Nq):
+            t = int(g.integers(0, lens[b]))
+            x_q[b, i, m + pi[t]] = 1.0
+            want[b, i, :m] = x_kv[b, t, m:]
+    first = np.concatenate([np.eye(m), np.zeros((m, m))], axis=1)     # reads features [0, m)
+    second = np.concatenate([np.zeros((m, m)), np.eye(m)], axis=1)    # reads features [m, 2m)
+    W_O = np.concatenate([np.eye(m), np.zeros((m, m))], axis=0)       # [D, m]
+    out = orc.mha_proj(x_q, x_kv, second, first, second, W_O, H=1, key_lens=lens, scale=scale,
+                       nthreads=2)
+    _close(fails, "projected one-hot cross-attention", out, want, 1e-12)
+    return fails
+
+
+def pin_rejects_causal_cross(orc):
+    """The causal mask is defined for self-attention only ([TP] 'Why Masking Is
+    Required'); a causal call with Nq != Nk is rejected."""
+    fails = []
+    q, k, v, _ = _random_case(121, Nq=4, Nk=5)
+    try:
+        orc.attention(q, k, v, mask_kind=CAUSAL, nthreads=1)
+        fails.append("causal with Nq != Nk accepted")
+    except oracle_mod.OracleError:
+        pass
+    return fails
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_worked_example_projection,
+    pin_row_sums_and_zero_weights,
+    pin_zero_query_gives_mean,
+    pin_causal_first_row,
+    pin_one_hot_selection,
+    pin_large_logits,
+    pin_two_key_logistic,
+    pin_sqrt_dk_statistics,
+    pin_permutation_equivariance,
+    pin_future_tokens,
+    pin_padding_is_on_keys,
+    pin_empty_rows,
+    pin_projection_uniform_closed_form,
+    pin_projection_one_hot_cross,
+    pin_rejects_causal_cross,
+]
+
+
+def run_all(orc):
+    """{pin name: failures} for every pin, catching crashes as failures."""
+    res = {}
+    for pin in ALL_PINS:
+        try:
+            res[pin.__name__] = pin(orc)
+        except Exception as exc:  # a broken build may raise instead of returning
+            res[pin.__name__] = [f"raised {type(exc).__name__}: {exc}"]
+    return res

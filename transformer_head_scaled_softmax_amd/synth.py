@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and rounds them to the storage dtype; it
+holds none of the attention arithmetic, so both the GPU path and the fp64 oracle
+can be fed from it.  Inputs are numpy float32 arrays whose values are exactly
+representable in the workload's dtype (bf16 / fp16 / fp32), so the GPU receives
+them bit-exactly and the oracle converts them to fp64 exactly.
+
+Workload shapes follow the pages: d_model 512 with h = 8 and 1024 with h = 16,
+d_k = d_v = 64 ([TP] "Multi-Head Attention"; the model sizes in [AC] "The training
+recipe"), sentences of a few dozen tokens ([AC] "The problem the paper set out to
+fix"), and long contexts where the n^2 term dominates ([TP] "The Trade-Off:
+Quadratic Cost").  No dataset is read: the draws stand in for WMT 2014 batches.
+
+Recipe: ``numpy.random.Generator(PCG64(seed))``; fp32 N(0,1) draws in the order
+(x_q | q), (x_kv | k), (v), W_Q, W_K, W_V, W_O, key_lens; rounding to bf16 is
+round-to-nearest-even; Xavier-uniform weights are U(-a, a) with
+a = sqrt(6 / (fan_in + fan_out)); key lengths are i.i.d. discrete uniform over the
+inclusive range.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str                 # "f32" | "bf16" | "f16"
+    mask: int
+    lens: tuple | None          # inclusive (lo, hi) of key lengths, or None
+    proj: bool                  # with Q/K/V/O projections (d_model = H * d)
+    cross: bool                 # keys/values from a second sequence
+    seed: int
+    description: str
+
+    @property
+    def D(self) -> int:
+        return self.H * self.d
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_encoder_f32", 1, 8, 16, 16, 64, "f32", MASK_NONE, None, False, False, 1,
+                 "tiny encoder self-attention, no mask, fp32 (B=1, n=16, h=8, d=64)"),
+        Workload("base_encoder_proj", 64, 8, 64, 64, 64, "bf16", MASK_NONE, (10, 64), True, False, 2,
+                 "Transformer-base encoder self-attention with projections and key padding "
+                 "(B=64, n=64, d_model=512, h=8, lengths U{10..64})"),
+        Workload("base_decoder_causal", 64, 8, 64, 64, 64, "bf16", MASK_CAUSAL, (10, 64), False, False, 3,
+                 "Transformer-base decoder masked self-attention with key padding "
+                 "(B=64, n=64, h=8, d=64, lengths U{10..64})"),
+        Workload("big_cross_proj", 32, 16, 64, 80, 64, "bf16", MASK_NONE, (20, 80), True, True, 4,
+                 "Transformer-big encoder-decoder cross-attention with projections "
+                 "(B=32, Nq=64, Nk=80, d_model=1024, h=16, source lengths U{20..80})"),
+        Workload("long_causal", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 5,
+                 "long-context causal self-attention (B=2, n=8192, h=16, d=64)"),
+    ]
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f16":
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def generator(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def normal(g: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    return round_to(g.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def xavier_uniform(g: np.random.Generator, fan_out: int, fan_in: int, dtype: str) -> np.ndarray:
+    """[fan_out, fan_in] weight (the nn.Linear layout), U(-a, a)."""
+    a = math.sqrt(6.0 / (fan_in + fan_out))
+    return round_to(g.uniform(-a, a, size=(fan_out, fan_in)).astype(np.float32), dtype)
+
+
+def key_lengths(g: np.random.Generator, B: int, lo: int, hi: int) -> np.ndarray:
+    return g.integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def core_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None):
+    """q [B,H,Nq,dk], k [B,H,Nk,dk], v [B,H,Nk,dv] ~ N(0,1); key_lens drawn from
+    ``lens`` = (lo, hi) if given."""
+    g = generator(seed)
+    q = normal(g, (B, H, Nq, dk), dtype)
+    k = normal(g, (B, H, Nk, dk), dtype)
+    v = normal(g, (B, H, Nk, dv), dtype)
+    key_lens = key_lengths(g, B, *lens) if lens is not None else None
+    return {"q": q, "k": k, "v": v, "key_lens": key_lens}
+
+
+def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None):
+    """x_q [B,Nq,D] (and x_kv [B,Nk,D] when ``cross``) ~ N(0,1); Xavier-uniform
+    W_Q, W_K [H*dk, D], W_V [H*dv, D], W_O [D, H*dv]; key_lens from ``lens``."""
+    g = generator(seed)
+    x_q = normal(g, (B, Nq, D), dtype)
+    x_kv = normal(g, (B, Nk, D), dtype) if cross else None
+    W_Q = xavier_uniform(g, H * dk, D, dtype)
+    W_K = xavier_uniform(g, H * dk, D, dtype)
+    W_V = xavier_uniform(g, H * dv, D, dtype)
+    W_O = xavier_uniform(g, D, H * dv, dtype)
+    key_lens = key_lengths(g, B, *lens) if lens is not None else None
+    return {"x_q": x_q, "x_kv": x_kv, "W_Q": W_Q, "W_K": W_K, "W_V": W_V, "W_O": W_O,
+            "key_lens": key_lens}
+
+
+def workload_inputs(w: Workload, seed: int | None = None):
+    seed = w.seed if seed is None else seed
+    if w.proj:
+        return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens)
+    return core_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
+
+
+def sample_rows(B: int, H: int, N: int, seed: int, n_random: int = 64):
+    """(b, h, i) triples for checking long sequences row by row: the tile edges
+    {0, 1, 63, 64, 65, 127, 128, N/2 - 1, N/2, N - 2, N - 1} of every (b, h) plus
+    ``n_random`` seeded random rows per (b, h)."""
+    g = generator(seed)
+    fixed = sorted({i for i in (0, 1, 63, 64, 65, 127, 128, N // 2 - 1, N // 2, N - 2, N - 1)
+                    if 0 <= i < N})
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            extra = g.integers(0, N, size=n_random)
+            for i in sorted(set(fixed) | set(int(x) for x in extra)):
+                rows.append((b, h, i))
+    return np.array(rows, dtype=np.int32)
