@@ -1,0 +1,139 @@
+/*
+ * mha.h -- C ABI of libmha, multi-head scaled dot-product attention (forward)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Attention Is All You Need" as explained on the pages cited
+ * below; trishampatil.com = [TP], aicassindra.com = [AC], alexdo.xyz = [AD],
+ * zeroshotmind.com = [ZS]):
+ *
+ *   out_i = sum_j softmax_j(scale * q_i . k_j over the visible keys j) * v_j
+ *
+ * per batch entry b and head h ([TP] "Scaled Dot-Product Attention: Step by
+ * Step"; [ZS] "Scaled dot-product attention").  A key j is visible to query i
+ * unless it is padding (j >= key_lens[b], [AD] "Two masks, not one") or, under
+ * the causal mask, in the future (j > i, [TP] "Why Masking Is Required").
+ * Masked keys get weight exactly 0.  The three roles of [ZS] "Where attention
+ * is used three ways" map onto the arguments: encoder self-attention
+ * (MHA_MASK_NONE, keys = queries' sequence), decoder masked self-attention
+ * (MHA_MASK_CAUSAL) and encoder-decoder cross-attention (MHA_MASK_NONE,
+ * Nq != Nk, keys/values from the encoder; [AD] "Multi-Head Attention (middle) -
+ * cross-attention").
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device memory owned by the caller unless stated otherwise;
+ *     the library never allocates, frees or keeps them.
+ *   - All tensors are dense row-major with the stated shapes; element type is
+ *     given by `dtype` (MHA_F32, MHA_BF16, MHA_F16), the same for every
+ *     floating-point tensor of a call.  bf16/f16 math accumulates in fp32;
+ *     outputs are rounded to nearest-even into the input type.
+ *   - `key_lens` is a device int32[B] or NULL (no padding).  Values are clamped
+ *     to [0, Nk] on the device; the host never reads them.  A query with no
+ *     visible key (key length 0) gets an output row of zeros.
+ *   - `scale` is the factor applied to q.k; pass 1/sqrt(d_k) for the pages'
+ *     scaling ([TP] "Why the sqrt(d_k) Scaling Exists").  It must be finite.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Argument errors are detected on the host before any HIP call
+ *     and return a negative status with nothing launched; launch failures
+ *     return MHA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  mha_last_error() gives a message for the last failure
+ *     on the calling thread.
+ *   - Entry points keep no state between calls and may be called from several
+ *     threads at once.
+ */
+#ifndef MHA_H_
+#define MHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* mask_kind */
+#define MHA_MASK_NONE 0   /* every key below key_lens[b] is visible */
+#define MHA_MASK_CAUSAL 1 /* additionally j <= i; requires Nq == Nk */
+
+/* dtype */
+#define MHA_F32 0
+#define MHA_BF16 1
+#define MHA_F16 2
+
+/* status codes */
+#define MHA_OK 0
+#define MHA_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad enum, ... */
+#define MHA_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for */
+#define MHA_ERR_WORKSPACE (-3)   /* workspace missing, too small or misaligned */
+#define MHA_ERR_HIP (-4)         /* the HIP runtime refused a launch */
+
+/*
+ * mha_forward -- attention on per-head tensors ([TP] "Scaled Dot-Product
+ * Attention: Step by Step", applied per head as in [TP] "Multi-Head Attention").
+ *
+ *   q   [B, H, Nq, d_k]     k [B, H, Nk, d_k]     v [B, H, Nk, d_v]
+ *   out [B, H, Nq, d_v]     written; may not overlap the inputs
+ *
+ * Sizes: B, H, Nq, Nk >= 0 (zero-sized problems return MHA_OK; with Nk == 0
+ * every output row is zero); d_k, d_v >= 1.  Supported: MHA_F32 with
+ * d_k, d_v <= 128; MHA_BF16 and MHA_F16 with d_k == d_v == 64.  bf16/f16
+ * tensors must be 16-byte aligned.  Returns MHA_OK or a negative status.
+ */
+int mha_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                int dtype, void* stream);
+
+/*
+ * mha_proj_workspace_bytes -- device workspace mha_proj_forward needs for these
+ * sizes (the projected Q, K, V and the concatenated head outputs, each 256-byte
+ * aligned).  Returns 0 for invalid sizes.
+ */
+size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype);
+
+/*
+ * mha_proj_forward -- multi-head attention with its projections ([TP] "Query /
+ * Key / Value Roles", "Multi-Head Attention", "The Output Projection W^O"; the
+ * layer of [AC] "A faithful layer in code"):
+ *
+ *   Q = x_q W_Q^T + b_Q,  K = x_kv W_K^T + b_K,  V = x_kv W_V^T + b_V
+ *   head h attends with feature columns [h*d, (h+1)*d) of Q, K and V
+ *   out = Concat(head_0 .. head_{H-1}) W_O^T + b_O
+ *
+ *   x_q  [B, Nq, D]      decoder/query side
+ *   x_kv [B, Nk, D]      encoder/key-value side, or NULL for self-attention
+ *                        (keys and values from x_q; then Nk must equal Nq)
+ *   W_Q, W_K [H*d_k, D]  W_V [H*d_v, D]  W_O [D, H*d_v]
+ *                        -- the [out_features, in_features] layout of the
+ *                        nn.Linear layers in [AC]'s listing, i.e. the transpose
+ *                        of the X*W matrices in [TP]'s formulas
+ *   b_Q, b_K [H*d_k], b_V [H*d_v], b_O [D]   nullable (no bias)
+ *   out  [B, Nq, D]      written
+ *   workspace            device memory of at least
+ *                        mha_proj_workspace_bytes(...) bytes, 256-byte aligned,
+ *                        owned by the caller; its contents are scratch.
+ *
+ * Supported: MHA_BF16 and MHA_F16 with d_k == d_v == 64, D a multiple of 8,
+ * all tensors 16-byte aligned.  The projected Q, K, V and the head outputs are
+ * rounded to the input type in the workspace.  Returns MHA_OK or a negative
+ * status.
+ */
+int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                     const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
+                     const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
+                     int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* mha_status_string(int status);
+
+/* Message for the last failed call on the calling thread ("" if none);
+ * valid until that thread's next call into the library. */
+const char* mha_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int mha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H_ */

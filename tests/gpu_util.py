@@ -1,0 +1,60 @@
+"""Helpers for the GPU parity tests: moving seeded inputs to the device and
+measuring the error against the oracle with the tolerances the tests use.
+
+Tolerances (stated for the whole suite):
+  fp32 inputs: max |out - ref| / max |ref| <= 1e-5
+  bf16 / f16 inputs (fp32 accumulation, unit-variance V): max |out - ref| <= 2e-2
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOL_F32_REL = 1e-5
+TOL_LOWP_ABS = 2e-2
+
+
+def torch_dtype(name: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[name]
+
+
+def to_dev(arr, dtype: str):
+    """numpy array (values exactly representable in ``dtype``) -> device tensor."""
+    import torch
+    if arr is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device="cuda", dtype=torch_dtype(dtype))
+
+
+def lens_dev(lens):
+    import torch
+    if lens is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to("cuda")
+
+
+def to_host(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def max_err(got: np.ndarray, ref: np.ndarray) -> float:
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    return float(np.max(np.abs(got - ref)))
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> float:
+    """Check ``got`` against the oracle ``ref`` at the suite's tolerance; returns the
+    error measure used."""
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    err = max_err(got, ref)
+    if dtype == "f32":
+        scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+        rel = err / scale if scale > 0 else err
+        assert rel <= TOL_F32_REL, f"{what}: relative error {rel:.3g} > {TOL_F32_REL}"
+        return rel
+    assert err <= TOL_LOWP_ABS, f"{what}: abs error {err:.3g} > {TOL_LOWP_ABS}"
+    return err

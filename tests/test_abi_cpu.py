@@ -1,0 +1,192 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/mha.h
+declares, and rejects bad arguments on the host before any HIP call.
+
+Pointers here are fake, aligned addresses that are never dereferenced: every call
+below fails validation first.  Nothing in this file launches a kernel.
+"""
+import ctypes
+import pathlib
+import re
+import subprocess
+import sys
+
+import pytest
+
+from transformer_head_scaled_softmax_amd import _binding as mb
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "mha.h"
+P = 0x100000  # fake, 256-byte aligned device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mb.load()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(mha_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(mb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(mb.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    for code in (mb.OK, mb.ERR_INVALID_ARG, mb.ERR_UNSUPPORTED, mb.ERR_WORKSPACE, mb.ERR_HIP):
+        assert lib.mha_status_string(code).decode()
+    assert lib.mha_status_string(12345).decode() == "unknown status"
+    assert lib.mha_version() >= 100
+
+
+def fwd(lib, q=P, k=P, v=P, out=P, B=2, H=3, Nq=5, Nk=5, dk=64, dv=64, mask=0, lens=None,
+        scale=0.125, dtype=mb.BF16):
+    return lib.mha_forward(q, k, v, out, B, H, Nq, Nk, dk, dv, mask, lens, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), mb.ERR_INVALID_ARG),
+    (dict(H=-2), mb.ERR_INVALID_ARG),
+    (dict(Nq=-1), mb.ERR_INVALID_ARG),
+    (dict(Nk=-1), mb.ERR_INVALID_ARG),
+    (dict(dk=0), mb.ERR_INVALID_ARG),
+    (dict(dv=-4), mb.ERR_INVALID_ARG),
+    (dict(mask=2), mb.ERR_INVALID_ARG),
+    (dict(mask=1, Nq=4, Nk=5), mb.ERR_INVALID_ARG),
+    (dict(dtype=3), mb.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mb.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), mb.ERR_INVALID_ARG),
+    (dict(dk=32, dv=32), mb.ERR_UNSUPPORTED),
+    (dict(dk=64, dv=128), mb.ERR_UNSUPPORTED),
+    (dict(dtype=mb.F16, dk=128, dv=128), mb.ERR_UNSUPPORTED),
+    (dict(dtype=mb.F32, dk=129), mb.ERR_UNSUPPORTED),
+    (dict(q=None), mb.ERR_INVALID_ARG),
+    (dict(out=None), mb.ERR_INVALID_ARG),
+    (dict(k=None), mb.ERR_INVALID_ARG),
+    (dict(v=None), mb.ERR_INVALID_ARG),
+    (dict(q=P + 8), mb.ERR_INVALID_ARG),
+    (dict(out=P + 2), mb.ERR_INVALID_ARG),
+    (dict(dtype=mb.F32, q=P + 2), mb.ERR_INVALID_ARG),
+    (dict(lens=P + 2), mb.ERR_INVALID_ARG),
+])
+def test_forward_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0), dict(B=0, q=None, out=None)])
+def test_forward_empty_problems_are_ok_without_launch(lib, kw):
+    assert fwd(lib, **kw) == mb.OK
+    assert lib.mha_last_error().decode() == ""
+
+
+def test_workspace_bytes(lib):
+    # Q, K, V, O regions of B*N*H*d bf16 values, each rounded up to 256 bytes.
+    assert lib.mha_proj_workspace_bytes(64, 64, 64, 512, 8, 64, 64, mb.BF16) == 4 * 64 * 64 * 512 * 2
+    q = 32 * 64 * 1024 * 2
+    kv = 32 * 80 * 1024 * 2
+    assert lib.mha_proj_workspace_bytes(32, 64, 80, 1024, 16, 64, 64, mb.BF16) == 2 * q + 2 * kv
+    # 3*64*2 = 384 -> 512; 5*64*2 = 640 -> 768 (twice); 384 -> 512
+    assert lib.mha_proj_workspace_bytes(1, 3, 5, 8, 1, 64, 64, mb.BF16) == 512 + 768 + 768 + 512
+    assert lib.mha_proj_workspace_bytes(-1, 3, 5, 8, 1, 64, 64, mb.BF16) == 0
+    assert lib.mha_proj_workspace_bytes(1, 3, 5, 8, 0, 64, 64, mb.BF16) == 0
+    assert lib.mha_proj_workspace_bytes(1, 3, 5, 8, 1, 64, 64, 9) == 0
+
+
+def proj(lib, x_q=P, x_kv=P, W_Q=P, W_K=P, W_V=P, W_O=P, out=P, B=2, Nq=4, Nk=6, D=64, H=1,
+         dk=64, dv=64, mask=0, lens=None, scale=0.125, dtype=mb.BF16, ws=P, ws_bytes=1 << 30,
+         biases=(None, None, None, None)):
+    return lib.mha_proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, *biases, out, B, Nq, Nk, D, H, dk,
+                                dv, mask, lens, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), mb.ERR_INVALID_ARG),
+    (dict(D=0), mb.ERR_INVALID_ARG),
+    (dict(H=0), mb.ERR_INVALID_ARG),
+    (dict(x_kv=None), mb.ERR_INVALID_ARG),              # self-attention needs Nk == Nq
+    (dict(mask=1), mb.ERR_INVALID_ARG),                 # causal cross-attention
+    (dict(mask=7), mb.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mb.ERR_INVALID_ARG),
+    (dict(dtype=mb.F32), mb.ERR_UNSUPPORTED),
+    (dict(dk=32), mb.ERR_UNSUPPORTED),
+    (dict(D=60), mb.ERR_UNSUPPORTED),
+    (dict(x_q=None), mb.ERR_INVALID_ARG),
+    (dict(W_O=None), mb.ERR_INVALID_ARG),
+    (dict(out=None), mb.ERR_INVALID_ARG),
+    (dict(W_K=P + 8), mb.ERR_INVALID_ARG),
+    (dict(biases=(P + 1, None, None, None)), mb.ERR_INVALID_ARG),
+    (dict(ws=None), mb.ERR_WORKSPACE),
+    (dict(ws=P + 16), mb.ERR_WORKSPACE),
+    (dict(ws_bytes=1000), mb.ERR_WORKSPACE),
+])
+def test_proj_rejects(lib, kw, status):
+    assert proj(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+def test_proj_workspace_exact_size_passes_validation_check(lib):
+    need = lib.mha_proj_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
+    assert proj(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+    assert "needed" in lib.mha_last_error().decode()
+
+
+def test_proj_empty_is_ok(lib):
+    assert proj(lib, B=0) == mb.OK
+    assert proj(lib, Nq=0, x_kv=P) == mb.OK
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+    assert fwd(lib, B=-1) == mb.ERR_INVALID_ARG
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.mha_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert lib.mha_last_error().decode()
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+hip = ctypes.CDLL("libamdhip64.so")
+n = ctypes.c_int(0)
+hip.hipGetDeviceCount(ctypes.byref(n))
+if n.value != 0:
+    print("SKIP device present"); sys.exit(0)
+sys.path.insert(0, sys.argv[1])
+from transformer_head_scaled_softmax_amd import _binding as mb
+lib = mb.load()
+P = 0x100000
+st = lib.mha_forward(P, P, P, P, 1, 1, 4, 4, 64, 64, 0, None, 0.125, mb.BF16, None)
+print("STATUS", st, lib.mha_last_error().decode())
+"""
+
+
+def test_valid_call_without_a_device_reports_hip_error():
+    """With no GPU, a call that passes validation must return MHA_ERR_HIP rather than
+    abort.  Runs in a child process that first confirms no device is visible (so no
+    kernel can be launched with the fake pointers)."""
+    res = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT, str(ROOT)], capture_output=True,
+                         text=True, timeout=120, env={"HIP_VISIBLE_DEVICES": "-1",
+                                                      "PATH": "/usr/bin:/bin",
+                                                      "LD_LIBRARY_PATH": "/opt/rocm/lib"})
+    if "SKIP" in res.stdout:
+        pytest.skip("a device is visible")
+    assert res.returncode == 0, res.stderr
+    assert f"STATUS {mb.ERR_HIP}" in res.stdout, res.stdout + res.stderr

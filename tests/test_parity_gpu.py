@@ -1,0 +1,294 @@
+"""GPU parity: libmha's kernels against the fp64 oracle on the same seeded inputs.
+
+Every call goes through the C ABI (via the ctypes binding).  Element-by-element
+comparisons use the suite tolerances of gpu_util (fp32: 1e-5 of the output
+scale; bf16/f16: 2e-2 absolute); masking properties are checked bit-exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, lens_dev, to_dev, to_host
+from transformer_head_scaled_softmax_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mha = pytest.importorskip("transformer_head_scaled_softmax_amd")
+
+CAUSAL, NONE = mha.MASK_CAUSAL, mha.MASK_NONE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mha.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_core(inp, dtype, mask, scale=None, lens_override="keep"):
+    q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
+    lens = inp["key_lens"] if lens_override == "keep" else lens_override
+    out = mha.forward(q, k, v, mask_kind=mask, key_lens=lens_dev(lens), scale=scale)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def ref_core(inp, mask, scale=None, lens_override="keep"):
+    lens = inp["key_lens"] if lens_override == "keep" else lens_override
+    return oracle.attention(inp["q"], inp["k"], inp["v"], mask_kind=mask, key_lens=lens, scale=scale)
+
+
+def check_core(B, H, Nq, Nk, d, dtype, mask, lens, seed, dv=None, scale=None):
+    dv = d if dv is None else dv
+    inp = synth.core_inputs(B, H, Nq, Nk, d, dv, dtype, seed)
+    if lens is not None:
+        inp["key_lens"] = np.asarray(lens, np.int32)
+    got = run_core(inp, dtype, mask, scale)
+    ref = ref_core(inp, mask, scale)
+    return assert_close(got, ref, dtype, f"B{B} H{H} Nq{Nq} Nk{Nk} d{d}/{dv} {dtype} mask{mask} lens{lens}")
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size.
+
+def test_tiny_encoder_f32():
+    w = synth.WORKLOADS["tiny_encoder_f32"]
+    inp = synth.workload_inputs(w)
+    assert_close(run_core(inp, "f32", w.mask), ref_core(inp, w.mask), "f32", w.name)
+
+
+def test_base_decoder_causal_full():
+    w = synth.WORKLOADS["base_decoder_causal"]
+    inp = synth.workload_inputs(w)
+    assert_close(run_core(inp, w.dtype, w.mask), ref_core(inp, w.mask), w.dtype, w.name)
+
+
+def _proj_dev(inp, dtype):
+    return {n: to_dev(inp[n], dtype) for n in ("x_q", "x_kv", "W_Q", "W_K", "W_V", "W_O")}
+
+
+def run_proj(inp, H, dtype, mask, biases=None):
+    d = _proj_dev(inp, dtype)
+    b = {n: to_dev(x, dtype) for n, x in (biases or {}).items()}
+    out = mha.proj_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=H,
+                           mask_kind=mask, key_lens=lens_dev(inp["key_lens"]), **b)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def ref_proj(inp, H, mask, biases=None):
+    return oracle.mha_proj(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
+                           H=H, mask_kind=mask, key_lens=inp["key_lens"], **(biases or {}))
+
+
+def test_base_encoder_proj_full():
+    """The benchmark's workload, in the launch configuration it times."""
+    w = synth.WORKLOADS["base_encoder_proj"]
+    inp = synth.workload_inputs(w)
+    assert_close(run_proj(inp, w.H, w.dtype, w.mask), ref_proj(inp, w.H, w.mask), w.dtype, w.name)
+
+
+def test_big_cross_proj_full():
+    w = synth.WORKLOADS["big_cross_proj"]
+    inp = synth.workload_inputs(w)
+    assert_close(run_proj(inp, w.H, w.dtype, w.mask), ref_proj(inp, w.H, w.mask), w.dtype, w.name)
+
+
+def test_long_causal_sampled_rows():
+    """B=2, n=8192, h=16 causal: GPU output rows compared with the oracle one by one
+    on tile-edge rows plus seeded random rows of every (b, h)."""
+    w = synth.WORKLOADS["long_causal"]
+    inp = synth.workload_inputs(w)
+    got = run_core(inp, w.dtype, w.mask)
+    rows = synth.sample_rows(w.B, w.H, w.Nq, seed=55)
+    ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, mask_kind=w.mask)
+    assert_close(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref, w.dtype, w.name)
+
+
+# ---------------------------------------------------------------------------
+# Shapes: tile edges, ragged tails, cross-attention, padding.
+
+EDGE_N = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 80, 127, 128, 129, 200, 257]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("n", EDGE_N)
+def test_causal_square_edges(dtype, n):
+    g = synth.generator(1000 + n)
+    lens = [n, int(g.integers(0, n + 1)), max(1, n // 3)]
+    check_core(3, 2, n, n, 64, dtype, CAUSAL, lens, seed=n)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("nq,nk", [(1, 1), (1, 129), (7, 64), (64, 80), (65, 63), (130, 17),
+                                   (33, 300), (200, 129), (128, 1)])
+def test_cross_shapes(dtype, nq, nk):
+    g = synth.generator(2000 + nq * 7 + nk)
+    lens = [nk, int(g.integers(1, nk + 1)), 0]
+    check_core(3, 2, nq, nk, 64, dtype, NONE, lens, seed=nq * 1000 + nk)
+
+
+@pytest.mark.parametrize("nq,nk,dk,dv,mask", [
+    (1, 1, 1, 1, NONE), (5, 9, 7, 3, NONE), (16, 16, 64, 64, CAUSAL), (65, 65, 100, 128, CAUSAL),
+    (70, 130, 128, 64, NONE), (3, 200, 32, 96, NONE), (129, 129, 64, 64, CAUSAL)])
+def test_f32_shapes(nq, nk, dk, dv, mask):
+    g = synth.generator(3000 + nq + nk)
+    lens = [nk, int(g.integers(0, nk + 1))]
+    check_core(2, 3, nq, nk, dk, "f32", mask, lens, seed=nq + 17 * nk, dv=dv)
+
+
+def test_no_key_lens_and_single_head():
+    check_core(1, 1, 100, 100, 64, "bf16", CAUSAL, None, seed=5)
+    check_core(1, 1, 40, 90, 64, "bf16", NONE, None, seed=6)
+
+
+def test_key_lens_out_of_range_are_clamped():
+    inp = synth.core_inputs(3, 2, 20, 20, 64, 64, "bf16", seed=7)
+    inp["key_lens"] = np.array([-5, 1000, 7], np.int32)
+    got = run_core(inp, "bf16", NONE)
+    assert np.all(got[0] == 0.0)
+    assert_close(got, ref_core(inp, NONE), "bf16", "clamped lengths")
+
+
+def test_scale_variants():
+    for scale in (1.0, 0.0, -0.125, 0.37):
+        inp = synth.core_inputs(2, 2, 70, 70, 64, 64, "bf16", seed=8)
+        inp["key_lens"] = np.array([70, 33], np.int32)
+        assert_close(run_core(inp, "bf16", CAUSAL, scale), ref_core(inp, CAUSAL, scale), "bf16",
+                     f"scale {scale}")
+
+
+def test_empty_key_set_gives_zeros():
+    inp = synth.core_inputs(2, 2, 10, 0, 64, 64, "bf16", seed=9)
+    assert np.all(run_core(inp, "bf16", NONE) == 0.0)
+    inp = synth.core_inputs(2, 2, 10, 0, 64, 64, "f32", seed=9)
+    assert np.all(run_core(inp, "f32", NONE) == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Masking is bit-exact.
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,mask", [(64, NONE), (64, CAUSAL), (300, NONE), (300, CAUSAL)])
+def test_padded_slots_never_reach_the_output(dtype, n, mask):
+    """Whatever sits in padded key/value rows j >= key_lens[b] -- huge finite values
+    or NaN -- leaves every output bit unchanged."""
+    inp = synth.core_inputs(3, 2, n, n, 64, 64, dtype, seed=10 + n)
+    inp["key_lens"] = np.array([n, n // 2 + 3, 1], np.int32)
+    clean = run_core(inp, dtype, mask)
+    big = 3.0e38
+    for poison in (big, float("nan")):
+        k, v = inp["k"].copy(), inp["v"].copy()
+        for b, L in enumerate(inp["key_lens"]):
+            k[b, :, L:] = poison
+            v[b, :, L:] = -poison
+        got = run_core(dict(inp, k=k, v=v), dtype, mask)
+        assert np.array_equal(got, clean), f"poison {poison} changed the output"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_future_tokens_never_change_earlier_outputs(dtype):
+    n = 300
+    inp = synth.core_inputs(2, 2, n, n, 64, 64, dtype, seed=11)
+    inp["key_lens"] = None
+    base = run_core(inp, dtype, CAUSAL)
+    g = synth.generator(12)
+    for i0 in (0, 31, 63, 64, 130, 298):
+        pert = {n_: inp[n_].copy() for n_ in ("q", "k", "v")}
+        for t in pert.values():
+            t[:, :, i0 + 1:] = synth.round_to(g.standard_normal(t[:, :, i0 + 1:].shape) * 30.0, dtype)
+        got = run_core(dict(inp, **pert), dtype, CAUSAL)
+        assert np.array_equal(got[:, :, :i0 + 1], base[:, :, :i0 + 1]), f"rows <= {i0} changed"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_causal_first_row_is_first_value_row(dtype):
+    inp = synth.core_inputs(2, 3, 150, 150, 64, 64, dtype, seed=13)
+    inp["key_lens"] = np.array([150, 1], np.int32)
+    got = run_core(inp, dtype, CAUSAL)
+    assert np.array_equal(got[:, :, 0], inp["v"][:, :, 0].astype(np.float64))
+    # with one visible key every row of the second sequence is V row 0
+    assert np.array_equal(got[1], np.broadcast_to(inp["v"][1, :, :1], got[1].shape).astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_queries_average_the_visible_values(dtype):
+    n = 130
+    inp = synth.core_inputs(2, 2, n, n, 64, 64, dtype, seed=14)
+    inp["q"][:] = 0.0
+    inp["key_lens"] = np.array([n, 45], np.int32)
+    got = run_core(inp, dtype, CAUSAL)
+    want = np.zeros_like(got)
+    for b in range(2):
+        for i in range(n):
+            m = min(int(inp["key_lens"][b]), i + 1)
+            want[b, :, i] = inp["v"][b, :, :m].astype(np.float64).mean(axis=1)
+    tol = 1e-6 if dtype == "f32" else 8e-3  # bf16: rounding of the mean only
+    assert np.max(np.abs(got - want)) <= tol
+
+
+def test_deterministic():
+    inp = synth.core_inputs(2, 4, 500, 500, 64, 64, "bf16", seed=15)
+    a = run_core(inp, "bf16", CAUSAL)
+    b = run_core(inp, "bf16", CAUSAL)
+    assert np.array_equal(a, b)
+
+
+def test_worked_example_on_the_gpu():
+    """The pages' 3-token example (aicomputerinstitute.com, 'Worked example: attention
+    weights and outputs by hand') through the GPU kernels: features zero-padded from
+    2 to 64 leave every dot product unchanged, scale = 1/sqrt(2)."""
+    import json
+    import pathlib
+    gold = json.loads((pathlib.Path(__file__).parent / "golden" / "worked_example.json").read_text())
+    for case in gold["cases"]:
+        x = np.zeros((1, 1, 3, 64), np.float32)
+        x[0, 0, :, :2] = np.array(case["X"], np.float32)
+        want = np.array([case["outputs"][t] for t in gold["tokens"] if t in case["outputs"]])
+        idx = [i for i, t in enumerate(gold["tokens"]) if t in case["outputs"]]
+        for dtype, tol in (("f32", 1e-6), ("bf16", 4e-3)):
+            inp = {"q": x, "k": x, "v": x, "key_lens": None}
+            got = run_core(inp, dtype, NONE, scale=case["scale"])
+            assert np.max(np.abs(got[0, 0, idx, :2] - want)) <= tol, (case["name"], dtype)
+
+
+# ---------------------------------------------------------------------------
+# Projection path.
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,Nq,Nk,D,H,cross,mask", [
+    (2, 5, 5, 64, 1, False, CAUSAL), (3, 17, 33, 128, 2, True, NONE), (2, 70, 70, 256, 4, False, NONE),
+    (1, 130, 130, 192, 3, False, CAUSAL), (4, 64, 80, 1024, 16, True, NONE), (2, 9, 200, 200, 2, True, NONE)])
+def test_proj_shapes_with_biases(dtype, B, Nq, Nk, D, H, cross, mask):
+    inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed=B * 100 + Nq + D, cross=cross)
+    g = synth.generator(D + Nq)
+    inp["key_lens"] = g.integers(1, Nk + 1, size=B).astype(np.int32)
+    biases = {n: synth.normal(g, (size,), dtype) * np.float32(0.5)
+              for n, size in (("b_Q", H * 64), ("b_K", H * 64), ("b_V", H * 64), ("b_O", D))}
+    biases = {n: synth.round_to(x, dtype) for n, x in biases.items()}
+    got = run_proj(inp, H, dtype, mask, biases)
+    ref = ref_proj(inp, H, mask, biases)
+    assert_close(got, ref, dtype, f"proj B{B} Nq{Nq} Nk{Nk} D{D} H{H}")
+
+
+def test_proj_worked_example_identity():
+    """H = 1 with identity projections reproduces the printed example outputs."""
+    import json
+    import pathlib
+    gold = json.loads((pathlib.Path(__file__).parent / "golden" / "worked_example.json").read_text())
+    case = gold["cases"][0]
+    D = 64
+    x = np.zeros((1, 3, D), np.float32)
+    x[0, :, :2] = np.array(case["X"], np.float32)
+    eye = np.eye(D, dtype=np.float32)
+    inp = {"x_q": x, "x_kv": None, "W_Q": eye, "W_K": eye, "W_V": eye, "W_O": eye, "key_lens": None}
+    d = _proj_dev(inp, "bf16")
+    out = mha.proj_forward(d["x_q"], None, d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=1,
+                           scale=case["scale"])
+    got = to_host(out)[0, :, :2]
+    want = np.array([case["outputs"][t] for t in gold["tokens"]])
+    assert np.max(np.abs(got - want)) <= 4e-3

@@ -1,1 +1,110 @@
-"""MI355X-native multi-head scaled dot-product attention (forward)."""
+"""MI355X-native multi-head scaled dot-product attention (forward).
+
+Thin PyTorch-facing wrappers over libmha's C ABI (include/mha.h).  PyTorch only
+provides device memory and the current HIP stream; the computation is the
+library's HIP kernels.  Functions raise ``MhaError`` on a non-zero status and
+``RuntimeError`` if the library is not built.
+
+    forward(q, k, v, mask_kind=MASK_NONE, key_lens=None, scale=None)
+        q [B,H,Nq,d_k], k [B,H,Nk,d_k], v [B,H,Nk,d_v] -> out [B,H,Nq,d_v]
+    proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H, ...)
+        x_q [B,Nq,D], x_kv [B,Nk,D] or None -> out [B,Nq,D]
+"""
+from __future__ import annotations
+
+import math
+
+from ._binding import (BF16, EXPORTS, F16, F32, MASK_CAUSAL, MASK_NONE, MhaError, check,
+                       load)
+
+__all__ = ["forward", "proj_forward", "proj_workspace_bytes", "MASK_NONE", "MASK_CAUSAL",
+           "MhaError", "load", "EXPORTS"]
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _lens_ptr(key_lens, B):
+    import torch
+    if key_lens is None:
+        return None
+    if key_lens.dtype != torch.int32 or key_lens.shape != (B,):
+        raise ValueError(f"key_lens must be an int32 tensor of shape ({B},)")
+    return _dev_ptr(key_lens, "key_lens")
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def forward(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None,
+            out=None, stream=None):
+    """Attention per head; see mha_forward in include/mha.h."""
+    import torch
+    B, H, Nq, dk = q.shape
+    Nk, dv = k.shape[2], v.shape[3]
+    if k.shape != (B, H, Nk, dk) or v.shape != (B, H, Nk, dv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=q.device)
+    lib = load()
+    st = lib.mha_forward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                         B, H, Nq, Nk, dk, dv, int(mask_kind), _lens_ptr(key_lens, B), float(scale),
+                         _dtype_code(q), _stream(stream))
+    check(lib, st)
+    return out
+
+
+def proj_workspace_bytes(B, Nq, Nk, D, H, d_k, d_v, dtype_code: int = BF16) -> int:
+    return int(load().mha_proj_workspace_bytes(B, Nq, Nk, D, H, d_k, d_v, dtype_code))
+
+
+def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None, b_O=None,
+                 mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None, out=None,
+                 workspace=None, stream=None):
+    """Multi-head attention with projections; see mha_proj_forward in include/mha.h.
+
+    Weights are [out_features, in_features] (nn.Linear layout)."""
+    import torch
+    B, Nq, D = x_q.shape
+    Nk = Nq if x_kv is None else x_kv.shape[1]
+    dk = W_Q.shape[0] // H
+    dv = W_V.shape[0] // H
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    code = _dtype_code(x_q)
+    if out is None:
+        out = torch.empty((B, Nq, D), dtype=x_q.dtype, device=x_q.device)
+    lib = load()
+    need = int(lib.mha_proj_workspace_bytes(B, Nq, Nk, D, H, dk, dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
+    ptrs = [_dev_ptr(t, n) for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (W_Q, "W_Q"), (W_K, "W_K"),
+                                        (W_V, "W_V"), (W_O, "W_O"), (b_Q, "b_Q"), (b_K, "b_K"),
+                                        (b_V, "b_V"), (b_O, "b_O"), (out, "out"))]
+    st = lib.mha_proj_forward(*ptrs, B, Nq, Nk, D, H, dk, dv, int(mask_kind),
+                              _lens_ptr(key_lens, B), float(scale), code,
+                              _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+    check(lib, st)
+    return out

@@ -1,0 +1,69 @@
+"""ctypes binding of libmha.so, the C ABI declared in include/mha.h.
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library has not been built, loading it raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = PKG / "libmha.so"
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+F32, BF16, F16 = 0, 1, 2
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE = -3
+ERR_HIP = -4
+
+# Every symbol include/mha.h declares.
+EXPORTS = ("mha_forward", "mha_proj_workspace_bytes", "mha_proj_forward", "mha_status_string",
+           "mha_last_error", "mha_version")
+
+
+class MhaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
+    """Load libmha.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = pathlib.Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is not built; run `python -m transformer_head_scaled_softmax_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.mha_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, f, i, vp]
+    lib.mha_forward.restype = i
+    lib.mha_proj_workspace_bytes.argtypes = [i] * 8
+    lib.mha_proj_workspace_bytes.restype = ctypes.c_size_t
+    lib.mha_proj_forward.argtypes = [vp] * 11 + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]
+    lib.mha_proj_forward.restype = i
+    lib.mha_status_string.argtypes = [i]
+    lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_last_error.argtypes = []
+    lib.mha_last_error.restype = ctypes.c_char_p
+    lib.mha_version.argtypes = []
+    lib.mha_version.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(lib: ctypes.CDLL, status: int) -> None:
+    if status != OK:
+        detail = lib.mha_last_error().decode() or lib.mha_status_string(status).decode()
+        raise MhaError(status, detail)

@@ -1,0 +1,254 @@
+// mha_api.cpp -- the C ABI declared in include/mha.h: host-side argument
+// validation (no HIP call before it passes), workspace layout, and dispatch to
+// the kernels.  Every entry point returns a status; none aborts or throws.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "../../include/mha.h"
+#include "mha_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MHA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t elem_size(int dtype) { return dtype == MHA_F32 ? 4 : 2; }
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Checks common to both entry points.
+int check_common(int mask_kind, int Nq, int Nk, int dtype, float scale) {
+  if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
+    return fail(MHA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (mask_kind == MHA_MASK_CAUSAL && Nq != Nk)
+    return fail(MHA_ERR_INVALID_ARG, "the causal mask needs Nq == Nk (got %d, %d)", Nq, Nk);
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
+    return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!std::isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "scale must be finite");
+  return MHA_OK;
+}
+
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+
+struct ProjLayout {
+  size_t q_off, k_off, v_off, o_off, total;
+};
+
+bool proj_layout(int B, int Nq, int Nk, int H, int d_k, int d_v, int dtype, ProjLayout* L) {
+  if (B < 0 || Nq < 0 || Nk < 0 || H < 1 || d_k < 1 || d_v < 1) return false;
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return false;
+  const size_t es = elem_size(dtype);
+  const size_t q = round256(size_t(B) * Nq * H * d_k * es);
+  const size_t k = round256(size_t(B) * Nk * H * d_k * es);
+  const size_t v = round256(size_t(B) * Nk * H * d_v * es);
+  const size_t o = round256(size_t(B) * Nq * H * d_v * es);
+  L->q_off = 0;
+  L->k_off = q;
+  L->v_off = q + k;
+  L->o_off = q + k + v;
+  L->total = q + k + v + o;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                int dtype, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
+  if (d_k < 1 || d_v < 1) return fail(MHA_ERR_INVALID_ARG, "d_k, d_v must be >= 1 (got %d, %d)", d_k, d_v);
+  int st = check_common(mask_kind, Nq, Nk, dtype, scale);
+  if (st) return st;
+  if (dtype == MHA_F32) {
+    if (d_k > mha::kF32MaxHeadDim || d_v > mha::kF32MaxHeadDim)
+      return fail(MHA_ERR_UNSUPPORTED, "fp32 supports d_k, d_v <= %d (got %d, %d)",
+                  mha::kF32MaxHeadDim, d_k, d_v);
+  } else if (d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim) {
+    return fail(MHA_ERR_UNSUPPORTED, "bf16/f16 support d_k == d_v == %d (got %d, %d)",
+                mha::kMfmaHeadDim, d_k, d_v);
+  }
+  if (B == 0 || H == 0 || Nq == 0) return MHA_OK;  // nothing to write
+  if (!q || !out) return fail(MHA_ERR_INVALID_ARG, "q and out must be non-null");
+  if (Nk > 0 && (!k || !v)) return fail(MHA_ERR_INVALID_ARG, "k and v must be non-null when Nk > 0");
+  const uintptr_t align = dtype == MHA_F32 ? 4 : 16;
+  if (!aligned(q, align) || !aligned(k, align) || !aligned(v, align) || !aligned(out, align))
+    return fail(MHA_ERR_INVALID_ARG, "q, k, v, out must be %d-byte aligned", (int)align);
+  if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
+  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 128 : 64);
+  if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
+    return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  mha::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.key_lens = key_lens;
+  a.q_sn = d_k;
+  a.q_sh = int64_t(Nq) * d_k;
+  a.q_sb = int64_t(H) * Nq * d_k;
+  a.k_sn = d_k;
+  a.k_sh = int64_t(Nk) * d_k;
+  a.k_sb = int64_t(H) * Nk * d_k;
+  a.v_sn = d_v;
+  a.v_sh = int64_t(Nk) * d_v;
+  a.v_sb = int64_t(H) * Nk * d_v;
+  a.o_sn = d_v;
+  a.o_sh = int64_t(Nq) * d_v;
+  a.o_sb = int64_t(H) * Nq * d_v;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.causal = mask_kind == MHA_MASK_CAUSAL;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == MHA_F32 ? mha::launch_attn_f32(a, s)
+                                  : mha::launch_attn_mfma(a, static_cast<mha::DType>(dtype), s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return MHA_OK;
+}
+
+size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype) {
+  ProjLayout L;
+  if (D < 1 || !proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L)) return 0;
+  return L.total;
+}
+
+int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                     const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
+                     const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
+                     int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || Nq < 0 || Nk < 0)
+    return fail(MHA_ERR_INVALID_ARG, "B, Nq, Nk must be >= 0 (got %d, %d, %d)", B, Nq, Nk);
+  if (D < 1 || H < 1 || d_k < 1 || d_v < 1)
+    return fail(MHA_ERR_INVALID_ARG, "D, H, d_k, d_v must be >= 1 (got %d, %d, %d, %d)", D, H, d_k, d_v);
+  if (!x_kv && Nk != Nq)
+    return fail(MHA_ERR_INVALID_ARG, "self-attention (x_kv == NULL) needs Nk == Nq (got %d, %d)", Nq, Nk);
+  int st = check_common(mask_kind, Nq, Nk, dtype, scale);
+  if (st) return st;
+  if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "the projection path supports bf16 and f16 only");
+  if (d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim)
+    return fail(MHA_ERR_UNSUPPORTED, "the projection path supports d_k == d_v == %d (got %d, %d)",
+                mha::kMfmaHeadDim, d_k, d_v);
+  if (D % 8 != 0) return fail(MHA_ERR_UNSUPPORTED, "D must be a multiple of 8 (got %d)", D);
+  if (B == 0 || Nq == 0) return MHA_OK;  // nothing to write
+  if (!x_q || !W_Q || !W_K || !W_V || !W_O || !out)
+    return fail(MHA_ERR_INVALID_ARG, "x_q, W_Q, W_K, W_V, W_O and out must be non-null");
+  const void* xkv = x_kv ? x_kv : x_q;
+  for (const void* p : {x_q, xkv, W_Q, W_K, W_V, W_O, (const void*)out})
+    if (!aligned(p, 16)) return fail(MHA_ERR_INVALID_ARG, "x_q, x_kv, W_*, out must be 16-byte aligned");
+  for (const void* p : {b_Q, b_K, b_V, b_O})
+    if (p && !aligned(p, 2)) return fail(MHA_ERR_INVALID_ARG, "biases must be 2-byte aligned");
+  if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
+  ProjLayout L;
+  proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L);
+  if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  const int64_t nqb = (Nq + 63) / 64;
+  if (nqb * H * B > kMaxBlocks || int64_t(B) * std::max(Nq, Nk) > (int64_t(1) << 31) / 64)
+    return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+
+  char* ws = static_cast<char*>(workspace);
+  void* Qw = ws + L.q_off;
+  void* Kw = ws + L.k_off;
+  void* Vw = ws + L.v_off;
+  void* Ow = ws + L.o_off;
+  const int HK = H * d_k, HV = H * d_v;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mha::DType dt = static_cast<mha::DType>(dtype);
+
+  // 1. Q, K, V projections in one launch; outputs row-major [B*N, H*d].
+  mha::GemmBatch g{};
+  g.p[0] = {x_q, W_Q, b_Q, Qw, B * Nq, HK, D, D, HK};
+  g.p[1] = {xkv, W_K, b_K, Kw, B * Nk, HK, D, D, HK};
+  g.p[2] = {xkv, W_V, b_V, Vw, B * Nk, HV, D, D, HV};
+  g.count = 3;
+  hipError_t e = mha::launch_gemm_mfma(g, dt, s);
+  if (e != hipSuccess) return hip_fail(e, "Q/K/V projection launch");
+
+  // 2. Attention per head, reading the projections in place (head h = columns
+  //    [h*d, (h+1)*d)) and writing the head-major concatenation [B*Nq, H*d_v].
+  mha::AttnArgs a{};
+  a.q = Qw;
+  a.k = Kw;
+  a.v = Vw;
+  a.out = Ow;
+  a.key_lens = key_lens;
+  a.q_sn = HK;
+  a.q_sh = d_k;
+  a.q_sb = int64_t(Nq) * HK;
+  a.k_sn = HK;
+  a.k_sh = d_k;
+  a.k_sb = int64_t(Nk) * HK;
+  a.v_sn = HV;
+  a.v_sh = d_v;
+  a.v_sb = int64_t(Nk) * HV;
+  a.o_sn = HV;
+  a.o_sh = d_v;
+  a.o_sb = int64_t(Nq) * HV;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.causal = mask_kind == MHA_MASK_CAUSAL;
+  a.scale = scale;
+  e = mha::launch_attn_mfma(a, dt, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+
+  // 3. Output projection.
+  mha::GemmBatch go{};
+  go.p[0] = {Ow, W_O, b_O, out, B * Nq, D, HV, HV, D};
+  go.count = 1;
+  e = mha::launch_gemm_mfma(go, dt, s);
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  return MHA_OK;
+}
+
+const char* mha_status_string(int status) {
+  switch (status) {
+    case MHA_OK: return "ok";
+    case MHA_ERR_INVALID_ARG: return "invalid argument";
+    case MHA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MHA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MHA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mha_last_error(void) { return g_last_error.c_str(); }
+
+int mha_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// mha_internal.h -- kernel parameter blocks and launchers shared by the host
+// dispatch (mha_api.cpp) and the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+enum class DType : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+// Attention over strided [B, H, N, d] views.  Element (b, h, n, c) of a tensor
+// lives at base + b*s_b + h*s_h + n*s_n + c (strides in elements), so the same
+// kernels read per-head tensors and the row-major projection outputs
+// [B*N, H*d] (where s_h = d and s_n = H*d) without a reshuffle.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* key_lens;  // device int32[B] or nullptr
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int B, H, Nq, Nk, dk, dv;
+  int causal;
+  float scale;
+};
+
+// One projection problem: C[m, n] = sum_k X[m, k] * W[n, k] (+ bias[n]).
+// X [M, K] row-major with row stride ldx; W [N, K] row-major (stride K);
+// C [M, N] row-major with row stride ldc.
+struct GemmProblem {
+  const void* x;
+  const void* w;
+  const void* bias;  // nullable, [N]
+  void* c;
+  int M, N, K;
+  int64_t ldx, ldc;
+};
+
+constexpr int kMaxGemmProblems = 3;
+
+struct GemmBatch {
+  GemmProblem p[kMaxGemmProblems];
+  int count;
+};
+
+// Launchers return hipSuccess or the launch error; they validate nothing
+// beyond what their kernels assume (the public entry points validate first).
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream);
+hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream);
+
+// Limits the launchers rely on.
+constexpr int kF32MaxHeadDim = 128;
+constexpr int kMfmaHeadDim = 64;
+
+}  // namespace mha
