@@ -1,0 +1,417 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-head attention forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input.  The
+default workload is the Transformer-base encoder self-attention with projections
+and key padding (B=64, n=64, d_model=512, h=8, lengths U{10..64}): Q/K/V
+projections, masked scaled dot-product attention per head, head concatenation and
+the output projection, via mha_proj_forward.  Inputs are seeded N(0,1) / Xavier
+draws, resident in HBM before timing; each step reads the next of several
+rotating input sets so that caches cannot hold the batch between steps.
+
+Prints one JSON line: whole-job throughput (algorithmic TFLOP/s), tokens/s, the
+roofline of the dominant kernel (its time measured with HIP events around it on
+the launch stream) and the fp64 oracle timed on the host as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import pathlib
+import sys
+import time
+
+import numpy as np
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "MHA fwd TFLOP/s + % bf16 MFMA peak (and HBM GB/s); tokens/s, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA bf16/f16; fp32 vector
+PEAK_HBM_GBPS = 8000.0
+ES = {"bf16": 2, "f16": 2, "f32": 4}
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+CSRC = ROOT / "transformer_head_scaled_softmax_amd" / "csrc"
+KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip"], "attention": ["attn_mfma.hip"],
+                  "out_projection": ["gemm_mfma.hip"], "attention_f32": ["attn_f32.hip"]}
+KERNEL_SYMBOLS = {"qkv_projection": "gemm_mfma_kernel", "attention": "attn_mfma_kernel",
+                  "out_projection": "gemm_mfma_kernel", "attention_f32": "attn_f32_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (visible scores only; padded or masked work is not counted).
+
+def visible_counts(w, lens):
+    """Number of visible (query, key) pairs per (b, h)."""
+    Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
+    i = np.arange(w.Nq)
+    tot = 0
+    for L in Ls:
+        tot += int(np.minimum(L, i + 1).sum()) if w.mask == 1 else int(L) * w.Nq
+    return tot * w.H
+
+
+def attention_flops(w, lens):
+    return 4.0 * w.d * visible_counts(w, lens)  # 2d for q.k, 2d for p*v per visible pair
+
+
+def attention_bytes(w, lens):
+    es = ES[w.dtype]
+    Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
+    qo = 2 * w.B * w.H * w.Nq * w.d * es
+    kv = 2 * int(Ls.sum()) * w.H * w.d * es
+    return qo + kv + (0 if lens is None else 4 * w.B)
+
+
+def projection_flops(w):
+    D, HD = w.D, w.H * w.d
+    qkv = 2.0 * w.B * (w.Nq * D * HD + 2 * w.Nk * D * HD)
+    out = 2.0 * w.B * w.Nq * HD * D
+    return qkv, out
+
+
+def proj_path_bytes(w, lens):
+    """Inputs + weights + output of the whole projection path."""
+    es = ES[w.dtype]
+    D, HD = w.D, w.H * w.d
+    x = w.B * w.Nq * D + (w.B * w.Nk * D if w.cross else 0)
+    weights = 3 * HD * D + D * HD
+    return (x + weights + w.B * w.Nq * D) * es + (0 if lens is None else 4 * w.B)
+
+
+def stage_work(w, lens):
+    """(flops, bytes) per launch of each kernel of the projection path."""
+    es = ES[w.dtype]
+    D, HD = w.D, w.H * w.d
+    qkv_f, out_f = projection_flops(w)
+    x_bytes = (w.B * w.Nq * D + (w.B * w.Nk * D if w.cross else 0)) * es
+    qkv_b = x_bytes + 3 * HD * D * es + (w.B * w.Nq * HD + 2 * w.B * w.Nk * HD) * es
+    out_b = (w.B * w.Nq * HD + D * HD + w.B * w.Nq * D) * es
+    return {"qkv_projection": (qkv_f, qkv_b),
+            "attention": (attention_flops(w, lens), attention_bytes(w, lens)),
+            "out_projection": (out_f, out_b)}
+
+
+# ---------------------------------------------------------------------------
+# HIP events through the runtime's C API (torch's events only see torch's stream
+# objects; these are recorded by the library on the launch stream).
+
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        st = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert st == 0, f"hipEventElapsedTime failed ({st})"
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+# ---------------------------------------------------------------------------
+
+def traffic_for(kernel_key: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    absent or taken on a different version of the kernel's source."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    data = json.loads(TRAFFIC_FILE.read_text())
+    ent = data.get(f"{workload}:{kernel_key}")
+    if not ent:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel_key, []):
+        h.update((CSRC / f).read_bytes())
+    if ent.get("source_sha256") != h.hexdigest():
+        return None
+    return ent["fetch_bytes"] + ent["write_bytes"]
+
+
+def roofline(kind_flops, kind_bytes, seconds, dtype, kernel_key, workload):
+    ai = kind_flops / kind_bytes
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if ai >= ridge:
+        ach = kind_flops / seconds / 1e12
+        peak = PEAK_TFLOPS[dtype]
+        bound, unit = ("mfma" if dtype != "f32" else "alu"), "TFLOP/s"
+    else:
+        ach = kind_bytes / seconds / 1e9
+        peak, bound, unit = PEAK_HBM_GBPS, "hbm", "GB/s"
+    return {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic_for(kernel_key, workload),
+            "kernel": kernel_key, "algorithmic_flops": kind_flops, "algorithmic_bytes": kind_bytes}
+
+
+def cpu_baseline(w, inp_sets, seconds_target):
+    """Time the fp64 oracle on whole batches of the same workload (long sequences:
+    sampled rows) until about ``seconds_target`` seconds of CPU work."""
+    import oracle
+    threads = oracle.default_threads()
+    done_flops, t0, n = 0.0, time.perf_counter(), 0
+    while True:
+        inp = inp_sets[n % len(inp_sets)]
+        if w.proj:
+            oracle.mha_proj(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
+                            H=w.H, mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
+            qkv_f, out_f = projection_flops(w)
+            done_flops += qkv_f + out_f + attention_flops(w, inp["key_lens"])
+            sample = "whole batches"
+        elif w.Nq * w.Nk > 1 << 22:
+            from transformer_head_scaled_softmax_amd import synth
+            rows = synth.sample_rows(w.B, w.H, w.Nq, seed=100 + n, n_random=4)
+            oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, mask_kind=w.mask,
+                                  key_lens=inp["key_lens"], nthreads=threads)
+            i = rows[:, 2]
+            vis = np.minimum(i + 1, w.Nk) if w.mask == 1 else np.full(len(i), w.Nk)
+            done_flops += 4.0 * w.d * float(vis.sum())
+            sample = f"sampled rows ({len(rows)} per pass)"
+        else:
+            oracle.attention(inp["q"], inp["k"], inp["v"], mask_kind=w.mask,
+                             key_lens=inp["key_lens"], nthreads=threads)
+            done_flops += attention_flops(w, inp["key_lens"])
+            sample = "whole batches"
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target:
+            break
+    return {"value": round(done_flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": f"{n} {sample} of {w.name}, fp64, {el:.1f} s",
+            "tokens_per_s": round(n * w.B * w.Nq / el, 1) if sample == "whole batches" else None}
+
+
+def main():
+    from transformer_head_scaled_softmax_amd import synth
+
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="base_encoder_proj", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import transformer_head_scaled_softmax_amd as mha
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    lib = mha.load()
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+    es = ES[w.dtype]
+
+    def to_dev(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev, tdt)
+
+    # Input sets: a batch's own inputs and output.  Weights are the model's and are
+    # shared by every batch.
+    if w.proj:
+        per_set = (w.B * w.Nq * w.D * 2 + (w.B * w.Nk * w.D if w.cross else 0)) * es
+    else:
+        per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.H * w.Nk * w.d) * es
+    nsets = args.sets or int(min(64, max(2, math.ceil((1 << 30) / per_set))))
+    log(f"[bench] workload {w.name}: {w.description}; {nsets} rotating input sets "
+        f"({per_set * nsets / 2**20:.0f} MiB)")
+    host_sets, dev_sets = [], []
+    for s in range(nsets):
+        inp = synth.workload_inputs(w, seed=w.seed * 1000 + s)
+        lens_t = None if inp["key_lens"] is None else torch.from_numpy(inp["key_lens"]).to(dev)
+        if w.proj:
+            d = {"x_q": to_dev(inp["x_q"]), "x_kv": to_dev(inp["x_kv"]), "key_lens": lens_t,
+                 "out": torch.empty((w.B, w.Nq, w.D), dtype=tdt, device=dev)}
+        else:
+            d = {n_: to_dev(inp[n_]) for n_ in ("q", "k", "v")}
+            d["key_lens"] = lens_t
+            d["out"] = torch.empty((w.B, w.H, w.Nq, w.d), dtype=tdt, device=dev)
+        dev_sets.append(d)
+        host_sets.append(inp if s < 2 else {"key_lens": inp["key_lens"]})
+    lens_list = [h["key_lens"] for h in host_sets]
+
+    hip = Hip()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    code = {"f32": 0, "bf16": 1, "f16": 2}[w.dtype]
+    scale = ctypes.c_float(1.0 / math.sqrt(w.d))
+
+    if w.proj:
+        wts = synth.workload_inputs(w)  # seed of the workload: the model weights
+        W = {n_: to_dev(wts[n_]) for n_ in ("W_Q", "W_K", "W_V", "W_O")}
+        need = lib.mha_proj_workspace_bytes(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, code)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def step(i, sp, events=None):
+            d = dev_sets[i % nsets]
+            lp = None if d["key_lens"] is None else d["key_lens"].data_ptr()
+            xkv = None if d["x_kv"] is None else d["x_kv"].data_ptr()
+            argsv = (d["x_q"].data_ptr(), xkv, W["W_Q"].data_ptr(), W["W_K"].data_ptr(),
+                     W["W_V"].data_ptr(), W["W_O"].data_ptr(), None, None, None, None,
+                     d["out"].data_ptr(), w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.mask, lp, scale,
+                     code, ws.data_ptr(), need, sp)
+            st = (lib.mha_proj_forward(*argsv) if events is None
+                  else lib.mha_proj_forward_timed(*argsv, events))
+            if st != 0:
+                raise RuntimeError(lib.mha_last_error().decode())
+        stage_names = ["qkv_projection", "attention", "out_projection"]
+    else:
+        def step(i, sp, events=None):
+            d = dev_sets[i % nsets]
+            lp = None if d["key_lens"] is None else d["key_lens"].data_ptr()
+            argsv = (d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["out"].data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.mask, lp, scale, code, sp)
+            st = lib.mha_forward(*argsv) if events is None else lib.mha_forward_timed(*argsv, events)
+            if st != 0:
+                raise RuntimeError(lib.mha_last_error().decode())
+        stage_names = ["attention_f32" if w.dtype == "f32" else "attention"]
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    t0 = time.perf_counter()
+    for i in range(args.warmup):
+        step(i, sp)
+    torch.cuda.synchronize()
+    host_us_per_step = (time.perf_counter() - t0) / max(1, args.warmup) * 1e6
+
+    # Timed region 1 (the reported throughput): the K steps replayed from HIP
+    # graphs, as a serving loop would issue them, so host launch overhead does
+    # not stall the GPU.  One graph holds one step per input set.
+    K = args.steps
+    G = min(nsets, K)
+    cap = torch.cuda.Stream()
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            step(0, ctypes.c_void_p(cap.cuda_stream))  # warm the capture stream
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            csp = ctypes.c_void_p(cap.cuda_stream)
+            for i in range(n):
+                step(args.warmup + i, csp)
+        return g
+
+    g_full = capture(G)
+    g_rest = capture(K % G) if K % G else None
+    reps = K // G
+    for _ in range(2):
+        g_full.replay()
+    torch.cuda.synchronize()
+    start, end = hip.event(), hip.event()
+    cur = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    hip.lib.hipEventRecord(start, cur)
+    for _ in range(reps):
+        g_full.replay()
+    if g_rest is not None:
+        g_rest.replay()
+    hip.lib.hipEventRecord(end, cur)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = hip.elapsed_ms(start, end) / K
+
+    # Timed region 2 (per-kernel times): the same K steps issued directly on the
+    # stream through the timed entry points, whose events take each kernel's own
+    # start and end timestamps from its dispatch (hipExtLaunchKernel).
+    nst = len(stage_names)
+    ev_arrays = [(ctypes.c_void_p * (2 * nst))(*[hip.event() for _ in range(2 * nst)])
+                 for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(args.warmup + i, sp, ev_arrays[i])
+    torch.cuda.synchronize()
+    per = {n_: [] for n_ in stage_names}
+    for evs in ev_arrays:
+        for k_, n_ in enumerate(stage_names):
+            per[n_].append(hip.elapsed_ms(evs[2 * k_], evs[2 * k_ + 1]))
+    avg = {n_: float(np.mean(v)) for n_, v in per.items()}
+    eager_ms_step = hip.elapsed_ms(ev_arrays[0][0], ev_arrays[-1][2 * nst - 1]) / K
+
+    used = [lens_list[(args.warmup + i) % nsets] for i in range(K)]
+    att_f = float(np.mean([attention_flops(w, L) for L in used]))
+    if w.proj:
+        qkv_f, out_f = projection_flops(w)
+        flops = qkv_f + out_f + att_f
+        bytes_ = float(np.mean([proj_path_bytes(w, L) for L in used]))
+    else:
+        flops = att_f
+        bytes_ = float(np.mean([attention_bytes(w, L) for L in used]))
+    sec = ms_step / 1e3
+    result = {
+        "metric": METRIC, "value": round(flops / sec / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, Xavier-uniform weights, uniform key lengths)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d_k": w.d,
+                   "d_v": w.d, "D": w.D if w.proj else None, "projections": w.proj,
+                   "mask": "causal" if w.mask == 1 else "none",
+                   "key_lens": None if w.lens is None else f"U{{{w.lens[0]}..{w.lens[1]}}}",
+                   "input_sets": nsets, "issue": "HIP graph replay"},
+        "tokens_per_s": round(w.B * w.Nq / sec, 1),
+        "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 5),
+        "hbm_gbps_algorithmic": round(bytes_ / sec / 1e9, 1),
+        "ms_per_step_eager": round(eager_ms_step, 6),
+        "host_us_per_step": round(host_us_per_step, 2),
+        "wall_s_timed": round(t_wall, 4),
+        "kernel_ms": {n_: round(v, 6) for n_, v in avg.items()},
+    }
+
+    # Roofline of the dominant kernel.
+    dom = max(avg, key=avg.get)
+    if w.proj:
+        f_, b_ = stage_work(w, None)[dom]
+        if dom == "attention":
+            f_ = att_f
+            b_ = float(np.mean([attention_bytes(w, L) for L in used]))
+    else:
+        f_, b_ = flops, bytes_
+    result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom, w.name)
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] GPU done: {ms_step * 1e3:.2f} us/step; timing the fp64 oracle "
+            f"for ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline(w, [h for h in host_sets if "x_q" in h or "q" in h],
+                                              args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

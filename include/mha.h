@@ -122,6 +122,29 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
                      int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Timed variants, for profiling.  Same arguments, validation and results as the
+ * entry point they extend, plus `events`: caller-created hipEvent_t handles
+ * (hipEventCreate; the caller owns them) that receive the start and end
+ * timestamps of each kernel the call launches, taken by the dispatch itself
+ * (hipExtLaunchKernel), so hipEventElapsedTime(events[2k], events[2k+1]) is
+ * kernel k's own duration.  NULL records nothing.
+ *
+ * mha_forward_timed: 2 events -- the attention kernel.
+ * mha_proj_forward_timed: 6 events -- the Q/K/V projection, the attention
+ * kernel and the output projection, in that order.
+ */
+int mha_forward_timed(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                      int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                      int dtype, void* stream, void* const* events);
+
+int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                           const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
+                           const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk,
+                           int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
+                           float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events);
+
 /* Static description of a status code; never NULL. */
 const char* mha_status_string(int status);
 

@@ -292,3 +292,44 @@ def test_proj_worked_example_identity():
     got = to_host(out)[0, :, :2]
     want = np.array([case["outputs"][t] for t in gold["tokens"]])
     assert np.max(np.abs(got - want)) <= 4e-3
+
+
+def test_graph_replays_match_eager():
+    """Both entry points captured in one HIP graph: every replay, with eager work
+    and synchronisations in between, reproduces the eager result bit for bit."""
+    w = synth.WORKLOADS["base_encoder_proj"]
+    inp = synth.workload_inputs(w)
+    d = _proj_dev(inp, "bf16")
+    lens = lens_dev(inp["key_lens"])
+    core = synth.core_inputs(2, 2, 200, 200, 64, 64, "bf16", seed=21)
+    q, k, v = (to_dev(core[n], "bf16") for n in ("q", "k", "v"))
+    ws = torch.empty(mha.proj_workspace_bytes(w.B, w.Nq, w.Nk, w.D, w.H, 64, 64), dtype=torch.uint8,
+                     device="cuda")
+    out_p = torch.empty((w.B, w.Nq, w.D), dtype=torch.bfloat16, device="cuda")
+    out_c = torch.empty((2, 2, 200, 64), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        mha.proj_forward(d["x_q"], None, d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=w.H,
+                         key_lens=lens, out=out_p, workspace=ws)
+        mha.forward(q, k, v, mask_kind=CAUSAL, out=out_c)
+
+    run()
+    torch.cuda.synchronize()
+    want_p, want_c = out_p.clone(), out_c.clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for _ in range(4):
+        out_p.zero_()
+        out_c.zero_()
+        run_eager_noise = torch.randn(1000, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_p, want_p)
+        assert torch.equal(out_c, want_c)
+        del run_eager_noise

@@ -23,8 +23,8 @@ ERR_WORKSPACE = -3
 ERR_HIP = -4
 
 # Every symbol include/mha.h declares.
-EXPORTS = ("mha_forward", "mha_proj_workspace_bytes", "mha_proj_forward", "mha_status_string",
-           "mha_last_error", "mha_version")
+EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
+           "mha_proj_forward_timed", "mha_status_string", "mha_last_error", "mha_version")
 
 
 class MhaError(RuntimeError):
@@ -48,10 +48,14 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.mha_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, f, i, vp]
     lib.mha_forward.restype = i
+    lib.mha_forward_timed.argtypes = lib.mha_forward.argtypes + [vp]
+    lib.mha_forward_timed.restype = i
     lib.mha_proj_workspace_bytes.argtypes = [i] * 8
     lib.mha_proj_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_proj_forward.argtypes = [vp] * 11 + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]
     lib.mha_proj_forward.restype = i
+    lib.mha_proj_forward_timed.argtypes = lib.mha_proj_forward.argtypes + [vp]
+    lib.mha_proj_forward_timed.restype = i
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_last_error.argtypes = []

@@ -108,11 +108,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int nqb) {
 
 }  // namespace
 
-hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const int nqb = (a.Nq + kRows - 1) / kRows;
   const int64_t blocks = (int64_t)nqb * a.H * a.B;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, nqb);
+  hipExtLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, t0, t1, 0, a, nqb);
   return hipGetLastError();
 }
 

@@ -300,23 +300,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
 }
 
 template <class Op, int NW>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const int nqb = (a.Nq + NW * 32 - 1) / (NW * 32);
   const int64_t blocks = (int64_t)nqb * a.H * a.B;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_mfma_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a, nqb);
+  hipExtLaunchKernelGGL((attn_mfma_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0, t1,
+                        0, a, nqb);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream) {
+hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   // Short query blocks (sentence-length sequences) use 2 waves per workgroup
   // so the grid has many workgroups; long ones use 4 waves to share each
   // staged K/V tile among 128 queries.
   const bool longq = a.Nq > 64;
-  if (dt == DType::BF16) return longq ? launch<BF16, 4>(a, stream) : launch<BF16, 2>(a, stream);
-  return longq ? launch<F16, 4>(a, stream) : launch<F16, 2>(a, stream);
+  if (dt == DType::BF16) return longq ? launch<BF16, 4>(a, stream, t0, t1) : launch<BF16, 2>(a, stream, t0, t1);
+  return longq ? launch<F16, 4>(a, stream, t0, t1) : launch<F16, 2>(a, stream, t0, t1);
 }
 
 }  // namespace mha

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmBatch g, TileMa
 
 }  // namespace
 
-hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream) {
+hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   TileMap tm{};
   int total = 0;
   for (int i = 0; i < g.count; ++i) {
@@ -192,9 +192,9 @@ hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream) {
   for (int i = g.count; i <= kMaxGemmProblems; ++i) tm.start[i] = total;
   if (total == 0) return hipSuccess;
   if (dt == DType::BF16)
-    hipLaunchKernelGGL(gemm_mfma_kernel<BF16>, dim3(total), dim3(kThreads), 0, stream, g, tm);
+    hipExtLaunchKernelGGL(gemm_mfma_kernel<BF16>, dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
   else
-    hipLaunchKernelGGL(gemm_mfma_kernel<F16>, dim3(total), dim3(kThreads), 0, stream, g, tm);
+    hipExtLaunchKernelGGL(gemm_mfma_kernel<F16>, dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
   return hipGetLastError();
 }
 

@@ -73,9 +73,13 @@ bool proj_layout(int B, int Nq, int Nk, int H, int d_k, int d_v, int dtype, Proj
 
 extern "C" {
 
-int mha_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
-                int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
-                int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                 int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                 int dtype, void* stream, hipEvent_t const* ev) {
   g_last_error.clear();
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
@@ -128,10 +132,29 @@ int mha_forward(const void* q, const void* k, const void* v, void* out, int B, i
   a.causal = mask_kind == MHA_MASK_CAUSAL;
   a.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == MHA_F32 ? mha::launch_attn_f32(a, s)
-                                  : mha::launch_attn_mfma(a, static_cast<mha::DType>(dtype), s);
+  hipEvent_t t0 = ev ? ev[0] : nullptr, t1 = ev ? ev[1] : nullptr;
+  hipError_t e = dtype == MHA_F32 ? mha::launch_attn_f32(a, s, t0, t1)
+                                  : mha::launch_attn_mfma(a, static_cast<mha::DType>(dtype), s, t0, t1);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                int dtype, void* stream) {
+  return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype,
+                      stream, nullptr);
+}
+
+int mha_forward_timed(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
+                      int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                      int dtype, void* stream, void* const* events) {
+  return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype,
+                      stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
 size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype) {
@@ -140,11 +163,17 @@ size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, in
   return L.total;
 }
 
-int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
-                     const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
-                     const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
-                     int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
-                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// mha_proj_forward with optional profiling events (ev == nullptr: none).
+int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                      const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
+                      const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
+                      int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                      int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                      hipEvent_t const* ev) {
   g_last_error.clear();
   if (B < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, Nq, Nk must be >= 0 (got %d, %d, %d)", B, Nq, Nk);
@@ -187,13 +216,15 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mha::DType dt = static_cast<mha::DType>(dtype);
 
+  auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
+
   // 1. Q, K, V projections in one launch; outputs row-major [B*N, H*d].
   mha::GemmBatch g{};
   g.p[0] = {x_q, W_Q, b_Q, Qw, B * Nq, HK, D, D, HK};
   g.p[1] = {xkv, W_K, b_K, Kw, B * Nk, HK, D, D, HK};
   g.p[2] = {xkv, W_V, b_V, Vw, B * Nk, HV, D, D, HV};
   g.count = 3;
-  hipError_t e = mha::launch_gemm_mfma(g, dt, s);
+  hipError_t e = mha::launch_gemm_mfma(g, dt, s, evt(0), evt(1));
   if (e != hipSuccess) return hip_fail(e, "Q/K/V projection launch");
 
   // 2. Attention per head, reading the projections in place (head h = columns
@@ -224,16 +255,41 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
   a.dv = d_v;
   a.causal = mask_kind == MHA_MASK_CAUSAL;
   a.scale = scale;
-  e = mha::launch_attn_mfma(a, dt, s);
+  e = mha::launch_attn_mfma(a, dt, s, evt(2), evt(3));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
 
   // 3. Output projection.
   mha::GemmBatch go{};
   go.p[0] = {Ow, W_O, b_O, out, B * Nq, D, HV, HV, D};
   go.count = 1;
-  e = mha::launch_gemm_mfma(go, dt, s);
+  e = mha::launch_gemm_mfma(go, dt, s, evt(4), evt(5));
   if (e != hipSuccess) return hip_fail(e, "output projection launch");
   return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                     const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
+                     const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
+                     int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
+                           d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
+                           stream, nullptr);
+}
+
+int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                           const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
+                           const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk,
+                           int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
+                           float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events) {
+  return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
+                           d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
+                           stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
 const char* mha_status_string(int status) {

@@ -2,6 +2,7 @@
 // dispatch (mha_api.cpp) and the kernel files.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,9 +50,14 @@ struct GemmBatch {
 
 // Launchers return hipSuccess or the launch error; they validate nothing
 // beyond what their kernels assume (the public entry points validate first).
-hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream);
-hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream);
+// Non-null t0/t1 receive the kernel's own start and end timestamps
+// (hipExtLaunchKernel events).
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream, hipEvent_t t0 = nullptr,
+                           hipEvent_t t1 = nullptr);
+hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
+                            hipEvent_t t1 = nullptr);
+hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
+                            hipEvent_t t1 = nullptr);
 
 // Limits the launchers rely on.
 constexpr int kF32MaxHeadDim = 128;
