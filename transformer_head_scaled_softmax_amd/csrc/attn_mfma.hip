@@ -23,11 +23,17 @@
 // m + 32*(k/8), element k%8; B[k][n] from lane n + 32*(k/8), element k%8;
 // C[m][n] lands in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
 //
-// Softmax bookkeeping, per query: m_ref is the running reference maximum (in
-// log2 units), p = exp2(s * scale * log2e - m_ref).  m_ref is raised (and the
-// accumulators rescaled) only when a tile's maximum exceeds it by more than
-// kLazyLog2 -- otherwise p may grow up to 2^kLazyLog2, which fp32 holds
-// exactly as well; the final division by the running sum cancels m_ref.
+// Softmax bookkeeping, per query: m_ref is a reference maximum (in log2
+// units) and p = exp2(s * scale * log2e - m_ref), accumulated into a running
+// sum and the O^T accumulators; the final division by the sum cancels m_ref, so
+// any reference gives the same result in exact arithmetic.  Each tile is first
+// exponentiated against the current reference without computing its maximum;
+// only if a query's partial sum is not finite or exceeds a guard (2^64 for
+// bf16 P, 2^15 for f16 P) -- its first visible tile, or a new maximum far above
+// the reference -- does that query take the tile's true maximum as its new
+// reference, rescale its accumulators and exponentiate the tile again.  Row
+// sums come from the packed P values with v_dot2, i.e. from exactly the
+// rounded values the P*V product multiplies.
 #include "mha_internal.h"
 
 namespace mha {
@@ -44,11 +50,16 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kD = kMfmaHeadDim;  // 64
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKS = 72;           // K tile row stride (elements): 144 B -> conflict-free 16 B reads
-constexpr int kVS = 68;           // V^T tile row stride (elements): 136 B -> conflict-free 8 B reads
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyLog2 = 8.0f;
+constexpr int kDeadOffset = (int)0x80000000u;  // beyond any range check: loads return zeros
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 
 struct BF16 {
+  static constexpr float kGuard = 18446744073709551616.0f;  // 2^64: p stays far inside bf16/fp32
+  __device__ static float sum2(uint32_t packed, float acc) {  // acc + lo + hi of a packed pair
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), bf16x2_t{(__bf16)1.0f, (__bf16)1.0f},
+                                           acc, false);
+  }
   __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -60,6 +71,11 @@ struct BF16 {
 };
 
 struct F16 {
+  static constexpr float kGuard = 32768.0f;  // 2^15: p stays inside the f16 range
+  __device__ static float sum2(uint32_t packed, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, acc,
+                                  false);
+  }
   __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
@@ -69,6 +85,13 @@ struct F16 {
     return __builtin_bit_cast(uint32_t, r);
   }
 };
+
+// Buffer resource over `bytes` bytes from `base` (clamped to the 32-bit range
+// check); loads at or beyond `bytes` return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kBufferWord3);
+}
 
 __device__ inline float lanes_max(float x) {  // max over lanes l and l^32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -80,16 +103,16 @@ __device__ inline float lanes_sum(float x) {  // sum over lanes l and l^32
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <class Op, int NW>
+template <class Op, int NW, int QS>
 __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int nqb) {
   constexpr int NT = NW * 64;
-  constexpr int QB = NW * 32;
-  constexpr int KCH = (kBN * 8) / NT;       // 16-byte K chunks per thread per tile
-  constexpr int VCH = (kBN / 2 * 8) / NT;   // 16-byte chunk pairs (two key rows) of V
-  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
+  constexpr int QW = 32 * QS;         // queries per wave: QS sub-blocks of 32
+  constexpr int QB = NW * QW;         // queries per workgroup
+  constexpr int CH = (kBN * 8) / NT;  // 16-byte chunks of K (and of V) per thread per tile
+  static_assert(CH >= 1, "tile too small for the workgroup");
 
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][kBN * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kD * kVS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kBN * kD];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
@@ -103,178 +126,216 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
   int L = a.Nk;
   if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
   const int q0 = qb * QB;
-  const int qw0 = q0 + wave * 32;
-  const int qi = qw0 + col;
-  const bool qvalid = qi < a.Nq;
-  const int kend = a.causal ? min(L, qi + 1) : L;               // keys this query sees
-  const int kend_blk = a.causal ? min(L, min(q0 + QB, a.Nq)) : L;  // keys the block needs
-  const int kmin_wave = a.causal ? min(L, qw0 + 1) : L;          // tiles below: no masking
+  const int qw0 = q0 + wave * QW;
+  int qi[QS], kend[QS];
+  bool qvalid[QS];
+#pragma unroll
+  for (int u = 0; u < QS; ++u) {
+    qi[u] = qw0 + 32 * u + col;
+    qvalid[u] = qi[u] < a.Nq;
+    kend[u] = a.causal ? min(L, qi[u] + 1) : L;  // keys this query sees
+  }
+  const int kend_blk = a.causal ? min(L, min(q0 + QB, a.Nq)) : L;     // keys the workgroup needs
+  const int kmin_wave = a.causal ? min(L, qw0 + 1) : L;               // tiles below: no masking
+  const int kmax_wave = a.causal ? min(L, min(qw0 + QW, a.Nq)) : L;   // tiles from here: skip
   const int ntiles = (kend_blk + kBN - 1) / kBN;
 
+  // Range-checked buffers over this (b, h): query rows past Nq and key/value
+  // rows at or past the workgroup's key end read as zeros, so padded rows are
+  // never loaded and the loads need no branches.
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(qbase, ((int64_t)(a.Nq - 1) * a.q_sn + kD) * 2);
+  const __amdgpu_buffer_rsrc_t ksrc =
+      make_rsrc(kbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.k_sn + kD) * 2 : 0);
+  const __amdgpu_buffer_rsrc_t vsrc =
+      make_rsrc(vbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.v_sn + kD) * 2 : 0);
 
-  // This lane's query as the B operand of S^T = K Q^T: features 16kk + 8half .. +7.
+  // This lane's queries as B operands of S^T = K Q^T: features 16kk + 8half .. +7.
   // A negative scale is folded in by negating q (exact), so the softmax below
   // always multiplies by a non-negative c2.
   const uint32_t qsign = a.scale < 0.0f ? 0x80008000u : 0u;
   const float c2 = fabsf(a.scale) * kLog2e;
-  u32x4_t qreg[4];
+  u32x4_t qreg[QS][4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (qvalid) v = *reinterpret_cast<const u32x4_t*>(qbase + (int64_t)qi * a.q_sn + kk * 16 + half * 8);
-    qreg[kk] = v ^ qsign;
+  for (int u = 0; u < QS; ++u) {
+    const int qoff = qvalid[u] ? (int)(qi[u] * a.q_sn * 2) + half * 16 : kDeadOffset;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qreg[u][kk] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff + kk * 32, 0, 0) ^ qsign;
   }
 
-  u32x4_t kreg[KCH];
-  u32x4_t vreg[VCH][2];
+  // Staging: each thread moves CH 16-byte chunks of the K tile and of the V
+  // tile.  K rows keep a padded stride (conflict-free 16-byte operand reads);
+  // V rows are dense 128-byte rows whose chunks are XOR-swizzled by bit 1 of
+  // the row, which makes the transposing operand reads below conflict-free.
+  int koff[CH], voff[CH], kpos[CH], vpos[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = tid + c * NT, row = idx >> 3, ch = idx & 7;
+    koff[c] = (int)((row * a.k_sn + ch * 8) * 2);
+    voff[c] = (int)((row * a.v_sn + ch * 8) * 2);
+    kpos[c] = row * kKS + ch * 8;
+    vpos[c] = row * kD + ((ch ^ (((row >> 1) & 1) << 2)) << 3);
+  }
+  const int ktile = (int)(kBN * a.k_sn * 2), vtile = (int)(kBN * a.v_sn * 2);
+  // Tiles at or past the workgroup's key end fall outside the range check, so
+  // the prefetch issued after the last tile reads nothing.
+  u32x4_t kreg[CH], vreg[CH];
   auto load_tile = [&](int t) {
-    const int j0 = t * kBN;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * NT, row = idx >> 3, ch = idx & 7, j = j0 + row;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (j < kend_blk) v = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)j * a.k_sn + ch * 8);
-      kreg[c] = v;
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + c * NT, pr = idx >> 3, ch = idx & 7, j = j0 + 2 * pr;
-      u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-      if (j < kend_blk) v0 = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)j * a.v_sn + ch * 8);
-      if (j + 1 < kend_blk) v1 = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)(j + 1) * a.v_sn + ch * 8);
-      vreg[c][0] = v0;
-      vreg[c][1] = v1;
+    for (int c = 0; c < CH; ++c) {
+      kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(ksrc, koff[c] + t * ktile, 0, 0);
+      vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, voff[c] + t * vtile, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * NT, row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4_t*>(&ks[buf][row * kKS + ch * 8]) = kreg[c];
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + c * NT, pr = idx >> 3, ch = idx & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = vreg[c][0][e >> 1], w1 = vreg[c][1][e >> 1];
-        const uint32_t pair = (e & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
-        *reinterpret_cast<uint32_t*>(&vt[buf][(ch * 8 + e) * kVS + 2 * pr]) = pair;
-      }
+    for (int c = 0; c < CH; ++c) {
+      *reinterpret_cast<u32x4_t*>(&ks[buf][kpos[c]]) = kreg[c];
+      *reinterpret_cast<u32x4_t*>(&vs[buf][vpos[c]]) = vreg[c];
     }
   };
 
-  f32x16_t o[2];
+  // V^T operand of O^T += V^T P^T through ds_read_b64_tr_b16.  In each group of
+  // 16 lanes the instruction hands lane l element l%4 of the 4-element runs read
+  // by lanes l/4 + 4k (k = 0..3); so lane 4k + q points at key row (k0 + k),
+  // features (c0 + 4q .. +3), and lane l' then holds features c0 + l' of keys
+  // k0 .. k0+3 -- the A-operand layout (feature row, 4 consecutive keys).
+  // Group g = lane/16 covers features 16(g%2) of the block and key half g/2.
+  const int tr_k = (lane & 15) >> 2, tr_q = lane & 3, tr_cg = (lane >> 4) & 1;
+  const int tr_row = 4 * half + tr_k;  // + 16 t4 (+ 8 for keys 8..15 of the step)
+  int tr_col[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
-  float m_ref = -INFINITY, lsum = 0.0f;
-
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int cb = 0; cb < 2; ++cb) {
+    const int cidx = cb * 32 + 16 * tr_cg + 4 * tr_q;
+    tr_col[cb] = ((((cidx >> 3) ^ (((tr_k >> 1) & 1) << 2))) << 3) + (cidx & 7);
   }
+  auto vread = [&](int buf, int row, int cb) -> u32x2_t {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    lds_s16x4_t* p = (lds_s16x4_t*)(const __attribute__((address_space(3))) uint16_t*)&vs[buf][row * kD + tr_col[cb]];
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+  };
+
+  f32x16_t o[QS][2];
+  float m_ref[QS], lsum[QS];
+#pragma unroll
+  for (int u = 0; u < QS; ++u) {
+    m_ref[u] = -INFINITY;
+    lsum[u] = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[u][cb][r] = 0.0f;
+  }
+
+  load_tile(0);
+  store_tile(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int j0 = t * kBN;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    load_tile(t + 1);
 
-    // S^T = K_tile Q^T: two 32-key blocks.
-    f32x16_t s[2];
+    if (j0 < kmax_wave) {  // wave-uniform: tiles past all of this wave's rows are skipped
+      // S^T = K_tile Q^T: two 32-key blocks; each K operand read serves every
+      // query sub-block of the wave.
+      f32x16_t s[QS][2];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+      for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[jb][r] = 0.0f;
+        for (int u = 0; u < QS; ++u)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kKS + kk * 16 + half * 8]);
-        s[jb] = Op::mma(av, qreg[kk], s[jb]);
+          for (int r = 0; r < 16; ++r) s[u][jb][r] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kKS + kk * 16 + half * 8]);
+#pragma unroll
+          for (int u = 0; u < QS; ++u) s[u][jb] = Op::mma(av, qreg[u][kk], s[u][jb]);
+        }
       }
-    }
 
-    // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4.
-    const bool masked = j0 + kBN > kmin_wave;  // wave-uniform
-    const int lim = kend - j0 - 4 * half;
-    float mx = -INFINITY;
-    if (masked) {
+      u32x4_t pb[QS][4];
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int u = 0; u < QS; ++u) {
+        // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4;
+        // invisible keys become -inf.
+        if (j0 + kBN > kmin_wave) {  // only diagonal and tail tiles
+          const int lim = kend[u] - j0 - 4 * half;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = jb * 32 + (r >> 2) * 8 + (r & 3);
-          if (off >= lim) s[jb][r] = -INFINITY;
-          mx = fmaxf(mx, s[jb][r]);
+          for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (jb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[u][jb][r] = -INFINITY;
         }
-    } else {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-    }
-    mx = lanes_max(mx);
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
 
-    // Each query decides for itself (never because of another row of the
-    // wave), so a row's arithmetic does not depend on its neighbours' data.
-    const bool need = mt > m_ref + kLazyLog2;  // implies mt is finite
-    if (__any(need)) {
-      const float m_new = need ? mt : m_ref;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-      lsum *= alpha;
+        // P = exp2(s * c2 - m_ref), packed to the MFMA input type in the order
+        // the P^T operand needs (step t4 takes registers 8(t4%2) .. +7 of
+        // s[t4/2]); the row sum comes from the packed values with v_dot2.
+        float ls = 0.0f;
+        auto exponentiate = [&](float mu, bool select_masked) {
+          ls = 0.0f;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+          for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
-      m_ref = m_new;
-    }
-    const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
-
-    float ls = 0.0f;
-    if (masked) {
+            for (int w = 0; w < 4; ++w) {
+              const int jb = t4 >> 1, r = (t4 & 1) * 8 + 2 * w;
+              float p0 = __builtin_amdgcn_exp2f(fmaf(s[u][jb][r], c2, -mu));
+              float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][jb][r + 1], c2, -mu));
+              if (select_masked) {
+                p0 = s[u][jb][r] == -INFINITY ? 0.0f : p0;
+                p1 = s[u][jb][r + 1] == -INFINITY ? 0.0f : p1;
+              }
+              pb[u][t4][w] = Op::pack(p0, p1);
+              ls = Op::sum2(pb[u][t4][w], ls);
+            }
+        };
+        // Optimistic pass against the current reference.  It is kept unless
+        // this query's partial sum is not finite or exceeds kGuard (first tile,
+        // a new maximum far above the reference, or masked keys with no
+        // reference yet).
+        exponentiate(m_ref[u], false);
+        const bool need = lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f;
+        if (__any(need)) {
+          float mx = -INFINITY;
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+          for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = (s[jb][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -mu));
-          s[jb][r] = p;
-          ls += p;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][jb][r]);
+          mx = lanes_max(mx);
+          const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+          // Queries that passed keep their reference, so a row's arithmetic
+          // never depends on other rows' data.
+          const float m_new = need ? fmaxf(m_ref[u], mt) : m_ref[u];
+          const float alpha = (need && m_new != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref[u] - m_new) : 1.0f;
+          lsum[u] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[u][cb][r] *= alpha;
+          m_ref[u] = m_new;
+          // Masked keys get exactly 0, also when scale is 0 or no key is visible yet.
+          exponentiate(m_ref[u] == -INFINITY ? 0.0f : m_ref[u], true);
         }
-    } else {
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -mu));
-          s[jb][r] = p;
-          ls += p;
-        }
-    }
-    lsum += ls;
+        lsum[u] += ls;
+      }
 
-    // O^T += V^T P^T over four 16-key steps.  For step t4 this lane's P values
-    // are registers 8(t4%2) .. +7 of s[t4/2]: keys 16t4 + 4half + {0..3} and
-    // 16t4 + 8 + 4half + {0..3}; V^T supplies the same keys for feature rows.
+      // O^T += V^T P^T over four 16-key steps: V^T supplies keys 16t4 + 4half +
+      // {0..3} and 16t4 + 8 + 4half + {0..3} for this lane's feature row; each
+      // V operand read serves every query sub-block.
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int jb = t4 >> 1, base = (t4 & 1) * 8;
-      u32x4_t pb;
-      pb[0] = Op::pack(s[jb][base + 0], s[jb][base + 1]);
-      pb[1] = Op::pack(s[jb][base + 2], s[jb][base + 3]);
-      pb[2] = Op::pack(s[jb][base + 4], s[jb][base + 5]);
-      pb[3] = Op::pack(s[jb][base + 6], s[jb][base + 7]);
+      for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const uint16_t* vrow = &vt[buf][(cb * 32 + col) * kVS + t4 * 16 + half * 4];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 8);
-        const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
-        o[cb] = Op::mma(av, pb, o[cb]);
+        for (int cb = 0; cb < 2; ++cb) {
+          const u32x2_t lo = vread(buf, 16 * t4 + tr_row, cb);
+          const u32x2_t hi = vread(buf, 16 * t4 + 8 + tr_row, cb);
+          const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int u = 0; u < QS; ++u) o[u][cb] = Op::mma(av, pb[u][t4], o[u][cb]);
+        }
       }
     }
 
@@ -282,30 +343,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
     __syncthreads();
   }
 
-  const float ltot = lanes_sum(lsum);
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  if (qvalid) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_sn;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+  for (int u = 0; u < QS; ++u) {
+    const float ltot = lanes_sum(lsum[u]);
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    if (qvalid[u]) {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + b * a.o_sb + h * a.o_sh + (int64_t)qi[u] * a.o_sn;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = cb * 32 + g * 8 + half * 4;
-        u32x2_t w;
-        w[0] = Op::pack(o[cb][4 * g + 0] * inv, o[cb][4 * g + 1] * inv);
-        w[1] = Op::pack(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + c) = w;
-      }
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = cb * 32 + g * 8 + half * 4;
+          u32x2_t w;
+          w[0] = Op::pack(o[u][cb][4 * g + 0] * inv, o[u][cb][4 * g + 1] * inv);
+          w[1] = Op::pack(o[u][cb][4 * g + 2] * inv, o[u][cb][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + c) = w;
+        }
+    }
   }
 }
 
-template <class Op, int NW>
+template <class Op, int NW, int QS>
 hipError_t launch(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const int nqb = (a.Nq + NW * 32 - 1) / (NW * 32);
+  constexpr int QB = NW * 32 * QS;
+  const int nqb = (a.Nq + QB - 1) / QB;
   const int64_t blocks = (int64_t)nqb * a.H * a.B;
   if (blocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((attn_mfma_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0, t1,
-                        0, a, nqb);
+  hipExtLaunchKernelGGL((attn_mfma_kernel<Op, NW, QS>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0,
+                        t1, 0, a, nqb);
   return hipGetLastError();
 }
 
@@ -316,8 +381,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hip
   // so the grid has many workgroups; long ones use 4 waves to share each
   // staged K/V tile among 128 queries.
   const bool longq = a.Nq > 64;
-  if (dt == DType::BF16) return longq ? launch<BF16, 4>(a, stream, t0, t1) : launch<BF16, 2>(a, stream, t0, t1);
-  return longq ? launch<F16, 4>(a, stream, t0, t1) : launch<F16, 2>(a, stream, t0, t1);
+  if (dt == DType::BF16)
+    return longq ? launch<BF16, 4, 2>(a, stream, t0, t1) : launch<BF16, 2, 1>(a, stream, t0, t1);
+  return longq ? launch<F16, 4, 2>(a, stream, t0, t1) : launch<F16, 2, 1>(a, stream, t0, t1);
 }
 
 }  // namespace mha

@@ -9,10 +9,16 @@
 //
 // Up to three independent problems (Q, K and V) share one launch: the grid is
 // the concatenation of their tile grids.  A workgroup of four waves computes a
-// 64 (rows of X) x 128 (rows of W) tile; each wave a 32 x 64 sub-tile as two
+// 64 (rows of X) x TN (rows of W) tile; each wave a 32 x TN/2 sub-tile as
 // 32x32 MFMA blocks of C^T = W X^T, so that a lane ends up with four
 // consecutive output features of one row and stores them as one 8-byte write.
-// K advances 64 at a time through double-buffered LDS tiles.
+//
+// Latency hiding: K advances 64 at a time through two LDS buffers, and global
+// loads run two steps ahead in two register sets, so each load has two steps of
+// MFMA work to arrive.  Loads are buffer loads whose range check returns zeros
+// past the tile's last valid row, so they need no branches.  Tiles are ordered
+// so that the workgroups of one XCD (block id mod 8) take consecutive tiles,
+// which share rows of X in that XCD's L2.
 #include "mha_internal.h"
 
 namespace mha {
@@ -27,10 +33,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kTM = 64;    // rows of X per tile
-constexpr int kTN = 128;   // rows of W (output features) per tile
 constexpr int kBK = 64;    // contraction step
 constexpr int kLS = 72;    // LDS row stride (elements): 144 B -> conflict-free 16 B reads
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
+constexpr int kDeadOffset = (int)0x80000000u;     // beyond any range check: loads return zeros
 
 struct BF16 {
   __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -57,110 +65,153 @@ struct F16 {
 };
 
 struct TileMap {
-  int start[kMaxGemmProblems + 1];  // first workgroup of each problem
+  int start[kMaxGemmProblems + 1];  // first tile of each problem
   int tiles_n[kMaxGemmProblems];    // tiles along N of each problem
+  int total;
 };
 
-template <class Op>
-__global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
+// Buffer resource over `bytes` bytes from `base` (clamped to the 32-bit range
+// check); loads at or beyond `bytes` return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kBufferWord3);
+}
+
+template <class Op, int TN>
+__global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
+  constexpr int NB = TN / 64;                 // 32-wide MFMA blocks per wave along N
+  constexpr int XC = kTM * 8 / kThreads;      // 16-byte X chunks per thread per step (2)
+  constexpr int WC = TN * 8 / kThreads;       // 16-byte W chunks per thread per step (2 or 4)
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTM * kLS];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kTN * kLS];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][TN * kLS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int bid = blockIdx.x;
-  // Select this workgroup's problem with unrolled compares (a runtime index
-  // into the kernel-argument array would be lowered through scratch memory).
+
+  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a
+  // contiguous range of tiles (tiles of one row band are adjacent).
+  const int T = tm.total, q = T / kXcds, rem = T % kXcds;
+  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int tile = x * q + min(x, rem) + j;
+
+  // Select this tile's problem with unrolled compares (a runtime index into the
+  // kernel-argument array would be lowered through scratch memory).
   GemmProblem P = g.p[0];
   int start = 0, tiles_n = tm.tiles_n[0];
 #pragma unroll
   for (int i = 1; i < kMaxGemmProblems; ++i)
-    if (i < g.count && bid >= tm.start[i]) {
+    if (i < g.count && tile >= tm.start[i]) {
       P = g.p[i];
       start = tm.start[i];
       tiles_n = tm.tiles_n[i];
     }
-  const int local = bid - start;
+  const int local = tile - start;
   const int m0 = (local / tiles_n) * kTM;
-  const int n0 = (local % tiles_n) * kTN;
-
-  const uint16_t* X = static_cast<const uint16_t*>(P.x);
-  const uint16_t* W = static_cast<const uint16_t*>(P.w);
+  const int n0 = (local % tiles_n) * TN;
   const int M = P.M, N = P.N, K = P.K;
 
-  // Staging: X tile 64 x 64 -> 512 chunks of 8 elements (2 per thread);
-  // W tile 128 x 64 -> 1024 chunks (4 per thread).
-  u32x4_t xr[2], wr[4];
-  auto load = [&](int k0) {
+  // The tile's rows of X and W as range-checked buffers: rows past M (or N)
+  // read as zeros.
+  const uint16_t* X = static_cast<const uint16_t*>(P.x) + (int64_t)m0 * P.ldx;
+  const uint16_t* W = static_cast<const uint16_t*>(P.w) + (int64_t)n0 * K;
+  const int xrows = min(kTM, M - m0), wrows = min(TN, N - n0);
+  const __amdgpu_buffer_rsrc_t xr_src = make_rsrc(X, ((int64_t)(xrows - 1) * P.ldx + K) * 2);
+  const __amdgpu_buffer_rsrc_t wr_src = make_rsrc(W, ((int64_t)(wrows - 1) * K + K) * 2);
+
+  int xoff[XC], woff[WC];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-      const int m = m0 + row, k = k0 + ch * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (m < M && k < K) v = *reinterpret_cast<const u32x4_t*>(X + (int64_t)m * P.ldx + k);
-      xr[c] = v;
-    }
+  for (int c = 0; c < XC; ++c) {
+    const int idx = tid + c * kThreads;
+    xoff[c] = ((idx >> 3) * (int)P.ldx + (idx & 7) * 8) * 2;
+  }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-      const int n = n0 + row, k = k0 + ch * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (n < N && k < K) v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)n * K + k);
-      wr[c] = v;
-    }
+  for (int c = 0; c < WC; ++c) {
+    const int idx = tid + c * kThreads;
+    woff[c] = ((idx >> 3) * K + (idx & 7) * 8) * 2;
+  }
+
+  // Steps at or past K load from an offset that fails the range check (zeros,
+  // no memory access), so the loads are unconditional and never branch.
+  auto load = [&](int k0, u32x4_t (&xr)[XC], u32x4_t (&wr)[WC]) {
+    const bool live = k0 < K;
+#pragma unroll
+    for (int c = 0; c < XC; ++c)
+      xr[c] = __builtin_amdgcn_raw_buffer_load_b128(xr_src, live ? xoff[c] + k0 * 2 : kDeadOffset, 0, 0);
+#pragma unroll
+    for (int c = 0; c < WC; ++c)
+      wr[c] = __builtin_amdgcn_raw_buffer_load_b128(wr_src, live ? woff[c] + k0 * 2 : kDeadOffset, 0, 0);
   };
-  auto store = [&](int buf) {
+  // Chunks past K (only in the last step when K is not a multiple of 64) would
+  // read the next row, so they are stored as zeros.
+  auto store = [&](int buf, int k0, const u32x4_t (&xr)[XC], const u32x4_t (&wr)[WC]) {
+    const bool tail = k0 + kBK > K;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < XC; ++c) {
       const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4_t*>(&xs[buf][row * kLS + ch * 8]) = xr[c];
+      const bool ok = !tail || k0 + ch * 8 < K;
+      *reinterpret_cast<u32x4_t*>(&xs[buf][row * kLS + ch * 8]) = ok ? xr[c] : zero;
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < WC; ++c) {
       const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4_t*>(&ws[buf][row * kLS + ch * 8]) = wr[c];
+      const bool ok = !tail || k0 + ch * 8 < K;
+      *reinterpret_cast<u32x4_t*>(&ws[buf][row * kLS + ch * 8]) = ok ? wr[c] : zero;
     }
   };
 
-  // Wave (wm, wn): rows [32wm, 32wm+32) of the X tile, features [64wn, 64wn+64).
+  // Wave (wm, wn): rows [32wm, 32wm+32) of the X tile, features [wn*TN/2, +TN/2).
   const int wm = wave & 1, wn = wave >> 1;
-  f32x16_t acc[2];
+  f32x16_t acc[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
 
-  const int nk = (K + kBK - 1) / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const u32x4_t bx = *reinterpret_cast<const u32x4_t*>(&xs[buf][(wm * 32 + col) * kLS + kk * 16 + half * 8]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const u32x4_t aw = *reinterpret_cast<const u32x4_t*>(
-            &ws[buf][(wn * 64 + nb * 32 + col) * kLS + kk * 16 + half * 8]);
+            &ws[buf][(wn * (TN / 2) + nb * 32 + col) * kLS + kk * 16 + half * 8]);
         acc[nb] = Op::mma(aw, bx, acc[nb]);
       }
     }
-    if (kt + 1 < nk) store(buf ^ 1);
+  };
+
+  const int nk = (K + kBK - 1) / kBK;
+  u32x4_t xa[XC], wa[WC], xb[XC], wb[WC];  // two register sets: steps of even / odd index
+  load(0, xa, wa);
+  load(kBK, xb, wb);
+  store(0, 0, xa, wa);
+  __syncthreads();
+  // Step kt computes LDS buffer kt%2, refills the register set it emptied with
+  // step kt+2, and stores step kt+1 (loaded one step earlier) into the other
+  // buffer.  Unrolled by two so each register set keeps a fixed name.
+  for (int kt = 0; kt < nk; kt += 2) {
+    load((kt + 2) * kBK, xa, wa);
+    compute(0);
+    if (kt + 1 < nk) store(1, (kt + 1) * kBK, xb, wb);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    load((kt + 3) * kBK, xb, wb);
+    compute(1);
+    if (kt + 2 < nk) store(0, (kt + 2) * kBK, xa, wa);
     __syncthreads();
   }
 
-  // acc[nb] register r holds C[m0 + 32wm + col][n0 + 64wn + 32nb + 8(r/4) + 4half + r%4].
+  // acc[nb] register r holds C[m0 + 32wm + col][n0 + wn*TN/2 + 32nb + 8(r/4) + 4half + r%4].
   const int m = m0 + wm * 32 + col;
   if (m >= M) return;
   uint16_t* C = static_cast<uint16_t*>(P.c) + (int64_t)m * P.ldc;
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int n = n0 + wn * 64 + nb * 32 + gq * 8 + half * 4;
+      const int n = n0 + wn * (TN / 2) + nb * 32 + gq * 8 + half * 4;
       if (n >= N) continue;  // N is a multiple of 4, so the 4-run is whole
       float v0 = acc[nb][4 * gq + 0], v1 = acc[nb][4 * gq + 1];
       float v2 = acc[nb][4 * gq + 2], v3 = acc[nb][4 * gq + 3];
@@ -177,25 +228,35 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmBatch g, TileMa
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+template <class Op, int TN>
+hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   TileMap tm{};
   int total = 0;
   for (int i = 0; i < g.count; ++i) {
     const int tmn = (g.p[i].M + kTM - 1) / kTM;
-    const int tnn = (g.p[i].N + kTN - 1) / kTN;
+    const int tnn = (g.p[i].N + TN - 1) / TN;
     tm.start[i] = total;
     tm.tiles_n[i] = tnn > 0 ? tnn : 1;
     total += tmn * tnn;
   }
   for (int i = g.count; i <= kMaxGemmProblems; ++i) tm.start[i] = total;
+  tm.total = total;
   if (total == 0) return hipSuccess;
-  if (dt == DType::BF16)
-    hipExtLaunchKernelGGL(gemm_mfma_kernel<BF16>, dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
-  else
-    hipExtLaunchKernelGGL(gemm_mfma_kernel<F16>, dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
+  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TN>), dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  // 128-wide tiles unless that leaves fewer than two workgroups per CU.
+  int64_t tiles128 = 0;
+  for (int i = 0; i < g.count; ++i)
+    tiles128 += (int64_t)((g.p[i].M + kTM - 1) / kTM) * ((g.p[i].N + 127) / 128);
+  const bool narrow = tiles128 < 512;
+  if (dt == DType::BF16)
+    return narrow ? launch<BF16, 64>(g, stream, t0, t1) : launch<BF16, 128>(g, stream, t0, t1);
+  return narrow ? launch<F16, 64>(g, stream, t0, t1) : launch<F16, 128>(g, stream, t0, t1);
 }
 
 }  // namespace mha

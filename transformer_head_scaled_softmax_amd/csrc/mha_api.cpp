@@ -48,6 +48,7 @@ int check_common(int mask_kind, int Nq, int Nk, int dtype, float scale) {
 }
 
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxBufferBytes = int64_t(1) << 31;
 
 struct ProjLayout {
   size_t q_off, k_off, v_off, o_off, total;
@@ -104,6 +105,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 128 : 64);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+  // The matrix-core kernel addresses one (b, h) slice with 32-bit byte offsets.
+  if (dtype != MHA_F32 && (int64_t(Nk) + 128) * d_k * 2 >= kMaxBufferBytes)
+    return fail(MHA_ERR_UNSUPPORTED, "sequences too long for 32-bit per-head offsets");
 
   mha::AttnArgs a{};
   a.q = q;
@@ -206,6 +210,12 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   const int64_t nqb = (Nq + 63) / 64;
   if (nqb * H * B > kMaxBlocks || int64_t(B) * std::max(Nq, Nk) > (int64_t(1) << 31) / 64)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+  // 32-bit byte offsets: a 128-row tile of x or W, and one head's rows of the
+  // projected Q, K, V (row stride H*d) must each span less than 2^31 bytes.
+  const int64_t hd = int64_t(H) * std::max(d_k, d_v);
+  if (128 * int64_t(std::max<int64_t>(D, hd)) * 2 >= kMaxBufferBytes ||
+      (int64_t(std::max(Nq, Nk)) + 128) * hd * 2 >= kMaxBufferBytes)
+    return fail(MHA_ERR_UNSUPPORTED, "dimensions too large for 32-bit tile offsets");
 
   char* ws = static_cast<char*>(workspace);
   void* Qw = ws + L.q_off;
