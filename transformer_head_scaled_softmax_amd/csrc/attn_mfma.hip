@@ -343,22 +343,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
     __syncthreads();
   }
 
+  // Epilogue through LDS so the output rows leave as whole 128-byte segments:
+  // register (cb, 4g + e) of this lane is feature 32cb + 8g + 4half + e of query
+  // 32u + col.  Each wave stages one 32-query sub-block at a time in its own
+  // quarter of the K buffer (free after the loop's last barrier) and copies it
+  // out 16 bytes per lane.
+  static_assert(NW * 32 * kKS <= 2 * kBN * kKS, "staging does not fit");
+  uint16_t* stage = &ks[0][0] + wave * 32 * kKS;
 #pragma unroll
   for (int u = 0; u < QS; ++u) {
     const float ltot = lanes_sum(lsum[u]);
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-    if (qvalid[u]) {
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + b * a.o_sb + h * a.o_sh + (int64_t)qi[u] * a.o_sn;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = cb * 32 + g * 8 + half * 4;
-          u32x2_t w;
-          w[0] = Op::pack(o[u][cb][4 * g + 0] * inv, o[u][cb][4 * g + 1] * inv);
-          w[1] = Op::pack(o[u][cb][4 * g + 2] * inv, o[u][cb][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2_t*>(orow + c) = w;
-        }
+      for (int g = 0; g < 4; ++g) {
+        u32x2_t w;
+        w[0] = Op::pack(o[u][cb][4 * g + 0] * inv, o[u][cb][4 * g + 1] * inv);
+        w[1] = Op::pack(o[u][cb][4 * g + 2] * inv, o[u][cb][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(&stage[col * kKS + cb * 32 + g * 8 + half * 4]) = w;
+      }
+    uint16_t* obase = static_cast<uint16_t*>(a.out) + b * a.o_sb + h * a.o_sh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = lane + 64 * i, row = id >> 3, ch = id & 7;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage[row * kKS + ch * 8]);
+      const int q = qw0 + 32 * u + row;
+      if (q < a.Nq) *reinterpret_cast<u32x4_t*>(obase + (int64_t)q * a.o_sn + ch * 8) = v;
     }
   }
 }

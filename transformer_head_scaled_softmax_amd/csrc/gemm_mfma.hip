@@ -8,10 +8,12 @@
 // Accumulation is fp32; C is rounded to nearest-even into the input type.
 //
 // Up to three independent problems (Q, K and V) share one launch: the grid is
-// the concatenation of their tile grids.  A workgroup of four waves computes a
-// 64 (rows of X) x TN (rows of W) tile; each wave a 32 x TN/2 sub-tile as
-// 32x32 MFMA blocks of C^T = W X^T, so that a lane ends up with four
-// consecutive output features of one row and stores them as one 8-byte write.
+// the concatenation of their tile grids.  A workgroup of four waves (2 x 2)
+// computes a TM (rows of X) x TN (rows of W) tile, 128 x 128 when the problem
+// has enough tiles to fill the chip; each wave holds a (TM/2) x (TN/2)
+// sub-tile as 32x32 MFMA blocks of C^T = W X^T, so a lane ends up with four
+// consecutive output features of one row (one 8-byte store), and each operand
+// read from LDS feeds two MFMAs.
 //
 // Latency hiding: K advances 64 at a time through two LDS buffers, and global
 // loads run two steps ahead in two register sets, so each load has two steps of
@@ -32,7 +34,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kTM = 64;    // rows of X per tile
 constexpr int kBK = 64;    // contraction step
 constexpr int kLS = 72;    // LDS row stride (elements): 144 B -> conflict-free 16 B reads
 constexpr int kThreads = 256;
@@ -77,12 +78,14 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kBufferWord3);
 }
 
-template <class Op, int TN>
+template <class Op, int TM, int TN>
 __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
-  constexpr int NB = TN / 64;                 // 32-wide MFMA blocks per wave along N
-  constexpr int XC = kTM * 8 / kThreads;      // 16-byte X chunks per thread per step (2)
-  constexpr int WC = TN * 8 / kThreads;       // 16-byte W chunks per thread per step (2 or 4)
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kTM * kLS];
+  constexpr int WM = TM / 2, WN = TN / 2;  // wave tile: rows of X x rows of W
+  constexpr int MB = WM / 32, NB = WN / 32;  // 32x32 MFMA blocks per wave
+  constexpr int XC = TM * 8 / kThreads;      // 16-byte X chunks per thread per step
+  constexpr int WC = TN * 8 / kThreads;      // 16-byte W chunks per thread per step
+  static_assert(MB >= 1 && NB >= 1 && XC >= 1 && WC >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kLS];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][TN * kLS];
 
   const int tid = threadIdx.x;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
       tiles_n = tm.tiles_n[i];
     }
   const int local = tile - start;
-  const int m0 = (local / tiles_n) * kTM;
+  const int m0 = (local / tiles_n) * TM;
   const int n0 = (local % tiles_n) * TN;
   const int M = P.M, N = P.N, K = P.K;
 
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
   // read as zeros.
   const uint16_t* X = static_cast<const uint16_t*>(P.x) + (int64_t)m0 * P.ldx;
   const uint16_t* W = static_cast<const uint16_t*>(P.w) + (int64_t)n0 * K;
-  const int xrows = min(kTM, M - m0), wrows = min(TN, N - n0);
+  const int xrows = min(TM, M - m0), wrows = min(TN, N - n0);
   const __amdgpu_buffer_rsrc_t xr_src = make_rsrc(X, ((int64_t)(xrows - 1) * P.ldx + K) * 2);
   const __amdgpu_buffer_rsrc_t wr_src = make_rsrc(W, ((int64_t)(wrows - 1) * K + K) * 2);
 
@@ -160,24 +163,31 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
     }
   };
 
-  // Wave (wm, wn): rows [32wm, 32wm+32) of the X tile, features [wn*TN/2, +TN/2).
+  // Wave (wm, wn): rows [wm*WM, +WM) of the X tile, features [wn*WN, +WN).
   const int wm = wave & 1, wn = wave >> 1;
-  f32x16_t acc[NB];
+  f32x16_t acc[MB][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
+  // Each k16 step reads MB X operands and NB W operands and issues MB*NB MFMAs.
   auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const u32x4_t bx = *reinterpret_cast<const u32x4_t*>(&xs[buf][(wm * 32 + col) * kLS + kk * 16 + half * 8]);
+      u32x4_t bx[MB], aw[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const u32x4_t aw = *reinterpret_cast<const u32x4_t*>(
-            &ws[buf][(wn * (TN / 2) + nb * 32 + col) * kLS + kk * 16 + half * 8]);
-        acc[nb] = Op::mma(aw, bx, acc[nb]);
-      }
+      for (int mb = 0; mb < MB; ++mb)
+        bx[mb] = *reinterpret_cast<const u32x4_t*>(&xs[buf][(wm * WM + mb * 32 + col) * kLS + kk * 16 + half * 8]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        aw[nb] = *reinterpret_cast<const u32x4_t*>(&ws[buf][(wn * WN + nb * 32 + col) * kLS + kk * 16 + half * 8]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Op::mma(aw[nb], bx[mb], acc[mb][nb]);
     }
   };
 
@@ -202,38 +212,55 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
     __syncthreads();
   }
 
-  // acc[nb] register r holds C[m0 + 32wm + col][n0 + wn*TN/2 + 32nb + 8(r/4) + 4half + r%4].
-  const int m = m0 + wm * 32 + col;
-  if (m >= M) return;
-  uint16_t* C = static_cast<uint16_t*>(P.c) + (int64_t)m * P.ldc;
+  // Epilogue through LDS, so global stores are whole 128-byte row segments:
+  // acc[mb][nb] register r holds C[m0 + wm*WM + 32mb + col][n0 + wn*WN + 32nb +
+  // 8(r/4) + 4half + r%4]; each wave writes its WM x WN sub-tile (bias added,
+  // rounded) row-major into its own slice of the X staging buffer, then copies
+  // it out 16 bytes per lane.  The main loop ended with a barrier, so the
+  // staging buffer is free.
+  constexpr int SS = WN + 8;  // staging row stride (elements)
+  static_assert(4 * WM * SS <= 2 * TM * kLS, "staging does not fit");
+  uint16_t* stage = &xs[0][0] + wave * WM * SS;
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int n = n0 + wn * (TN / 2) + nb * 32 + gq * 8 + half * 4;
-      if (n >= N) continue;  // N is a multiple of 4, so the 4-run is whole
-      float v0 = acc[nb][4 * gq + 0], v1 = acc[nb][4 * gq + 1];
-      float v2 = acc[nb][4 * gq + 2], v3 = acc[nb][4 * gq + 3];
-      if (bias) {
-        v0 += Op::to_float(bias[n + 0]);
-        v1 += Op::to_float(bias[n + 1]);
-        v2 += Op::to_float(bias[n + 2]);
-        v3 += Op::to_float(bias[n + 3]);
+      const int cl = nb * 32 + gq * 8 + half * 4;  // column within the wave tile
+      const int n = n0 + wn * WN + cl;
+      float b0 = 0.0f, b1 = 0.0f, b2 = 0.0f, b3 = 0.0f;
+      if (bias && n < N) {  // N is a multiple of 4, so the 4-run is whole
+        b0 = Op::to_float(bias[n + 0]);
+        b1 = Op::to_float(bias[n + 1]);
+        b2 = Op::to_float(bias[n + 2]);
+        b3 = Op::to_float(bias[n + 3]);
       }
-      u32x2_t w;
-      w[0] = Op::pack(v0, v1);
-      w[1] = Op::pack(v2, v3);
-      *reinterpret_cast<u32x2_t*>(C + n) = w;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        u32x2_t w;
+        w[0] = Op::pack(acc[mb][nb][4 * gq + 0] + b0, acc[mb][nb][4 * gq + 1] + b1);
+        w[1] = Op::pack(acc[mb][nb][4 * gq + 2] + b2, acc[mb][nb][4 * gq + 3] + b3);
+        *reinterpret_cast<u32x2_t*>(&stage[(mb * 32 + col) * SS + cl]) = w;
+      }
     }
+  __syncthreads();
+  constexpr int CPR = WN / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int i = 0; i < WM * CPR / 64; ++i) {
+    const int id = lane + 64 * i, row = id / CPR, ch = id % CPR;
+    const int m = m0 + wm * WM + row, n = n0 + wn * WN + ch * 8;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage[row * SS + ch * 8]);
+    if (m < M && n < N)  // N is a multiple of 8, so the 8-run is whole
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(P.c) + (int64_t)m * P.ldc + n) = v;
+  }
 }
 
-template <class Op, int TN>
+template <class Op, int TM, int TN>
 hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   TileMap tm{};
   int total = 0;
   for (int i = 0; i < g.count; ++i) {
-    const int tmn = (g.p[i].M + kTM - 1) / kTM;
+    const int tmn = (g.p[i].M + TM - 1) / TM;
     const int tnn = (g.p[i].N + TN - 1) / TN;
     tm.start[i] = total;
     tm.tiles_n[i] = tnn > 0 ? tnn : 1;
@@ -242,21 +269,28 @@ hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEven
   for (int i = g.count; i <= kMaxGemmProblems; ++i) tm.start[i] = total;
   tm.total = total;
   if (total == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TN>), dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
+  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TM, TN>), dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
   return hipGetLastError();
+}
+
+int64_t count_tiles(const GemmBatch& g, int tm, int tn) {
+  int64_t n = 0;
+  for (int i = 0; i < g.count; ++i) n += (int64_t)((g.p[i].M + tm - 1) / tm) * ((g.p[i].N + tn - 1) / tn);
+  return n;
+}
+
+template <class Op>
+hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  // The largest tile that still gives every CU a workgroup.
+  if (count_tiles(g, 128, 128) >= 256) return launch<Op, 128, 128>(g, stream, t0, t1);
+  if (count_tiles(g, 128, 64) >= 256) return launch<Op, 128, 64>(g, stream, t0, t1);
+  return launch<Op, 64, 64>(g, stream, t0, t1);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  // 128-wide tiles unless that leaves fewer than two workgroups per CU.
-  int64_t tiles128 = 0;
-  for (int i = 0; i < g.count; ++i)
-    tiles128 += (int64_t)((g.p[i].M + kTM - 1) / kTM) * ((g.p[i].N + 127) / 128);
-  const bool narrow = tiles128 < 512;
-  if (dt == DType::BF16)
-    return narrow ? launch<BF16, 64>(g, stream, t0, t1) : launch<BF16, 128>(g, stream, t0, t1);
-  return narrow ? launch<F16, 64>(g, stream, t0, t1) : launch<F16, 128>(g, stream, t0, t1);
+  return dt == DType::BF16 ? launch_sized<BF16>(g, stream, t0, t1) : launch_sized<F16>(g, stream, t0, t1);
 }
 
 }  // namespace mha
