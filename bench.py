@@ -37,10 +37,13 @@ PEAK_HBM_GBPS = 8000.0
 ES = {"bf16": 2, "f16": 2, "f32": 4}
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 CSRC = ROOT / "transformer_head_scaled_softmax_amd" / "csrc"
-KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip"], "attention": ["attn_mfma.hip"],
-                  "out_projection": ["gemm_mfma.hip"], "attention_f32": ["attn_f32.hip"]}
+KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip", "mfma_util.h"],
+                  "attention": ["attn_mfma.hip", "mfma_util.h"],
+                  "qkv_attention": ["proj_attn.hip", "mfma_util.h"],
+                  "out_projection": ["gemm_mfma.hip", "mfma_util.h"], "attention_f32": ["attn_f32.hip"]}
 KERNEL_SYMBOLS = {"qkv_projection": "gemm_mfma_kernel", "attention": "attn_mfma_kernel",
-                  "out_projection": "gemm_mfma_kernel", "attention_f32": "attn_f32_kernel"}
+                  "qkv_attention": "proj_attn_kernel", "out_projection": "gemm_mfma_kernel",
+                  "attention_f32": "attn_f32_kernel"}
 
 
 def log(*a):
@@ -89,15 +92,20 @@ def proj_path_bytes(w, lens):
 
 
 def stage_work(w, lens):
-    """(flops, bytes) per launch of each kernel of the projection path."""
+    """(flops, bytes) per launch of each kernel of the projection path: the
+    unfused plan's three kernels and the fused plan's projection+attention
+    kernel (whose bytes are x, the three input weights, the head outputs it
+    writes and the key lengths)."""
     es = ES[w.dtype]
     D, HD = w.D, w.H * w.d
     qkv_f, out_f = projection_flops(w)
     x_bytes = (w.B * w.Nq * D + (w.B * w.Nk * D if w.cross else 0)) * es
     qkv_b = x_bytes + 3 * HD * D * es + (w.B * w.Nq * HD + 2 * w.B * w.Nk * HD) * es
     out_b = (w.B * w.Nq * HD + D * HD + w.B * w.Nq * D) * es
+    fused_b = x_bytes + 3 * HD * D * es + w.B * w.Nq * HD * es + (0 if lens is None else 4 * w.B)
     return {"qkv_projection": (qkv_f, qkv_b),
             "attention": (attention_flops(w, lens), attention_bytes(w, lens)),
+            "qkv_attention": (qkv_f + attention_flops(w, lens), fused_b),
             "out_projection": (out_f, out_b)}
 
 
@@ -288,7 +296,12 @@ def main():
                   else lib.mha_proj_forward_timed(*argsv, events))
             if st != 0:
                 raise RuntimeError(lib.mha_last_error().decode())
-        stage_names = ["qkv_projection", "attention", "out_projection"]
+        # Kernel -> (start, end) event indices of mha_proj_forward_timed.
+        if lib.mha_proj_fused(w.B, w.Nq, w.Nk, w.D, w.d, w.d, 0 if w.cross else 1):
+            stage_events = {"qkv_attention": (0, 1), "out_projection": (4, 5)}
+        else:
+            stage_events = {"qkv_projection": (0, 1), "attention": (2, 3), "out_projection": (4, 5)}
+        n_events = 6
     else:
         def step(i, sp, events=None):
             d = dev_sets[i % nsets]
@@ -298,7 +311,8 @@ def main():
             st = lib.mha_forward(*argsv) if events is None else lib.mha_forward_timed(*argsv, events)
             if st != 0:
                 raise RuntimeError(lib.mha_last_error().decode())
-        stage_names = ["attention_f32" if w.dtype == "f32" else "attention"]
+        stage_events = {("attention_f32" if w.dtype == "f32" else "attention"): (0, 1)}
+        n_events = 2
 
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -349,19 +363,18 @@ def main():
     # Timed region 2 (per-kernel times): the same K steps issued directly on the
     # stream through the timed entry points, whose events take each kernel's own
     # start and end timestamps from its dispatch (hipExtLaunchKernel).
-    nst = len(stage_names)
-    ev_arrays = [(ctypes.c_void_p * (2 * nst))(*[hip.event() for _ in range(2 * nst)])
+    ev_arrays = [(ctypes.c_void_p * n_events)(*[hip.event() for _ in range(n_events)])
                  for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
         step(args.warmup + i, sp, ev_arrays[i])
     torch.cuda.synchronize()
-    per = {n_: [] for n_ in stage_names}
+    per = {n_: [] for n_ in stage_events}
     for evs in ev_arrays:
-        for k_, n_ in enumerate(stage_names):
-            per[n_].append(hip.elapsed_ms(evs[2 * k_], evs[2 * k_ + 1]))
+        for n_, (a_, b_) in stage_events.items():
+            per[n_].append(hip.elapsed_ms(evs[a_], evs[b_]))
     avg = {n_: float(np.mean(v)) for n_, v in per.items()}
-    eager_ms_step = hip.elapsed_ms(ev_arrays[0][0], ev_arrays[-1][2 * nst - 1]) / K
+    eager_ms_step = hip.elapsed_ms(ev_arrays[0][0], ev_arrays[-1][n_events - 1]) / K
 
     used = [lens_list[(args.warmup + i) % nsets] for i in range(K)]
     att_f = float(np.mean([attention_flops(w, L) for L in used]))
@@ -396,9 +409,9 @@ def main():
     dom = max(avg, key=avg.get)
     if w.proj:
         f_, b_ = stage_work(w, None)[dom]
-        if dom == "attention":
-            f_ = att_f
-            b_ = float(np.mean([attention_bytes(w, L) for L in used]))
+        if dom in ("attention", "qkv_attention"):  # these depend on the drawn key lengths
+            f_ = float(np.mean([stage_work(w, L)[dom][0] for L in used]))
+            b_ = float(np.mean([stage_work(w, L)[dom][1] for L in used]))
     else:
         f_, b_ = flops, bytes_
     result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom, w.name)

@@ -113,8 +113,9 @@ size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, in
  *
  * Supported: MHA_BF16 and MHA_F16 with d_k == d_v == 64, D a multiple of 8,
  * all tensors 16-byte aligned.  The projected Q, K, V and the head outputs are
- * rounded to the input type in the workspace.  Returns MHA_OK or a negative
- * status.
+ * rounded to the input type (in the workspace, or in on-chip memory when the
+ * call is fused -- see mha_proj_fused; the results are the same).  Returns
+ * MHA_OK or a negative status.
  */
 int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
                      const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
@@ -132,7 +133,10 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
  *
  * mha_forward_timed: 2 events -- the attention kernel.
  * mha_proj_forward_timed: 6 events -- the Q/K/V projection, the attention
- * kernel and the output projection, in that order.
+ * kernel and the output projection, in that order.  A fused call (see
+ * mha_proj_fused) launches two kernels: events[0..1] time the fused
+ * projection+attention kernel, events[4..5] the output projection, and
+ * events[2..3] are left untouched.
  */
 int mha_forward_timed(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
                       int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
@@ -144,6 +148,17 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
                            float scale, int dtype, void* workspace, size_t workspace_bytes,
                            void* stream, void* const* events);
+
+/*
+ * mha_proj_fused -- 1 if mha_proj_forward with these sizes runs as two
+ * kernels (the Q/K/V projections fused with attention, then the output
+ * projection), 0 if it runs as three (projections, attention, output
+ * projection).  self_attention: nonzero when x_kv is NULL or equal to x_q.
+ * The fused form applies to self-attention with Nq == Nk <= 128, D a
+ * multiple of 64 and d_k == d_v == 64 (bf16 or f16).  Pure function of its
+ * arguments; no device access.
+ */
+int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention);
 
 /* Static description of a status code; never NULL. */
 const char* mha_status_string(int status);

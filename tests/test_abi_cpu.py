@@ -147,6 +147,20 @@ def test_proj_empty_is_ok(lib):
     assert proj(lib, Nq=0, x_kv=P) == mb.OK
 
 
+@pytest.mark.parametrize("args,fused", [
+    ((64, 64, 64, 512, 64, 64, 1), 1),     # sentence-length self-attention
+    ((3, 128, 128, 64, 64, 64, 1), 1),     # longest fused sequence
+    ((3, 129, 129, 64, 64, 64, 1), 0),     # too long for one tile
+    ((32, 64, 80, 1024, 64, 64, 0), 0),    # cross-attention
+    ((32, 64, 64, 1024, 64, 64, 0), 0),    # x_kv distinct from x_q
+    ((2, 64, 64, 200, 64, 64, 1), 0),      # D not a multiple of 64
+    ((2, 64, 64, 512, 32, 32, 1), 0),      # head size other than 64
+    ((2, 64, 32, 512, 64, 64, 1), 0),      # Nq != Nk
+])
+def test_proj_fused_plan(lib, args, fused):
+    assert lib.mha_proj_fused(*args) == fused
+
+
 def test_last_error_is_per_thread(lib):
     import threading
     assert fwd(lib, B=-1) == mb.ERR_INVALID_ARG

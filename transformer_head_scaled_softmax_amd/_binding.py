@@ -24,7 +24,7 @@ ERR_HIP = -4
 
 # Every symbol include/mha.h declares.
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
-           "mha_proj_forward_timed", "mha_status_string", "mha_last_error", "mha_version")
+           "mha_proj_forward_timed", "mha_proj_fused", "mha_status_string", "mha_last_error", "mha_version")
 
 
 class MhaError(RuntimeError):
@@ -56,6 +56,8 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_proj_forward.restype = i
     lib.mha_proj_forward_timed.argtypes = lib.mha_proj_forward.argtypes + [vp]
     lib.mha_proj_forward_timed.restype = i
+    lib.mha_proj_fused.argtypes = [i] * 7
+    lib.mha_proj_fused.restype = i
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_last_error.argtypes = []

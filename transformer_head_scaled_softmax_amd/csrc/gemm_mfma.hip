@@ -8,19 +8,26 @@
 // Accumulation is fp32; C is rounded to nearest-even into the input type.
 //
 // Up to three independent problems (Q, K and V) share one launch: the grid is
-// the concatenation of their tile grids.  A workgroup of four waves (2 x 2)
-// computes a TM (rows of X) x TN (rows of W) tile, 128 x 128 when the problem
-// has enough tiles to fill the chip; each wave holds a (TM/2) x (TN/2)
-// sub-tile as 32x32 MFMA blocks of C^T = W X^T, so a lane ends up with four
-// consecutive output features of one row (one 8-byte store), and each operand
-// read from LDS feeds two MFMAs.
+// the concatenation of their tile grids.  A workgroup computes a TM (rows of X)
+// x TN (rows of W) tile; its waves form a WGM x WGN grid and each holds a
+// (TM/WGM) x (TN/WGN) sub-tile as 32x32 MFMA blocks of C^T = W X^T, so a lane
+// ends up with four consecutive output features of one row.
 //
-// Latency hiding: K advances 64 at a time through two LDS buffers, and global
-// loads run two steps ahead in two register sets, so each load has two steps of
-// MFMA work to arrive.  Loads are buffer loads whose range check returns zeros
-// past the tile's last valid row, so they need no branches.  Tiles are ordered
-// so that the workgroups of one XCD (block id mod 8) take consecutive tiles,
-// which share rows of X in that XCD's L2.
+// Operand staging: K advances 64 at a time through S stages of LDS that are
+// filled by LDS-direct buffer loads (each lane's 16 bytes go straight from
+// memory into LDS, with no register round trip), issued S-1 steps ahead.  A
+// step's wait is an explicit vmcnt that lets the later stages stay in flight,
+// followed by one barrier.  A 64-element row of a stage is 128 bytes of eight
+// 16-byte chunks; chunk c of row r sits in slot c ^ (r & 7) ^ ((r >> 3) & 1),
+// which keeps the MFMA operand reads (16 bytes per lane, 32 consecutive rows)
+// free of bank conflicts; the loads place chunks by choosing, for each lane's
+// fixed LDS slot, the global chunk that belongs there.
+//
+// The buffer range check returns zeros past a tile's last valid row, so edge
+// tiles need no branches (rows past M or N only feed outputs that are never
+// stored).  Tiles are ordered so that the workgroups of one XCD (block id mod
+// 8) take consecutive tiles, which share rows of X in that XCD's L2.  The tile
+// shape is chosen per launch from the problem sizes (see choose_config).
 #include "mha_internal.h"
 
 namespace mha {
@@ -34,12 +41,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;    // contraction step
-constexpr int kLS = 72;    // LDS row stride (elements): 144 B -> conflict-free 16 B reads
-constexpr int kThreads = 256;
+constexpr int kBK = 64;  // contraction step (one 128-byte row per operand row)
 constexpr int kXcds = 8;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
-constexpr int kDeadOffset = (int)0x80000000u;     // beyond any range check: loads return zeros
+
+#define MHA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 struct BF16 {
   __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -78,18 +84,40 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t byt
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kBufferWord3);
 }
 
-template <class Op, int TM, int TN>
-__global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
-  constexpr int WM = TM / 2, WN = TN / 2;  // wave tile: rows of X x rows of W
-  constexpr int MB = WM / 32, NB = WN / 32;  // 32x32 MFMA blocks per wave
-  constexpr int XC = TM * 8 / kThreads;      // 16-byte X chunks per thread per step
-  constexpr int WC = TN * 8 / kThreads;      // 16-byte W chunks per thread per step
-  static_assert(MB >= 1 && NB >= 1 && XC >= 1 && WC >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kLS];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][TN * kLS];
+// s_waitcnt with the vector-memory count set to N and the other counters left
+// unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Barrier without the memory fence of __syncthreads (whose release semantics
+// would wait for every load in flight, including the later stages); the empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ inline void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
+  constexpr int NW = WGM * WGN, NT = 64 * NW;
+  constexpr int WM = TM / WGM, WN = TN / WGN;  // wave tile: rows of X x rows of W
+  constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA blocks per wave
+  constexpr int ROWS = TM + TN;                // operand rows per stage (X, then W)
+  constexpr int STAGE = ROWS * kBK;            // elements per stage
+  constexpr int LPW = ROWS / 8 / NW;           // 1 KiB loads per wave per stage
+  static_assert(MB >= 1 && NB >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave tile");
+  static_assert((ROWS / 8) % NW == 0 && NW % 2 == 0, "loads must split evenly over an even wave count");
+  static_assert(S >= 2 && (S - 1) * LPW < 64, "too many loads in flight");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[S * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  // The wave index as a scalar: it selects buffer resources and LDS addresses.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
 
   // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a
   // contiguous range of tiles (tiles of one row band are adjacent).
@@ -112,59 +140,52 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
   const int m0 = (local / tiles_n) * TM;
   const int n0 = (local % tiles_n) * TN;
   const int M = P.M, N = P.N, K = P.K;
+  const int ldx = (int)P.ldx;
 
-  // The tile's rows of X and W as range-checked buffers: rows past M (or N)
-  // read as zeros.
+  // The tile's rows of X and W as range-checked buffers.
   const uint16_t* X = static_cast<const uint16_t*>(P.x) + (int64_t)m0 * P.ldx;
   const uint16_t* W = static_cast<const uint16_t*>(P.w) + (int64_t)n0 * K;
   const int xrows = min(TM, M - m0), wrows = min(TN, N - n0);
-  const __amdgpu_buffer_rsrc_t xr_src = make_rsrc(X, ((int64_t)(xrows - 1) * P.ldx + K) * 2);
+  const __amdgpu_buffer_rsrc_t xr_src = make_rsrc(X, ((int64_t)(xrows - 1) * ldx + K) * 2);
   const __amdgpu_buffer_rsrc_t wr_src = make_rsrc(W, ((int64_t)(wrows - 1) * K + K) * 2);
 
-  int xoff[XC], woff[WC];
+  // Load i of this wave fills 1 KiB chunk c = wave + NW*i of a stage: rows
+  // 8c .. 8c+7, lane l at row 8c + l/8, slot l%8.  The global chunk for that
+  // slot is slot ^ (row & 7) ^ ((row >> 3) & 1) = (l%8) ^ (l/8) ^ (c & 1), and
+  // c & 1 == wave & 1 because NW is even.
+  const int gchunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  const int lrow = lane >> 3;
+  int goff[LPW];
 #pragma unroll
-  for (int c = 0; c < XC; ++c) {
-    const int idx = tid + c * kThreads;
-    xoff[c] = ((idx >> 3) * (int)P.ldx + (idx & 7) * 8) * 2;
+  for (int i = 0; i < LPW; ++i) {
+    const int row = 8 * (wave + NW * i) + lrow;
+    goff[i] = row < TM ? (row * ldx + gchunk * 8) * 2 : ((row - TM) * K + gchunk * 8) * 2;
   }
+  const int nk = (K + kBK - 1) / kBK;
+  // Issue the loads of step kt into stage kt % S; steps at or past nk (and the
+  // chunks of the last step that lie past K) read nothing, so every step
+  // issues the same number of loads and the vmcnt waits stay exact.
+  auto issue = [&](int kt) {
+    uint16_t* dst = lds + (kt % S) * STAGE;
+    const int k0 = kt * kBK;
+    // Bit 31 set = past every range check.  Arithmetic rather than a select,
+    // so that the compiler cannot split the load into two predicated copies
+    // (which would make the number of loads per step data-dependent).
+    const int dead = (int)((uint32_t)(kt >= nk || k0 + gchunk * 8 >= K) << 31);
 #pragma unroll
-  for (int c = 0; c < WC; ++c) {
-    const int idx = tid + c * kThreads;
-    woff[c] = ((idx >> 3) * K + (idx & 7) * 8) * 2;
-  }
-
-  // Steps at or past K load from an offset that fails the range check (zeros,
-  // no memory access), so the loads are unconditional and never branch.
-  auto load = [&](int k0, u32x4_t (&xr)[XC], u32x4_t (&wr)[WC]) {
-    const bool live = k0 < K;
-#pragma unroll
-    for (int c = 0; c < XC; ++c)
-      xr[c] = __builtin_amdgcn_raw_buffer_load_b128(xr_src, live ? xoff[c] + k0 * 2 : kDeadOffset, 0, 0);
-#pragma unroll
-    for (int c = 0; c < WC; ++c)
-      wr[c] = __builtin_amdgcn_raw_buffer_load_b128(wr_src, live ? woff[c] + k0 * 2 : kDeadOffset, 0, 0);
-  };
-  // Chunks past K (only in the last step when K is not a multiple of 64) would
-  // read the next row, so they are stored as zeros.
-  auto store = [&](int buf, int k0, const u32x4_t (&xr)[XC], const u32x4_t (&wr)[WC]) {
-    const bool tail = k0 + kBK > K;
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int c = 0; c < XC; ++c) {
-      const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-      const bool ok = !tail || k0 + ch * 8 < K;
-      *reinterpret_cast<u32x4_t*>(&xs[buf][row * kLS + ch * 8]) = ok ? xr[c] : zero;
-    }
-#pragma unroll
-    for (int c = 0; c < WC; ++c) {
-      const int idx = tid + c * kThreads, row = idx >> 3, ch = idx & 7;
-      const bool ok = !tail || k0 + ch * 8 < K;
-      *reinterpret_cast<u32x4_t*>(&ws[buf][row * kLS + ch * 8]) = ok ? wr[c] : zero;
+    for (int i = 0; i < LPW; ++i) {
+      const int c = wave + NW * i;  // uniform per wave
+      const int off = (goff[i] + k0 * 2) | dead;
+      uint16_t* d = dst + c * 512;
+      if (c < TM / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr_src, MHA_LDS(d), 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr_src, MHA_LDS(d), 16, off, 0, 0, 0);
     }
   };
 
   // Wave (wm, wn): rows [wm*WM, +WM) of the X tile, features [wn*WN, +WN).
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   f32x16_t acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -173,17 +194,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  // Each k16 step reads MB X operands and NB W operands and issues MB*NB MFMAs.
+  // Operand rows start at multiples of 32, so the swizzle of a lane's row
+  // depends on the lane alone.
+  const int swz = (lane & 7) ^ ((lane >> 3) & 1);
   auto compute = [&](int buf) {
+    const uint16_t* st = lds + buf * STAGE;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int slot = (kk * 2 + half) ^ swz;
       u32x4_t bx[MB], aw[NB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        bx[mb] = *reinterpret_cast<const u32x4_t*>(&xs[buf][(wm * WM + mb * 32 + col) * kLS + kk * 16 + half * 8]);
+        bx[mb] = *reinterpret_cast<const u32x4_t*>(&st[(wm * WM + mb * 32 + col) * kBK + slot * 8]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        aw[nb] = *reinterpret_cast<const u32x4_t*>(&ws[buf][(wn * WN + nb * 32 + col) * kLS + kk * 16 + half * 8]);
+        aw[nb] = *reinterpret_cast<const u32x4_t*>(&st[(TM + wn * WN + nb * 32 + col) * kBK + slot * 8]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -191,36 +216,49 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
     }
   };
 
-  const int nk = (K + kBK - 1) / kBK;
-  u32x4_t xa[XC], wa[WC], xb[XC], wb[WC];  // two register sets: steps of even / odd index
-  load(0, xa, wa);
-  load(kBK, xb, wb);
-  store(0, 0, xa, wa);
-  __syncthreads();
-  // Step kt computes LDS buffer kt%2, refills the register set it emptied with
-  // step kt+2, and stores step kt+1 (loaded one step earlier) into the other
-  // buffer.  Unrolled by two so each register set keeps a fixed name.
-  for (int kt = 0; kt < nk; kt += 2) {
-    load((kt + 2) * kBK, xa, wa);
-    compute(0);
-    if (kt + 1 < nk) store(1, (kt + 1) * kBK, xb, wb);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    load((kt + 3) * kBK, xb, wb);
-    compute(1);
-    if (kt + 2 < nk) store(0, (kt + 2) * kBK, xa, wa);
-    __syncthreads();
+  // Chunks of the last step that lie past K were not loaded; zero them (only
+  // when K is not a multiple of 64).
+  auto zero_tail = [&](int buf) {
+    uint16_t* st = lds + buf * STAGE;
+    const int kvalid = K - (nk - 1) * kBK;  // 8..56, a multiple of 8
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < ROWS * 8; i += NT) {
+      const int row = i >> 3, c = i & 7;
+      if (c * 8 >= kvalid) {
+        const int slot = c ^ (row & 7) ^ ((row >> 3) & 1);
+        *reinterpret_cast<u32x4_t*>(&st[row * kBK + slot * 8]) = zero;
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // This wave's loads of step kt have landed once at most the S-2 later
+    // steps are still in flight; the barrier then publishes every wave's
+    // loads and retires every wave's reads of stage (kt - 1) % S, which the
+    // next issue overwrites.
+    wait_vmcnt<(S - 2) * LPW>();
+    stage_barrier();
+    issue(kt + S - 1);
+    if ((K & (kBK - 1)) && kt == nk - 1) {
+      zero_tail(kt % S);
+      stage_barrier();
+    }
+    compute(kt % S);
   }
 
-  // Epilogue through LDS, so global stores are whole 128-byte row segments:
+  // Epilogue through LDS, so global stores are whole row segments:
   // acc[mb][nb] register r holds C[m0 + wm*WM + 32mb + col][n0 + wn*WN + 32nb +
   // 8(r/4) + 4half + r%4]; each wave writes its WM x WN sub-tile (bias added,
-  // rounded) row-major into its own slice of the X staging buffer, then copies
-  // it out 16 bytes per lane.  The main loop ended with a barrier, so the
-  // staging buffer is free.
+  // rounded) row-major into its own slice of LDS, then copies it out 16 bytes
+  // per lane.  First drain the loads of steps past the end and let every wave
+  // finish its last reads.
+  wait_vmcnt<0>();
+  stage_barrier();
   constexpr int SS = WN + 8;  // staging row stride (elements)
-  static_assert(4 * WM * SS <= 2 * TM * kLS, "staging does not fit");
-  uint16_t* stage = &xs[0][0] + wave * WM * SS;
+  static_assert(NW * WM * SS <= S * STAGE, "staging does not fit");
+  uint16_t* stage = lds + wave * WM * SS;
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -245,6 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
     }
   __syncthreads();
   constexpr int CPR = WN / 8;  // 16-byte chunks per staged row
+  static_assert((WM * CPR) % 64 == 0, "staged tile must split over the lanes");
 #pragma unroll
   for (int i = 0; i < WM * CPR / 64; ++i) {
     const int id = lane + 64 * i, row = id / CPR, ch = id % CPR;
@@ -255,7 +294,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_mfma_kernel(GemmBatch g, Til
   }
 }
 
-template <class Op, int TM, int TN>
+// A tile configuration: TM x TN tile, WGM x WGN waves, S stages, MINB
+// workgroups per CU (what the LDS footprint allows).
+struct Config {
+  int tm, tn, wgm, wgn, s, minb;
+};
+
+template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB>
 hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   TileMap tm{};
   int total = 0;
@@ -269,28 +314,68 @@ hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEven
   for (int i = g.count; i <= kMaxGemmProblems; ++i) tm.start[i] = total;
   tm.total = total;
   if (total == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TM, TN>), dim3(total), dim3(kThreads), 0, stream, t0, t1, 0, g, tm);
+  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TM, TN, WGM, WGN, S, MINB>), dim3(total), dim3(64 * WGM * WGN), 0,
+                        stream, t0, t1, 0, g, tm);
   return hipGetLastError();
 }
 
-int64_t count_tiles(const GemmBatch& g, int tm, int tn) {
-  int64_t n = 0;
-  for (int i = 0; i < g.count; ++i) n += (int64_t)((g.p[i].M + tm - 1) / tm) * ((g.p[i].N + tn - 1) / tn);
-  return n;
-}
+// The instantiated configurations.  LDS per workgroup is S * (TM + TN) * 128
+// bytes; a CU has 160 KiB.
+constexpr Config kConfigs[] = {
+    {128, 256, 2, 2, 3, 1},  // 144 KiB
+    {128, 128, 2, 2, 4, 1},  // 128 KiB
+    {64, 128, 2, 2, 3, 2},   // 72 KiB
+    {64, 64, 2, 2, 4, 2},    // 64 KiB
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 template <class Op>
-hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  // The largest tile that still gives every CU a workgroup.
-  if (count_tiles(g, 128, 128) >= 256) return launch<Op, 128, 128>(g, stream, t0, t1);
-  if (count_tiles(g, 128, 64) >= 256) return launch<Op, 128, 64>(g, stream, t0, t1);
-  return launch<Op, 64, 64>(g, stream, t0, t1);
+hipError_t launch_config(int c, const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  switch (c) {
+    case 0: return launch<Op, 128, 256, 2, 2, 3, 1>(g, stream, t0, t1);
+    case 1: return launch<Op, 128, 128, 2, 2, 4, 1>(g, stream, t0, t1);
+    case 2: return launch<Op, 64, 128, 2, 2, 3, 2>(g, stream, t0, t1);
+    default: return launch<Op, 64, 64, 2, 2, 4, 2>(g, stream, t0, t1);
+  }
+}
+
+// Cost model for picking a configuration: the launch runs in rounds of
+// 256 * MINB workgroups; a workgroup's step costs the larger of its MFMA time
+// (4096 FLOP per clock per CU) and its operand traffic into the CU (about 64
+// bytes per clock), both shared by the workgroups resident on a CU, plus a
+// fixed start-up and epilogue cost.
+int choose_config(const GemmBatch& g) {
+  int best = 0;
+  double best_cost = 0.0;
+  for (int c = 0; c < kNumConfigs; ++c) {
+    const Config& f = kConfigs[c];
+    int64_t tiles = 0;
+    int kmax = 0;
+    for (int i = 0; i < g.count; ++i) {
+      tiles += (int64_t)((g.p[i].M + f.tm - 1) / f.tm) * ((g.p[i].N + f.tn - 1) / f.tn);
+      kmax = g.p[i].K > kmax ? g.p[i].K : kmax;
+    }
+    const int64_t slots = 256LL * f.minb;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double resident = tiles < slots ? (double)tiles / 256.0 : (double)f.minb;
+    const double share = resident > 1.0 ? resident : 1.0;
+    const double mfma = (double)f.tm * f.tn * kBK * 2.0 / 4096.0;
+    const double feed = (double)(f.tm + f.tn) * kBK * 2.0 / 64.0;
+    const double step = (mfma > feed ? mfma : feed) * share;
+    const double cost = (double)rounds * (((kmax + kBK - 1) / kBK) * step + 2000.0 * share);
+    if (c == 0 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  return dt == DType::BF16 ? launch_sized<BF16>(g, stream, t0, t1) : launch_sized<F16>(g, stream, t0, t1);
+  const int c = choose_config(g);
+  return dt == DType::BF16 ? launch_config<BF16>(c, g, stream, t0, t1) : launch_config<F16>(c, g, stream, t0, t1);
 }
 
 }  // namespace mha

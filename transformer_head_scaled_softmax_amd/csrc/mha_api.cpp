@@ -171,6 +171,13 @@ size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, in
 
 namespace {
 
+// Whether the projection path runs as the fused projection+attention kernel
+// plus the output projection (self-attention on short sequences).
+bool use_fused(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
+  return self && Nq == Nk && mha::proj_attn_supported(Nq, D, d_k, d_v) &&
+         int64_t(B) * Nq * D * 2 < kMaxBufferBytes;
+}
+
 // mha_proj_forward with optional profiling events (ev == nullptr: none).
 int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
                       const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
@@ -210,10 +217,10 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   const int64_t nqb = (Nq + 63) / 64;
   if (nqb * H * B > kMaxBlocks || int64_t(B) * std::max(Nq, Nk) > (int64_t(1) << 31) / 64)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
-  // 32-bit byte offsets: a 128-row tile of x or W, and one head's rows of the
+  // 32-bit byte offsets: a 256-row tile of x or W, and one head's rows of the
   // projected Q, K, V (row stride H*d) must each span less than 2^31 bytes.
   const int64_t hd = int64_t(H) * std::max(d_k, d_v);
-  if (128 * int64_t(std::max<int64_t>(D, hd)) * 2 >= kMaxBufferBytes ||
+  if (256 * int64_t(std::max<int64_t>(D, hd)) * 2 >= kMaxBufferBytes ||
       (int64_t(std::max(Nq, Nk)) + 128) * hd * 2 >= kMaxBufferBytes)
     return fail(MHA_ERR_UNSUPPORTED, "dimensions too large for 32-bit tile offsets");
 
@@ -227,6 +234,35 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   const mha::DType dt = static_cast<mha::DType>(dtype);
 
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
+
+  // Short self-attention: projections and attention in one fused launch that
+  // writes the head-major concatenation directly, then the output projection.
+  if (use_fused(x_kv == nullptr || x_kv == x_q, B, Nq, Nk, D, d_k, d_v)) {
+    mha::ProjAttnArgs pa{};
+    pa.x = x_q;
+    pa.wq = W_Q;
+    pa.wk = W_K;
+    pa.wv = W_V;
+    pa.bq = b_Q;
+    pa.bk = b_K;
+    pa.bv = b_V;
+    pa.o = Ow;
+    pa.key_lens = key_lens;
+    pa.B = B;
+    pa.N = Nq;
+    pa.D = D;
+    pa.H = H;
+    pa.causal = mask_kind == MHA_MASK_CAUSAL;
+    pa.scale = scale;
+    hipError_t e = mha::launch_proj_attn(pa, dt, s, evt(0), evt(1));
+    if (e != hipSuccess) return hip_fail(e, "fused projection/attention launch");
+    mha::GemmBatch go{};
+    go.p[0] = {Ow, W_O, b_O, out, B * Nq, D, HV, HV, D};
+    go.count = 1;
+    e = mha::launch_gemm_mfma(go, dt, s, evt(4), evt(5));
+    if (e != hipSuccess) return hip_fail(e, "output projection launch");
+    return MHA_OK;
+  }
 
   // 1. Q, K, V projections in one launch; outputs row-major [B*N, H*d].
   mha::GemmBatch g{};
@@ -300,6 +336,10 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
   return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
                            d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
                            stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention) {
+  return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;
 }
 
 const char* mha_status_string(int status) {

@@ -48,6 +48,24 @@ struct GemmBatch {
   int count;
 };
 
+// Fused Q/K/V projection and attention for self-attention on short
+// sequences: x [B*N, D] row-major, W_* [H*64, D], biases [H*64] (nullable),
+// o [B*N, H*64] (head-major concatenation).
+struct ProjAttnArgs {
+  const void* x;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* bq;
+  const void* bk;
+  const void* bv;
+  void* o;
+  const int32_t* key_lens;  // device int32[B] or nullptr
+  int B, N, D, H;
+  int causal;
+  float scale;
+};
+
 // Launchers return hipSuccess or the launch error; they validate nothing
 // beyond what their kernels assume (the public entry points validate first).
 // Non-null t0/t1 receive the kernel's own start and end timestamps
@@ -58,6 +76,11 @@ hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hip
                             hipEvent_t t1 = nullptr);
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
+hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
+                            hipEvent_t t1 = nullptr);
+// Whether launch_proj_attn handles a problem: N <= 128, D a multiple of 64,
+// head size 64.
+bool proj_attn_supported(int N, int D, int d_k, int d_v);
 
 // Limits the launchers rely on.
 constexpr int kF32MaxHeadDim = 128;
