@@ -34,74 +34,15 @@
 // reference, rescale its accumulators and exponentiate the tile again.  Row
 // sums come from the packed P values with v_dot2, i.e. from exactly the
 // rounded values the P*V product multiplies.
-#include "mha_internal.h"
+#include "mfma_util.h"
 
 namespace mha {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
 constexpr int kD = kMfmaHeadDim;  // 64
 constexpr int kBN = 64;           // keys per tile
 constexpr int kKS = 72;           // K tile row stride (elements): 144 B -> conflict-free 16 B reads
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDeadOffset = (int)0x80000000u;  // beyond any range check: loads return zeros
-constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
-
-struct BF16 {
-  static constexpr float kGuard = 18446744073709551616.0f;  // 2^64: p stays far inside bf16/fp32
-  __device__ static float sum2(uint32_t packed, float acc) {  // acc + lo + hi of a packed pair
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), bf16x2_t{(__bf16)1.0f, (__bf16)1.0f},
-                                           acc, false);
-  }
-  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack(float x, float y) {  // round to nearest even
-    bf16x2_t r = {(__bf16)x, (__bf16)y};
-    return __builtin_bit_cast(uint32_t, r);
-  }
-};
-
-struct F16 {
-  static constexpr float kGuard = 32768.0f;  // 2^15: p stays inside the f16 range
-  __device__ static float sum2(uint32_t packed, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, acc,
-                                  false);
-  }
-  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack(float x, float y) {
-    f16x2_t r = {(_Float16)x, (_Float16)y};
-    return __builtin_bit_cast(uint32_t, r);
-  }
-};
-
-// Buffer resource over `bytes` bytes from `base` (clamped to the 32-bit range
-// check); loads at or beyond `bytes` return zeros.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kBufferWord3);
-}
-
-__device__ inline float lanes_max(float x) {  // max over lanes l and l^32
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ inline float lanes_sum(float x) {  // sum over lanes l and l^32
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <class Op, int NW, int QS>
 __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int nqb) {
@@ -258,12 +199,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
         }
       }
 
-      u32x4_t pb[QS][4];
+      // V^T operands of O^T += V^T P^T for the whole tile, read once and used
+      // by every query sub-block: step t4 supplies keys 16t4 + 4half + {0..3}
+      // and 16t4 + 8 + 4half + {0..3} of this lane's feature row.
+      u32x4_t vop[4][2];
 #pragma unroll
-      for (int u = 0; u < QS; ++u) {
-        // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4;
-        // invisible keys become -inf.
-        if (j0 + kBN > kmin_wave) {  // only diagonal and tail tiles
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const u32x2_t lo = vread(buf, 16 * t4 + tr_row, cb);
+          const u32x2_t hi = vread(buf, 16 * t4 + 8 + tr_row, cb);
+          vop[t4][cb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+
+      // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4;
+      // invisible keys become -inf (only diagonal and tail tiles have any).
+      if (j0 + kBN > kmin_wave) {
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
           const int lim = kend[u] - j0 - 4 * half;
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb)
@@ -271,6 +224,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
             for (int r = 0; r < 16; ++r)
               if (jb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[u][jb][r] = -INFINITY;
         }
+      }
+
+      // Sub-blocks one after the other: softmax, then P V, with no branch
+      // between one sub-block's P V MFMAs and the next one's softmax
+      // arithmetic, so the two can be interleaved.
+#pragma unroll
+      for (int u = 0; u < QS; ++u) {
+        u32x4_t pb[4];
 
         // P = exp2(s * c2 - m_ref), packed to the MFMA input type in the order
         // the P^T operand needs (step t4 takes registers 8(t4%2) .. +7 of
@@ -289,8 +250,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
                 p0 = s[u][jb][r] == -INFINITY ? 0.0f : p0;
                 p1 = s[u][jb][r + 1] == -INFINITY ? 0.0f : p1;
               }
-              pb[u][t4][w] = Op::pack(p0, p1);
-              ls = Op::sum2(pb[u][t4][w], ls);
+              pb[t4][w] = Op::pack(p0, p1);
+              ls = Op::sum2(pb[t4][w], ls);
             }
         };
         // Optimistic pass against the current reference.  It is kept unless
@@ -321,21 +282,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
           exponentiate(m_ref[u] == -INFINITY ? 0.0f : m_ref[u], true);
         }
         lsum[u] += ls;
-      }
 
-      // O^T += V^T P^T over four 16-key steps: V^T supplies keys 16t4 + 4half +
-      // {0..3} and 16t4 + 8 + 4half + {0..3} for this lane's feature row; each
-      // V operand read serves every query sub-block.
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const u32x2_t lo = vread(buf, 16 * t4 + tr_row, cb);
-          const u32x2_t hi = vread(buf, 16 * t4 + 8 + tr_row, cb);
-          const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int u = 0; u < QS; ++u) o[u][cb] = Op::mma(av, pb[u][t4], o[u][cb]);
-        }
+          for (int cb = 0; cb < 2; ++cb) o[u][cb] = Op::mma(vop[t4][cb], pb[t4], o[u][cb]);
       }
     }
 

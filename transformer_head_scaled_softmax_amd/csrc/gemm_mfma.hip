@@ -28,78 +28,19 @@
 // stored).  Tiles are ordered so that the workgroups of one XCD (block id mod
 // 8) take consecutive tiles, which share rows of X in that XCD's L2.  The tile
 // shape is chosen per launch from the problem sizes (see choose_config).
-#include "mha_internal.h"
+#include "mfma_util.h"
 
 namespace mha {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
 constexpr int kBK = 64;  // contraction step (one 128-byte row per operand row)
 constexpr int kXcds = 8;
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
-
-#define MHA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-struct BF16 {
-  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack(float x, float y) {
-    bf16x2_t r = {(__bf16)x, (__bf16)y};
-    return __builtin_bit_cast(uint32_t, r);
-  }
-  __device__ static float to_float(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
-};
-
-struct F16 {
-  __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-  __device__ static uint32_t pack(float x, float y) {
-    f16x2_t r = {(_Float16)x, (_Float16)y};
-    return __builtin_bit_cast(uint32_t, r);
-  }
-  __device__ static float to_float(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
-};
 
 struct TileMap {
   int start[kMaxGemmProblems + 1];  // first tile of each problem
   int tiles_n[kMaxGemmProblems];    // tiles along N of each problem
   int total;
 };
-
-// Buffer resource over `bytes` bytes from `base` (clamped to the 32-bit range
-// check); loads at or beyond `bytes` return zeros.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kBufferWord3);
-}
-
-// s_waitcnt with the vector-memory count set to N and the other counters left
-// unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Barrier without the memory fence of __syncthreads (whose release semantics
-// would wait for every load in flight, including the later stages); the empty
-// asm statements keep the compiler from moving LDS accesses across it.
-__device__ inline void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
@@ -196,7 +137,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
 
   // Operand rows start at multiples of 32, so the swizzle of a lane's row
   // depends on the lane alone.
-  const int swz = (lane & 7) ^ ((lane >> 3) & 1);
+  const int swz = operand_swizzle(lane);
   auto compute = [&](int buf) {
     const uint16_t* st = lds + buf * STAGE;
 #pragma unroll
@@ -225,7 +166,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
     for (int i = tid; i < ROWS * 8; i += NT) {
       const int row = i >> 3, c = i & 7;
       if (c * 8 >= kvalid) {
-        const int slot = c ^ (row & 7) ^ ((row >> 3) & 1);
+        const int slot = c ^ operand_swizzle(row);
         *reinterpret_cast<u32x4_t*>(&st[row * kBK + slot * 8]) = zero;
       }
     }

@@ -25,8 +25,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 #define MHA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// kGuard: the largest partial softmax sum a query may reach before its
+// reference maximum is raised -- far inside the range of the P type.
 struct BF16 {
-  static constexpr float kGuard = 18446744073709551616.0f;  // 2^64: p stays far inside bf16/fp32
+  static constexpr float kGuard = 18446744073709551616.0f;  // 2^64
   __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -43,7 +45,7 @@ struct BF16 {
 };
 
 struct F16 {
-  static constexpr float kGuard = 32768.0f;  // 2^15: p stays inside the f16 range
+  static constexpr float kGuard = 32768.0f;  // 2^15
   __device__ static f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
