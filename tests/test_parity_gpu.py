@@ -275,6 +275,21 @@ def test_proj_shapes_with_biases(dtype, B, Nq, Nk, D, H, cross, mask):
     assert_close(got, ref, dtype, f"proj B{B} Nq{Nq} Nk{Nk} D{D} H{H}")
 
 
+@pytest.mark.parametrize("B,N,D,H", [
+    (21, 130, 1000, 16),  # 528 tiles of 128 x 128 -> the 128 x 128 configuration; K tail 40
+    (21, 130, 520, 8),    # 264 of 128 x 128, 528 of 128 x 64 -> the 128 x 64 one; K tail 8
+    (3, 100, 200, 2),     # 48 of 128 x 64 -> the 64 x 64 one; K tail 8
+])
+def test_proj_gemm_tile_shapes(B, N, D, H):
+    """Projection GEMMs large enough for the bigger tile shapes, with ragged row
+    counts and a contraction that is not a multiple of 64 (cross-attention, so
+    the projections run as separate GEMM launches)."""
+    inp = synth.proj_inputs(B, N, N, D, H, 64, 64, "bf16", seed=B + N + D, cross=True, lens=(1, N))
+    got = run_proj(inp, H, "bf16", NONE)
+    ref = ref_proj(inp, H, NONE)
+    assert_close(got, ref, "bf16", f"proj tiles B{B} N{N} D{D} H{H}")
+
+
 def test_proj_worked_example_identity():
     """H = 1 with identity projections reproduces the printed example outputs."""
     import json

@@ -15,7 +15,9 @@
 //
 // Operand staging: K advances 64 at a time through S stages of LDS that are
 // filled by LDS-direct buffer loads (each lane's 16 bytes go straight from
-// memory into LDS, with no register round trip), issued S-1 steps ahead.  A
+// memory into LDS, with no register round trip), issued S-1 steps ahead
+// (S = 2 in the configurations used: latency is hidden by a second
+// workgroup or a second wave per SIMD rather than by deeper staging).  A
 // step's wait is an explicit vmcnt that lets the later stages stay in flight,
 // followed by one barrier.  A 64-element row of a stage is 128 bytes of eight
 // 16-byte chunks; chunk c of row r sits in slot c ^ (r & 7) ^ ((r >> 3) & 1),
@@ -27,7 +29,7 @@
 // tiles need no branches (rows past M or N only feed outputs that are never
 // stored).  Tiles are ordered so that the workgroups of one XCD (block id mod
 // 8) take consecutive tiles, which share rows of X in that XCD's L2.  The tile
-// shape is chosen per launch from the problem sizes (see choose_config).
+// shape is chosen per launch from the problem sizes (see launch_sized).
 #include "mfma_util.h"
 
 namespace mha {
@@ -235,12 +237,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
   }
 }
 
-// A tile configuration: TM x TN tile, WGM x WGN waves, S stages, MINB
-// workgroups per CU (what the LDS footprint allows).
-struct Config {
-  int tm, tn, wgm, wgn, s, minb;
-};
-
 template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB>
 hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   TileMap tm{};
@@ -260,63 +256,32 @@ hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEven
   return hipGetLastError();
 }
 
-// The instantiated configurations.  LDS per workgroup is S * (TM + TN) * 128
-// bytes; a CU has 160 KiB.
-constexpr Config kConfigs[] = {
-    {128, 256, 2, 2, 3, 1},  // 144 KiB
-    {128, 128, 2, 2, 4, 1},  // 128 KiB
-    {64, 128, 2, 2, 3, 2},   // 72 KiB
-    {64, 64, 2, 2, 4, 2},    // 64 KiB
-};
-constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-
-template <class Op>
-hipError_t launch_config(int c, const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  switch (c) {
-    case 0: return launch<Op, 128, 256, 2, 2, 3, 1>(g, stream, t0, t1);
-    case 1: return launch<Op, 128, 128, 2, 2, 4, 1>(g, stream, t0, t1);
-    case 2: return launch<Op, 64, 128, 2, 2, 3, 2>(g, stream, t0, t1);
-    default: return launch<Op, 64, 64, 2, 2, 4, 2>(g, stream, t0, t1);
-  }
+// The instantiated configurations, with the rule that picks one.  LDS per
+// workgroup is S * (TM + TN) * 128 bytes; a CU has 160 KiB, so each of these
+// runs two workgroups per CU.  Measured on the device (projection shapes from
+// 4096 x 512 x 512 up to 16384 x 6144 x 2048): two stages beat three or four
+// at every tile size (the smaller footprint lets a second workgroup share the
+// CU), eight waves per CU beat four, 128 x 128 tiles win once they give at
+// least one and a half rounds of the chip, and below that the shape that
+// still gives every CU a workgroup wins (within 5% of the best in every case
+// measured).
+int tiles(const GemmBatch& g, int tm, int tn) {
+  int n = 0;
+  for (int i = 0; i < g.count; ++i) n += ((g.p[i].M + tm - 1) / tm) * ((g.p[i].N + tn - 1) / tn);
+  return n;
 }
 
-// Cost model for picking a configuration: the launch runs in rounds of
-// 256 * MINB workgroups; a workgroup's step costs the larger of its MFMA time
-// (4096 FLOP per clock per CU) and its operand traffic into the CU (about 64
-// bytes per clock), both shared by the workgroups resident on a CU, plus a
-// fixed start-up and epilogue cost.
-int choose_config(const GemmBatch& g) {
-  int best = 0;
-  double best_cost = 0.0;
-  for (int c = 0; c < kNumConfigs; ++c) {
-    const Config& f = kConfigs[c];
-    int64_t tiles = 0;
-    int kmax = 0;
-    for (int i = 0; i < g.count; ++i) {
-      tiles += (int64_t)((g.p[i].M + f.tm - 1) / f.tm) * ((g.p[i].N + f.tn - 1) / f.tn);
-      kmax = g.p[i].K > kmax ? g.p[i].K : kmax;
-    }
-    const int64_t slots = 256LL * f.minb;
-    const int64_t rounds = (tiles + slots - 1) / slots;
-    const double resident = tiles < slots ? (double)tiles / 256.0 : (double)f.minb;
-    const double share = resident > 1.0 ? resident : 1.0;
-    const double mfma = (double)f.tm * f.tn * kBK * 2.0 / 4096.0;
-    const double feed = (double)(f.tm + f.tn) * kBK * 2.0 / 64.0;
-    const double step = (mfma > feed ? mfma : feed) * share;
-    const double cost = (double)rounds * (((kmax + kBK - 1) / kBK) * step + 2000.0 * share);
-    if (c == 0 || cost < best_cost) {
-      best = c;
-      best_cost = cost;
-    }
-  }
-  return best;
+template <class Op>
+hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (tiles(g, 128, 128) >= 384) return launch<Op, 128, 128, 2, 4, 2, 2>(g, stream, t0, t1);  // 64 KiB, 8 waves
+  if (tiles(g, 128, 64) >= 256) return launch<Op, 128, 64, 2, 2, 2, 2>(g, stream, t0, t1);    // 48 KiB
+  return launch<Op, 64, 64, 2, 2, 2, 2>(g, stream, t0, t1);                                    // 32 KiB
 }
 
 }  // namespace
 
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const int c = choose_config(g);
-  return dt == DType::BF16 ? launch_config<BF16>(c, g, stream, t0, t1) : launch_config<F16>(c, g, stream, t0, t1);
+  return dt == DType::BF16 ? launch_sized<BF16>(g, stream, t0, t1) : launch_sized<F16>(g, stream, t0, t1);
 }
 
 }  // namespace mha
