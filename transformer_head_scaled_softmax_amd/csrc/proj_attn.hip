@@ -16,7 +16,8 @@
 // (NP = 32, 64 or 128) -- and one head, so the projections' K/V never leave
 // the CU: the projection phase is a 128 x 192 GEMM tile (rows of x times the
 // 192 rows W_Q[h], W_K[h], W_V[h]) with the contraction over D streamed through
-// a three-stage LDS pipeline of LDS-direct loads; the Q, K, V tiles then sit
+// a two-stage LDS pipeline of LDS-direct loads (eight waves, two per SIMD);
+// the Q, K, V tiles then sit
 // in LDS for the attention phase, where each wave takes 32 query rows of one
 // sequence and all of that sequence's (at most 128) keys at once, so the
 // softmax is the plain one: exact row maximum, exponentials, sum.
@@ -31,13 +32,15 @@ constexpr int kRows = 128;                       // token rows per workgroup
 constexpr int kWRows = 3 * kD;                   // W_Q, W_K, W_V rows of one head
 constexpr int kStageRows = kRows + kWRows;       // 320 rows of 128 bytes
 constexpr int kStage = kStageRows * kBK;         // elements per stage
-constexpr int kS = 3;                            // pipeline stages (120 KiB)
-constexpr int kNW = 4;                           // waves
-constexpr int kLPW = kStageRows / 8 / kNW;       // 1 KiB loads per wave per stage (10)
-constexpr int kXLoads = kRows / 8 / kNW;         // the first 4 of them are rows of x
+constexpr int kS = 2;                            // pipeline stages (80 KiB)
+constexpr int kNW = 8;                           // waves (two per SIMD)
+constexpr int kLPW = kStageRows / 8 / kNW;       // 1 KiB loads per wave per stage (5)
+constexpr int kXLoads = kRows / 8 / kNW;         // the first 2 of them are rows of x
+constexpr int kXB = 2 * 4 / kNW;                 // 32-token blocks per wave in the projection
 constexpr int kXcds = 8;
 constexpr uint32_t kDead = 0x80000000u;          // beyond any range check: nothing is read
-static_assert(kRows % (8 * kNW) == 0 && kWRows % (8 * kNW * 2) == 0, "loads must split evenly");
+static_assert(kRows % (8 * kNW) == 0 && kWRows % (8 * kNW) == 0 && kD % 8 == 0, "loads must split evenly");
+static_assert(kNW == 4 || kNW == 8, "wave layouts are written for 4 or 8 waves");
 
 template <class Op, int NP>
 __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, int groups) {
@@ -69,17 +72,19 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   const __amdgpu_buffer_rsrc_t wsrc1 = make_rsrc(static_cast<const uint16_t*>(a.wk) + hoff, (int64_t)kD * D * 2);
   const __amdgpu_buffer_rsrc_t wsrc2 = make_rsrc(static_cast<const uint16_t*>(a.wv) + hoff, (int64_t)kD * D * 2);
 
-  // Load i of this wave fills 1 KiB chunk c = wave + 4i of a stage: rows
+  // Load i of this wave fills 1 KiB chunk c = wave + NW*i of a stage: rows
   // 8c .. 8c+7, lane l at row 8c + l/8, slot l%8, which holds global chunk
   // slot ^ operand_swizzle(row) = (l%8) ^ (l/8) ^ (c & 1), and c & 1 = wave & 1.
   // Stage rows 0..127 are token rows (sequence r / NP, token r % NP), rows
-  // 128 + 64w + r are row r of W_Q[h], W_K[h], W_V[h] for w = 0, 1, 2; load i
-  // >= 4 reads weight matrix (i - 4) / 2.
+  // 128 + 64w + r are row r of W_Q[h], W_K[h], W_V[h] for w = 0, 1, 2; the
+  // loads i >= kXLoads read weight rows.
   const int gchunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
   uint32_t goff[kLPW];
+  int wmat[kLPW];  // weight matrix of load i (uniform per wave)
 #pragma unroll
   for (int i = 0; i < kLPW; ++i) {
     const int row = 8 * (wave + kNW * i) + (lane >> 3);
+    wmat[i] = (8 * (wave + kNW * i) - kRows) / kD;
     if (i < kXLoads) {
       const int item = row / NP, t = row % NP;
       const bool valid = t < N && b0 + item < a.B;
@@ -99,24 +104,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
       uint16_t* d = dst + (wave + kNW * i) * 512;
       if (i < kXLoads)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, MHA_LDS(d), 16, off, 0, 0, 0);
-      else if ((i - kXLoads) / 2 == 0)
+      else if (wmat[i] == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc0, MHA_LDS(d), 16, off, 0, 0, 0);
-      else if ((i - kXLoads) / 2 == 1)
+      else if (wmat[i] == 1)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc1, MHA_LDS(d), 16, off, 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc2, MHA_LDS(d), 16, off, 0, 0, 0);
     }
   };
 
-  // Wave (wx, ww) = (wave & 1, wave >> 1): token blocks 2wx, 2wx+1 times the
-  // 32-feature half ww of each of Q, K, V -- six 32x32 blocks, five operand
-  // reads per 16-wide step.
-  const int wx = wave & 1, ww = wave >> 1;
-  f32x16_t acc[3][2];
+  // Wave (wx, ww) = (wave % (NW/2), wave / (NW/2)): token blocks
+  // kXB*wx .. kXB*wx + kXB-1 times the 32-feature half ww of each of Q, K, V
+  // -- 3*kXB blocks of 32x32, kXB + 3 operand reads per 16-wide step.
+  const int wx = wave % (kNW / 2), ww = wave / (kNW / 2);
+  f32x16_t acc[3][kXB];
 #pragma unroll
   for (int m = 0; m < 3; ++m)
 #pragma unroll
-    for (int xb = 0; xb < 2; ++xb)
+    for (int xb = 0; xb < kXB; ++xb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][xb][r] = 0.0f;
   auto compute = [&](int buf) {
@@ -124,17 +129,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int slot = (kk * 2 + half) ^ swz;
-      u32x4_t bx[2], aw[3];
+      u32x4_t bx[kXB], aw[3];
 #pragma unroll
-      for (int xb = 0; xb < 2; ++xb)
-        bx[xb] = *reinterpret_cast<const u32x4_t*>(&st[(64 * wx + 32 * xb + col) * kBK + slot * 8]);
+      for (int xb = 0; xb < kXB; ++xb)
+        bx[xb] = *reinterpret_cast<const u32x4_t*>(&st[(32 * (kXB * wx + xb) + col) * kBK + slot * 8]);
 #pragma unroll
       for (int m = 0; m < 3; ++m)
         aw[m] = *reinterpret_cast<const u32x4_t*>(&st[(kRows + 64 * m + 32 * ww + col) * kBK + slot * 8]);
 #pragma unroll
       for (int m = 0; m < 3; ++m)
 #pragma unroll
-        for (int xb = 0; xb < 2; ++xb) acc[m][xb] = Op::mma(aw[m], bx[xb], acc[m][xb]);
+        for (int xb = 0; xb < kXB; ++xb) acc[m][xb] = Op::mma(aw[m], bx[xb], acc[m][xb]);
     }
   };
 
@@ -177,8 +182,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
       }
       const int c = f0 >> 3;  // 16-byte chunk of the row
 #pragma unroll
-      for (int xb = 0; xb < 2; ++xb) {
-        const int t = 64 * wx + 32 * xb + col;
+      for (int xb = 0; xb < kXB; ++xb) {
+        const int t = 32 * (kXB * wx + xb) + col;
         const bool valid = t % NP < N && b0 + t / NP < a.B;
         u32x2_t v = {0u, 0u};
         if (valid) {
@@ -196,12 +201,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   }
   __syncthreads();
 
-  // ---- Attention phase: wave w takes token rows 32w .. 32w+31 of the tile,
-  // i.e. queries q0 .. q0+31 of sequence `item`; the sequence's keys are tile
-  // rows kb0 .. kb0+NP-1.
+  // ---- Attention phase: wave w < 4 takes token rows 32w .. 32w+31 of the
+  // tile, i.e. queries q0 .. q0+31 of sequence `item`; the sequence's keys are
+  // tile rows kb0 .. kb0+NP-1.  Further waves are done.
+  if (wave >= kRows / 32) return;  // wave-uniform; no barrier follows
   const int item = (32 * wave) / NP, q0 = (32 * wave) % NP, kb0 = item * NP;
   const int b = b0 + item;
-  if (b >= a.B || q0 >= N) return;  // wave-uniform; no barrier follows
+  if (b >= a.B || q0 >= N) return;
   int L = N;
   if (a.key_lens) L = min(max(a.key_lens[b], 0), N);
   const int qi = q0 + col;
