@@ -293,7 +293,7 @@ def main():
                      d["out"].data_ptr(), w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.mask, lp, scale,
                      code, ws.data_ptr(), need, sp)
             st = (lib.mha_proj_forward(*argsv) if events is None
-                  else lib.mha_proj_forward_timed(*argsv, events))
+                  else lib.mha_proj_forward_timed(*argsv, events, 0))
             if st != 0:
                 raise RuntimeError(lib.mha_last_error().decode())
         # Kernel -> (start, end) event indices of mha_proj_forward_timed.

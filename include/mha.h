@@ -59,6 +59,11 @@ extern "C" {
 #define MHA_BF16 1
 #define MHA_F16 2
 
+/* kernel plans of mha_proj_forward_timed */
+#define MHA_PLAN_AUTO 0    /* what mha_proj_forward does (see mha_proj_fused) */
+#define MHA_PLAN_UNFUSED 1 /* projection GEMM, attention kernel, output GEMM */
+#define MHA_PLAN_FUSED 2   /* fused projection+attention kernel, output GEMM */
+
 /* status codes */
 #define MHA_OK 0
 #define MHA_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad enum, ... */
@@ -133,10 +138,14 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
  *
  * mha_forward_timed: 2 events -- the attention kernel.
  * mha_proj_forward_timed: 6 events -- the Q/K/V projection, the attention
- * kernel and the output projection, in that order.  A fused call (see
- * mha_proj_fused) launches two kernels: events[0..1] time the fused
- * projection+attention kernel, events[4..5] the output projection, and
- * events[2..3] are left untouched.
+ * kernel and the output projection, in that order.  A fused call launches two
+ * kernels: events[0..1] time the fused projection+attention kernel,
+ * events[4..5] the output projection, and events[2..3] are left untouched.
+ * Its last argument selects the kernel plan: MHA_PLAN_AUTO (the plan
+ * mha_proj_forward takes), MHA_PLAN_UNFUSED, or MHA_PLAN_FUSED (returns
+ * MHA_ERR_UNSUPPORTED when mha_proj_fused is 0 for these sizes); an unknown
+ * value is MHA_ERR_INVALID_ARG.  Both plans compute the same function; they
+ * agree bit for bit when every sequence has at most 64 keys.
  */
 int mha_forward_timed(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
                       int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
@@ -147,16 +156,18 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk,
                            int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
                            float scale, int dtype, void* workspace, size_t workspace_bytes,
-                           void* stream, void* const* events);
+                           void* stream, void* const* events, int plan);
 
 /*
  * mha_proj_fused -- 1 if mha_proj_forward with these sizes runs as two
  * kernels (the Q/K/V projections fused with attention, then the output
  * projection), 0 if it runs as three (projections, attention, output
  * projection).  self_attention: nonzero when x_kv is NULL or equal to x_q.
- * The fused form applies to self-attention with Nq == Nk <= 128, D a
- * multiple of 64 and d_k == d_v == 64 (bf16 or f16).  Pure function of its
- * arguments; no device access.
+ * The fused form applies when D is a multiple of 64, d_k == d_v == 64
+ * (bf16 or f16), and either self-attention with Nq == Nk <= 128 or
+ * cross-attention with Nq <= 64 and Nk <= 128 -- sentence-length encoder,
+ * decoder and encoder-decoder layers.  Pure function of its arguments; no
+ * device access.
  */
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention);
 

@@ -151,14 +151,24 @@ def test_proj_empty_is_ok(lib):
     ((64, 64, 64, 512, 64, 64, 1), 1),     # sentence-length self-attention
     ((3, 128, 128, 64, 64, 64, 1), 1),     # longest fused sequence
     ((3, 129, 129, 64, 64, 64, 1), 0),     # too long for one tile
-    ((32, 64, 80, 1024, 64, 64, 0), 0),    # cross-attention
-    ((32, 64, 64, 1024, 64, 64, 0), 0),    # x_kv distinct from x_q
+    ((32, 64, 80, 1024, 64, 64, 0), 1),    # sentence-length cross-attention
+    ((32, 65, 80, 1024, 64, 64, 0), 0),    # cross-attention with more than 64 queries
+    ((32, 64, 129, 1024, 64, 64, 0), 0),   # cross-attention with more than 128 keys
     ((2, 64, 64, 200, 64, 64, 1), 0),      # D not a multiple of 64
     ((2, 64, 64, 512, 32, 32, 1), 0),      # head size other than 64
     ((2, 64, 32, 512, 64, 64, 1), 0),      # Nq != Nk
 ])
 def test_proj_fused_plan(lib, args, fused):
     assert lib.mha_proj_fused(*args) == fused
+
+
+def test_proj_timed_rejects_unknown_plan(lib):
+    import ctypes
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+    args = [fake, None, fake, fake, fake, fake, None, None, None, None, fake, 2, 8, 8, 64, 1, 64, 64, 0, None,
+            ctypes.c_float(0.125), 1, fake, 1 << 20, None, None]
+    assert lib.mha_proj_forward_timed(*args, 3) == mb.ERR_INVALID_ARG
+    assert lib.mha_proj_forward_timed(*args, -1) == mb.ERR_INVALID_ARG
 
 
 def test_last_error_is_per_thread(lib):

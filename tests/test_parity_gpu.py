@@ -310,46 +310,63 @@ def test_proj_worked_example_identity():
 
 
 # ---------------------------------------------------------------------------
-# Fused Q/K/V projection + attention (self-attention, N <= 128, D % 64 == 0).
+# Fused Q/K/V projection + attention (D % 64 == 0; self-attention N <= 128,
+# cross-attention Nq <= 64, Nk <= 128).
 
-FUSED_CASES = [  # (B, N, D, H, mask): each row padding (32, 64, 128), partial last groups
-    (5, 1, 64, 2, NONE), (5, 31, 128, 2, CAUSAL), (3, 32, 64, 3, NONE), (3, 33, 192, 2, CAUSAL),
-    (3, 64, 256, 4, NONE), (1, 65, 64, 1, CAUSAL), (2, 100, 128, 2, NONE), (3, 128, 64, 2, CAUSAL)]
+FUSED_CASES = [  # (B, Nq, Nk, D, H, cross, mask): every row padding, partial last groups
+    (5, 1, 1, 64, 2, False, NONE), (5, 31, 31, 128, 2, False, CAUSAL), (3, 32, 32, 64, 3, False, NONE),
+    (3, 33, 33, 192, 2, False, CAUSAL), (3, 64, 64, 256, 4, False, NONE), (1, 65, 65, 64, 1, False, CAUSAL),
+    (2, 100, 100, 128, 2, False, NONE), (3, 128, 128, 64, 2, False, CAUSAL),
+    (3, 1, 5, 64, 2, True, NONE), (5, 20, 40, 128, 2, True, NONE), (3, 32, 64, 64, 2, True, NONE),
+    (3, 40, 70, 192, 3, True, NONE), (4, 64, 80, 256, 4, True, NONE), (1, 64, 96, 64, 1, True, NONE),
+    (3, 50, 128, 128, 2, True, NONE), (2, 64, 64, 64, 2, True, CAUSAL)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("B,N,D,H,mask", FUSED_CASES)
-def test_fused_proj_attention(dtype, B, N, D, H, mask):
-    assert mha.load().mha_proj_fused(B, N, N, D, 64, 64, 1) == 1
-    inp = synth.proj_inputs(B, N, N, D, H, 64, 64, dtype, seed=7 * B + N + D, cross=False)
-    g = synth.generator(31 * N + D)
-    inp["key_lens"] = g.integers(0, N + 3, size=B).astype(np.int32)  # 0 and > N included
+@pytest.mark.parametrize("B,Nq,Nk,D,H,cross,mask", FUSED_CASES)
+def test_fused_proj_attention(dtype, B, Nq, Nk, D, H, cross, mask):
+    assert mha.load().mha_proj_fused(B, Nq, Nk, D, 64, 64, 0 if cross else 1) == 1
+    inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed=7 * B + Nq + Nk + D, cross=cross)
+    g = synth.generator(31 * Nk + D)
+    inp["key_lens"] = g.integers(0, Nk + 3, size=B).astype(np.int32)  # 0 and > Nk included
     biases = {n: synth.round_to(synth.normal(g, (size,), dtype) * np.float32(0.5), dtype)
               for n, size in (("b_Q", H * 64), ("b_K", H * 64), ("b_V", H * 64), ("b_O", D))}
     got = run_proj(inp, H, dtype, mask, biases)
     ref = ref_proj(inp, H, mask, biases)
-    assert_close(got, ref, dtype, f"fused B{B} N{N} D{D} H{H}")
+    assert_close(got, ref, dtype, f"fused B{B} Nq{Nq} Nk{Nk} D{D} H{H} cross{cross}")
 
 
-@pytest.mark.parametrize("N,scale", [(17, None), (64, None), (40, -0.3), (64, 0.0), (100, None)])
-def test_fused_matches_three_kernel_path(N, scale):
-    """x_kv given as a separate copy of x_q takes the three-kernel path; both
-    paths round Q, K, V identically and, within one key tile (N <= 64), do the
-    same arithmetic in the same order, so they agree bit for bit there."""
-    B, D, H = 4, 128, 2
+@pytest.mark.parametrize("Nq,Nk,cross,scale", [
+    (17, 17, False, None), (64, 64, False, None), (40, 40, False, -0.3), (64, 64, False, 0.0),
+    (100, 100, False, None), (33, 50, True, None), (64, 64, True, -0.5), (20, 120, True, None)])
+def test_fused_matches_three_kernel_path(Nq, Nk, cross, scale):
+    """Both plans round Q, K, V identically and, when every sequence's keys fit
+    one 64-key tile, do the same arithmetic in the same order, so they agree bit
+    for bit there; beyond that they agree to rounding."""
+    B, D, H = 5, 128, 2
     lib = mha.load()
-    assert lib.mha_proj_fused(B, N, N, D, 64, 64, 1) == 1 and lib.mha_proj_fused(B, N, N, D, 64, 64, 0) == 0
-    inp = synth.proj_inputs(B, N, N, D, H, 64, 64, "bf16", seed=N, cross=False, lens=(1, N))
+    assert lib.mha_proj_fused(B, Nq, Nk, D, 64, 64, 0 if cross else 1) == 1
+    inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, "bf16", seed=Nq + Nk, cross=cross, lens=(1, Nk))
     d = _proj_dev(inp, "bf16")
     lens = lens_dev(inp["key_lens"])
     w = (d["W_Q"], d["W_K"], d["W_V"], d["W_O"])
-    fused = mha.proj_forward(d["x_q"], None, *w, H=H, mask_kind=CAUSAL, key_lens=lens, scale=scale)
-    three = mha.proj_forward(d["x_q"], d["x_q"].clone(), *w, H=H, mask_kind=CAUSAL, key_lens=lens, scale=scale)
+    mask = NONE if cross and Nq != Nk else CAUSAL
+    runs = {p: mha.proj_forward(d["x_q"], d["x_kv"], *w, H=H, mask_kind=mask, key_lens=lens, scale=scale, plan=p)
+            for p in (mha.PLAN_FUSED, mha.PLAN_UNFUSED)}
     torch.cuda.synchronize()
-    if N <= 64:
+    fused, three = runs[mha.PLAN_FUSED], runs[mha.PLAN_UNFUSED]
+    if Nk <= 64:
         assert torch.equal(fused, three)
     else:
-        assert_close(to_host(fused), to_host(three), "bf16", f"fused vs three-kernel N{N}")
+        assert_close(to_host(fused), to_host(three), "bf16", f"fused vs three-kernel Nq{Nq} Nk{Nk}")
+
+
+def test_fused_plan_rejected_when_unsupported():
+    inp = synth.proj_inputs(2, 70, 70, 128, 2, 64, 64, "bf16", seed=3, cross=True)
+    d = _proj_dev(inp, "bf16")
+    with pytest.raises(mha.MhaError) as e:
+        mha.proj_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=2, plan=mha.PLAN_FUSED)
+    assert e.value.status == -2  # MHA_ERR_UNSUPPORTED: 70 queries exceed the cross-attention tile
 
 
 def test_graph_replays_match_eager():

@@ -14,11 +14,11 @@ from __future__ import annotations
 
 import math
 
-from ._binding import (BF16, EXPORTS, F16, F32, MASK_CAUSAL, MASK_NONE, MhaError, check,
-                       load)
+from ._binding import (BF16, EXPORTS, F16, F32, MASK_CAUSAL, MASK_NONE, PLAN_AUTO, PLAN_FUSED, PLAN_UNFUSED,
+                       MhaError, check, load)
 
-__all__ = ["forward", "proj_forward", "proj_workspace_bytes", "MASK_NONE", "MASK_CAUSAL",
-           "MhaError", "load", "EXPORTS"]
+__all__ = ["forward", "proj_forward", "proj_workspace_bytes", "MASK_NONE", "MASK_CAUSAL", "PLAN_AUTO",
+           "PLAN_UNFUSED", "PLAN_FUSED", "MhaError", "load", "EXPORTS"]
 
 
 def _dtype_code(t) -> int:
@@ -82,10 +82,12 @@ def proj_workspace_bytes(B, Nq, Nk, D, H, d_k, d_v, dtype_code: int = BF16) -> i
 
 def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None, b_O=None,
                  mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None, out=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, plan: int | None = None):
     """Multi-head attention with projections; see mha_proj_forward in include/mha.h.
 
-    Weights are [out_features, in_features] (nn.Linear layout)."""
+    Weights are [out_features, in_features] (nn.Linear layout).  ``plan``
+    (PLAN_UNFUSED / PLAN_FUSED) forces a kernel plan through
+    mha_proj_forward_timed; None lets the library choose."""
     import torch
     B, Nq, D = x_q.shape
     Nk = Nq if x_kv is None else x_kv.shape[1]
@@ -103,8 +105,11 @@ def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=
     ptrs = [_dev_ptr(t, n) for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (W_Q, "W_Q"), (W_K, "W_K"),
                                         (W_V, "W_V"), (W_O, "W_O"), (b_Q, "b_Q"), (b_K, "b_K"),
                                         (b_V, "b_V"), (b_O, "b_O"), (out, "out"))]
-    st = lib.mha_proj_forward(*ptrs, B, Nq, Nk, D, H, dk, dv, int(mask_kind),
-                              _lens_ptr(key_lens, B), float(scale), code,
-                              _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+    args = (*ptrs, B, Nq, Nk, D, H, dk, dv, int(mask_kind), _lens_ptr(key_lens, B), float(scale), code,
+            _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
+    if plan is None:
+        st = lib.mha_proj_forward(*args)
+    else:
+        st = lib.mha_proj_forward_timed(*args, None, int(plan))
     check(lib, st)
     return out

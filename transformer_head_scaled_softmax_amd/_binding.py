@@ -14,6 +14,7 @@ LIB_PATH = PKG / "libmha.so"
 
 MASK_NONE = 0
 MASK_CAUSAL = 1
+PLAN_AUTO, PLAN_UNFUSED, PLAN_FUSED = 0, 1, 2
 F32, BF16, F16 = 0, 1, 2
 
 OK = 0
@@ -54,7 +55,7 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_proj_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_proj_forward.argtypes = [vp] * 11 + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]
     lib.mha_proj_forward.restype = i
-    lib.mha_proj_forward_timed.argtypes = lib.mha_proj_forward.argtypes + [vp]
+    lib.mha_proj_forward_timed.argtypes = lib.mha_proj_forward.argtypes + [vp, i]
     lib.mha_proj_forward_timed.restype = i
     lib.mha_proj_fused.argtypes = [i] * 7
     lib.mha_proj_fused.restype = i

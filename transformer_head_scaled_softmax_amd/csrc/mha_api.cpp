@@ -172,10 +172,10 @@ size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, in
 namespace {
 
 // Whether the projection path runs as the fused projection+attention kernel
-// plus the output projection (self-attention on short sequences).
+// plus the output projection (short sequences).
 bool use_fused(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
-  return self && Nq == Nk && mha::proj_attn_supported(Nq, D, d_k, d_v) &&
-         int64_t(B) * Nq * D * 2 < kMaxBufferBytes;
+  return mha::proj_attn_supported(self, Nq, Nk, D, d_k, d_v) && int64_t(B) * Nq * D * 2 < kMaxBufferBytes &&
+         int64_t(B) * Nk * D * 2 < kMaxBufferBytes;
 }
 
 // mha_proj_forward with optional profiling events (ev == nullptr: none).
@@ -184,8 +184,9 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
                       const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
                       int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                      hipEvent_t const* ev) {
+                      hipEvent_t const* ev, int plan) {
   g_last_error.clear();
+  if (plan < MHA_PLAN_AUTO || plan > MHA_PLAN_FUSED) return fail(MHA_ERR_INVALID_ARG, "unknown plan %d", plan);
   if (B < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, Nq, Nk must be >= 0 (got %d, %d, %d)", B, Nq, Nk);
   if (D < 1 || H < 1 || d_k < 1 || d_v < 1)
@@ -237,9 +238,13 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
 
   // Short self-attention: projections and attention in one fused launch that
   // writes the head-major concatenation directly, then the output projection.
-  if (use_fused(x_kv == nullptr || x_kv == x_q, B, Nq, Nk, D, d_k, d_v)) {
+  const bool fusable = use_fused(xkv == x_q, B, Nq, Nk, D, d_k, d_v);
+  if (plan == MHA_PLAN_FUSED && !fusable)
+    return fail(MHA_ERR_UNSUPPORTED, "these sizes have no fused projection+attention kernel");
+  if (fusable && plan != MHA_PLAN_UNFUSED) {
     mha::ProjAttnArgs pa{};
-    pa.x = x_q;
+    pa.xq = x_q;
+    pa.xkv = xkv;
     pa.wq = W_Q;
     pa.wk = W_K;
     pa.wv = W_V;
@@ -249,7 +254,8 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     pa.o = Ow;
     pa.key_lens = key_lens;
     pa.B = B;
-    pa.N = Nq;
+    pa.Nq = Nq;
+    pa.Nk = Nk;
     pa.D = D;
     pa.H = H;
     pa.causal = mask_kind == MHA_MASK_CAUSAL;
@@ -324,7 +330,7 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
                            d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
-                           stream, nullptr);
+                           stream, nullptr, MHA_PLAN_AUTO);
 }
 
 int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
@@ -332,10 +338,10 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk,
                            int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
                            float scale, int dtype, void* workspace, size_t workspace_bytes,
-                           void* stream, void* const* events) {
+                           void* stream, void* const* events, int plan) {
   return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
                            d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
-                           stream, reinterpret_cast<hipEvent_t const*>(events));
+                           stream, reinterpret_cast<hipEvent_t const*>(events), plan);
 }
 
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention) {

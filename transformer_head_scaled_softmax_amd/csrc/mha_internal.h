@@ -48,11 +48,12 @@ struct GemmBatch {
   int count;
 };
 
-// Fused Q/K/V projection and attention for self-attention on short
-// sequences: x [B*N, D] row-major, W_* [H*64, D], biases [H*64] (nullable),
-// o [B*N, H*64] (head-major concatenation).
+// Fused Q/K/V projection and attention on short sequences: x_q [B*Nq, D] and
+// x_kv [B*Nk, D] row-major (xkv == xq for self-attention), W_* [H*64, D],
+// biases [H*64] (nullable), o [B*Nq, H*64] (head-major concatenation).
 struct ProjAttnArgs {
-  const void* x;
+  const void* xq;
+  const void* xkv;
   const void* wq;
   const void* wk;
   const void* wv;
@@ -61,7 +62,7 @@ struct ProjAttnArgs {
   const void* bv;
   void* o;
   const int32_t* key_lens;  // device int32[B] or nullptr
-  int B, N, D, H;
+  int B, Nq, Nk, D, H;
   int causal;
   float scale;
 };
@@ -78,9 +79,10 @@ hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hi
                             hipEvent_t t1 = nullptr);
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
-// Whether launch_proj_attn handles a problem: N <= 128, D a multiple of 64,
-// head size 64.
-bool proj_attn_supported(int N, int D, int d_k, int d_v);
+// Whether launch_proj_attn handles a problem: head size 64, D a multiple of
+// 64, and self-attention with Nq == Nk <= 128 or cross-attention with
+// Nq <= 64, Nk <= 128.
+bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v);
 
 // Limits the launchers rely on.
 constexpr int kF32MaxHeadDim = 128;

@@ -1,53 +1,73 @@
-// proj_attn.hip -- fused Q/K/V projection and attention for short
-// self-attention (N <= 128 tokens per sequence, head size 64).
+// proj_attn.hip -- fused Q/K/V projection and attention for short sequences
+// (Nq, Nk <= 128 tokens, head size 64), self-attention and encoder-decoder
+// cross-attention.
 //
-// Per head h this computes Q = x W_Q^T, K = x W_K^T, V = x W_V^T restricted to
-// the head's 64 output features ("Query / Key / Value Roles", "Multi-Head
-// Attention", trishampatil.com; weights in the [out_features, in_features]
-// layout of nn.Linear, "A faithful layer in code", aicassindra.com), rounds
-// them to the input type exactly as the unfused path stores them, and then
-// softmax(scale * Q K^T) V with padded keys (j >= L) and, under the causal
-// mask, future keys (j > i) given weight exactly 0 ("Scaled Dot-Product
-// Attention: Step by Step", "Why Masking Is Required", trishampatil.com).
-// The head's output goes straight into its columns of the head-major
-// concatenation that the output projection reads.
+// Per head h this computes Q = x_q W_Q^T, K = x_kv W_K^T, V = x_kv W_V^T
+// restricted to the head's 64 output features ("Query / Key / Value Roles",
+// "Multi-Head Attention", "Cross-Attention", trishampatil.com; weights in the
+// [out_features, in_features] layout of nn.Linear, "A faithful layer in code",
+// aicassindra.com), rounds them to the input type exactly as the unfused path
+// stores them, and then softmax(scale * Q K^T) V with padded keys (j >= L)
+// and, under the causal mask, future keys (j > i) given weight exactly 0
+// ("Scaled Dot-Product Attention: Step by Step", "Why Masking Is Required",
+// trishampatil.com).  The head's output goes straight into its columns of the
+// head-major concatenation that the output projection reads.
 //
-// A workgroup owns 128 token rows -- 128/NP whole sequences padded to NP rows
-// (NP = 32, 64 or 128) -- and one head, so the projections' K/V never leave
-// the CU: the projection phase is a 128 x 192 GEMM tile (rows of x times the
-// 192 rows W_Q[h], W_K[h], W_V[h]) with the contraction over D streamed through
-// a two-stage LDS pipeline of LDS-direct loads (eight waves, two per SIMD);
-// the Q, K, V tiles then sit
-// in LDS for the attention phase, where each wave takes 32 query rows of one
-// sequence and all of that sequence's (at most 128) keys at once, so the
-// softmax is the plain one: exact row maximum, exponentials, sum.
+// A workgroup owns one head and a few whole sequences: their x_q rows, each
+// sequence padded to NPQ rows, and (cross-attention) their x_kv rows padded to
+// NPK rows -- for self-attention the x_q rows serve for K and V too.  The
+// projection phase is one GEMM tile (those token rows times the 192 rows
+// W_Q[h], W_K[h], W_V[h]) with the contraction over D streamed through a
+// two-stage pipeline of LDS-direct loads; eight waves (two per SIMD) split it
+// into equal tasks of 32x32 MFMA blocks.  The Q, K, V tiles then sit in LDS
+// for the attention phase, where each wave takes 32 queries of one sequence
+// and all of that sequence's (at most 128) keys at once, so the softmax is the
+// plain one: exact row maximum, exponentials, sum.  For a sequence whose keys
+// fit one 64-key tile of the streaming kernel its arithmetic is step for step
+// the same, so both plans return bit-identical results there.
 #include "mfma_util.h"
 
 namespace mha {
 namespace {
 
-constexpr int kD = kMfmaHeadDim;                 // 64
-constexpr int kBK = 64;                          // contraction step
-constexpr int kRows = 128;                       // token rows per workgroup
-constexpr int kWRows = 3 * kD;                   // W_Q, W_K, W_V rows of one head
-constexpr int kStageRows = kRows + kWRows;       // 320 rows of 128 bytes
-constexpr int kStage = kStageRows * kBK;         // elements per stage
-constexpr int kS = 2;                            // pipeline stages (80 KiB)
-constexpr int kNW = 8;                           // waves (two per SIMD)
-constexpr int kLPW = kStageRows / 8 / kNW;       // 1 KiB loads per wave per stage (5)
-constexpr int kXLoads = kRows / 8 / kNW;         // the first 2 of them are rows of x
-constexpr int kXB = 2 * 4 / kNW;                 // 32-token blocks per wave in the projection
+constexpr int kD = kMfmaHeadDim;         // 64
+constexpr int kBK = 64;                  // contraction step
+constexpr int kWRows = 3 * kD;           // W_Q, W_K, W_V rows of one head
+constexpr int kNW = 8;                   // waves (two per SIMD)
+constexpr int kS = 2;                    // pipeline stages
 constexpr int kXcds = 8;
-constexpr uint32_t kDead = 0x80000000u;          // beyond any range check: nothing is read
-static_assert(kRows % (8 * kNW) == 0 && kWRows % (8 * kNW) == 0 && kD % 8 == 0, "loads must split evenly");
-static_assert(kNW == 4 || kNW == 8, "wave layouts are written for 4 or 8 waves");
+constexpr uint32_t kDead = 0x80000000u;  // beyond any range check: nothing is read
 
-template <class Op, int NP>
+// The tile of one workgroup.  Stage rows: [0, XQ) x_q, [XQ, XQ + XK) x_kv
+// (cross-attention only), then 64 rows each of W_Q[h], W_K[h], W_V[h].
+// Projection tasks of MPT MFMA blocks per 16-wide step -- self: (token block,
+// feature half) x {Q, K, V}; cross: an x_q block x {Q half 0, Q half 1}, then
+// (x_kv block, feature half) x {K, V}.
+template <bool SELF, int NPQ, int NPK>
+struct Tile {
+  static constexpr int IPW = SELF ? 128 / NPQ : 2;  // sequences per workgroup
+  static constexpr int XQ = IPW * NPQ;
+  static constexpr int XK = SELF ? 0 : IPW * NPK;
+  static constexpr int KR = SELF ? XQ : XK;         // rows of the K and V tiles
+  static constexpr int XQB = XQ / 32, KRB = KR / 32;
+  static constexpr int WR0 = XQ + XK;                // first weight row
+  static constexpr int ROWS = WR0 + kWRows;
+  static constexpr int STAGE = ROWS * kBK;           // elements per stage
+  static constexpr int LPW = ROWS / 8 / kNW;         // 1 KiB loads per wave per stage
+  static constexpr int MPT = SELF ? 3 : 2;
+  static constexpr int T = SELF ? 2 * XQB : XQB + 2 * KRB;
+  static constexpr int TPW = (T + kNW - 1) / kNW;    // tasks of the busiest wave
+  static_assert(NPQ % 32 == 0 && NPK % 32 == 0 && NPQ <= 128 && NPK <= 128, "row padding");
+  static_assert(ROWS % (8 * kNW) == 0, "loads must split evenly over the waves");
+  static_assert(XQ <= 32 * kNW / 2, "one wave per 32 queries in the attention phase");
+  static_assert((XQ + 2 * KR) * kD <= kS * STAGE, "Q, K, V tiles must fit in the stages");
+};
+
+template <class Op, bool SELF, int NPQ, int NPK>
 __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, int groups) {
-  constexpr int IPW = kRows / NP;  // sequences per workgroup
-  constexpr int KB = NP / 32;      // 32-key blocks per sequence
-  static_assert(NP == 32 || NP == 64 || NP == 128, "unsupported padding");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kS * kStage];
+  using TL = Tile<SELF, NPQ, NPK>;
+  constexpr int KB = NPK / 32;  // 32-key blocks per sequence
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kS * TL::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: selects resources
@@ -57,16 +77,16 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   // XCD-aware order over (group, head) units, head fastest: the workgroups of
   // one XCD (block id mod 8) take a contiguous range, so they share the group's
   // rows of x and the heads' weights in that XCD's L2.
-  const int T = groups * a.H, q = T / kXcds, rem = T % kXcds;
+  const int U = groups * a.H, q = U / kXcds, rem = U % kXcds;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
   const int unit = xcd * q + min(xcd, rem) + j;
   const int grp = unit / a.H, h = unit % a.H;
-  const int b0 = grp * IPW;
-  const int N = a.N, D = a.D;
+  const int b0 = grp * TL::IPW;
+  const int Nq = a.Nq, Nk = a.Nk, D = a.D;
 
-  // ---- Projection phase: C^T[f][t] = sum_k W[f][k] x[t][k], f over the 192
-  // rows of the head's three weight matrices, t over the 128 token rows.
-  const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a.x, (int64_t)a.B * N * D * 2);
+  // ---- Projection phase: C^T[f][t] = sum_k W[f][k] x[t][k].
+  const __amdgpu_buffer_rsrc_t xqsrc = make_rsrc(a.xq, (int64_t)a.B * Nq * D * 2);
+  const __amdgpu_buffer_rsrc_t xkvsrc = make_rsrc(a.xkv, (int64_t)a.B * Nk * D * 2);
   const int64_t hoff = (int64_t)h * kD * D;
   const __amdgpu_buffer_rsrc_t wsrc0 = make_rsrc(static_cast<const uint16_t*>(a.wq) + hoff, (int64_t)kD * D * 2);
   const __amdgpu_buffer_rsrc_t wsrc1 = make_rsrc(static_cast<const uint16_t*>(a.wk) + hoff, (int64_t)kD * D * 2);
@@ -75,71 +95,116 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   // Load i of this wave fills 1 KiB chunk c = wave + NW*i of a stage: rows
   // 8c .. 8c+7, lane l at row 8c + l/8, slot l%8, which holds global chunk
   // slot ^ operand_swizzle(row) = (l%8) ^ (l/8) ^ (c & 1), and c & 1 = wave & 1.
-  // Stage rows 0..127 are token rows (sequence r / NP, token r % NP), rows
-  // 128 + 64w + r are row r of W_Q[h], W_K[h], W_V[h] for w = 0, 1, 2; the
-  // loads i >= kXLoads read weight rows.
+  // A chunk lies in one region (all region bounds are multiples of 32 rows):
+  // src[i] = 0 x_q, 1 x_kv, 2..4 W_Q, W_K, W_V -- uniform per wave.
   const int gchunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
-  uint32_t goff[kLPW];
-  int wmat[kLPW];  // weight matrix of load i (uniform per wave)
+  uint32_t goff[TL::LPW];
+  int src[TL::LPW];
 #pragma unroll
-  for (int i = 0; i < kLPW; ++i) {
-    const int row = 8 * (wave + kNW * i) + (lane >> 3);
-    wmat[i] = (8 * (wave + kNW * i) - kRows) / kD;
-    if (i < kXLoads) {
-      const int item = row / NP, t = row % NP;
-      const bool valid = t < N && b0 + item < a.B;
-      goff[i] = valid ? (uint32_t)((((b0 + item) * N + t) * D + gchunk * 8) * 2) : kDead;
+  for (int i = 0; i < TL::LPW; ++i) {
+    const int row0 = 8 * (wave + kNW * i), row = row0 + (lane >> 3);
+    if (row0 < TL::XQ) {
+      src[i] = 0;
+      const int item = row / NPQ, t = row % NPQ;
+      const bool valid = t < Nq && b0 + item < a.B;
+      goff[i] = valid ? (uint32_t)((((b0 + item) * Nq + t) * D + gchunk * 8) * 2) : kDead;
+    } else if (row0 < TL::WR0) {
+      src[i] = 1;
+      const int r = row - TL::XQ, item = r / NPK, t = r % NPK;
+      const bool valid = t < Nk && b0 + item < a.B;
+      goff[i] = valid ? (uint32_t)((((b0 + item) * Nk + t) * D + gchunk * 8) * 2) : kDead;
     } else {
-      goff[i] = (uint32_t)((((row - kRows) % kD) * D + gchunk * 8) * 2);
+      src[i] = 2 + (row0 - TL::WR0) / kD;
+      goff[i] = (uint32_t)((((row - TL::WR0) % kD) * D + gchunk * 8) * 2);
     }
   }
   const int nk = D / kBK;
+  // Every step issues exactly LPW loads per wave (steps past the end read
+  // nothing), so the vmcnt waits below stay exact.
   auto issue = [&](int kt) {
-    uint16_t* dst = lds + (kt % kS) * kStage;
+    uint16_t* dst = lds + (kt % kS) * TL::STAGE;
     const uint32_t k0 = (uint32_t)kt * kBK * 2;
-    const uint32_t dead = kt < nk ? 0u : kDead;  // steps past the end read nothing
+    const uint32_t dead = kt < nk ? 0u : kDead;
 #pragma unroll
-    for (int i = 0; i < kLPW; ++i) {
+    for (int i = 0; i < TL::LPW; ++i) {
       const int off = (int)((goff[i] + k0) | dead);
       uint16_t* d = dst + (wave + kNW * i) * 512;
-      if (i < kXLoads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrc, MHA_LDS(d), 16, off, 0, 0, 0);
-      else if (wmat[i] == 0)
+      if (src[i] == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xqsrc, MHA_LDS(d), 16, off, 0, 0, 0);
+      else if (src[i] == 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xkvsrc, MHA_LDS(d), 16, off, 0, 0, 0);
+      else if (src[i] == 2)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc0, MHA_LDS(d), 16, off, 0, 0, 0);
-      else if (wmat[i] == 1)
+      else if (src[i] == 3)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc1, MHA_LDS(d), 16, off, 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc2, MHA_LDS(d), 16, off, 0, 0, 0);
     }
   };
 
-  // Wave (wx, ww) = (wave % (NW/2), wave / (NW/2)): token blocks
-  // kXB*wx .. kXB*wx + kXB-1 times the 32-feature half ww of each of Q, K, V
-  // -- 3*kXB blocks of 32x32, kXB + 3 operand reads per 16-wide step.
-  const int wx = wave % (kNW / 2), ww = wave / (kNW / 2);
-  f32x16_t acc[3][kXB];
+  // Task tau = wave + NW*jt (live if tau < T): its token block (stage row
+  // 32*xrow + col) and the first stage row of each of its MPT weight blocks;
+  // block m lands in tile tdst (0 Q, 1 K, 2 V) at feature half tfh and tile
+  // row block tblk.
+  int xrow[TL::TPW], wrow[TL::TPW][TL::MPT], tdst[TL::TPW][TL::MPT], tfh[TL::TPW][TL::MPT], tblk[TL::TPW];
+  bool tlive[TL::TPW];
 #pragma unroll
-  for (int m = 0; m < 3; ++m)
+  for (int jt = 0; jt < TL::TPW; ++jt) {
+    const int tau = wave + kNW * jt;
+    tlive[jt] = tau < TL::T;
+    if (SELF) {
+      const int xb = tau % TL::XQB, hf = tau / TL::XQB;
+      xrow[jt] = xb;
+      tblk[jt] = xb;
 #pragma unroll
-    for (int xb = 0; xb < kXB; ++xb)
+      for (int m = 0; m < TL::MPT; ++m) {
+        wrow[jt][m] = TL::WR0 + 64 * m + 32 * hf;
+        tdst[jt][m] = m;
+        tfh[jt][m] = hf;
+      }
+    } else if (tau < TL::XQB) {  // Q task: both halves of W_Q
+      xrow[jt] = tau;
+      tblk[jt] = tau;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[m][xb][r] = 0.0f;
+      for (int m = 0; m < TL::MPT; ++m) {
+        wrow[jt][m] = TL::WR0 + 32 * m;
+        tdst[jt][m] = 0;
+        tfh[jt][m] = m;
+      }
+    } else {  // K/V task: one half of W_K and of W_V
+      const int t2 = tau - TL::XQB, xb = t2 % TL::KRB, hf = t2 / TL::KRB;
+      xrow[jt] = TL::XQB + xb;
+      tblk[jt] = xb;
+#pragma unroll
+      for (int m = 0; m < TL::MPT; ++m) {
+        wrow[jt][m] = TL::WR0 + 64 * (m + 1) + 32 * hf;
+        tdst[jt][m] = m + 1;
+        tfh[jt][m] = hf;
+      }
+    }
+  }
+  f32x16_t acc[TL::TPW][TL::MPT];
+#pragma unroll
+  for (int jt = 0; jt < TL::TPW; ++jt)
+#pragma unroll
+    for (int m = 0; m < TL::MPT; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[jt][m][r] = 0.0f;
   auto compute = [&](int buf) {
-    const uint16_t* st = lds + buf * kStage;
+    const uint16_t* st = lds + buf * TL::STAGE;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int slot = (kk * 2 + half) ^ swz;
-      u32x4_t bx[kXB], aw[3];
 #pragma unroll
-      for (int xb = 0; xb < kXB; ++xb)
-        bx[xb] = *reinterpret_cast<const u32x4_t*>(&st[(32 * (kXB * wx + xb) + col) * kBK + slot * 8]);
+      for (int jt = 0; jt < TL::TPW; ++jt) {
+        if (!tlive[jt]) continue;  // wave-uniform
+        const u32x4_t bx = *reinterpret_cast<const u32x4_t*>(&st[(32 * xrow[jt] + col) * kBK + slot * 8]);
 #pragma unroll
-      for (int m = 0; m < 3; ++m)
-        aw[m] = *reinterpret_cast<const u32x4_t*>(&st[(kRows + 64 * m + 32 * ww + col) * kBK + slot * 8]);
-#pragma unroll
-      for (int m = 0; m < 3; ++m)
-#pragma unroll
-        for (int xb = 0; xb < kXB; ++xb) acc[m][xb] = Op::mma(aw[m], bx[xb], acc[m][xb]);
+        for (int m = 0; m < TL::MPT; ++m) {
+          const u32x4_t aw = *reinterpret_cast<const u32x4_t*>(&st[(wrow[jt][m] + col) * kBK + slot * 8]);
+          acc[jt][m] = Op::mma(aw, bx, acc[jt][m]);
+        }
+      }
     }
   };
 
@@ -149,7 +214,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
     // This wave's loads of step kt have landed once at most the kS-2 later
     // steps are in flight; the barrier publishes every wave's loads and
     // retires every wave's reads of the stage the next issue overwrites.
-    wait_vmcnt<(kS - 2) * kLPW>();
+    wait_vmcnt<(kS - 2) * TL::LPW>();
     stage_barrier();
     issue(kt + kS - 1);
     compute(kt % kS);
@@ -157,59 +222,62 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   wait_vmcnt<0>();  // the loads of steps past the end
   stage_barrier();
 
-  // ---- Q, K, V tiles into LDS (over the stages, now free): 128 rows of 64
-  // features each, rounded to the input type with the bias added.  Q and K
-  // use the operand swizzle; V uses the layout of the transposing reads
-  // below.  Rows of padding tokens are zero, so masked keys multiply finite
-  // values.  A negative scale is folded into Q by negating it (exact).
+  // ---- Q, K, V tiles into LDS (over the stages, now free), 64 features per
+  // row, rounded to the input type with the bias added.  Q and K use the
+  // operand swizzle; V uses the layout of the transposing reads below.  Rows
+  // of padding tokens are zero, so masked keys multiply finite values.  A
+  // negative scale is folded into Q by negating it (exact).
   uint16_t* qt = lds;
-  uint16_t* kt_ = lds + kRows * kD;
-  uint16_t* vt = lds + 2 * kRows * kD;
+  uint16_t* kt_ = lds + TL::XQ * kD;
+  uint16_t* vt = kt_ + TL::KR * kD;
   const uint32_t qsign = a.scale < 0.0f ? 0x80008000u : 0u;
   const uint16_t* bias[3] = {static_cast<const uint16_t*>(a.bq), static_cast<const uint16_t*>(a.bk),
                              static_cast<const uint16_t*>(a.bv)};
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    uint16_t* dst = m == 0 ? qt : (m == 1 ? kt_ : vt);
+  for (int jt = 0; jt < TL::TPW; ++jt) {
+    if (!tlive[jt]) continue;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      // Registers 4jj .. 4jj+3 of acc[m][xb]: features f0 .. f0+3 of token t.
-      const int f0 = 32 * ww + 8 * jj + 4 * half;
-      float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (bias[m]) {
+    for (int m = 0; m < TL::MPT; ++m) {
+      const int mat = tdst[jt][m];
+      uint16_t* dst = mat == 0 ? qt : (mat == 1 ? kt_ : vt);
+      const int np = mat == 0 ? NPQ : NPK, nvalid = mat == 0 ? Nq : Nk;
+      const int t = 32 * tblk[jt] + col;  // tile row
+      const bool valid = t % np < nvalid && b0 + t / np < a.B;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bb[e] = Op::to_float(bias[m][h * kD + f0 + e]);
-      }
-      const int c = f0 >> 3;  // 16-byte chunk of the row
+      for (int jj = 0; jj < 4; ++jj) {
+        // Registers 4jj .. 4jj+3: features f0 .. f0+3 of tile row t.
+        const int f0 = 32 * tfh[jt][m] + 8 * jj + 4 * half;
+        float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias[mat]) {
 #pragma unroll
-      for (int xb = 0; xb < kXB; ++xb) {
-        const int t = 32 * (kXB * wx + xb) + col;
-        const bool valid = t % NP < N && b0 + t / NP < a.B;
+          for (int e = 0; e < 4; ++e) bb[e] = Op::to_float(bias[mat][h * kD + f0 + e]);
+        }
         u32x2_t v = {0u, 0u};
         if (valid) {
-          v[0] = Op::pack(acc[m][xb][4 * jj + 0] + bb[0], acc[m][xb][4 * jj + 1] + bb[1]);
-          v[1] = Op::pack(acc[m][xb][4 * jj + 2] + bb[2], acc[m][xb][4 * jj + 3] + bb[3]);
-          if (m == 0) {
+          v[0] = Op::pack(acc[jt][m][4 * jj + 0] + bb[0], acc[jt][m][4 * jj + 1] + bb[1]);
+          v[1] = Op::pack(acc[jt][m][4 * jj + 2] + bb[2], acc[jt][m][4 * jj + 3] + bb[3]);
+          if (mat == 0) {
             v[0] ^= qsign;
             v[1] ^= qsign;
           }
         }
-        const int slot = m == 2 ? (c ^ (((t >> 1) & 1) << 2)) : (c ^ operand_swizzle(t));
+        const int c = f0 >> 3;  // 16-byte chunk of the row
+        const int slot = mat == 2 ? (c ^ (((t >> 1) & 1) << 2)) : (c ^ operand_swizzle(t));
         *reinterpret_cast<u32x2_t*>(&dst[t * kD + slot * 8 + 4 * half]) = v;
       }
     }
   }
   __syncthreads();
 
-  // ---- Attention phase: wave w < 4 takes token rows 32w .. 32w+31 of the
-  // tile, i.e. queries q0 .. q0+31 of sequence `item`; the sequence's keys are
-  // tile rows kb0 .. kb0+NP-1.  Further waves are done.
-  if (wave >= kRows / 32) return;  // wave-uniform; no barrier follows
-  const int item = (32 * wave) / NP, q0 = (32 * wave) % NP, kb0 = item * NP;
+  // ---- Attention phase: wave w < XQ/32 takes Q tile rows 32w .. 32w+31,
+  // i.e. queries q0 .. q0+31 of sequence `item`, whose keys are K/V tile rows
+  // kb0 .. kb0+NPK-1.  Further waves are done.
+  if (wave >= TL::XQ / 32) return;  // wave-uniform; no barrier follows
+  const int item = (32 * wave) / NPQ, q0 = (32 * wave) % NPQ, kb0 = item * NPK;
   const int b = b0 + item;
-  if (b >= a.B || q0 >= N) return;
-  int L = N;
-  if (a.key_lens) L = min(max(a.key_lens[b], 0), N);
+  if (b >= a.B || q0 >= Nq) return;
+  int L = Nk;
+  if (a.key_lens) L = min(max(a.key_lens[b], 0), Nk);
   const int qi = q0 + col;
   const int kend = a.causal ? min(L, qi + 1) : L;  // keys this lane's query sees
   const float c2 = fabsf(a.scale) * kLog2e;
@@ -309,37 +377,49 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
       *reinterpret_cast<u32x2_t*>(&stage[col * kD + ((4 * cb + g) ^ swz) * 8 + 4 * half]) = w;
     }
   const int ldo = a.H * kD;
-  uint16_t* obase = static_cast<uint16_t*>(a.o) + ((int64_t)b * N + q0) * ldo + h * kD;
+  uint16_t* obase = static_cast<uint16_t*>(a.o) + ((int64_t)b * Nq + q0) * ldo + h * kD;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int id = lane + 64 * i, row = id >> 3, ch = id & 7;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage[row * kD + (ch ^ operand_swizzle(row)) * 8]);
-    if (q0 + row < N) *reinterpret_cast<u32x4_t*>(obase + (int64_t)row * ldo + ch * 8) = v;
+    if (q0 + row < Nq) *reinterpret_cast<u32x4_t*>(obase + (int64_t)row * ldo + ch * 8) = v;
   }
 }
 
-template <class Op, int NP>
+template <class Op, bool SELF, int NPQ, int NPK>
 hipError_t launch(const ProjAttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  constexpr int IPW = kRows / NP;
+  constexpr int IPW = Tile<SELF, NPQ, NPK>::IPW;
   const int groups = (a.B + IPW - 1) / IPW;
   const int64_t blocks = (int64_t)groups * a.H;
   if (blocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((proj_attn_kernel<Op, NP>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream, t0, t1, 0, a,
-                        groups);
+  hipExtLaunchKernelGGL((proj_attn_kernel<Op, SELF, NPQ, NPK>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream,
+                        t0, t1, 0, a, groups);
   return hipGetLastError();
+}
+
+template <class Op, int NPQ>
+hipError_t launch_cross(const ProjAttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (a.Nk <= 32) return launch<Op, false, NPQ, 32>(a, stream, t0, t1);
+  if (a.Nk <= 64) return launch<Op, false, NPQ, 64>(a, stream, t0, t1);
+  if (a.Nk <= 96) return launch<Op, false, NPQ, 96>(a, stream, t0, t1);
+  return launch<Op, false, NPQ, 128>(a, stream, t0, t1);
 }
 
 template <class Op>
 hipError_t launch_sized(const ProjAttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  if (a.N <= 32) return launch<Op, 32>(a, stream, t0, t1);
-  if (a.N <= 64) return launch<Op, 64>(a, stream, t0, t1);
-  return launch<Op, 128>(a, stream, t0, t1);
+  if (a.xkv == a.xq) {
+    if (a.Nq <= 32) return launch<Op, true, 32, 32>(a, stream, t0, t1);
+    if (a.Nq <= 64) return launch<Op, true, 64, 64>(a, stream, t0, t1);
+    return launch<Op, true, 128, 128>(a, stream, t0, t1);
+  }
+  return a.Nq <= 32 ? launch_cross<Op, 32>(a, stream, t0, t1) : launch_cross<Op, 64>(a, stream, t0, t1);
 }
 
 }  // namespace
 
-bool proj_attn_supported(int N, int D, int d_k, int d_v) {
-  return N >= 1 && N <= kRows && D >= kBK && D % kBK == 0 && d_k == kD && d_v == kD;
+bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v) {
+  if (D < kBK || D % kBK != 0 || d_k != kD || d_v != kD || Nq < 1 || Nk < 1) return false;
+  return self ? (Nq == Nk && Nq <= 128) : (Nq <= 64 && Nk <= 128);
 }
 
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
