@@ -89,8 +89,9 @@ class Oracle:
         lib.oracle_attention_rows.argtypes = [_dp, _dp, _dp, _dp, i, i, i, i, i, i, i, _ip,
                                               ctypes.c_double, i, _ip, i]
         lib.oracle_mha_proj.argtypes = [_dp] * 11 + [i] * 8 + [_ip, ctypes.c_double, i]
+        lib.oracle_decode.argtypes = [_dp] * 4 + [i] * 8 + [_ip, ctypes.c_double, i]
         for f in (lib.oracle_attention, lib.oracle_scores, lib.oracle_attention_rows,
-                  lib.oracle_mha_proj):
+                  lib.oracle_mha_proj, lib.oracle_decode):
             f.restype = ctypes.c_int
         self._lib = lib
 
@@ -174,6 +175,30 @@ class Oracle:
         self._check(st, "oracle_mha_proj")
         return out
 
+    # -- one decoding step against a key/value cache ----------------------------
+    def decode(self, q, k_cache, v_cache, mask_kind: int = MASK_CAUSAL, cache_lens=None,
+               scale=None, nthreads: int | None = None):
+        """q [B,H,Nq,dk] (the Nq newest positions); k_cache [B,Hkv,S,dk] and
+        v_cache [B,Hkv,S,dv] with cache_lens[b] filled slots (None: all S).
+        CAUSAL: query i sits at position cache_lens[b] - Nq + i; NONE: every
+        query sees the whole filled cache.  Query head h reads cache head
+        h // (H // Hkv).  Returns out [B,H,Nq,dv]."""
+        q, k, v = _f64(q), _f64(k_cache), _f64(v_cache)
+        B, H, Nq, dk = q.shape
+        Hkv, S = k.shape[1], k.shape[2]
+        dv = v.shape[3]
+        if k.shape != (B, Hkv, S, dk) or v.shape != (B, Hkv, S, dv):
+            raise ValueError("q/k_cache/v_cache shapes disagree")
+        if scale is None:
+            scale = 1.0 / np.sqrt(dk)
+        lens, lens_p = _lens(cache_lens, B)
+        out = np.empty((B, H, Nq, dv), np.float64)
+        st = self._lib.oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hkv, Nq, S, dk,
+                                     dv, int(mask_kind), lens_p, float(scale),
+                                     nthreads or default_threads())
+        self._check(st, "oracle_decode")
+        return out
+
 
 _DEFAULT: Oracle | None = None
 
@@ -202,3 +227,7 @@ def attention_rows(*args, **kwargs):
 
 def mha_proj(*args, **kwargs):
     return get().mha_proj(*args, **kwargs)
+
+
+def decode(*args, **kwargs):
+    return get().decode(*args, **kwargs)

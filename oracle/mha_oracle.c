@@ -43,6 +43,9 @@
  *     instead of the NaN the pages warn about ([AC] "Pitfalls");
  *   - key lengths are clamped to [0, Nk]; padded query rows are ordinary rows;
  *   - the causal mask is defined only for Nq == Nk (self-attention).
+ *   - decoding against a cache (oracle_decode): the new queries are the last
+ *     Nq positions of the filled cache, and a run of H / Hkv consecutive query
+ *     heads shares one cache head.
  *
  * Everything is fp64; inputs arrive as fp64 (bf16 and fp32 values convert
  * exactly).  Sums run in index order.  Threads split independent (b, h) pairs
@@ -379,4 +382,79 @@ int oracle_mha_proj(const double *x_q, const double *x_kv, const double *W_Q, co
     free(V);
     free(O);
     return st;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One decoding step against a key/value cache.                               */
+/*
+ * [AD] "How predictions are generated, per downstream task", "Translation and
+ * summarization (encoder-decoder)": during generation the keys and values of
+ * the positions already produced are kept (the KV cache) and only the newest
+ * position is computed; the cross-attention keys and values are computed once
+ * from the encoder output.  [TP] "Inference (Autoregressive Loop)": one new
+ * token per step; [AD] "This parallelism is a training-time property": the
+ * cache saves recomputing past keys and values, it does not change the result.
+ *
+ * q [B,H,Nq,dk]      the Nq newest positions of each sequence;
+ * k [B,Hkv,S,dk]     key cache, S slots per (b, cache head);
+ * v [B,Hkv,S,dv]     value cache;
+ * cache_lens [B]     filled slots L_b = clamp(cache_lens[b], 0, S) (NULL: S);
+ *                    slots >= L_b are never read.
+ * mask_kind CAUSAL   decoder self-attention: the cache already holds the new
+ *                    positions, query i sits at position p = L_b - Nq + i and
+ *                    sees keys j <= p; a query with p < 0 sees none (output 0).
+ * mask_kind NONE     cross-attention against a source's cache: every query
+ *                    sees the keys j < L_b.
+ * Shared key/value heads ([TP] "Limitations of the Original Design", on the
+ * quadratic parameter count: multi-query and grouped-query attention share the
+ * key/value projections across heads; [ZS] "Many heads, many subspaces": they
+ * are multi-head attention with key/value heads shared): H must be a multiple
+ * of Hkv and query head h reads cache head h / (H / Hkv), so each run of
+ * H / Hkv consecutive query heads shares one cache head.  Hkv == H is ordinary
+ * multi-head attention, Hkv == 1 multi-query attention.
+ */
+struct decode_ctx {
+    const double *q, *k, *v;
+    double *out;
+    int B, H, Hkv, Nq, S, dk, dv, mask_kind;
+    const int32_t *cache_lens;
+    double scale;
+};
+
+/* Number of cache slots query i may see when the cache holds L entries: all
+ * of them for cross-attention, those up to its own position when causal. */
+static int decode_visible_keys(int i, int Nq, int L, int mask_kind) {
+    if (mask_kind != ORACLE_MASK_CAUSAL) return L;
+    int p = L - Nq + i; /* position of query i in its sequence */
+    if (p < 0) return 0;
+    return p + 1;
+}
+
+static void decode_unit(void *vctx, long unit, double *scratch) {
+    struct decode_ctx *c = (struct decode_ctx *)vctx;
+    int b = (int)(unit / c->H), h = (int)(unit % c->H);
+    int g = h / (c->H / c->Hkv); /* cache head shared by query head h */
+    long bg = (long)b * c->Hkv + g;
+    const double *kc = c->k + bg * c->S * (long)c->dk;
+    const double *vc = c->v + bg * c->S * (long)c->dv;
+    int L = key_length(c->cache_lens, b, c->S);
+    for (int i = 0; i < c->Nq; ++i) {
+        int n = decode_visible_keys(i, c->Nq, L, c->mask_kind);
+        /* keys 0..n-1 are exactly the visible ones: attend to all of them */
+        attend_row(c->q + (unit * c->Nq + i) * (long)c->dk, kc, c->dk, vc, c->dv, i, n, n,
+                   ORACLE_MASK_NONE, c->dk, c->dv, c->scale, c->out + (unit * c->Nq + i) * (long)c->dv,
+                   scratch);
+    }
+}
+
+/* out [B,H,Nq,dv]. */
+int oracle_decode(const double *q, const double *k, const double *v, double *out, int B, int H,
+                  int Hkv, int Nq, int S, int dk, int dv, int mask_kind, const int32_t *cache_lens,
+                  double scale, int nthreads) {
+    if (B < 0 || H < 0 || Nq < 0 || S < 0 || dk <= 0 || dv <= 0) return ORACLE_EINVAL;
+    if (mask_kind != ORACLE_MASK_NONE && mask_kind != ORACLE_MASK_CAUSAL) return ORACLE_EINVAL;
+    if (Hkv <= 0 || Hkv > H || H % Hkv != 0) return ORACLE_EINVAL;
+    if (!q || !k || !v || !out) return ORACLE_EINVAL;
+    struct decode_ctx ctx = {q, k, v, out, B, H, Hkv, Nq, S, dk, dv, mask_kind, cache_lens, scale};
+    return parallel_for((long)B * H, nthreads, S > 0 ? S : 1, decode_unit, &ctx);
 }

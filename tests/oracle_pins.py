@@ -415,6 +415,138 @@ def pin_rejects_causal_cross(orc):
     return fails
 
 
+# --------------------------------------------------------------------------
+# Decoding against a key/value cache.
+
+def _decode_case(seed, B, H, Hkv, S, dk=16, dv=12):
+    g = _rng(seed)
+    return (g, g.standard_normal((B, H, S, dk)), g.standard_normal((B, Hkv, S, dk)),
+            g.standard_normal((B, Hkv, S, dv)))
+
+
+def _poison_tail(cache, lens):
+    """Copy of ``cache`` [B, Hkv, S, d] with every slot >= clamp(len_b, 0, S) set
+    to NaN: a correct decoder never reads them."""
+    out = cache.copy()
+    S = cache.shape[2]
+    for b, L in enumerate(lens):
+        out[b, :, min(max(int(L), 0), S):] = np.nan
+    return out
+
+
+def pin_decode_matches_full_recompute(orc):
+    """A decoding step against the cache equals causal attention recomputed over
+    the whole prefix: the cache only saves recomputing past keys and values
+    ([AD] 'This parallelism is a training-time property'; [AD] 'Translation and
+    summarization (encoder-decoder)': only the new position is computed).  The Nq
+    new queries of sequence b are rows L_b - Nq .. L_b - 1 of the full causal
+    result; a query whose position would be negative sees no key and gives 0.
+    Cache slots past L_b hold NaN.  Both sides sum the same keys in the same
+    order, so the match is exact."""
+    fails = []
+    B, H, S, Nq = 6, 3, 29, 3
+    g, q, k, _ = _decode_case(131, B, H, H, S)
+    v = g.standard_normal((B, H, S, 12))
+    full = orc.attention(q, k, v, mask_kind=CAUSAL, nthreads=2)
+    for lens in (np.array([S + 6, S, 17, 3, 1, 0], np.int32), None):
+        Ls = [S] * B if lens is None else [min(max(int(L), 0), S) for L in lens]
+        qd = np.zeros((B, H, Nq, q.shape[3]))
+        want = np.zeros((B, H, Nq, 12))
+        for b, L in enumerate(Ls):
+            for i in range(Nq):
+                p = L - Nq + i
+                if p >= 0:
+                    qd[b, :, i] = q[b, :, p]
+                    want[b, :, i] = full[b, :, p]
+                else:
+                    qd[b, :, i] = g.standard_normal((H, q.shape[3]))
+        kc = _poison_tail(k, Ls)
+        vc = _poison_tail(v, Ls)
+        out = orc.decode(qd, kc, vc, mask_kind=CAUSAL, cache_lens=lens, nthreads=2)
+        _same(fails, f"decode == full causal rows (lens={'ragged' if lens is not None else 'none'})",
+              out, want)
+    return fails
+
+
+def pin_decode_cross_is_padded_attention(orc):
+    """Cross-attention against a source's cached keys and values (computed once,
+    [AD] 'Translation and summarization (encoder-decoder)') is attention with the
+    source padding mask: every new query sees the L_b filled slots and nothing
+    else, so it equals the padded attention result exactly."""
+    fails = []
+    B, H, S, Nq = 5, 2, 23, 5
+    g, _, k, v = _decode_case(141, B, H, H, S)
+    q = g.standard_normal((B, H, Nq, k.shape[3]))
+    lens = np.array([23, 0, 40, 7, 1], np.int32)
+    want = orc.attention(q, k, v, mask_kind=NONE, key_lens=lens, nthreads=2)
+    out = orc.decode(q, _poison_tail(k, lens), _poison_tail(v, lens), mask_kind=NONE,
+                     cache_lens=lens, nthreads=2)
+    _same(fails, "cross decode == padded attention", out, want)
+    return fails
+
+
+def pin_decode_shared_heads(orc):
+    """Grouped-query and multi-query attention are multi-head attention whose
+    key/value heads are shared ([ZS] 'Many heads, many subspaces'; [TP]
+    'Limitations of the Original Design'): with Hkv cache heads, the result equals
+    ordinary multi-head decoding with each cache head repeated for its run of
+    H / Hkv consecutive query heads."""
+    fails = []
+    B, H, S, Nq = 3, 6, 19, 2
+    lens = np.array([19, 11, 2], np.int32)
+    for Hkv in (1, 2, 3):
+        g, _, k, v = _decode_case(150 + Hkv, B, H, Hkv, S)
+        q = g.standard_normal((B, H, Nq, k.shape[3]))
+        G = H // Hkv
+        for mask in (CAUSAL, NONE):
+            out = orc.decode(q, k, v, mask_kind=mask, cache_lens=lens, nthreads=2)
+            want = orc.decode(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), mask_kind=mask,
+                              cache_lens=lens, nthreads=2)
+            _same(fails, f"Hkv={Hkv} mask={mask} vs repeated heads", out, want)
+    return fails
+
+
+def pin_decode_short_caches(orc):
+    """Closed forms on short caches.  One filled slot: the single visible key
+    has weight 1, so the output is that value row exactly, whatever the query.
+    No filled slot: output 0.  Q = 0 under the causal mask: equal scores, so
+    query i returns the mean of the first L_b - Nq + i + 1 cached values."""
+    fails = []
+    B, H, S, Nq = 4, 2, 9, 3
+    g, _, k, v = _decode_case(161, B, H, H, S)
+    q = g.standard_normal((B, H, 1, k.shape[3])) * 10.0
+    out = orc.decode(q, k, v, mask_kind=CAUSAL, cache_lens=np.array([1, 1, 0, 0], np.int32),
+                     nthreads=2)
+    _same(fails, "one cached key -> its value row", out[:2, :, 0], v[:2, :, 0])
+    _same(fails, "empty cache -> 0", out[2:], np.zeros_like(out[2:]))
+    lens = np.array([9, 5, 3, 2], np.int32)
+    out = orc.decode(np.zeros((B, H, Nq, k.shape[3])), k, v, mask_kind=CAUSAL, cache_lens=lens,
+                     nthreads=2)
+    want = np.zeros_like(out)
+    for b in range(B):
+        for i in range(Nq):
+            n = int(lens[b]) - Nq + i + 1
+            if n > 0:
+                want[b, :, i] = v[b, :, :n].mean(axis=1)
+    _close(fails, "Q=0 causal decode -> mean of visible prefix", out, want, 1e-13)
+    return fails
+
+
+def pin_decode_rejects_bad_heads(orc):
+    """The query heads must split evenly over the cache heads."""
+    fails = []
+    _, q, k, v = _decode_case(171, 1, 6, 4, 5)
+    for Hkv in (4, 7):
+        kk = np.zeros((1, Hkv, 5, 16))
+        vv = np.zeros((1, Hkv, 5, 12))
+        try:
+            orc.decode(q[:, :, :1], kk, vv, nthreads=1)
+            fails.append(f"H=6, Hkv={Hkv} accepted")
+        except oracle_mod.OracleError:
+            pass
+    return fails
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_worked_example_projection,
@@ -432,6 +564,11 @@ ALL_PINS = [
     pin_projection_uniform_closed_form,
     pin_projection_one_hot_cross,
     pin_rejects_causal_cross,
+    pin_decode_matches_full_recompute,
+    pin_decode_cross_is_padded_attention,
+    pin_decode_shared_heads,
+    pin_decode_short_caches,
+    pin_decode_rejects_bad_heads,
 ]
 
 

@@ -2,7 +2,7 @@
 
 Every mutant is the oracle's C source with one textual change (a dropped term, a
 wrong sign, index or operand), compiled with gcc into a temporary directory on the
-CPU.  The pins of ``oracle_pins.py`` are run against it, and at least one must
+CPU.  Mutants run in this process, so none may read or write outside its arrays.  The pins of ``oracle_pins.py`` are run against it, and at least one must
 fail.  This shows the pins constrain every step of the oracle, not just the ones a
 particular example happens to touch.
 """
@@ -43,6 +43,12 @@ MUTANTS = [
     ("head outputs concatenated in reverse", "double *oi = c->O + ((long)b * c->Nq + i) * ldv + (long)h * c->dv;",
      "double *oi = c->O + ((long)b * c->Nq + i) * ldv + (long)(c->H - 1 - h) * c->dv;"),
     ("causal cross-attention accepted", "if (mask_kind == ORACLE_MASK_CAUSAL && Nq != Nk) return ORACLE_EINVAL;", ""),
+    ("decode position one too early", "int p = L - Nq + i;", "int p = L - Nq + i - 1;"),
+    ("decode position ignores the cache length", "int p = L - Nq + i;", "int p = i;"),
+    ("decode causal mask ignored", "if (mask_kind != ORACLE_MASK_CAUSAL) return L;", "return L;"),
+    ("decode cache head by modulo", "int g = h / (c->H / c->Hkv);", "int g = h % c->Hkv;"),
+    ("decode cache length clamped one short", "int L = key_length(c->cache_lens, b, c->S);",
+     "int L = key_length(c->cache_lens, b, c->S - 1);"),
 ]
 
 
