@@ -52,7 +52,8 @@ extern "C" {
 
 /* mask_kind */
 #define MHA_MASK_NONE 0   /* every key below key_lens[b] is visible */
-#define MHA_MASK_CAUSAL 1 /* additionally j <= i; requires Nq == Nk */
+#define MHA_MASK_CAUSAL 1 /* additionally j <= i; requires Nq == Nk (decoding: see
+                             mha_decode_forward) */
 
 /* dtype */
 #define MHA_F32 0
@@ -170,6 +171,72 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
  * device access.
  */
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention);
+
+/*
+ * Decoding against a key/value cache ([AD] "How predictions are generated, per
+ * downstream task", "Translation and summarization (encoder-decoder)": during
+ * generation the keys and values of the positions already produced are kept
+ * and only the newest position is computed, and the cross-attention keys and
+ * values are computed once from the encoder output; [TP] "Inference
+ * (Autoregressive Loop)").  Query heads may share cache heads: multi-query and
+ * grouped-query attention ([TP] "Limitations of the Original Design"; [ZS]
+ * "Many heads, many subspaces").
+ *
+ *   q       [B, H, Nq, d_k]      the Nq newest positions of each sequence
+ *   k_cache [B, H_kv, S, d_k]    key cache: S slots per (sequence, cache head)
+ *   v_cache [B, H_kv, S, d_v]    value cache
+ *   out     [B, H, Nq, d_v]      written; may not overlap the inputs
+ *   cache_lens                   device int32[B] or NULL: sequence b has
+ *                                L_b = clamp(cache_lens[b], 0, S) filled slots
+ *                                (NULL: S), already including the Nq new
+ *                                positions; slots >= L_b are never read
+ *   mask_kind  MHA_MASK_CAUSAL   decoder self-attention: query i sits at
+ *                                position L_b - Nq + i and sees the slots
+ *                                j <= L_b - Nq + i (a query whose position is
+ *                                negative sees none and gets zeros)
+ *              MHA_MASK_NONE     cross-attention against a source's cache:
+ *                                every query sees the L_b filled slots
+ *
+ * Query head h reads cache head h / (H / H_kv): each run of H / H_kv
+ * consecutive query heads shares one cache head.  H_kv == H is ordinary
+ * multi-head attention, H_kv == 1 multi-query attention.  Sizes: B, Nq,
+ * S >= 0; 1 <= H_kv <= H with H a multiple of H_kv (else MHA_ERR_INVALID_ARG);
+ * supported types and head sizes as for mha_forward, and S + 1024 slots of one
+ * cache head must span less than 2^31 bytes.  Nq need not equal S and the
+ * causal mask needs no Nq == S.
+ *
+ * The cache is cut along its slots so that a step over few sequences still
+ * fills the GPU; the pieces are combined in a second kernel, which needs
+ * `workspace`: device memory of at least mha_decode_workspace_bytes(...) bytes,
+ * 256-byte aligned, owned by the caller, contents scratch (may be NULL when
+ * that size is 0).  Calls that share a workspace must not run concurrently.
+ * Returns MHA_OK or a negative status.
+ */
+size_t mha_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype);
+
+int mha_decode_forward(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                       int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mha_decode_forward_timed -- as mha_decode_forward, plus 4 events (see the
+ * timed variants above): events[0..1] time the decoding kernel, events[2..3]
+ * the combining kernel (left untouched when mha_decode_split is 0 or 1).
+ */
+int mha_decode_forward_timed(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                             int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                             float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events);
+
+/*
+ * mha_decode_split -- how mha_decode_forward runs these sizes: the number of
+ * slot chunks each cache is cut into by the split decoding kernel (bf16/f16,
+ * d_k == d_v == 64, at most 64 query rows (H / H_kv) * Nq per cache head;
+ * 1 = no combining kernel), or 0 when the call runs on the attention kernels
+ * instead (fp32, or more query rows per cache head).  Pure function of its
+ * arguments; 0 for invalid sizes.
+ */
+int mha_decode_split(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype);
 
 /* Static description of a status code; never NULL. */
 const char* mha_status_string(int status);

@@ -214,3 +214,79 @@ def test_valid_call_without_a_device_reports_hip_error():
         pytest.skip("a device is visible")
     assert res.returncode == 0, res.stderr
     assert f"STATUS {mb.ERR_HIP}" in res.stdout, res.stdout + res.stderr
+
+
+# --------------------------------------------------------------------------
+# Decoding against a key/value cache.
+
+def dec(lib, q=P, k=P, v=P, out=P, B=2, H=4, Hkv=2, Nq=1, S=300, dk=64, dv=64, mask=1, lens=None,
+        scale=0.125, dtype=mb.BF16, ws=P, ws_bytes=1 << 30):
+    return lib.mha_decode_forward(q, k, v, out, B, H, Hkv, Nq, S, dk, dv, mask, lens, scale, dtype, ws,
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), mb.ERR_INVALID_ARG),
+    (dict(Nq=-1), mb.ERR_INVALID_ARG),
+    (dict(S=-1), mb.ERR_INVALID_ARG),
+    (dict(H=0, Hkv=0), mb.ERR_INVALID_ARG),
+    (dict(Hkv=0), mb.ERR_INVALID_ARG),
+    (dict(Hkv=3), mb.ERR_INVALID_ARG),        # 4 query heads do not split over 3 cache heads
+    (dict(Hkv=8), mb.ERR_INVALID_ARG),        # more cache heads than query heads
+    (dict(dk=0), mb.ERR_INVALID_ARG),
+    (dict(mask=2), mb.ERR_INVALID_ARG),
+    (dict(dtype=5), mb.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mb.ERR_INVALID_ARG),
+    (dict(dk=128, dv=128), mb.ERR_UNSUPPORTED),
+    (dict(dtype=mb.F32, dk=160), mb.ERR_UNSUPPORTED),
+    (dict(S=1 << 24), mb.ERR_UNSUPPORTED),    # past 32-bit offsets within one cache head
+    (dict(q=None), mb.ERR_INVALID_ARG),
+    (dict(out=None), mb.ERR_INVALID_ARG),
+    (dict(k=None), mb.ERR_INVALID_ARG),
+    (dict(v=P + 8), mb.ERR_INVALID_ARG),
+    (dict(lens=P + 1), mb.ERR_INVALID_ARG),
+])
+def test_decode_rejects(lib, kw, status):
+    assert dec(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+def test_decode_workspace_checked_when_split(lib):
+    # B=2, Hkv=2, S=8192: split into chunks, so a workspace is required.
+    need = lib.mha_decode_workspace_bytes(2, 4, 2, 1, 8192, 64, 64, mb.BF16)
+    assert need > 0
+    assert dec(lib, S=8192, ws=None) == mb.ERR_WORKSPACE
+    assert dec(lib, S=8192, ws=P + 16) == mb.ERR_WORKSPACE
+    assert dec(lib, S=8192, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+    assert "needed" in lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(B=0, q=None, out=None)])
+def test_decode_empty_is_ok(lib, kw):
+    assert dec(lib, **kw) == mb.OK
+    assert lib.mha_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("args,split", [
+    ((16, 16, 16, 1, 8192, 64, 64, mb.BF16), 8),   # long caches over few heads: 8 chunks of 1024
+    ((64, 8, 8, 1, 100, 64, 64, mb.BF16), 1),      # sentence-length caches: one chunk, no combine
+    ((1, 8, 1, 4, 4096, 64, 64, mb.F16), 16),      # multi-query, 32 rows, chunks of 256 keys
+    ((4, 8, 8, 8, 2048, 64, 64, mb.BF16), 8),
+    ((2, 64, 1, 1, 1000, 64, 64, mb.BF16), 4),     # 64 rows share the single cache head
+    ((2, 64, 1, 2, 1000, 64, 64, mb.BF16), 0),     # 128 rows: attention kernels
+    ((2, 8, 8, 1, 1000, 64, 64, mb.F32), 0),       # fp32: attention kernels
+    ((2, 8, 8, 1, 0, 64, 64, mb.BF16), 1),         # empty caches
+    ((2, 8, 3, 1, 100, 64, 64, mb.BF16), 0),       # invalid head split
+])
+def test_decode_split_plan(lib, args, split):
+    assert lib.mha_decode_split(*args) == split
+
+
+def test_decode_workspace_bytes(lib):
+    # one partial state (68 fp32) per (sequence, cache head, chunk, row), 256-byte rounded
+    assert lib.mha_decode_workspace_bytes(16, 16, 16, 1, 8192, 64, 64, mb.BF16) == 16 * 16 * 8 * 1 * 68 * 4
+    assert lib.mha_decode_workspace_bytes(1, 8, 1, 4, 4096, 64, 64, mb.F16) == 16 * 32 * 68 * 4
+    assert lib.mha_decode_workspace_bytes(64, 8, 8, 1, 100, 64, 64, mb.BF16) == 0   # one chunk
+    assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, mb.F32) == 0
+    assert lib.mha_decode_workspace_bytes(2, 8, 3, 1, 1000, 64, 64, mb.BF16) == 0
+    assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, 9) == 0

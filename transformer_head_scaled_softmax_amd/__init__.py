@@ -9,6 +9,8 @@ library's HIP kernels.  Functions raise ``MhaError`` on a non-zero status and
         q [B,H,Nq,d_k], k [B,H,Nk,d_k], v [B,H,Nk,d_v] -> out [B,H,Nq,d_v]
     proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H, ...)
         x_q [B,Nq,D], x_kv [B,Nk,D] or None -> out [B,Nq,D]
+    decode_forward(q, k_cache, v_cache, cache_lens=None, mask_kind=MASK_CAUSAL, ...)
+        q [B,H,Nq,d_k], k_cache [B,H_kv,S,d_k], v_cache [B,H_kv,S,d_v] -> out [B,H,Nq,d_v]
 """
 from __future__ import annotations
 
@@ -17,8 +19,9 @@ import math
 from ._binding import (BF16, EXPORTS, F16, F32, MASK_CAUSAL, MASK_NONE, PLAN_AUTO, PLAN_FUSED, PLAN_UNFUSED,
                        MhaError, check, load)
 
-__all__ = ["forward", "proj_forward", "proj_workspace_bytes", "MASK_NONE", "MASK_CAUSAL", "PLAN_AUTO",
-           "PLAN_UNFUSED", "PLAN_FUSED", "MhaError", "load", "EXPORTS"]
+__all__ = ["forward", "proj_forward", "proj_workspace_bytes", "decode_forward", "decode_workspace_bytes",
+           "decode_split", "MASK_NONE", "MASK_CAUSAL", "PLAN_AUTO", "PLAN_UNFUSED", "PLAN_FUSED", "MhaError",
+           "load", "EXPORTS"]
 
 
 def _dtype_code(t) -> int:
@@ -111,5 +114,50 @@ def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=
         st = lib.mha_proj_forward(*args)
     else:
         st = lib.mha_proj_forward_timed(*args, None, int(plan))
+    check(lib, st)
+    return out
+
+
+def decode_workspace_bytes(B, H, H_kv, Nq, S, d_k, d_v, dtype_code: int = BF16) -> int:
+    return int(load().mha_decode_workspace_bytes(B, H, H_kv, Nq, S, d_k, d_v, dtype_code))
+
+
+def decode_split(B, H, H_kv, Nq, S, d_k, d_v, dtype_code: int = BF16) -> int:
+    """Chunks per cache of the split decoding kernel (0: attention kernels)."""
+    return int(load().mha_decode_split(B, H, H_kv, Nq, S, d_k, d_v, dtype_code))
+
+
+def decode_forward(q, k_cache, v_cache, cache_lens=None, mask_kind: int = MASK_CAUSAL,
+                   scale: float | None = None, out=None, workspace=None, stream=None, events=None):
+    """One decoding step against a key/value cache; see mha_decode_forward in
+    include/mha.h.  ``events``: None, or 4 hipEvent_t handles (ints) for
+    mha_decode_forward_timed."""
+    import torch
+    B, H, Nq, dk = q.shape
+    Hkv, S = k_cache.shape[1], k_cache.shape[2]
+    dv = v_cache.shape[3]
+    if k_cache.shape != (B, Hkv, S, dk) or v_cache.shape != (B, Hkv, S, dv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k_cache {tuple(k_cache.shape)}, "
+                         f"v_cache {tuple(v_cache.shape)}")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, k_cache, v_cache must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=q.device)
+    lib = load()
+    need = int(lib.mha_decode_workspace_bytes(B, H, Hkv, Nq, S, dk, dv, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = (_dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), _dev_ptr(out, "out"),
+            B, H, Hkv, Nq, S, dk, dv, int(mask_kind), _lens_ptr(cache_lens, B), float(scale), code,
+            _dev_ptr(workspace, "workspace"), 0 if workspace is None else workspace.numel(), _stream(stream))
+    if events is None:
+        st = lib.mha_decode_forward(*args)
+    else:
+        import ctypes
+        arr = (ctypes.c_void_p * 4)(*events)
+        st = lib.mha_decode_forward_timed(*args, arr)
     check(lib, st)
     return out

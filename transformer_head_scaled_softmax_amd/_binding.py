@@ -25,7 +25,9 @@ ERR_HIP = -4
 
 # Every symbol include/mha.h declares.
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
-           "mha_proj_forward_timed", "mha_proj_fused", "mha_status_string", "mha_last_error", "mha_version")
+           "mha_proj_forward_timed", "mha_proj_fused", "mha_decode_workspace_bytes", "mha_decode_forward",
+           "mha_decode_forward_timed", "mha_decode_split", "mha_status_string", "mha_last_error",
+           "mha_version")
 
 
 class MhaError(RuntimeError):
@@ -59,6 +61,14 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_proj_forward_timed.restype = i
     lib.mha_proj_fused.argtypes = [i] * 7
     lib.mha_proj_fused.restype = i
+    lib.mha_decode_workspace_bytes.argtypes = [i] * 8
+    lib.mha_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.mha_decode_forward.argtypes = [vp] * 4 + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]
+    lib.mha_decode_forward.restype = i
+    lib.mha_decode_forward_timed.argtypes = lib.mha_decode_forward.argtypes + [vp]
+    lib.mha_decode_forward_timed.restype = i
+    lib.mha_decode_split.argtypes = [i] * 8
+    lib.mha_decode_split.restype = i
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_last_error.argtypes = []

@@ -46,13 +46,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int nqb) {
   if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
   const int i = qb * kRows + wave;
   const bool valid = i < a.Nq;
-  const int kend = valid ? (a.causal ? min(L, i + 1) : L) : 0;
+  const int coff = a.causal_end ? L - a.Nq : 0;  // causal: query i sees keys j <= i + coff
+  const int kend = valid ? (a.causal ? min(L, i + 1 + coff) : L) : 0;
   const int ilast = min(qb * kRows + kRows, a.Nq) - 1;
-  const int kend_blk = a.causal ? min(L, ilast + 1) : L;
+  const int kend_blk = a.causal ? min(L, ilast + 1 + coff) : L;
+  const int kvh = a.kv_group > 1 ? h / a.kv_group : h;  // key/value head read by head h
 
   const float* qp = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)i * a.q_sn;
-  const float* kp = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const float* vp = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const float* kp = static_cast<const float*>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const float* vp = static_cast<const float*>(a.v) + b * a.v_sb + kvh * a.v_sh;
   for (int c = lane; c < a.dk; c += 64) qs[wave][c] = valid ? qp[c] : 0.0f;
 
   // Scores are kept in log2 units: s * scale * log2(e), exponentiated with exp2.

@@ -66,6 +66,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
 
   int L = a.Nk;
   if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
+  const int kvh = a.kv_group > 1 ? h / a.kv_group : h;  // key/value head read by head h
+  const int coff = a.causal_end ? L - a.Nq : 0;         // causal: query i sees keys j <= i + coff
   const int q0 = qb * QB;
   const int qw0 = q0 + wave * QW;
   int qi[QS], kend[QS];
@@ -74,19 +76,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
   for (int u = 0; u < QS; ++u) {
     qi[u] = qw0 + 32 * u + col;
     qvalid[u] = qi[u] < a.Nq;
-    kend[u] = a.causal ? min(L, qi[u] + 1) : L;  // keys this query sees
+    kend[u] = a.causal ? min(L, qi[u] + 1 + coff) : L;  // keys this query sees (<= 0: none)
   }
-  const int kend_blk = a.causal ? min(L, min(q0 + QB, a.Nq)) : L;     // keys the workgroup needs
-  const int kmin_wave = a.causal ? min(L, qw0 + 1) : L;               // tiles below: no masking
-  const int kmax_wave = a.causal ? min(L, min(qw0 + QW, a.Nq)) : L;   // tiles from here: skip
-  const int ntiles = (kend_blk + kBN - 1) / kBN;
+  const int kend_blk = a.causal ? min(L, min(q0 + QB, a.Nq) + coff) : L;    // keys the workgroup needs
+  const int kmin_wave = a.causal ? min(L, qw0 + 1 + coff) : L;              // tiles below: no masking
+  const int kmax_wave = a.causal ? min(L, min(qw0 + QW, a.Nq) + coff) : L;  // tiles from here: skip
+  const int ntiles = (max(kend_blk, 0) + kBN - 1) / kBN;
 
   // Range-checked buffers over this (b, h): query rows past Nq and key/value
   // rows at or past the workgroup's key end read as zeros, so padded rows are
   // never loaded and the loads need no branches.
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_sb + kvh * a.v_sh;
   const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(qbase, ((int64_t)(a.Nq - 1) * a.q_sn + kD) * 2);
   const __amdgpu_buffer_rsrc_t ksrc =
       make_rsrc(kbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.k_sn + kD) * 2 : 0);

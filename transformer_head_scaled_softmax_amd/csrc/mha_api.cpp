@@ -348,6 +348,186 @@ int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_atte
   return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;
 }
 
+}  // extern "C"
+
+namespace {
+
+// How mha_decode_forward runs a problem: the split-key decoding kernel for
+// bf16/f16 head size 64 with at most kDecodeMaxRows query rows per cache head,
+// else the attention kernels (with shared key/value heads and the causal mask
+// anchored at the end of the cache).  A pure function of the sizes, so the
+// workspace query and the call agree.
+struct DecodePlan {
+  bool split_kernel;
+  int chunk, nsplit;
+  size_t workspace;
+};
+
+DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype) {
+  DecodePlan p{false, 0, 1, 0};
+  if (dtype == MHA_F32 || d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim) return p;
+  const int64_t R = int64_t(H / H_kv) * Nq;
+  if (R > mha::kDecodeMaxRows) return p;
+  p.split_kernel = true;
+  // Chunks of at least 256 keys (two 32-key blocks per wave), as many as give
+  // about 2048 workgroups when every cache is full: enough to spread caches of
+  // unequal length over all compute units.
+  const int64_t pairs = int64_t(B) * H_kv, quantum = mha::kDecodeChunkQuantum;
+  const int64_t max_split = std::max<int64_t>(1, (int64_t(S) + 255) / 256);
+  int64_t ns = std::min<int64_t>(max_split, std::max<int64_t>(1, (2048 + pairs - 1) / std::max<int64_t>(pairs, 1)));
+  int64_t chunk = std::max<int64_t>(quantum, (int64_t(S) + ns - 1) / ns);
+  chunk = (chunk + quantum - 1) / quantum * quantum;
+  ns = std::max<int64_t>(1, (int64_t(S) + chunk - 1) / chunk);
+  p.chunk = int(chunk);
+  p.nsplit = int(ns);
+  p.workspace = ns > 1 ? round256(size_t(pairs) * ns * R * mha::kDecodePartFloats * sizeof(float)) : 0;
+  return p;
+}
+
+int check_decode_sizes(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v) {
+  if (B < 0 || Nq < 0 || S < 0)
+    return fail(MHA_ERR_INVALID_ARG, "B, Nq, S must be >= 0 (got %d, %d, %d)", B, Nq, S);
+  if (H < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(MHA_ERR_INVALID_ARG, "need 1 <= H_kv <= H with H a multiple of H_kv (got H=%d, H_kv=%d)", H, H_kv);
+  if (d_k < 1 || d_v < 1) return fail(MHA_ERR_INVALID_ARG, "d_k, d_v must be >= 1 (got %d, %d)", d_k, d_v);
+  return MHA_OK;
+}
+
+int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                        int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                        float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        hipEvent_t const* ev) {
+  g_last_error.clear();
+  int st = check_decode_sizes(B, H, H_kv, Nq, S, d_k, d_v);
+  if (st) return st;
+  if (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)
+    return fail(MHA_ERR_INVALID_ARG, "unknown mask_kind %d", mask_kind);
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16)
+    return fail(MHA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!std::isfinite(scale)) return fail(MHA_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype == MHA_F32) {
+    if (d_k > mha::kF32MaxHeadDim || d_v > mha::kF32MaxHeadDim)
+      return fail(MHA_ERR_UNSUPPORTED, "fp32 supports d_k, d_v <= %d (got %d, %d)", mha::kF32MaxHeadDim, d_k, d_v);
+  } else if (d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim) {
+    return fail(MHA_ERR_UNSUPPORTED, "bf16/f16 support d_k == d_v == %d (got %d, %d)", mha::kMfmaHeadDim, d_k,
+                d_v);
+  }
+  if (B == 0 || Nq == 0) return MHA_OK;  // nothing to write
+  if (!q || !out) return fail(MHA_ERR_INVALID_ARG, "q and out must be non-null");
+  if (S > 0 && (!k_cache || !v_cache))
+    return fail(MHA_ERR_INVALID_ARG, "k_cache and v_cache must be non-null when S > 0");
+  const uintptr_t align = dtype == MHA_F32 ? 4 : 16;
+  if (!aligned(q, align) || !aligned(k_cache, align) || !aligned(v_cache, align) || !aligned(out, align))
+    return fail(MHA_ERR_INVALID_ARG, "q, k_cache, v_cache, out must be %d-byte aligned", (int)align);
+  if (cache_lens && !aligned(cache_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "cache_lens must be 4-byte aligned");
+  // 32-bit byte offsets within one cache head (plus the loads past its end).
+  if ((int64_t(S) + 1024) * std::max(d_k, d_v) * elem_size(dtype) >= kMaxBufferBytes)
+    return fail(MHA_ERR_UNSUPPORTED, "cache too long for 32-bit per-head offsets");
+
+  const DecodePlan plan = decode_plan(B, H, H_kv, Nq, S, d_k, d_v, dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
+  if (plan.split_kernel) {
+    if (int64_t(B) * H_kv * plan.nsplit > kMaxBlocks || int64_t(B) * H * Nq * 8 / 256 > kMaxBlocks)
+      return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (plan.workspace > 0) {
+      if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.workspace);
+      if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      if (workspace_bytes < plan.workspace)
+        return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.workspace);
+    }
+    mha::DecodeArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.cache_lens = cache_lens;
+    a.part = static_cast<float*>(workspace);
+    a.B = B;
+    a.H = H;
+    a.Hkv = H_kv;
+    a.Nq = Nq;
+    a.S = S;
+    a.causal = mask_kind == MHA_MASK_CAUSAL;
+    a.scale = scale;
+    a.chunk = plan.chunk;
+    a.nsplit = plan.nsplit;
+    hipError_t e = mha::launch_decode_mfma(a, static_cast<mha::DType>(dtype), s, evt(0), evt(1), evt(2), evt(3));
+    if (e != hipSuccess) return hip_fail(e, "decoding launch");
+    return MHA_OK;
+  }
+
+  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 128 : 64);
+  if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
+    return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+  mha::AttnArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.key_lens = cache_lens;
+  a.q_sn = d_k;
+  a.q_sh = int64_t(Nq) * d_k;
+  a.q_sb = int64_t(H) * Nq * d_k;
+  a.k_sn = d_k;
+  a.k_sh = int64_t(S) * d_k;
+  a.k_sb = int64_t(H_kv) * S * d_k;
+  a.v_sn = d_v;
+  a.v_sh = int64_t(S) * d_v;
+  a.v_sb = int64_t(H_kv) * S * d_v;
+  a.o_sn = d_v;
+  a.o_sh = int64_t(Nq) * d_v;
+  a.o_sb = int64_t(H) * Nq * d_v;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = S;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.causal = mask_kind == MHA_MASK_CAUSAL;
+  a.scale = scale;
+  a.kv_group = H / H_kv;
+  a.causal_end = 1;
+  hipError_t e = dtype == MHA_F32 ? mha::launch_attn_f32(a, s, evt(0), evt(1))
+                                  : mha::launch_attn_mfma(a, static_cast<mha::DType>(dtype), s, evt(0), evt(1));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mha_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype) {
+  if (B < 0 || Nq < 0 || S < 0 || H < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || d_k < 1 || d_v < 1)
+    return 0;
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  return decode_plan(B, H, H_kv, Nq, S, d_k, d_v, dtype).workspace;
+}
+
+int mha_decode_forward(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                       int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                       float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_forward_impl(q, k_cache, v_cache, out, B, H, H_kv, Nq, S, d_k, d_v, mask_kind, cache_lens, scale,
+                             dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mha_decode_forward_timed(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                             int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                             float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events) {
+  return decode_forward_impl(q, k_cache, v_cache, out, B, H, H_kv, Nq, S, d_k, d_v, mask_kind, cache_lens, scale,
+                             dtype, workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+int mha_decode_split(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype) {
+  if (B < 0 || Nq < 0 || S < 0 || H < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || d_k < 1 || d_v < 1)
+    return 0;
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  const DecodePlan p = decode_plan(B, H, H_kv, Nq, S, d_k, d_v, dtype);
+  return p.split_kernel ? p.nsplit : 0;
+}
+
 const char* mha_status_string(int status) {
   switch (status) {
     case MHA_OK: return "ok";
@@ -361,6 +541,6 @@ const char* mha_status_string(int status) {
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 
-int mha_version(void) { return 100; }
+int mha_version(void) { return 200; }
 
 }  // extern "C"

@@ -27,6 +27,35 @@ struct AttnArgs {
   int B, H, Nq, Nk, dk, dv;
   int causal;
   float scale;
+  // Query heads per key/value head: head h reads key/value head h / kv_group
+  // (0 or 1: one each).  Strides k_sh, v_sh step over key/value heads.
+  int kv_group;
+  // Causal mask anchored at the end of the filled keys (decoding against a
+  // cache): query i sits at position L - Nq + i and sees keys j <= L - Nq + i.
+  // 0: query i sees keys j <= i (self-attention, Nq == Nk).
+  int causal_end;
+};
+
+// One decoding step against a key/value cache, head size 64: q [B, H, Nq, 64]
+// (the Nq newest positions), caches k, v [B, Hkv, S, 64], out [B, H, Nq, 64].
+// Query head h reads cache head h / (H / Hkv); the R = (H / Hkv) * Nq query
+// rows that share a cache head are consecutive in q and out.  Sequence b has
+// L = clamp(cache_lens[b], 0, S) filled slots; with `causal`, query i sees
+// slots j <= L - Nq + i, otherwise all L.  The keys are cut into `nsplit`
+// chunks of `chunk` slots (a multiple of kDecodeChunkQuantum); with
+// nsplit > 1 each chunk leaves a partial state in `part` and
+// launch_decode_mfma runs the combining kernel after it.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* cache_lens;  // device int32[B] or nullptr
+  float* part;                // [B*Hkv, nsplit, R, kDecodePartFloats] when nsplit > 1
+  int B, H, Hkv, Nq, S;
+  int causal;
+  float scale;
+  int chunk, nsplit;
 };
 
 // One projection problem: C[m, n] = sum_k X[m, k] * W[n, k] (+ bias[n]).
@@ -79,6 +108,8 @@ hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hi
                             hipEvent_t t1 = nullptr);
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
+hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
+                              hipEvent_t t1 = nullptr, hipEvent_t t2 = nullptr, hipEvent_t t3 = nullptr);
 // Whether launch_proj_attn handles a problem: head size 64, D a multiple of
 // 64, and self-attention with Nq == Nk <= 128 or cross-attention with
 // Nq <= 64, Nk <= 128.
@@ -87,5 +118,11 @@ bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v);
 // Limits the launchers rely on.
 constexpr int kF32MaxHeadDim = 128;
 constexpr int kMfmaHeadDim = 64;
+// Decoding kernel: at most this many query rows per cache head (H / Hkv * Nq);
+// key chunks are multiples of the quantum; a partial state is (reference
+// maximum, sum, 2 pad, 64 accumulators) in fp32.
+constexpr int kDecodeMaxRows = 64;
+constexpr int kDecodeChunkQuantum = 128;
+constexpr int kDecodePartFloats = 68;
 
 }  // namespace mha

@@ -12,8 +12,13 @@ recipe"), sentences of a few dozen tokens ([AC] "The problem the paper set out t
 fix"), and long contexts where the n^2 term dominates ([TP] "The Trade-Off:
 Quadratic Cost").  No dataset is read: the draws stand in for WMT 2014 batches.
 
+Decoding workloads (one new token against long key/value caches) follow the
+pages' generation loop ([AD] "Translation and summarization (encoder-decoder)":
+keys and values of earlier positions are cached, only the new one is computed).
+
 Recipe: ``numpy.random.Generator(PCG64(seed))``; fp32 N(0,1) draws in the order
-(x_q | q), (x_kv | k), (v), W_Q, W_K, W_V, W_O, key_lens; rounding to bf16 is
+(x_q | q), (x_kv | k | k_cache), (v | v_cache), W_Q, W_K, W_V, W_O,
+(key_lens | cache_lens); rounding to bf16 is
 round-to-nearest-even; Xavier-uniform weights are U(-a, a) with
 a = sqrt(6 / (fan_in + fan_out)); key lengths are i.i.d. discrete uniform over the
 inclusive range.
@@ -44,10 +49,18 @@ class Workload:
     cross: bool                 # keys/values from a second sequence
     seed: int
     description: str
+    # Decoding against a key/value cache: Nq new positions per sequence, Nk the
+    # cache capacity S, ``lens`` the filled slots, Hkv cache heads (None: H).
+    decode: bool = False
+    Hkv: int | None = None
 
     @property
     def D(self) -> int:
         return self.H * self.d
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
 
 WORKLOADS = {
@@ -66,6 +79,12 @@ WORKLOADS = {
                  "(B=32, Nq=64, Nk=80, d_model=1024, h=16, source lengths U{20..80})"),
         Workload("long_causal", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 5,
                  "long-context causal self-attention (B=2, n=8192, h=16, d=64)"),
+        Workload("long_decode", 16, 16, 1, 8192, 64, "bf16", MASK_CAUSAL, (1024, 8192), False, False, 6,
+                 "one decoding step against long key/value caches (B=16, h=16, d=64, one new token, "
+                 "cache of 8192 slots filled U{1024..8192})", decode=True),
+        Workload("long_decode_gqa", 16, 16, 1, 8192, 64, "bf16", MASK_CAUSAL, (1024, 8192), False, False, 7,
+                 "one decoding step with grouped-query attention (B=16, h=16 query heads over 4 cache "
+                 "heads, d=64, one new token, cache of 8192 slots filled U{1024..8192})", decode=True, Hkv=4),
     ]
 }
 
@@ -131,8 +150,22 @@ def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None):
             "key_lens": key_lens}
 
 
+def decode_inputs(B, H, Hkv, Nq, S, dk, dv, dtype, seed, lens=None):
+    """q [B,H,Nq,dk] (the new positions), k_cache [B,Hkv,S,dk], v_cache
+    [B,Hkv,S,dv] ~ N(0,1) over every slot; cache_lens drawn from ``lens`` =
+    (lo, hi) if given."""
+    g = generator(seed)
+    q = normal(g, (B, H, Nq, dk), dtype)
+    k = normal(g, (B, Hkv, S, dk), dtype)
+    v = normal(g, (B, Hkv, S, dv), dtype)
+    cache_lens = key_lengths(g, B, *lens) if lens is not None else None
+    return {"q": q, "k_cache": k, "v_cache": v, "cache_lens": cache_lens}
+
+
 def workload_inputs(w: Workload, seed: int | None = None):
     seed = w.seed if seed is None else seed
+    if w.decode:
+        return decode_inputs(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
     if w.proj:
         return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens)
     return core_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
