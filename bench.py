@@ -40,10 +40,12 @@ CSRC = ROOT / "transformer_head_scaled_softmax_amd" / "csrc"
 KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip", "mfma_util.h"],
                   "attention": ["attn_mfma.hip", "mfma_util.h"],
                   "qkv_attention": ["proj_attn.hip", "mfma_util.h"],
-                  "out_projection": ["gemm_mfma.hip", "mfma_util.h"], "attention_f32": ["attn_f32.hip"]}
+                  "out_projection": ["gemm_mfma.hip", "mfma_util.h"], "attention_f32": ["attn_f32.hip"],
+                  "decode": ["decode_mfma.hip", "mfma_util.h"], "decode_combine": ["decode_mfma.hip", "mfma_util.h"]}
 KERNEL_SYMBOLS = {"qkv_projection": "gemm_mfma_kernel", "attention": "attn_mfma_kernel",
                   "qkv_attention": "proj_attn_kernel", "out_projection": "gemm_mfma_kernel",
-                  "attention_f32": "attn_f32_kernel"}
+                  "attention_f32": "attn_f32_kernel", "decode": "decode_mfma_kernel",
+                  "decode_combine": "decode_combine_kernel"}
 
 
 def log(*a):
@@ -73,6 +75,33 @@ def attention_bytes(w, lens):
     qo = 2 * w.B * w.H * w.Nq * w.d * es
     kv = 2 * int(Ls.sum()) * w.H * w.d * es
     return qo + kv + (0 if lens is None else 4 * w.B)
+
+
+def decode_visible(w, lens):
+    """Visible (query, cache slot) pairs of one decoding step, over all query heads:
+    query i of Nq sees slots j <= L - Nq + i under the causal mask, all L otherwise."""
+    Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
+    i = np.arange(w.Nq)
+    tot = 0
+    for L in Ls:
+        tot += int(np.clip(L - w.Nq + i + 1, 0, None).sum()) if w.mask == 1 else int(L) * w.Nq
+    return tot * w.H
+
+
+def decode_work(w, lens, nsplit):
+    """(flops, bytes) per launch of the decoding kernel and of the combining
+    kernel.  Bytes: the new queries, the filled cache slots of every cache head
+    (read once whatever the head grouping), the fill lengths, and the output rows
+    (written by the combining kernel when the caches are cut into chunks)."""
+    es = ES[w.dtype]
+    Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
+    qo = w.B * w.H * w.Nq * w.d * es
+    kv = 2 * int(Ls.sum()) * w.kv_heads * w.d * es
+    lb = 0 if lens is None else 4 * w.B
+    f = 4.0 * w.d * decode_visible(w, lens)
+    if nsplit > 1:
+        return {"decode": (f, qo + kv + lb), "decode_combine": (0.0, qo + lb)}
+    return {"decode": (f, 2 * qo + kv + lb)}
 
 
 def projection_flops(w):
@@ -184,6 +213,11 @@ def cpu_baseline(w, inp_sets, seconds_target):
             qkv_f, out_f = projection_flops(w)
             done_flops += qkv_f + out_f + attention_flops(w, inp["key_lens"])
             sample = "whole batches"
+        elif w.decode:
+            oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"], mask_kind=w.mask,
+                          cache_lens=inp["cache_lens"], nthreads=threads)
+            done_flops += 4.0 * w.d * decode_visible(w, inp["cache_lens"])
+            sample = "whole batches"
         elif w.Nq * w.Nk > 1 << 22:
             from transformer_head_scaled_softmax_amd import synth
             rows = synth.sample_rows(w.B, w.H, w.Nq, seed=100 + n, n_random=4)
@@ -253,6 +287,8 @@ def main():
     # shared by every batch.
     if w.proj:
         per_set = (w.B * w.Nq * w.D * 2 + (w.B * w.Nk * w.D if w.cross else 0)) * es
+    elif w.decode:
+        per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.kv_heads * w.Nk * w.d) * es
     else:
         per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.H * w.Nk * w.d) * es
     nsets = args.sets or int(min(64, max(2, math.ceil((1 << 30) / per_set))))
@@ -261,10 +297,16 @@ def main():
     host_sets, dev_sets = [], []
     for s in range(nsets):
         inp = synth.workload_inputs(w, seed=w.seed * 1000 + s)
+        if w.decode:
+            inp["key_lens"] = inp["cache_lens"]
         lens_t = None if inp["key_lens"] is None else torch.from_numpy(inp["key_lens"]).to(dev)
         if w.proj:
             d = {"x_q": to_dev(inp["x_q"]), "x_kv": to_dev(inp["x_kv"]), "key_lens": lens_t,
                  "out": torch.empty((w.B, w.Nq, w.D), dtype=tdt, device=dev)}
+        elif w.decode:
+            d = {n_: to_dev(inp[n_]) for n_ in ("q", "k_cache", "v_cache")}
+            d["key_lens"] = lens_t
+            d["out"] = torch.empty((w.B, w.H, w.Nq, w.d), dtype=tdt, device=dev)
         else:
             d = {n_: to_dev(inp[n_]) for n_ in ("q", "k", "v")}
             d["key_lens"] = lens_t
@@ -302,6 +344,26 @@ def main():
         else:
             stage_events = {"qkv_projection": (0, 1), "attention": (2, 3), "out_projection": (4, 5)}
         n_events = 6
+    elif w.decode:
+        Hkv = w.kv_heads
+        need = lib.mha_decode_workspace_bytes(w.B, w.H, Hkv, w.Nq, w.Nk, w.d, w.d, code)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        nsplit = lib.mha_decode_split(w.B, w.H, Hkv, w.Nq, w.Nk, w.d, w.d, code)
+        assert nsplit >= 1, "the decoding workloads run on the split decoding kernel"
+
+        def step(i, sp, events=None):
+            d = dev_sets[i % nsets]
+            lp = None if d["key_lens"] is None else d["key_lens"].data_ptr()
+            argsv = (d["q"].data_ptr(), d["k_cache"].data_ptr(), d["v_cache"].data_ptr(), d["out"].data_ptr(),
+                     w.B, w.H, Hkv, w.Nq, w.Nk, w.d, w.d, w.mask, lp, scale, code, ws.data_ptr(), need, sp)
+            st = (lib.mha_decode_forward(*argsv) if events is None
+                  else lib.mha_decode_forward_timed(*argsv, events))
+            if st != 0:
+                raise RuntimeError(lib.mha_last_error().decode())
+        stage_events = {"decode": (0, 1)}
+        if nsplit > 1:
+            stage_events["decode_combine"] = (2, 3)
+        n_events = 4
     else:
         def step(i, sp, events=None):
             d = dev_sets[i % nsets]
@@ -382,6 +444,10 @@ def main():
         qkv_f, out_f = projection_flops(w)
         flops = qkv_f + out_f + att_f
         bytes_ = float(np.mean([proj_path_bytes(w, L) for L in used]))
+    elif w.decode:
+        works = [decode_work(w, L, nsplit) for L in used]
+        flops = float(np.mean([sum(f for f, _ in wk.values()) for wk in works]))
+        bytes_ = float(np.mean([decode_work(w, L, 1)["decode"][1] for L in used]))  # whole step
     else:
         flops = att_f
         bytes_ = float(np.mean([attention_bytes(w, L) for L in used]))
@@ -395,7 +461,9 @@ def main():
                    "d_v": w.d, "D": w.D if w.proj else None, "projections": w.proj,
                    "mask": "causal" if w.mask == 1 else "none",
                    "key_lens": None if w.lens is None else f"U{{{w.lens[0]}..{w.lens[1]}}}",
-                   "input_sets": nsets, "issue": "HIP graph replay"},
+                   "input_sets": nsets, "issue": "HIP graph replay",
+                   **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "chunks": nsplit}
+                      if w.decode else {})},
         "tokens_per_s": round(w.B * w.Nq / sec, 1),
         "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 5),
         "hbm_gbps_algorithmic": round(bytes_ / sec / 1e9, 1),
@@ -412,6 +480,9 @@ def main():
         if dom in ("attention", "qkv_attention"):  # these depend on the drawn key lengths
             f_ = float(np.mean([stage_work(w, L)[dom][0] for L in used]))
             b_ = float(np.mean([stage_work(w, L)[dom][1] for L in used]))
+    elif w.decode:
+        f_ = float(np.mean([wk[dom][0] for wk in works]))
+        b_ = float(np.mean([wk[dom][1] for wk in works]))
     else:
         f_, b_ = flops, bytes_
     result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom, w.name)

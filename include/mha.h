@@ -205,12 +205,14 @@ int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_atte
  * cache head must span less than 2^31 bytes.  Nq need not equal S and the
  * causal mask needs no Nq == S.
  *
- * The cache is cut along its slots so that a step over few sequences still
- * fills the GPU; the pieces are combined in a second kernel, which needs
- * `workspace`: device memory of at least mha_decode_workspace_bytes(...) bytes,
- * 256-byte aligned, owned by the caller, contents scratch (may be NULL when
- * that size is 0).  Calls that share a workspace must not run concurrently.
- * Returns MHA_OK or a negative status.
+ * The filled slots of all caches are shared out evenly over the GPU, so that
+ * a step over few sequences or caches of unequal length still keeps every
+ * compute unit busy; caches cut between several workers are merged by a
+ * second kernel, which needs `workspace`: device memory of at least
+ * mha_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by the
+ * caller, contents scratch (may be NULL when that size is 0).  Calls that
+ * share a workspace must not run concurrently.  Returns MHA_OK or a negative
+ * status.
  */
 size_t mha_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype);
 
@@ -221,7 +223,8 @@ int mha_decode_forward(const void* q, const void* k_cache, const void* v_cache, 
 /*
  * mha_decode_forward_timed -- as mha_decode_forward, plus 4 events (see the
  * timed variants above): events[0..1] time the decoding kernel, events[2..3]
- * the combining kernel (left untouched when mha_decode_split is 0 or 1).
+ * the merging kernel (left untouched when mha_decode_split is 0: then
+ * events[0..1] time the attention kernel).
  */
 int mha_decode_forward_timed(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
                              int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
@@ -230,11 +233,11 @@ int mha_decode_forward_timed(const void* q, const void* k_cache, const void* v_c
 
 /*
  * mha_decode_split -- how mha_decode_forward runs these sizes: the number of
- * slot chunks each cache is cut into by the split decoding kernel (bf16/f16,
- * d_k == d_v == 64, at most 64 query rows (H / H_kv) * Nq per cache head;
- * 1 = no combining kernel), or 0 when the call runs on the attention kernels
- * instead (fp32, or more query rows per cache head).  Pure function of its
- * arguments; 0 for invalid sizes.
+ * workers (one wave each) the filled cache slots are shared out over by the
+ * decoding kernel (bf16/f16, d_k == d_v == 64, at most 64 query rows
+ * (H / H_kv) * Nq per cache head), or 0 when the call runs on the attention
+ * kernels instead (fp32, or more query rows per cache head).  Pure function of
+ * its arguments; 0 for invalid sizes.
  */
 int mha_decode_split(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype);
 

@@ -251,13 +251,12 @@ def test_decode_rejects(lib, kw, status):
     assert lib.mha_last_error().decode()
 
 
-def test_decode_workspace_checked_when_split(lib):
-    # B=2, Hkv=2, S=8192: split into chunks, so a workspace is required.
-    need = lib.mha_decode_workspace_bytes(2, 4, 2, 1, 8192, 64, 64, mb.BF16)
+def test_decode_workspace_checked(lib):
+    need = lib.mha_decode_workspace_bytes(2, 4, 2, 1, 300, 64, 64, mb.BF16)
     assert need > 0
-    assert dec(lib, S=8192, ws=None) == mb.ERR_WORKSPACE
-    assert dec(lib, S=8192, ws=P + 16) == mb.ERR_WORKSPACE
-    assert dec(lib, S=8192, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+    assert dec(lib, ws=None) == mb.ERR_WORKSPACE
+    assert dec(lib, ws=P + 16) == mb.ERR_WORKSPACE
+    assert dec(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
     assert "needed" in lib.mha_last_error().decode()
 
 
@@ -267,26 +266,32 @@ def test_decode_empty_is_ok(lib, kw):
     assert lib.mha_last_error().decode() == ""
 
 
-@pytest.mark.parametrize("args,split", [
-    ((16, 16, 16, 1, 8192, 64, 64, mb.BF16), 8),   # long caches over few heads: 8 chunks of 1024
-    ((64, 8, 8, 1, 100, 64, 64, mb.BF16), 1),      # sentence-length caches: one chunk, no combine
-    ((1, 8, 1, 4, 4096, 64, 64, mb.F16), 16),      # multi-query, 32 rows, chunks of 256 keys
-    ((4, 8, 8, 8, 2048, 64, 64, mb.BF16), 8),
-    ((2, 64, 1, 1, 1000, 64, 64, mb.BF16), 4),     # 64 rows share the single cache head
-    ((2, 64, 1, 2, 1000, 64, 64, mb.BF16), 0),     # 128 rows: attention kernels
-    ((2, 8, 8, 1, 1000, 64, 64, mb.F32), 0),       # fp32: attention kernels
-    ((2, 8, 8, 1, 0, 64, 64, mb.BF16), 1),         # empty caches
-    ((2, 8, 3, 1, 100, 64, 64, mb.BF16), 0),       # invalid head split
+@pytest.mark.parametrize("args,waves", [
+    ((16, 16, 16, 1, 8192, 64, 64, mb.BF16), 1024),   # one wave per SIMD of the 256 CUs
+    ((64, 8, 8, 1, 100, 64, 64, mb.BF16), 1024),
+    ((1, 8, 1, 4, 4096, 64, 64, mb.F16), 1024),       # multi-query, 32 rows
+    ((2, 64, 1, 1, 1000, 64, 64, mb.BF16), 1024),     # 64 rows share the single cache head
+    ((2, 64, 1, 2, 1000, 64, 64, mb.BF16), 0),        # 128 rows: attention kernels
+    ((2, 8, 8, 1, 1000, 64, 64, mb.F32), 0),          # fp32: attention kernels
+    ((2, 8, 8, 1, 0, 64, 64, mb.BF16), 1024),         # empty caches
+    ((2, 8, 3, 1, 100, 64, 64, mb.BF16), 0),          # invalid head split
 ])
-def test_decode_split_plan(lib, args, split):
-    assert lib.mha_decode_split(*args) == split
+def test_decode_split_plan(lib, args, waves):
+    assert lib.mha_decode_split(*args) == waves
+
+
+def _r256(n):
+    return (n + 255) // 256 * 256
 
 
 def test_decode_workspace_bytes(lib):
-    # one partial state (68 fp32) per (sequence, cache head, chunk, row), 256-byte rounded
-    assert lib.mha_decode_workspace_bytes(16, 16, 16, 1, 8192, 64, 64, mb.BF16) == 16 * 16 * 8 * 1 * 68 * 4
-    assert lib.mha_decode_workspace_bytes(1, 8, 1, 4, 4096, 64, 64, mb.F16) == 16 * 32 * 68 * 4
-    assert lib.mha_decode_workspace_bytes(64, 8, 8, 1, 100, 64, 64, mb.BF16) == 0   # one chunk
+    # one partial state (68 fp32) per (cache + wave) and row, then an int2 span per cache
+    assert lib.mha_decode_workspace_bytes(16, 16, 16, 1, 8192, 64, 64, mb.BF16) == \
+        _r256((256 + 1024) * 1 * 68 * 4) + _r256(256 * 8)
+    assert lib.mha_decode_workspace_bytes(1, 8, 1, 4, 4096, 64, 64, mb.F16) == \
+        _r256((1 + 1024) * 32 * 68 * 4) + _r256(8)
+    assert lib.mha_decode_workspace_bytes(2, 64, 1, 1, 1000, 64, 64, mb.BF16) == \
+        _r256((2 + 1024) * 64 * 68 * 4) + _r256(16)
     assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, mb.F32) == 0
     assert lib.mha_decode_workspace_bytes(2, 8, 3, 1, 1000, 64, 64, mb.BF16) == 0
     assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, 9) == 0

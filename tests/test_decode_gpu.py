@@ -1,11 +1,12 @@
 """GPU parity of mha_decode_forward (one decoding step against a key/value
 cache, with shared key/value heads) against the fp64 oracle's decode.
 
-Every call goes through the C ABI.  Shapes cover the split decoding kernel (one
-and several chunks per cache, 32-key blocks, 4 waves per chunk, 1..64 query
-rows per cache head) and the attention-kernel path it hands larger row counts
-and fp32 to; cache lengths cover 0, 1, block and chunk edges, clamping past S,
-and more new queries than filled slots.  Tolerances are the suite's (gpu_util).
+Every call goes through the C ABI.  Shapes cover the balanced decoding kernel
+(caches cut between waves and merged, caches covered whole by one wave, waves
+spanning many short caches, 32-slot blocks, 1..64 query rows per cache head)
+and the attention-kernel path it hands larger row counts and fp32 to; cache
+lengths cover 0, 1, block edges, clamping past S, and more new queries than
+filled slots.  Tolerances are the suite's (gpu_util).
 """
 import numpy as np
 import pytest
@@ -99,10 +100,19 @@ def test_causal_positions_near_edges(Nq, lens):
     check(len(lens), 8, 8, Nq, 4096, "bf16", CAUSAL, lens, 200 + Nq, expect_split=True)
 
 
-def test_multi_chunk_long_caches():
-    """Several chunks per cache with the combining kernel (2 caches x 8 heads)."""
+def test_long_caches_cut_between_waves():
+    """Few long caches: each is cut between many waves and merged."""
     assert mha.decode_split(2, 8, 8, 1, 16384, 64, 64, 1) > 1
     check(2, 8, 8, 1, 16384, "bf16", CAUSAL, [16384, 9000], 300, expect_split=True)
+
+
+@pytest.mark.parametrize("B,S,Hkv,H,Nq", [(300, 20, 8, 8, 1), (1000, 40, 2, 8, 2), (70, 3, 1, 4, 3)])
+def test_many_short_caches_per_wave(B, S, Hkv, H, Nq):
+    """Many short caches: waves span several caches (whole and cut ones), and
+    more than 64 batch entries exercise the lane-blocked prefix sums."""
+    lens = synth.key_lengths(synth.generator(800 + B), B, 0, S + 2)
+    check(B, H, Hkv, Nq, S, "bf16", CAUSAL, lens, 810 + B, expect_split=True)
+    check(B, H, Hkv, Nq, S, "bf16", NONE, lens, 820 + B, expect_split=True)
 
 
 def test_scale_variants():

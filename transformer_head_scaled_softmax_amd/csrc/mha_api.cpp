@@ -352,35 +352,28 @@ int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_atte
 
 namespace {
 
-// How mha_decode_forward runs a problem: the split-key decoding kernel for
+// How mha_decode_forward runs a problem: the balanced decoding kernel for
 // bf16/f16 head size 64 with at most kDecodeMaxRows query rows per cache head,
 // else the attention kernels (with shared key/value heads and the causal mask
 // anchored at the end of the cache).  A pure function of the sizes, so the
-// workspace query and the call agree.
+// workspace query and the call agree.  Workspace: one partial state per
+// (cache + wave) and row, then one span entry per cache.
 struct DecodePlan {
   bool split_kernel;
-  int chunk, nsplit;
-  size_t workspace;
+  int waves;
+  size_t span_off, workspace;
 };
 
-DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, int dtype) {
-  DecodePlan p{false, 0, 1, 0};
+DecodePlan decode_plan(int B, int H, int H_kv, int Nq, int d_k, int d_v, int dtype) {
+  DecodePlan p{false, 0, 0, 0};
   if (dtype == MHA_F32 || d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim) return p;
   const int64_t R = int64_t(H / H_kv) * Nq;
   if (R > mha::kDecodeMaxRows) return p;
   p.split_kernel = true;
-  // Chunks of at least 256 keys (two 32-key blocks per wave), as many as give
-  // about 2048 workgroups when every cache is full: enough to spread caches of
-  // unequal length over all compute units.
-  const int64_t pairs = int64_t(B) * H_kv, quantum = mha::kDecodeChunkQuantum;
-  const int64_t max_split = std::max<int64_t>(1, (int64_t(S) + 255) / 256);
-  int64_t ns = std::min<int64_t>(max_split, std::max<int64_t>(1, (2048 + pairs - 1) / std::max<int64_t>(pairs, 1)));
-  int64_t chunk = std::max<int64_t>(quantum, (int64_t(S) + ns - 1) / ns);
-  chunk = (chunk + quantum - 1) / quantum * quantum;
-  ns = std::max<int64_t>(1, (int64_t(S) + chunk - 1) / chunk);
-  p.chunk = int(chunk);
-  p.nsplit = int(ns);
-  p.workspace = ns > 1 ? round256(size_t(pairs) * ns * R * mha::kDecodePartFloats * sizeof(float)) : 0;
+  p.waves = mha::kDecodeWaves;
+  const size_t caches = size_t(B) * H_kv;
+  p.span_off = round256((caches + p.waves) * R * mha::kDecodePartFloats * sizeof(float));
+  p.workspace = p.span_off + round256(caches * 2 * sizeof(int32_t));
   return p;
 }
 
@@ -424,18 +417,16 @@ int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache,
   if ((int64_t(S) + 1024) * std::max(d_k, d_v) * elem_size(dtype) >= kMaxBufferBytes)
     return fail(MHA_ERR_UNSUPPORTED, "cache too long for 32-bit per-head offsets");
 
-  const DecodePlan plan = decode_plan(B, H, H_kv, Nq, S, d_k, d_v, dtype);
+  const DecodePlan plan = decode_plan(B, H, H_kv, Nq, d_k, d_v, dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
   if (plan.split_kernel) {
-    if (int64_t(B) * H_kv * plan.nsplit > kMaxBlocks || int64_t(B) * H * Nq * 8 / 256 > kMaxBlocks)
+    if (int64_t(B) * H * Nq / 4 > kMaxBlocks || int64_t(B) * H_kv + plan.waves > (int64_t(1) << 31) / 64)
       return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
-    if (plan.workspace > 0) {
-      if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.workspace);
-      if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-      if (workspace_bytes < plan.workspace)
-        return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.workspace);
-    }
+    if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.workspace);
+    if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < plan.workspace)
+      return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, plan.workspace);
     mha::DecodeArgs a{};
     a.q = q;
     a.k = k_cache;
@@ -443,6 +434,7 @@ int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache,
     a.out = out;
     a.cache_lens = cache_lens;
     a.part = static_cast<float*>(workspace);
+    a.span = reinterpret_cast<int2*>(static_cast<char*>(workspace) + plan.span_off);
     a.B = B;
     a.H = H;
     a.Hkv = H_kv;
@@ -450,8 +442,7 @@ int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache,
     a.S = S;
     a.causal = mask_kind == MHA_MASK_CAUSAL;
     a.scale = scale;
-    a.chunk = plan.chunk;
-    a.nsplit = plan.nsplit;
+    a.waves = plan.waves;
     hipError_t e = mha::launch_decode_mfma(a, static_cast<mha::DType>(dtype), s, evt(0), evt(1), evt(2), evt(3));
     if (e != hipSuccess) return hip_fail(e, "decoding launch");
     return MHA_OK;
@@ -502,7 +493,7 @@ size_t mha_decode_workspace_bytes(int B, int H, int H_kv, int Nq, int S, int d_k
   if (B < 0 || Nq < 0 || S < 0 || H < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || d_k < 1 || d_v < 1)
     return 0;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
-  return decode_plan(B, H, H_kv, Nq, S, d_k, d_v, dtype).workspace;
+  return decode_plan(B, H, H_kv, Nq, d_k, d_v, dtype).workspace;
 }
 
 int mha_decode_forward(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
@@ -524,8 +515,8 @@ int mha_decode_split(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, in
   if (B < 0 || Nq < 0 || S < 0 || H < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0 || d_k < 1 || d_v < 1)
     return 0;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
-  const DecodePlan p = decode_plan(B, H, H_kv, Nq, S, d_k, d_v, dtype);
-  return p.split_kernel ? p.nsplit : 0;
+  const DecodePlan p = decode_plan(B, H, H_kv, Nq, d_k, d_v, dtype);
+  return p.split_kernel ? p.waves : 0;
 }
 
 const char* mha_status_string(int status) {

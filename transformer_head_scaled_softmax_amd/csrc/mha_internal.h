@@ -41,21 +41,27 @@ struct AttnArgs {
 // Query head h reads cache head h / (H / Hkv); the R = (H / Hkv) * Nq query
 // rows that share a cache head are consecutive in q and out.  Sequence b has
 // L = clamp(cache_lens[b], 0, S) filled slots; with `causal`, query i sees
-// slots j <= L - Nq + i, otherwise all L.  The keys are cut into `nsplit`
-// chunks of `chunk` slots (a multiple of kDecodeChunkQuantum); with
-// nsplit > 1 each chunk leaves a partial state in `part` and
-// launch_decode_mfma runs the combining kernel after it.
+// slots j <= L - Nq + i, otherwise all L.
+//
+// The filled slots of all caches, laid end to end (cache (b, g) at
+// Hkv * sum_{b' < b} L_b' + g * L_b), are cut into `waves` equal ranges, one
+// per wave of the decoding kernel.  A wave's range falls into pieces at cache
+// boundaries; a piece that is a whole cache writes its output rows, any other
+// piece leaves its softmax state in record (cache + wave) of `part`, and the
+// wave that starts a cache writes the first and last wave over it to `span`.
+// The combining kernel then merges the records of the caches that were cut.
 struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
   void* out;
   const int32_t* cache_lens;  // device int32[B] or nullptr
-  float* part;                // [B*Hkv, nsplit, R, kDecodePartFloats] when nsplit > 1
+  float* part;                // [B*Hkv + waves, R, kDecodePartFloats]
+  int2* span;                 // [B*Hkv]
   int B, H, Hkv, Nq, S;
   int causal;
   float scale;
-  int chunk, nsplit;
+  int waves;
 };
 
 // One projection problem: C[m, n] = sum_k X[m, k] * W[n, k] (+ bias[n]).
@@ -119,10 +125,10 @@ bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v);
 constexpr int kF32MaxHeadDim = 128;
 constexpr int kMfmaHeadDim = 64;
 // Decoding kernel: at most this many query rows per cache head (H / Hkv * Nq);
-// key chunks are multiples of the quantum; a partial state is (reference
-// maximum, sum, 2 pad, 64 accumulators) in fp32.
+// one wave per workgroup and one per SIMD of the 256 compute units; a partial
+// state is (reference maximum, sum, 2 pad, 64 accumulators) in fp32.
 constexpr int kDecodeMaxRows = 64;
-constexpr int kDecodeChunkQuantum = 128;
+constexpr int kDecodeWaves = 256 * 4;
 constexpr int kDecodePartFloats = 68;
 
 }  // namespace mha
