@@ -462,7 +462,7 @@ def main():
                    "mask": "causal" if w.mask == 1 else "none",
                    "key_lens": None if w.lens is None else f"U{{{w.lens[0]}..{w.lens[1]}}}",
                    "input_sets": nsets, "issue": "HIP graph replay",
-                   **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "chunks": nsplit}
+                   **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "waves": nsplit}
                       if w.decode else {})},
         "tokens_per_s": round(w.B * w.Nq / sec, 1),
         "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 5),
