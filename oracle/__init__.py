@@ -90,8 +90,10 @@ class Oracle:
                                               ctypes.c_double, i, _ip, i]
         lib.oracle_mha_proj.argtypes = [_dp] * 11 + [i] * 8 + [_ip, ctypes.c_double, i]
         lib.oracle_decode.argtypes = [_dp] * 4 + [i] * 8 + [_ip, ctypes.c_double, i]
+        lib.oracle_mha_proj_ln.argtypes = ([_dp] * 12 + [ctypes.c_double, _dp] + [i] * 8
+                                           + [_ip, ctypes.c_double, i])
         for f in (lib.oracle_attention, lib.oracle_scores, lib.oracle_attention_rows,
-                  lib.oracle_mha_proj, lib.oracle_decode):
+                  lib.oracle_mha_proj, lib.oracle_decode, lib.oracle_mha_proj_ln):
             f.restype = ctypes.c_int
         self._lib = lib
 
@@ -175,6 +177,30 @@ class Oracle:
         self._check(st, "oracle_mha_proj")
         return out
 
+    def mha_proj_ln(self, x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None,
+                    b_O=None, gamma=None, beta=None, eps: float = 1e-5, mask_kind: int = MASK_NONE,
+                    key_lens=None, scale=None, nthreads: int | None = None):
+        """LayerNorm(x_q + MHA(x_q, x_kv)) per token over its D features; gamma, beta
+        [D] or None (1 and 0).  Other arguments as mha_proj.  Returns [B,Nq,D]."""
+        x_q = _f64(x_q)
+        B, Nq, D = x_q.shape
+        x_kv = None if x_kv is None else _f64(x_kv)
+        Nk = Nq if x_kv is None else x_kv.shape[1]
+        W_Q, W_K, W_V, W_O = _f64(W_Q), _f64(W_K), _f64(W_V), _f64(W_O)
+        dk = W_Q.shape[0] // H
+        dv = W_V.shape[0] // H
+        if scale is None:
+            scale = 1.0 / np.sqrt(dk)
+        vecs = [None if b is None else _f64(b) for b in (b_Q, b_K, b_V, b_O, gamma, beta)]
+        lens, lens_p = _lens(key_lens, B)
+        out = np.empty((B, Nq, D), np.float64)
+        st = self._lib.oracle_mha_proj_ln(_ptr(x_q), _ptr(x_kv), _ptr(W_Q), _ptr(W_K), _ptr(W_V),
+                                          _ptr(W_O), *[_ptr(v) for v in vecs], float(eps), _ptr(out),
+                                          B, Nq, Nk, D, H, dk, dv, int(mask_kind), lens_p,
+                                          float(scale), nthreads or default_threads())
+        self._check(st, "oracle_mha_proj_ln")
+        return out
+
     # -- one decoding step against a key/value cache ----------------------------
     def decode(self, q, k_cache, v_cache, mask_kind: int = MASK_CAUSAL, cache_lens=None,
                scale=None, nthreads: int | None = None):
@@ -231,3 +257,7 @@ def mha_proj(*args, **kwargs):
 
 def decode(*args, **kwargs):
     return get().decode(*args, **kwargs)
+
+
+def mha_proj_ln(*args, **kwargs):
+    return get().mha_proj_ln(*args, **kwargs)

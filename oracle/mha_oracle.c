@@ -46,6 +46,8 @@
  *   - decoding against a cache (oracle_decode): the new queries are the last
  *     Nq positions of the filled cache, and a run of H / Hkv consecutive query
  *     heads shares one cache head.
+ *   - residual + layer normalisation (oracle_mha_proj_ln): biased variance,
+ *     eps an argument, inference (no dropout).
  *
  * Everything is fp64; inputs arrive as fp64 (bf16 and fp32 values convert
  * exactly).  Sums run in index order.  Threads split independent (b, h) pairs
@@ -457,4 +459,59 @@ int oracle_decode(const double *q, const double *k, const double *v, double *out
     if (!q || !k || !v || !out) return ORACLE_EINVAL;
     struct decode_ctx ctx = {q, k, v, out, B, H, Hkv, Nq, S, dk, dv, mask_kind, cache_lens, scale};
     return parallel_for((long)B * H, nthreads, S > 0 ? S : 1, decode_unit, &ctx);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Residual connection and layer normalisation after the attention sublayer.  */
+/*
+ * [TP] "Residual Connections and Layer Normalization": every sublayer is
+ * wrapped as LayerNorm(x + Sublayer(x)), the normalisation after the residual
+ * addition (post-LN); layer normalisation normalises each token on its own,
+ * across its feature dimension.  [AD] "Add & Norm": add is the residual
+ * connection, norm normalises across the feature dimension of each token.
+ * [AC] "A faithful layer in code": the encoder layer applies the norm to
+ * x + attention(x), x being the sublayer's (query-side) input; its counting
+ * section gives each norm a scale and a shift per feature.
+ *
+ * Readings (the pages give no formula for the normalisation itself): the row
+ * z of D features becomes (z - mean) / sqrt(var + eps) * gamma + beta with the
+ * mean and the biased variance (divided by D) of the row, as the listing's
+ * nn.LayerNorm layers compute; eps is an argument (that layer's default is
+ * 1e-5); gamma and beta NULL mean 1 and 0; dropout is the identity (inference).
+ *
+ * x_q, W_*, b_*, mask, lengths and scale as in oracle_mha_proj; out [B,Nq,D]
+ * = LayerNorm(x_q + MHA(x_q, x_kv)).
+ */
+static void layer_norm_row(const double *z, const double *gamma, const double *beta, double eps, int D,
+                           double *y) {
+    double mean = 0.0;
+    for (int c = 0; c < D; ++c) mean += z[c];
+    mean /= D;
+    double var = 0.0;
+    for (int c = 0; c < D; ++c) var += (z[c] - mean) * (z[c] - mean);
+    var /= D;
+    const double rstd = 1.0 / sqrt(var + eps);
+    for (int c = 0; c < D; ++c) {
+        const double g = gamma ? gamma[c] : 1.0, b = beta ? beta[c] : 0.0;
+        y[c] = (z[c] - mean) * rstd * g + b;
+    }
+}
+
+int oracle_mha_proj_ln(const double *x_q, const double *x_kv, const double *W_Q, const double *W_K,
+                       const double *W_V, const double *W_O, const double *b_Q, const double *b_K,
+                       const double *b_V, const double *b_O, const double *gamma, const double *beta,
+                       double eps, double *out, int B, int Nq, int Nk, int D, int H, int dk, int dv,
+                       int mask_kind, const int32_t *key_lens, double scale, int nthreads) {
+    if (!(eps >= 0.0)) return ORACLE_EINVAL;
+    int st = oracle_mha_proj(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H, dk,
+                             dv, mask_kind, key_lens, scale, nthreads);
+    if (st) return st;
+    double *z = (double *)malloc(sizeof(double) * (size_t)(D > 0 ? D : 1));
+    if (!z) return ORACLE_ENOMEM;
+    for (long m = 0; m < (long)B * Nq; ++m) {
+        for (int c = 0; c < D; ++c) z[c] = x_q[m * D + c] + out[m * D + c]; /* the residual connection */
+        layer_norm_row(z, gamma, beta, eps, D, out + m * D);
+    }
+    free(z);
+    return ORACLE_OK;
 }

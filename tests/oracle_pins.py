@@ -547,6 +547,91 @@ def pin_decode_rejects_bad_heads(orc):
     return fails
 
 
+# --------------------------------------------------------------------------
+# Residual connection and layer normalisation after the sublayer.
+
+def _ln_case(seed, B=2, Nq=5, Nk=7, D=64, H=4, cross=True):
+    g = _rng(seed)
+    x_q = g.standard_normal((B, Nq, D))
+    x_kv = g.standard_normal((B, Nk, D)) if cross else None
+    W = [g.standard_normal((D, D)) * 0.2 for _ in range(4)]
+    lens = g.integers(1, (Nk if cross else Nq) + 1, size=B).astype(np.int32)
+    return g, x_q, x_kv, W, lens
+
+
+def pin_ln_two_features(orc):
+    """Two features and eps = 0: a normalised row is (-1, +1) or (+1, -1), by
+    which feature is larger, then scaled and shifted per feature -- a closed form
+    that holds only with the mean subtracted and the variance taken over the D
+    features ([AD] 'Add & Norm': normalisation across each token's features).
+    W_O = 0 makes the sublayer output exactly b_O, so the normalised row is that
+    of x_q + b_O: the residual is the query-side input ([AC] listing).  With
+    eps = 0.5 and z = (0, 2) the row becomes (-1, 1) / sqrt(1.5)."""
+    fails = []
+    g = _rng(181)
+    B, Nq, Nk, D = 3, 4, 6, 2
+    x_q = g.standard_normal((B, Nq, D))
+    x_kv = g.standard_normal((B, Nk, D))
+    W = [g.standard_normal((D, D)) for _ in range(3)] + [np.zeros((D, D))]
+    b_O = np.array([0.25, -0.5])
+    gamma, beta = np.array([2.0, -3.0]), np.array([0.5, 7.0])
+    out = orc.mha_proj_ln(x_q, x_kv, *W, H=1, b_O=b_O, gamma=gamma, beta=beta, eps=0.0, nthreads=1)
+    z = x_q + b_O
+    sgn = np.sign(z[..., 1] - z[..., 0])
+    want = np.stack([-sgn, sgn], axis=-1) * gamma + beta
+    _close(fails, "two-feature rows", out, want, 1e-12)
+    x0 = np.zeros((1, 1, 2))
+    out = orc.mha_proj_ln(x0, None, *[np.zeros((2, 2))] * 4, H=1, b_O=np.array([0.0, 2.0]), eps=0.5,
+                          nthreads=1)
+    _close(fails, "eps inside the root", out[0, 0], np.array([-1.0, 1.0]) / math.sqrt(1.5), 1e-15)
+    return fails
+
+
+def pin_ln_rows_standardised(orc):
+    """Without scale and shift every output row has mean 0 and mean square
+    var / (var + eps): exactly 1 for eps = 0, just below 1 for eps > 0."""
+    fails = []
+    _, x_q, x_kv, W, lens = _ln_case(191)
+    for eps in (0.0, 1e-3):
+        out = orc.mha_proj_ln(x_q, x_kv, *W, H=4, eps=eps, key_lens=lens, nthreads=2)
+        _close(fails, f"row means (eps={eps})", out.mean(-1), np.zeros(out.shape[:2]), 1e-12)
+        ms = (out ** 2).mean(-1)
+        if eps == 0.0:
+            _close(fails, "row mean squares", ms, np.ones(out.shape[:2]), 1e-12)
+        elif not (np.all(ms < 1.0 - 1e-6) and np.all(ms > 0.9)):
+            fails.append("eps does not shrink the row scale")
+    return fails
+
+
+def pin_ln_affine(orc):
+    """The per-feature scale and shift act last: out(gamma, beta) =
+    gamma * out(1, 0) + beta, for self- and cross-attention."""
+    fails = []
+    for cross in (False, True):
+        g, x_q, x_kv, W, lens = _ln_case(201 + cross, cross=cross, Nk=5)
+        gamma = g.standard_normal(64)
+        beta = g.standard_normal(64)
+        base = orc.mha_proj_ln(x_q, x_kv, *W, H=4, key_lens=lens, mask_kind=NONE, nthreads=2)
+        aff = orc.mha_proj_ln(x_q, x_kv, *W, H=4, gamma=gamma, beta=beta, key_lens=lens, nthreads=2)
+        _close(fails, f"affine (cross={cross})", aff, gamma * base + beta, 1e-12)
+    return fails
+
+
+def pin_ln_shift_invariance(orc):
+    """Adding the same amount to every feature of the sublayer output (a
+    constant b_O) leaves the normalised rows unchanged; a non-constant b_O
+    changes them."""
+    fails = []
+    g, x_q, x_kv, W, lens = _ln_case(211)
+    base = orc.mha_proj_ln(x_q, x_kv, *W, H=4, key_lens=lens, nthreads=2)
+    shifted = orc.mha_proj_ln(x_q, x_kv, *W, H=4, b_O=np.full(64, 3.75), key_lens=lens, nthreads=2)
+    _close(fails, "constant shift", shifted, base, 1e-11)
+    other = orc.mha_proj_ln(x_q, x_kv, *W, H=4, b_O=g.standard_normal(64), key_lens=lens, nthreads=2)
+    if np.max(np.abs(other - base)) < 1e-3:
+        fails.append("a non-constant b_O did not change the output")
+    return fails
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_worked_example_projection,
@@ -569,6 +654,10 @@ ALL_PINS = [
     pin_decode_shared_heads,
     pin_decode_short_caches,
     pin_decode_rejects_bad_heads,
+    pin_ln_two_features,
+    pin_ln_rows_standardised,
+    pin_ln_affine,
+    pin_ln_shift_invariance,
 ]
 
 

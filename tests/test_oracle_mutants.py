@@ -49,6 +49,12 @@ MUTANTS = [
     ("decode cache head by modulo", "int g = h / (c->H / c->Hkv);", "int g = h % c->Hkv;"),
     ("decode cache length clamped one short", "int L = key_length(c->cache_lens, b, c->S);",
      "int L = key_length(c->cache_lens, b, c->S - 1);"),
+    ("norm mean not subtracted", "y[c] = (z[c] - mean) * rstd * g + b;", "y[c] = z[c] * rstd * g + b;"),
+    ("norm unbiased variance", "var /= D;", "var /= (D - 1);"),
+    ("norm eps dropped", "1.0 / sqrt(var + eps);", "1.0 / sqrt(var);"),
+    ("norm scale and shift swapped", "const double g = gamma ? gamma[c] : 1.0, b = beta ? beta[c] : 0.0;",
+     "const double b = gamma ? gamma[c] : 1.0, g = beta ? beta[c] : 0.0;"),
+    ("residual connection dropped", "z[c] = x_q[m * D + c] + out[m * D + c];", "z[c] = out[m * D + c];"),
 ]
 
 
