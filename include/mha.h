@@ -160,6 +160,52 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            void* stream, void* const* events, int plan);
 
 /*
+ * mha_proj_ln_forward -- the attention sublayer with its residual connection and
+ * layer normalisation ([TP] "Residual Connections and Layer Normalization":
+ * LayerNorm(x + Sublayer(x)), the normalisation after the residual addition;
+ * [AD] "Add & Norm": normalised across each token's features; [AC] "A faithful
+ * layer in code": x is the sublayer's query-side input):
+ *
+ *   z = x_q + mha_proj_forward(...)            per token, D features
+ *   out = (z - mean(z)) / sqrt(var(z) + ln_eps) * ln_gamma + ln_beta
+ *
+ * with the biased variance (divided by D).  Arguments as mha_proj_forward,
+ * plus ln_gamma, ln_beta [D] (nullable: 1 and 0; 16-byte aligned) and ln_eps
+ * (finite, >= 0; nn.LayerNorm's default is 1e-5); b_O must then be 8-byte
+ * aligned.  Workspace: mha_proj_workspace_bytes.  Supported: as
+ * mha_proj_forward, with D <= 8192.  For D <= 512 the normalisation runs in
+ * the epilogue of the output projection, which then owns whole rows (see
+ * mha_proj_ln_fused); wider rows take the output projection and a separate
+ * normalisation pass.  z is formed in fp32 and rounded only at the output.
+ * Returns MHA_OK or a negative status.
+ */
+int mha_proj_ln_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K, const void* W_V,
+                        const void* W_O, const void* b_Q, const void* b_K, const void* b_V, const void* b_O,
+                        const void* ln_gamma, const void* ln_beta, float ln_eps, void* out, int B, int Nq, int Nk,
+                        int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mha_proj_ln_forward_timed -- as mha_proj_ln_forward, plus 8 events and a plan
+ * (as mha_proj_forward_timed): events[0..5] as there (events[4..5] time the
+ * output projection, with the normalisation when it is fused), events[6..7]
+ * the separate normalisation pass (untouched when mha_proj_ln_fused is 1).
+ */
+int mha_proj_ln_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                              const void* W_V, const void* W_O, const void* b_Q, const void* b_K, const void* b_V,
+                              const void* b_O, const void* ln_gamma, const void* ln_beta, float ln_eps, void* out,
+                              int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int mask_kind,
+                              const int32_t* key_lens, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream, void* const* events, int plan);
+
+/*
+ * mha_proj_ln_fused -- 1 if mha_proj_ln_forward normalises in the output
+ * projection's epilogue for rows of D features (1 <= D <= 512), 0 if it runs
+ * a separate normalisation pass.  Pure function; no device access.
+ */
+int mha_proj_ln_fused(int D);
+
+/*
  * mha_proj_fused -- 1 if mha_proj_forward with these sizes runs as two
  * kernels (the Q/K/V projections fused with attention, then the output
  * projection), 0 if it runs as three (projections, attention, output

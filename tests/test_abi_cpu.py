@@ -295,3 +295,41 @@ def test_decode_workspace_bytes(lib):
     assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, mb.F32) == 0
     assert lib.mha_decode_workspace_bytes(2, 8, 3, 1, 1000, 64, 64, mb.BF16) == 0
     assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, 9) == 0
+
+
+# --------------------------------------------------------------------------
+# The sublayer with its residual connection and layer normalisation.
+
+def proj_ln(lib, x_q=P, x_kv=P, W=(P, P, P, P), biases=(None, None, None, None), gamma=None, beta=None,
+            eps=1e-5, out=P, B=2, Nq=4, Nk=6, D=64, H=1, dk=64, dv=64, mask=0, lens=None, scale=0.125,
+            dtype=mb.BF16, ws=P, ws_bytes=1 << 30):
+    return lib.mha_proj_ln_forward(x_q, x_kv, *W, *biases, gamma, beta, eps, out, B, Nq, Nk, D, H, dk, dv,
+                                   mask, lens, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(eps=float("nan")), mb.ERR_INVALID_ARG),
+    (dict(eps=-1e-5), mb.ERR_INVALID_ARG),
+    (dict(eps=float("inf")), mb.ERR_INVALID_ARG),
+    (dict(gamma=P + 8), mb.ERR_INVALID_ARG),
+    (dict(beta=P + 2), mb.ERR_INVALID_ARG),
+    (dict(biases=(None, None, None, P + 4)), mb.ERR_INVALID_ARG),   # b_O needs 8-byte alignment here
+    (dict(D=8200, H=1, dk=64, dv=64), mb.ERR_UNSUPPORTED),          # wider than the normalisation pass
+    (dict(dtype=mb.F32), mb.ERR_UNSUPPORTED),
+    (dict(x_q=None), mb.ERR_INVALID_ARG),
+    (dict(ws=None), mb.ERR_WORKSPACE),
+    (dict(mask=1), mb.ERR_INVALID_ARG),
+])
+def test_proj_ln_rejects(lib, kw, status):
+    assert proj_ln(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+def test_proj_ln_empty_is_ok(lib):
+    assert proj_ln(lib, B=0) == mb.OK
+    assert proj_ln(lib, Nq=0) == mb.OK
+
+
+@pytest.mark.parametrize("D,fused", [(64, 1), (256, 1), (512, 1), (520, 0), (1024, 0), (0, 0)])
+def test_proj_ln_fused_plan(lib, D, fused):
+    assert lib.mha_proj_ln_fused(D) == fused

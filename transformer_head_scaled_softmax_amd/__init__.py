@@ -9,6 +9,8 @@ library's HIP kernels.  Functions raise ``MhaError`` on a non-zero status and
         q [B,H,Nq,d_k], k [B,H,Nk,d_k], v [B,H,Nk,d_v] -> out [B,H,Nq,d_v]
     proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H, ...)
         x_q [B,Nq,D], x_kv [B,Nk,D] or None -> out [B,Nq,D]
+    proj_ln_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H, ln_gamma=None, ln_beta=None, ln_eps=1e-5, ...)
+        LayerNorm(x_q + proj_forward(...)) -> out [B,Nq,D]
     decode_forward(q, k_cache, v_cache, cache_lens=None, mask_kind=MASK_CAUSAL, ...)
         q [B,H,Nq,d_k], k_cache [B,H_kv,S,d_k], v_cache [B,H_kv,S,d_v] -> out [B,H,Nq,d_v]
 """
@@ -19,7 +21,8 @@ import math
 from ._binding import (BF16, EXPORTS, F16, F32, MASK_CAUSAL, MASK_NONE, PLAN_AUTO, PLAN_FUSED, PLAN_UNFUSED,
                        MhaError, check, load)
 
-__all__ = ["forward", "proj_forward", "proj_workspace_bytes", "decode_forward", "decode_workspace_bytes",
+__all__ = ["forward", "proj_forward", "proj_ln_forward", "proj_workspace_bytes", "decode_forward",
+           "decode_workspace_bytes",
            "decode_split", "MASK_NONE", "MASK_CAUSAL", "PLAN_AUTO", "PLAN_UNFUSED", "PLAN_FUSED", "MhaError",
            "load", "EXPORTS"]
 
@@ -114,6 +117,41 @@ def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=
         st = lib.mha_proj_forward(*args)
     else:
         st = lib.mha_proj_forward_timed(*args, None, int(plan))
+    check(lib, st)
+    return out
+
+
+def proj_ln_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None, b_O=None,
+                    ln_gamma=None, ln_beta=None, ln_eps: float = 1e-5, mask_kind: int = MASK_NONE,
+                    key_lens=None, scale: float | None = None, out=None, workspace=None, stream=None,
+                    plan: int | None = None):
+    """The sublayer with its residual connection and layer normalisation,
+    LayerNorm(x_q + proj_forward(...)); see mha_proj_ln_forward in include/mha.h."""
+    import torch
+    B, Nq, D = x_q.shape
+    Nk = Nq if x_kv is None else x_kv.shape[1]
+    dk = W_Q.shape[0] // H
+    dv = W_V.shape[0] // H
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    code = _dtype_code(x_q)
+    if out is None:
+        out = torch.empty((B, Nq, D), dtype=x_q.dtype, device=x_q.device)
+    lib = load()
+    need = int(lib.mha_proj_workspace_bytes(B, Nq, Nk, D, H, dk, dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
+    ptrs = [_dev_ptr(t, n) for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (W_Q, "W_Q"), (W_K, "W_K"),
+                                        (W_V, "W_V"), (W_O, "W_O"), (b_Q, "b_Q"), (b_K, "b_K"),
+                                        (b_V, "b_V"), (b_O, "b_O"), (ln_gamma, "ln_gamma"),
+                                        (ln_beta, "ln_beta"))]
+    args = (*ptrs, float(ln_eps), _dev_ptr(out, "out"), B, Nq, Nk, D, H, dk, dv, int(mask_kind),
+            _lens_ptr(key_lens, B), float(scale), code, _dev_ptr(workspace, "workspace"), workspace.numel(),
+            _stream(stream))
+    if plan is None:
+        st = lib.mha_proj_ln_forward(*args)
+    else:
+        st = lib.mha_proj_ln_forward_timed(*args, None, int(plan))
     check(lib, st)
     return out
 

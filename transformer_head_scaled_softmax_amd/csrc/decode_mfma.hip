@@ -389,18 +389,6 @@ __global__ __launch_bounds__(64, 1) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-__device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // Merges the pieces of each cut cache: out = sum_p acc_p 2^(M_p - M) /
 // sum_p l_p 2^(M_p - M), M = max_p M_p, over the waves p that cover the cache.
 // One wave per row, lanes over the 64 features; the pieces are taken 32 at a

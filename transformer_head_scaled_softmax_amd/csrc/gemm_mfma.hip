@@ -44,16 +44,134 @@ struct TileMap {
   int total;
 };
 
-template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB>
+// Residual connection and layer normalisation of whole rows in the epilogue of
+// the output projection ("Residual Connections and Layer Normalization",
+// trishampatil.com: LayerNorm(x + Sublayer(x)), normalised across each token's
+// features; "Add & Norm", alexdo.xyz): z = C + bias + residual, then
+// (z - mean) / sqrt(var + eps) * gamma + beta with the biased variance, both
+// statistics taken in fp32 in two passes over the values held in registers.
+// Register 4gq + e of acc[mb][nb] holds row wm*WM + 32mb + col of the tile and
+// column wn*WN + 32nb + 8gq + 4half + e; a row's partial sums are combined over
+// the two lane halves, then over the WGN waves that share the row through
+// `red` ([WGN][TM] floats of LDS).  Columns past N are left out.  Rows past M
+// are computed from zeros and never stored.
+template <class Op, int TM, int WGN, int MB, int NB, int WM, int WN>
+__device__ inline void layer_norm_epilogue(f32x16_t (&acc)[MB][NB], const GemmProblem& P, int m0, int n0, int wm,
+                                           int wn, int col, int half, float* red) {
+  const int M = P.M, N = P.N;
+  const int64_t ldc = P.ldc;
+  const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
+  const uint16_t* res = static_cast<const uint16_t*>(P.residual);
+  const uint16_t* gam = static_cast<const uint16_t*>(P.gamma);
+  const uint16_t* bet = static_cast<const uint16_t*>(P.beta);
+  const float inv_n = 1.0f / (float)N;
+  auto unpack4 = [](u32x2_t v, float (&f)[4]) {
+    f[0] = Op::to_float((uint16_t)(v[0] & 0xffffu));
+    f[1] = Op::to_float((uint16_t)(v[0] >> 16));
+    f[2] = Op::to_float((uint16_t)(v[1] & 0xffffu));
+    f[3] = Op::to_float((uint16_t)(v[1] >> 16));
+  };
+
+  // z = C + bias + residual, and its row sums.
+  float s1[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + wm * WM + 32 * mb + col;
+    s1[mb] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * WN + 32 * nb + 8 * gq + 4 * half;
+        if (n < N) {  // N is a multiple of 8: the 4-run is whole
+          float add[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (bias) unpack4(*reinterpret_cast<const u32x2_t*>(bias + n), add);
+          if (m < M) {
+            float r4[4];
+            unpack4(*reinterpret_cast<const u32x2_t*>(res + (int64_t)m * ldc + n), r4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) add[e] += r4[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[mb][nb][4 * gq + e] += add[e];
+            s1[mb] += acc[mb][nb][4 * gq + e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mb][nb][4 * gq + e] = 0.0f;
+        }
+      }
+    s1[mb] = lanes_sum(s1[mb]);
+  }
+  const int rbase = wm * WM + col;
+  if (half == 0)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[wn * TM + rbase + 32 * mb] = s1[mb];
+  __syncthreads();
+  float mean[MB], s2[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WGN; ++w) t += red[w * TM + rbase + 32 * mb];
+    mean[mb] = t * inv_n;
+    s2[mb] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        if (n0 + wn * WN + 32 * nb + 8 * gq + 4 * half < N)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dz = acc[mb][nb][4 * gq + e] - mean[mb];
+            s2[mb] = fmaf(dz, dz, s2[mb]);
+          }
+    s2[mb] = lanes_sum(s2[mb]);
+  }
+  __syncthreads();  // every wave has read the row sums
+  if (half == 0)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) red[wn * TM + rbase + 32 * mb] = s2[mb];
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WGN; ++w) t += red[w * TM + rbase + 32 * mb];
+    const float rstd = 1.0f / sqrtf(t * inv_n + P.eps);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * WN + 32 * nb + 8 * gq + 4 * half;
+        float gv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (n < N) {
+          if (gam) unpack4(*reinterpret_cast<const u32x2_t*>(gam + n), gv);
+          if (bet) unpack4(*reinterpret_cast<const u32x2_t*>(bet + n), bv);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[mb][nb][4 * gq + e] = fmaf((acc[mb][nb][4 * gq + e] - mean[mb]) * rstd, gv[e], bv[e]);
+      }
+  }
+}
+
+// LN: the tile spans whole rows (TN >= N) and the epilogue applies the
+// residual connection and layer normalisation (launch_gemm_ln).
+template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB, bool LN = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
   constexpr int NW = WGM * WGN, NT = 64 * NW;
   constexpr int WM = TM / WGM, WN = TN / WGN;  // wave tile: rows of X x rows of W
   constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA blocks per wave
   constexpr int ROWS = TM + TN;                // operand rows per stage (X, then W)
   constexpr int STAGE = ROWS * kBK;            // elements per stage
-  constexpr int LPW = ROWS / 8 / NW;           // 1 KiB loads per wave per stage
+  constexpr int CHUNKS = ROWS / 8;             // 1 KiB loads per stage
+  constexpr int LPW = (CHUNKS + NW - 1) / NW;  // per wave (the last round may be partial)
   static_assert(MB >= 1 && NB >= 1 && WM % 32 == 0 && WN % 32 == 0, "bad wave tile");
-  static_assert((ROWS / 8) % NW == 0 && NW % 2 == 0, "loads must split evenly over an even wave count");
+  // With a partial last round the waves issue different numbers of loads, which
+  // only the two-stage schedule (it waits for all of them) tolerates.
+  static_assert((CHUNKS % NW == 0 || S == 2) && NW % 2 == 0, "loads must split over an even wave count");
   static_assert(S >= 2 && (S - 1) * LPW < 64, "too many loads in flight");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[S * STAGE];
 
@@ -118,6 +236,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int c = wave + NW * i;  // uniform per wave
+      if (c >= CHUNKS) break;
       const int off = (goff[i] + k0 * 2) | dead;
       uint16_t* d = dst + c * 512;
       if (c < TM / 8)
@@ -203,6 +322,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
   static_assert(NW * WM * SS <= S * STAGE, "staging does not fit");
   uint16_t* stage = lds + wave * WM * SS;
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
+  if constexpr (LN) {
+    layer_norm_epilogue<Op, TM, WGN, MB, NB, WM, WN>(acc, P, m0, n0, wm, wn, col, half,
+                                                    reinterpret_cast<float*>(lds + NW * WM * SS));
+    static_assert(NW * WM * SS * 2 + WGN * TM * 4 <= S * STAGE * 2, "norm scratch does not fit");
+    bias = nullptr;  // already added
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -237,7 +362,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
   }
 }
 
-template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB>
+template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB, bool LN = false>
 hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   TileMap tm{};
   int total = 0;
@@ -251,8 +376,8 @@ hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEven
   for (int i = g.count; i <= kMaxGemmProblems; ++i) tm.start[i] = total;
   tm.total = total;
   if (total == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TM, TN, WGM, WGN, S, MINB>), dim3(total), dim3(64 * WGM * WGN), 0,
-                        stream, t0, t1, 0, g, tm);
+  hipExtLaunchKernelGGL((gemm_mfma_kernel<Op, TM, TN, WGM, WGN, S, MINB, LN>), dim3(total), dim3(64 * WGM * WGN),
+                        0, stream, t0, t1, 0, g, tm);
   return hipGetLastError();
 }
 
@@ -278,7 +403,25 @@ hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, h
   return launch<Op, 64, 64, 2, 2, 2, 2>(g, stream, t0, t1);                                    // 32 KiB
 }
 
+// Whole rows of up to 512 features per workgroup: 32 rows x 512 columns, eight
+// waves side by side (32 x 64 each), two stages of (32 + 512) x 64 operands
+// (136 KiB of LDS, one workgroup per CU).  Every workgroup streams all of W
+// through its CU, which is why wider rows take the GEMM plus a separate
+// normalisation kernel instead.
+template <class Op>
+hipError_t launch_ln(const GemmProblem& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  static_assert(kLnFusedMaxN == 512, "tile width");
+  GemmBatch g{};
+  g.p[0] = p;
+  g.count = 1;
+  return launch<Op, 32, 512, 1, 8, 2, 1, true>(g, stream, t0, t1);
+}
+
 }  // namespace
+
+hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  return dt == DType::BF16 ? launch_ln<BF16>(p, stream, t0, t1) : launch_ln<F16>(p, stream, t0, t1);
+}
 
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   return dt == DType::BF16 ? launch_sized<BF16>(g, stream, t0, t1) : launch_sized<F16>(g, stream, t0, t1);

@@ -95,6 +95,18 @@ __device__ inline float lanes_sum(float x) {  // sum over lanes l and l^32
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ inline float wave_max(float x) {  // max over the 64 lanes
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ inline float wave_sum(float x) {  // sum over the 64 lanes
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 // Swizzle of 16-byte chunks within 128-byte LDS rows for MFMA operand reads
 // (16 bytes per lane from 32 consecutive rows): chunk c of row r sits in slot
 // c ^ operand_swizzle(r), which spreads the 32 rows over all banks.

@@ -178,13 +178,56 @@ bool use_fused(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
          int64_t(B) * Nk * D * 2 < kMaxBufferBytes;
 }
 
-// mha_proj_forward with optional profiling events (ev == nullptr: none).
+// The residual connection and layer normalisation after the sublayer
+// (mha_proj_ln_forward); nullptr in proj_forward_impl: none.
+struct LnSpec {
+  const void* gamma;
+  const void* beta;
+  float eps;
+};
+
+// Whether the normalisation runs in the output projection's epilogue.
+bool ln_fused(int D) { return D >= 1 && D <= mha::kLnFusedMaxN; }
+constexpr int kLnMaxD = 8192;  // widest row of the separate normalisation kernel
+
+// out = O_cat W_O^T + b_O; with ln, out = LayerNorm(x_q + that) * gamma + beta:
+// in the projection's epilogue for rows of up to kLnFusedMaxN features, else
+// as a separate pass over out.  Events 4..5 time the projection, 6..7 the
+// separate pass.
+int output_projection(const void* O, const void* W_O, const void* b_O, void* out, const void* x_q, int M, int D,
+                      int HV, mha::DType dt, hipStream_t s, const LnSpec* ln, hipEvent_t const* ev) {
+  auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
+  mha::GemmProblem p{O, W_O, b_O, out, M, D, HV, HV, D};
+  hipError_t e;
+  if (ln && ln_fused(D)) {
+    p.residual = x_q;
+    p.gamma = ln->gamma;
+    p.beta = ln->beta;
+    p.eps = ln->eps;
+    e = mha::launch_gemm_ln(p, dt, s, evt(4), evt(5));
+    if (e != hipSuccess) return hip_fail(e, "output projection + normalisation launch");
+    return MHA_OK;
+  }
+  mha::GemmBatch go{};
+  go.p[0] = p;
+  go.count = 1;
+  e = mha::launch_gemm_mfma(go, dt, s, evt(4), evt(5));
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  if (ln) {
+    e = mha::launch_residual_ln(out, x_q, ln->gamma, ln->beta, ln->eps, M, D, dt, s, evt(6), evt(7));
+    if (e != hipSuccess) return hip_fail(e, "normalisation launch");
+  }
+  return MHA_OK;
+}
+
+// mha_proj_forward (and, with ln, mha_proj_ln_forward) with optional profiling
+// events (ev == nullptr: none).
 int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
                       const void* W_V, const void* W_O, const void* b_Q, const void* b_K,
                       const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
                       int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                      hipEvent_t const* ev, int plan) {
+                      hipEvent_t const* ev, int plan, const LnSpec* ln) {
   g_last_error.clear();
   if (plan < MHA_PLAN_AUTO || plan > MHA_PLAN_FUSED) return fail(MHA_ERR_INVALID_ARG, "unknown plan %d", plan);
   if (B < 0 || Nq < 0 || Nk < 0)
@@ -200,6 +243,11 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     return fail(MHA_ERR_UNSUPPORTED, "the projection path supports d_k == d_v == %d (got %d, %d)",
                 mha::kMfmaHeadDim, d_k, d_v);
   if (D % 8 != 0) return fail(MHA_ERR_UNSUPPORTED, "D must be a multiple of 8 (got %d)", D);
+  if (ln) {
+    if (!std::isfinite(ln->eps) || ln->eps < 0.0f)
+      return fail(MHA_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
+    if (D > kLnMaxD) return fail(MHA_ERR_UNSUPPORTED, "layer normalisation supports D <= %d (got %d)", kLnMaxD, D);
+  }
   if (B == 0 || Nq == 0) return MHA_OK;  // nothing to write
   if (!x_q || !W_Q || !W_K || !W_V || !W_O || !out)
     return fail(MHA_ERR_INVALID_ARG, "x_q, W_Q, W_K, W_V, W_O and out must be non-null");
@@ -208,6 +256,10 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     if (!aligned(p, 16)) return fail(MHA_ERR_INVALID_ARG, "x_q, x_kv, W_*, out must be 16-byte aligned");
   for (const void* p : {b_Q, b_K, b_V, b_O})
     if (p && !aligned(p, 2)) return fail(MHA_ERR_INVALID_ARG, "biases must be 2-byte aligned");
+  if (ln) {
+    if (!aligned(ln->gamma, 16) || !aligned(ln->beta, 16) || !aligned(b_O, 8))
+      return fail(MHA_ERR_INVALID_ARG, "ln_gamma and ln_beta must be 16-byte aligned, b_O 8-byte aligned");
+  }
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   ProjLayout L;
   proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L);
@@ -262,12 +314,7 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     pa.scale = scale;
     hipError_t e = mha::launch_proj_attn(pa, dt, s, evt(0), evt(1));
     if (e != hipSuccess) return hip_fail(e, "fused projection/attention launch");
-    mha::GemmBatch go{};
-    go.p[0] = {Ow, W_O, b_O, out, B * Nq, D, HV, HV, D};
-    go.count = 1;
-    e = mha::launch_gemm_mfma(go, dt, s, evt(4), evt(5));
-    if (e != hipSuccess) return hip_fail(e, "output projection launch");
-    return MHA_OK;
+    return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ev);
   }
 
   // 1. Q, K, V projections in one launch; outputs row-major [B*N, H*d].
@@ -310,13 +357,8 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   e = mha::launch_attn_mfma(a, dt, s, evt(2), evt(3));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
 
-  // 3. Output projection.
-  mha::GemmBatch go{};
-  go.p[0] = {Ow, W_O, b_O, out, B * Nq, D, HV, HV, D};
-  go.count = 1;
-  e = mha::launch_gemm_mfma(go, dt, s, evt(4), evt(5));
-  if (e != hipSuccess) return hip_fail(e, "output projection launch");
-  return MHA_OK;
+  // 3. Output projection (and the residual connection and normalisation).
+  return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ev);
 }
 
 }  // namespace
@@ -330,7 +372,7 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
                            d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
-                           stream, nullptr, MHA_PLAN_AUTO);
+                           stream, nullptr, MHA_PLAN_AUTO, nullptr);
 }
 
 int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
@@ -341,8 +383,33 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            void* stream, void* const* events, int plan) {
   return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H,
                            d_k, d_v, mask_kind, key_lens, scale, dtype, workspace, workspace_bytes,
-                           stream, reinterpret_cast<hipEvent_t const*>(events), plan);
+                           stream, reinterpret_cast<hipEvent_t const*>(events), plan, nullptr);
 }
+
+int mha_proj_ln_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K, const void* W_V,
+                        const void* W_O, const void* b_Q, const void* b_K, const void* b_V, const void* b_O,
+                        const void* ln_gamma, const void* ln_beta, float ln_eps, void* out, int B, int Nq, int Nk,
+                        int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const LnSpec ln{ln_gamma, ln_beta, ln_eps};
+  return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H, d_k, d_v,
+                           mask_kind, key_lens, scale, dtype, workspace, workspace_bytes, stream, nullptr,
+                           MHA_PLAN_AUTO, &ln);
+}
+
+int mha_proj_ln_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                              const void* W_V, const void* W_O, const void* b_Q, const void* b_K, const void* b_V,
+                              const void* b_O, const void* ln_gamma, const void* ln_beta, float ln_eps, void* out,
+                              int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int mask_kind,
+                              const int32_t* key_lens, float scale, int dtype, void* workspace,
+                              size_t workspace_bytes, void* stream, void* const* events, int plan) {
+  const LnSpec ln{ln_gamma, ln_beta, ln_eps};
+  return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H, d_k, d_v,
+                           mask_kind, key_lens, scale, dtype, workspace, workspace_bytes, stream,
+                           reinterpret_cast<hipEvent_t const*>(events), plan, &ln);
+}
+
+int mha_proj_ln_fused(int D) { return ln_fused(D) ? 1 : 0; }
 
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention) {
   return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;

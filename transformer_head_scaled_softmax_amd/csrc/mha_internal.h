@@ -66,7 +66,8 @@ struct DecodeArgs {
 
 // One projection problem: C[m, n] = sum_k X[m, k] * W[n, k] (+ bias[n]).
 // X [M, K] row-major with row stride ldx; W [N, K] row-major (stride K);
-// C [M, N] row-major with row stride ldc.
+// C [M, N] row-major with row stride ldc.  For launch_gemm_ln the row is then
+// z = C + residual (same layout as C) and C = LayerNorm(z) * gamma + beta.
 struct GemmProblem {
   const void* x;
   const void* w;
@@ -74,6 +75,10 @@ struct GemmProblem {
   void* c;
   int M, N, K;
   int64_t ldx, ldc;
+  const void* residual;  // launch_gemm_ln only: [M, N], row stride ldc
+  const void* gamma;     // launch_gemm_ln only: nullable (1), [N]
+  const void* beta;      // launch_gemm_ln only: nullable (0), [N]
+  float eps;
 };
 
 constexpr int kMaxGemmProblems = 3;
@@ -112,6 +117,15 @@ hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hip
                             hipEvent_t t1 = nullptr);
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
+// Output projection with the residual connection and layer normalisation in
+// its epilogue: one workgroup owns whole rows.  Requires N <= kLnFusedMaxN.
+hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
+                          hipEvent_t t1 = nullptr);
+// out[m, :] = LayerNorm(out[m, :] + residual[m, :]) * gamma + beta in place,
+// rows of D features (D a multiple of 8), row stride D.
+hipError_t launch_residual_ln(void* out, const void* residual, const void* gamma, const void* beta, float eps,
+                              int M, int D, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
+                              hipEvent_t t1 = nullptr);
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
 hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
@@ -128,6 +142,8 @@ constexpr int kMfmaHeadDim = 64;
 // one wave per workgroup and one per SIMD of the 256 compute units; a partial
 // state is (reference maximum, sum, 2 pad, 64 accumulators) in fp32.
 constexpr int kDecodeMaxRows = 64;
+// Widest row the fused output-projection + layer-normalisation kernel owns.
+constexpr int kLnFusedMaxN = 512;
 constexpr int kDecodeWaves = 256 * 4;
 constexpr int kDecodePartFloats = 68;
 
