@@ -41,11 +41,13 @@ KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip", "mfma_util.h"],
                   "attention": ["attn_mfma.hip", "mfma_util.h"],
                   "qkv_attention": ["proj_attn.hip", "mfma_util.h"],
                   "out_projection": ["gemm_mfma.hip", "mfma_util.h"], "attention_f32": ["attn_f32.hip"],
-                  "decode": ["decode_mfma.hip", "mfma_util.h"], "decode_combine": ["decode_mfma.hip", "mfma_util.h"]}
+                  "decode": ["decode_mfma.hip", "mfma_util.h"], "decode_combine": ["decode_mfma.hip", "mfma_util.h"],
+                  "out_projection_ln": ["gemm_mfma.hip", "mfma_util.h"], "ln_rows": ["gemm_mfma.hip", "mfma_util.h"]}
 KERNEL_SYMBOLS = {"qkv_projection": "gemm_mfma_kernel", "attention": "attn_mfma_kernel",
                   "qkv_attention": "proj_attn_kernel", "out_projection": "gemm_mfma_kernel",
                   "attention_f32": "attn_f32_kernel", "decode": "decode_mfma_kernel",
-                  "decode_combine": "decode_combine_kernel"}
+                  "decode_combine": "decode_combine_kernel", "out_projection_ln": "gemm_mfma_kernel",
+                  "ln_rows": "ln_rows_kernel"}
 
 
 def log(*a):
@@ -112,11 +114,12 @@ def projection_flops(w):
 
 
 def proj_path_bytes(w, lens):
-    """Inputs + weights + output of the whole projection path."""
+    """Inputs + weights + output of the whole projection path (the norm's scale
+    and shift with it; x_q, its residual, is read once)."""
     es = ES[w.dtype]
     D, HD = w.D, w.H * w.d
     x = w.B * w.Nq * D + (w.B * w.Nk * D if w.cross else 0)
-    weights = 3 * HD * D + D * HD
+    weights = 3 * HD * D + D * HD + (2 * D if w.ln else 0)
     return (x + weights + w.B * w.Nq * D) * es + (0 if lens is None else 4 * w.B)
 
 
@@ -132,10 +135,16 @@ def stage_work(w, lens):
     qkv_b = x_bytes + 3 * HD * D * es + (w.B * w.Nq * HD + 2 * w.B * w.Nk * HD) * es
     out_b = (w.B * w.Nq * HD + D * HD + w.B * w.Nq * D) * es
     fused_b = x_bytes + 3 * HD * D * es + w.B * w.Nq * HD * es + (0 if lens is None else 4 * w.B)
+    rows = w.B * w.Nq * D * es
     return {"qkv_projection": (qkv_f, qkv_b),
             "attention": (attention_flops(w, lens), attention_bytes(w, lens)),
             "qkv_attention": (qkv_f + attention_flops(w, lens), fused_b),
-            "out_projection": (out_f, out_b)}
+            "out_projection": (out_f, out_b),
+            # with the norm, the projection's epilogue also reads the residual rows and
+            # stores per-row tile statistics; the second pass reads the rows and the
+            # statistics and writes the rows
+            "out_projection_ln": (out_f, out_b + rows + w.B * w.Nq * ((D + 63) // 64) * 8),
+            "ln_rows": (0.0, 2 * rows + w.B * w.Nq * ((D + 63) // 64) * 8 + 2 * D * es)}
 
 
 # ---------------------------------------------------------------------------
@@ -207,7 +216,11 @@ def cpu_baseline(w, inp_sets, seconds_target):
     done_flops, t0, n = 0.0, time.perf_counter(), 0
     while True:
         inp = inp_sets[n % len(inp_sets)]
-        if w.proj:
+        if w.proj and w.ln:
+            oracle.mha_proj_ln(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
+                               H=w.H, gamma=inp["ln_gamma"], beta=inp["ln_beta"], eps=1e-5,
+                               mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
+        elif w.proj:
             oracle.mha_proj(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
                             H=w.H, mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
             qkv_f, out_f = projection_flops(w)
@@ -322,20 +335,27 @@ def main():
 
     if w.proj:
         wts = synth.workload_inputs(w)  # seed of the workload: the model weights
-        W = {n_: to_dev(wts[n_]) for n_ in ("W_Q", "W_K", "W_V", "W_O")}
-        need = lib.mha_proj_workspace_bytes(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, code)
+        W = {n_: to_dev(wts[n_]) for n_ in ("W_Q", "W_K", "W_V", "W_O") + (("ln_gamma", "ln_beta") if w.ln else ())}
+        need = (lib.mha_proj_ln_workspace_bytes if w.ln else lib.mha_proj_workspace_bytes)(
+            w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, code)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
         def step(i, sp, events=None):
             d = dev_sets[i % nsets]
             lp = None if d["key_lens"] is None else d["key_lens"].data_ptr()
             xkv = None if d["x_kv"] is None else d["x_kv"].data_ptr()
-            argsv = (d["x_q"].data_ptr(), xkv, W["W_Q"].data_ptr(), W["W_K"].data_ptr(),
-                     W["W_V"].data_ptr(), W["W_O"].data_ptr(), None, None, None, None,
-                     d["out"].data_ptr(), w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.mask, lp, scale,
-                     code, ws.data_ptr(), need, sp)
-            st = (lib.mha_proj_forward(*argsv) if events is None
-                  else lib.mha_proj_forward_timed(*argsv, events, 0))
+            head = (d["x_q"].data_ptr(), xkv, W["W_Q"].data_ptr(), W["W_K"].data_ptr(),
+                    W["W_V"].data_ptr(), W["W_O"].data_ptr(), None, None, None, None)
+            tail = (w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.mask, lp, scale, code, ws.data_ptr(), need, sp)
+            if w.ln:
+                argsv = (*head, W["ln_gamma"].data_ptr(), W["ln_beta"].data_ptr(), ctypes.c_float(1e-5),
+                         d["out"].data_ptr(), *tail)
+                st = (lib.mha_proj_ln_forward(*argsv) if events is None
+                      else lib.mha_proj_ln_forward_timed(*argsv, events, 0))
+            else:
+                argsv = (*head, d["out"].data_ptr(), *tail)
+                st = (lib.mha_proj_forward(*argsv) if events is None
+                      else lib.mha_proj_forward_timed(*argsv, events, 0))
             if st != 0:
                 raise RuntimeError(lib.mha_last_error().decode())
         # Kernel -> (start, end) event indices of mha_proj_forward_timed.
@@ -344,6 +364,10 @@ def main():
         else:
             stage_events = {"qkv_projection": (0, 1), "attention": (2, 3), "out_projection": (4, 5)}
         n_events = 6
+        if w.ln:
+            stage_events["out_projection_ln"] = stage_events.pop("out_projection")
+            stage_events["ln_rows"] = (6, 7)
+            n_events = 8
     elif w.decode:
         Hkv = w.kv_heads
         need = lib.mha_decode_workspace_bytes(w.B, w.H, Hkv, w.Nq, w.Nk, w.d, w.d, code)
@@ -436,7 +460,8 @@ def main():
         for n_, (a_, b_) in stage_events.items():
             per[n_].append(hip.elapsed_ms(evs[a_], evs[b_]))
     avg = {n_: float(np.mean(v)) for n_, v in per.items()}
-    eager_ms_step = hip.elapsed_ms(ev_arrays[0][0], ev_arrays[-1][n_events - 1]) / K
+    last_end = max(b_ for _, b_ in stage_events.values())  # some events may stay unrecorded
+    eager_ms_step = hip.elapsed_ms(ev_arrays[0][0], ev_arrays[-1][last_end]) / K
 
     used = [lens_list[(args.warmup + i) % nsets] for i in range(K)]
     att_f = float(np.mean([attention_flops(w, L) for L in used]))
@@ -462,6 +487,7 @@ def main():
                    "mask": "causal" if w.mask == 1 else "none",
                    "key_lens": None if w.lens is None else f"U{{{w.lens[0]}..{w.lens[1]}}}",
                    "input_sets": nsets, "issue": "HIP graph replay",
+                   **({"residual_layer_norm": True} if w.ln else {}),
                    **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "waves": nsplit}
                       if w.decode else {})},
         "tokens_per_s": round(w.B * w.Nq / sec, 1),

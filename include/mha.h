@@ -172,12 +172,13 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
  * with the biased variance (divided by D).  Arguments as mha_proj_forward,
  * plus ln_gamma, ln_beta [D] (nullable: 1 and 0; 16-byte aligned) and ln_eps
  * (finite, >= 0; nn.LayerNorm's default is 1e-5); b_O must then be 8-byte
- * aligned.  Workspace: mha_proj_workspace_bytes.  Supported: as
- * mha_proj_forward, with D <= 8192.  For D <= 512 the normalisation runs in
- * the epilogue of the output projection, which then owns whole rows (see
- * mha_proj_ln_fused); wider rows take the output projection and a separate
- * normalisation pass.  z is formed in fp32 and rounded only at the output.
- * Returns MHA_OK or a negative status.
+ * aligned; the workspace must hold mha_proj_ln_workspace_bytes(...) bytes.
+ * Supported: as mha_proj_forward.  The residual addition and the row
+ * statistics run in the epilogue of the output projection (each output tile
+ * keeps its share of every row's statistics in fp32 and the rows as fp16
+ * differences from its own mean, in `out`); one more light kernel merges the
+ * statistics and normalises the rows in place.  Returns MHA_OK or a negative
+ * status.
  */
 int mha_proj_ln_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K, const void* W_V,
                         const void* W_O, const void* b_Q, const void* b_K, const void* b_V, const void* b_O,
@@ -186,10 +187,10 @@ int mha_proj_ln_forward(const void* x_q, const void* x_kv, const void* W_Q, cons
                         int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * mha_proj_ln_forward_timed -- as mha_proj_ln_forward, plus 8 events and a plan
- * (as mha_proj_forward_timed): events[0..5] as there (events[4..5] time the
- * output projection, with the normalisation when it is fused), events[6..7]
- * the separate normalisation pass (untouched when mha_proj_ln_fused is 1).
+ * mha_proj_ln_forward_timed -- as mha_proj_ln_forward, plus 8 events and a plan:
+ * events[0..5] and the plan as mha_proj_forward_timed (events[4..5] time the
+ * output projection with the residual and statistics), events[6..7] the
+ * normalisation pass.
  */
 int mha_proj_ln_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
                               const void* W_V, const void* W_O, const void* b_Q, const void* b_K, const void* b_V,
@@ -199,11 +200,11 @@ int mha_proj_ln_forward_timed(const void* x_q, const void* x_kv, const void* W_Q
                               size_t workspace_bytes, void* stream, void* const* events, int plan);
 
 /*
- * mha_proj_ln_fused -- 1 if mha_proj_ln_forward normalises in the output
- * projection's epilogue for rows of D features (1 <= D <= 512), 0 if it runs
- * a separate normalisation pass.  Pure function; no device access.
+ * mha_proj_ln_workspace_bytes -- device workspace mha_proj_ln_forward needs:
+ * mha_proj_workspace_bytes plus per-row tile statistics (a 256-byte aligned
+ * region of B*Nq*ceil(D/64) fp32 pairs).  Returns 0 for invalid sizes.
  */
-int mha_proj_ln_fused(int D);
+size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype);
 
 /*
  * mha_proj_fused -- 1 if mha_proj_forward with these sizes runs as two

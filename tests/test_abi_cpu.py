@@ -314,7 +314,6 @@ def proj_ln(lib, x_q=P, x_kv=P, W=(P, P, P, P), biases=(None, None, None, None),
     (dict(gamma=P + 8), mb.ERR_INVALID_ARG),
     (dict(beta=P + 2), mb.ERR_INVALID_ARG),
     (dict(biases=(None, None, None, P + 4)), mb.ERR_INVALID_ARG),   # b_O needs 8-byte alignment here
-    (dict(D=8200, H=1, dk=64, dv=64), mb.ERR_UNSUPPORTED),          # wider than the normalisation pass
     (dict(dtype=mb.F32), mb.ERR_UNSUPPORTED),
     (dict(x_q=None), mb.ERR_INVALID_ARG),
     (dict(ws=None), mb.ERR_WORKSPACE),
@@ -330,6 +329,18 @@ def test_proj_ln_empty_is_ok(lib):
     assert proj_ln(lib, Nq=0) == mb.OK
 
 
-@pytest.mark.parametrize("D,fused", [(64, 1), (256, 1), (512, 1), (520, 0), (1024, 0), (0, 0)])
-def test_proj_ln_fused_plan(lib, D, fused):
-    assert lib.mha_proj_ln_fused(D) == fused
+def test_proj_ln_workspace_bytes(lib):
+    base = lib.mha_proj_workspace_bytes(64, 64, 64, 512, 8, 64, 64, mb.BF16)
+    # + per row 512/64 tiles of (sum, centred sum of squares) fp32
+    assert lib.mha_proj_ln_workspace_bytes(64, 64, 64, 512, 8, 64, 64, mb.BF16) == base + 4096 * 8 * 8
+    base = lib.mha_proj_workspace_bytes(3, 5, 7, 520, 1, 64, 64, mb.BF16)
+    # 15 rows x 9 tiles x 8 B = 1080 -> 1280
+    assert lib.mha_proj_ln_workspace_bytes(3, 5, 7, 520, 1, 64, 64, mb.BF16) == base + 1280
+    assert lib.mha_proj_ln_workspace_bytes(3, 5, 7, 0, 1, 64, 64, mb.BF16) == 0
+
+
+def test_proj_ln_workspace_checked(lib):
+    need = lib.mha_proj_ln_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
+    assert need > lib.mha_proj_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
+    assert proj_ln(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+    assert "needed" in lib.mha_last_error().decode()

@@ -138,7 +138,7 @@ def proj_ln_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b
     if out is None:
         out = torch.empty((B, Nq, D), dtype=x_q.dtype, device=x_q.device)
     lib = load()
-    need = int(lib.mha_proj_workspace_bytes(B, Nq, Nk, D, H, dk, dv, code))
+    need = int(lib.mha_proj_ln_workspace_bytes(B, Nq, Nk, D, H, dk, dv, code))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
     ptrs = [_dev_ptr(t, n) for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (W_Q, "W_Q"), (W_K, "W_K"),

@@ -26,7 +26,7 @@ ERR_HIP = -4
 # Every symbol include/mha.h declares.
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
            "mha_proj_forward_timed", "mha_proj_fused", "mha_proj_ln_forward", "mha_proj_ln_forward_timed",
-           "mha_proj_ln_fused", "mha_decode_workspace_bytes", "mha_decode_forward",
+           "mha_proj_ln_workspace_bytes", "mha_decode_workspace_bytes", "mha_decode_forward",
            "mha_decode_forward_timed", "mha_decode_split", "mha_status_string", "mha_last_error",
            "mha_version")
 
@@ -66,8 +66,8 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_proj_ln_forward.restype = i
     lib.mha_proj_ln_forward_timed.argtypes = lib.mha_proj_ln_forward.argtypes + [vp, i]
     lib.mha_proj_ln_forward_timed.restype = i
-    lib.mha_proj_ln_fused.argtypes = [i]
-    lib.mha_proj_ln_fused.restype = i
+    lib.mha_proj_ln_workspace_bytes.argtypes = [i] * 8
+    lib.mha_proj_ln_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_decode_workspace_bytes.argtypes = [i] * 8
     lib.mha_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_decode_forward.argtypes = [vp] * 4 + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]

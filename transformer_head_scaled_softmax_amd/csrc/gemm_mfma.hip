@@ -30,6 +30,8 @@
 // stored).  Tiles are ordered so that the workgroups of one XCD (block id mod
 // 8) take consecutive tiles, which share rows of X in that XCD's L2.  The tile
 // shape is chosen per launch from the problem sizes (see launch_sized).
+#include <type_traits>
+
 #include "mfma_util.h"
 
 namespace mha {
@@ -44,35 +46,44 @@ struct TileMap {
   int total;
 };
 
-// Residual connection and layer normalisation of whole rows in the epilogue of
-// the output projection ("Residual Connections and Layer Normalization",
-// trishampatil.com: LayerNorm(x + Sublayer(x)), normalised across each token's
-// features; "Add & Norm", alexdo.xyz): z = C + bias + residual, then
-// (z - mean) / sqrt(var + eps) * gamma + beta with the biased variance, both
-// statistics taken in fp32 in two passes over the values held in registers.
-// Register 4gq + e of acc[mb][nb] holds row wm*WM + 32mb + col of the tile and
-// column wn*WN + 32nb + 8gq + 4half + e; a row's partial sums are combined over
-// the two lane halves, then over the WGN waves that share the row through
-// `red` ([WGN][TM] floats of LDS).  Columns past N are left out.  Rows past M
-// are computed from zeros and never stored.
+// Residual connection and layer normalisation after the output projection
+// ("Residual Connections and Layer Normalization", trishampatil.com:
+// LayerNorm(x + Sublayer(x)), normalised across each token's features; "Add &
+// Norm", alexdo.xyz): z = C + bias + residual, then (z - mean) / sqrt(var +
+// eps) * gamma + beta with the biased variance.
+//
+// A tile holds only TN of a row's N features, so the statistics are made in
+// two steps.  In the projection's epilogue each tile reduces its part of every
+// row -- the sum and the sum of squares about the tile's own mean, fp32, from
+// the values in registers -- and stores them, with the row values as
+// differences from the tile mean in fp16 (in place in the output rows: 2
+// bytes with 11 significant bits, so this intermediate rounding is 2^-12
+// relative to the row's spread rather than bf16's 2^-9 of its size).  A
+// second kernel then merges each row's parts (the pairwise update of Chan,
+// Golub and LeVeque for means and centred sums of squares) and normalises the
+// row in place.  The kernel boundary is what makes every tile's stores visible
+// to the second pass: within one launch that would take an agent-scope
+// release (an L2 write-back) in every workgroup and an acquire (an L2
+// invalidate) in every merging one, which measured several times slower.
+//
+// ln_tile_stats: register 4gq + e of acc[mb][nb] holds row wm*WM + 32mb + col
+// of the tile and column wn*WN + 32nb + 8gq + 4half + e; a row's partial sums
+// are combined over the lane halves, then over the WGN waves sharing the row
+// through `red` (2 x [WGN][TM] floats of LDS).  Columns past N are left out;
+// rows past M are computed from zeros and never stored.
 template <class Op, int TM, int WGN, int MB, int NB, int WM, int WN>
-__device__ inline void layer_norm_epilogue(f32x16_t (&acc)[MB][NB], const GemmProblem& P, int m0, int n0, int wm,
-                                           int wn, int col, int half, float* red) {
+__device__ inline void ln_tile_stats(f32x16_t (&acc)[MB][NB], const GemmProblem& P, int m0, int n0, int tcol,
+                                     int wm, int wn, int col, int half, float* red) {
   const int M = P.M, N = P.N;
   const int64_t ldc = P.ldc;
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
   const uint16_t* res = static_cast<const uint16_t*>(P.residual);
-  const uint16_t* gam = static_cast<const uint16_t*>(P.gamma);
-  const uint16_t* bet = static_cast<const uint16_t*>(P.beta);
-  const float inv_n = 1.0f / (float)N;
   auto unpack4 = [](u32x2_t v, float (&f)[4]) {
     f[0] = Op::to_float((uint16_t)(v[0] & 0xffffu));
     f[1] = Op::to_float((uint16_t)(v[0] >> 16));
     f[2] = Op::to_float((uint16_t)(v[1] & 0xffffu));
     f[3] = Op::to_float((uint16_t)(v[1] >> 16));
   };
-
-  // z = C + bias + residual, and its row sums.
   float s1[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -105,17 +116,21 @@ __device__ inline void layer_norm_epilogue(f32x16_t (&acc)[MB][NB], const GemmPr
     s1[mb] = lanes_sum(s1[mb]);
   }
   const int rbase = wm * WM + col;
+  float* red1 = red;
+  float* red2 = red + WGN * TM;
   if (half == 0)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[wn * TM + rbase + 32 * mb] = s1[mb];
+    for (int mb = 0; mb < MB; ++mb) red1[wn * TM + rbase + 32 * mb] = s1[mb];
   __syncthreads();
-  float mean[MB], s2[MB];
+  const float inv_nt = 1.0f / (float)min(N - n0, WGN * WN);  // valid columns of this tile
+  float sum[MB], s2[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WGN; ++w) t += red[w * TM + rbase + 32 * mb];
-    mean[mb] = t * inv_n;
+    for (int w = 0; w < WGN; ++w) t += red1[w * TM + rbase + 32 * mb];
+    sum[mb] = t;
+    const float mean_t = t * inv_nt;
     s2[mb] = 0.0f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -124,41 +139,81 @@ __device__ inline void layer_norm_epilogue(f32x16_t (&acc)[MB][NB], const GemmPr
         if (n0 + wn * WN + 32 * nb + 8 * gq + 4 * half < N)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float dz = acc[mb][nb][4 * gq + e] - mean[mb];
+            const float dz = acc[mb][nb][4 * gq + e] - mean_t;
+            acc[mb][nb][4 * gq + e] = dz;  // stored as the difference from the tile mean
             s2[mb] = fmaf(dz, dz, s2[mb]);
           }
     s2[mb] = lanes_sum(s2[mb]);
   }
-  __syncthreads();  // every wave has read the row sums
   if (half == 0)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[wn * TM + rbase + 32 * mb] = s2[mb];
+    for (int mb = 0; mb < MB; ++mb) red2[wn * TM + rbase + 32 * mb] = s2[mb];
   __syncthreads();
+  if (wn == 0 && half == 0) {
+    const int stride = ln_stats_stride(N);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    float t = 0.0f;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + wm * WM + 32 * mb + col;
+      float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < WGN; ++w) t += red[w * TM + rbase + 32 * mb];
-    const float rstd = 1.0f / sqrtf(t * inv_n + P.eps);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int n = n0 + wn * WN + 32 * nb + 8 * gq + 4 * half;
-        float gv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (n < N) {
-          if (gam) unpack4(*reinterpret_cast<const u32x2_t*>(gam + n), gv);
-          if (bet) unpack4(*reinterpret_cast<const u32x2_t*>(bet + n), bv);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[mb][nb][4 * gq + e] = fmaf((acc[mb][nb][4 * gq + e] - mean[mb]) * rstd, gv[e], bv[e]);
-      }
+      for (int w = 0; w < WGN; ++w) t += red2[w * TM + rbase + 32 * mb];
+      if (m < M) P.stats[(int64_t)m * stride + tcol] = float2{sum[mb], t};
+    }
   }
 }
 
-// LN: the tile spans whole rows (TN >= N) and the epilogue applies the
-// residual connection and layer normalisation (launch_gemm_ln).
+// The second pass: one wave per row; each lane takes 8-feature chunks lane,
+// lane + 64, ... of the row.  `tn` is the projection's tile width.
+template <class Op>
+__global__ __launch_bounds__(256) void ln_rows_kernel(GemmProblem P, int tn) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int M = P.M, N = P.N;
+  if (m >= M) return;
+  const int stride = ln_stats_stride(N), tiles = (N + tn - 1) / tn;
+  const float2* st = P.stats + m * stride;
+  // Merge the tile statistics: lanes take tiles, then reduce over the wave.
+  const float inv_n = 1.0f / (float)N;
+  float sum = 0.0f;
+  for (int j = lane; j < tiles; j += 64) sum += st[j].x;
+  const float mean = wave_sum(sum) * inv_n;
+  float m2 = 0.0f;
+  for (int j = lane; j < tiles; j += 64) {
+    const float nj = (float)min(tn, N - j * tn);
+    const float d = st[j].x / nj - mean;
+    m2 += st[j].y + nj * d * d;
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(m2) * inv_n + P.eps);
+  const uint16_t* gam = static_cast<const uint16_t*>(P.gamma);
+  const uint16_t* bet = static_cast<const uint16_t*>(P.beta);
+  uint16_t* row = static_cast<uint16_t*>(P.c) + m * P.ldc;
+  for (int f0 = lane * 8; f0 < N; f0 += 512) {  // N is a multiple of 8: chunks are whole
+    const u32x4_t z = *reinterpret_cast<const u32x4_t*>(row + f0);  // fp16 differences from the tile mean
+    const int jt = f0 / tn;
+    const float shift = st[jt].x / (float)min(tn, N - jt * tn) - mean;  // (stored + mean_t) - mean
+    u32x4_t gv = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
+    if (gam) gv = *reinterpret_cast<const u32x4_t*>(gam + f0);
+    if (bet) bv = *reinterpret_cast<const u32x4_t*>(bet + f0);
+    u32x4_t y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint16_t zs = (uint16_t)(z[i] >> (16 * e)), gs = (uint16_t)(gv[i] >> (16 * e)),
+                       bs = (uint16_t)(bv[i] >> (16 * e));
+        const float gf = gam ? Op::to_float(gs) : 1.0f;
+        const float bf = bet ? Op::to_float(bs) : 0.0f;
+        v[e] = fmaf((F16::to_float(zs) + shift) * rstd, gf, bf);
+      }
+      y[i] = Op::pack(v[0], v[1]);
+    }
+    *reinterpret_cast<u32x4_t*>(row + f0) = y;
+  }
+}
+
+// LN: the epilogue applies the residual connection and layer normalisation
+// (launch_gemm_ln).
 template <class Op, int TM, int TN, int WGM, int WGN, int S, int MINB, bool LN = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBatch g, TileMap tm) {
   constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -322,10 +377,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
   static_assert(NW * WM * SS <= S * STAGE, "staging does not fit");
   uint16_t* stage = lds + wave * WM * SS;
   const uint16_t* bias = static_cast<const uint16_t*>(P.bias);
+  float* ln_red = reinterpret_cast<float*>(lds + NW * WM * SS);  // after the staging area
   if constexpr (LN) {
-    layer_norm_epilogue<Op, TM, WGN, MB, NB, WM, WN>(acc, P, m0, n0, wm, wn, col, half,
-                                                    reinterpret_cast<float*>(lds + NW * WM * SS));
-    static_assert(NW * WM * SS * 2 + WGN * TM * 4 <= S * STAGE * 2, "norm scratch does not fit");
+    static_assert(NW * WM * SS * 2 + 2 * WGN * TM * 4 <= S * STAGE * 2, "norm scratch does not fit");
+    ln_tile_stats<Op, TM, WGN, MB, NB, WM, WN>(acc, P, m0, n0, n0 / TN, wm, wn, col, half, ln_red);
     bias = nullptr;  // already added
   }
 #pragma unroll
@@ -343,9 +398,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_mfma_kernel(GemmBat
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        using Store = typename std::conditional<LN, F16, Op>::type;  // LN: fp16 differences
         u32x2_t w;
-        w[0] = Op::pack(acc[mb][nb][4 * gq + 0] + b0, acc[mb][nb][4 * gq + 1] + b1);
-        w[1] = Op::pack(acc[mb][nb][4 * gq + 2] + b2, acc[mb][nb][4 * gq + 3] + b3);
+        w[0] = Store::pack(acc[mb][nb][4 * gq + 0] + b0, acc[mb][nb][4 * gq + 1] + b1);
+        w[1] = Store::pack(acc[mb][nb][4 * gq + 2] + b2, acc[mb][nb][4 * gq + 3] + b3);
         *reinterpret_cast<u32x2_t*>(&stage[(mb * 32 + col) * SS + cl]) = w;
       }
     }
@@ -403,24 +459,35 @@ hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, h
   return launch<Op, 64, 64, 2, 2, 2, 2>(g, stream, t0, t1);                                    // 32 KiB
 }
 
-// Whole rows of up to 512 features per workgroup: 32 rows x 512 columns, eight
-// waves side by side (32 x 64 each), two stages of (32 + 512) x 64 operands
-// (136 KiB of LDS, one workgroup per CU).  Every workgroup streams all of W
-// through its CU, which is why wider rows take the GEMM plus a separate
-// normalisation kernel instead.
 template <class Op>
-hipError_t launch_ln(const GemmProblem& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  static_assert(kLnFusedMaxN == 512, "tile width");
+hipError_t launch_ln(const GemmProblem& p, hipStream_t stream, hipEvent_t t0, hipEvent_t t1, hipEvent_t t2,
+                     hipEvent_t t3) {
   GemmBatch g{};
   g.p[0] = p;
   g.count = 1;
-  return launch<Op, 32, 512, 1, 8, 2, 1, true>(g, stream, t0, t1);
+  hipError_t e;
+  int tn;
+  if (tiles(g, 128, 128) >= 384) {
+    e = launch<Op, 128, 128, 2, 4, 2, 2, true>(g, stream, t0, t1);
+    tn = 128;
+  } else if (tiles(g, 128, 64) >= 256) {
+    e = launch<Op, 128, 64, 2, 2, 2, 2, true>(g, stream, t0, t1);
+    tn = 64;
+  } else {
+    e = launch<Op, 64, 64, 2, 2, 2, 2, true>(g, stream, t0, t1);
+    tn = 64;
+  }
+  if (e != hipSuccess || p.M == 0) return e;
+  hipExtLaunchKernelGGL((ln_rows_kernel<Op>), dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream, t2, t3, 0, p,
+                        tn);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  return dt == DType::BF16 ? launch_ln<BF16>(p, stream, t0, t1) : launch_ln<F16>(p, stream, t0, t1);
+hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1,
+                          hipEvent_t t2, hipEvent_t t3) {
+  return dt == DType::BF16 ? launch_ln<BF16>(p, stream, t0, t1, t2, t3) : launch_ln<F16>(p, stream, t0, t1, t2, t3);
 }
 
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {

@@ -70,6 +70,20 @@ bool proj_layout(int B, int Nq, int Nk, int H, int d_k, int d_v, int dtype, Proj
   return true;
 }
 
+// mha_proj_ln_forward's workspace: the projection path's, then the
+// normalisation's per-row tile statistics.
+struct LnLayout {
+  size_t stats_off, total;
+};
+
+LnLayout ln_layout(const ProjLayout& P, int B, int Nq, int D) {
+  const int M = B * Nq;
+  LnLayout L;
+  L.stats_off = P.total;
+  L.total = L.stats_off + round256(size_t(M) * mha::ln_stats_stride(D) * 2 * sizeof(float));
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,25 +200,24 @@ struct LnSpec {
   float eps;
 };
 
-// Whether the normalisation runs in the output projection's epilogue.
-bool ln_fused(int D) { return D >= 1 && D <= mha::kLnFusedMaxN; }
-constexpr int kLnMaxD = 8192;  // widest row of the separate normalisation kernel
 
 // out = O_cat W_O^T + b_O; with ln, out = LayerNorm(x_q + that) * gamma + beta:
-// in the projection's epilogue for rows of up to kLnFusedMaxN features, else
-// as a separate pass over out.  Events 4..5 time the projection, 6..7 the
-// separate pass.
+// residual and statistics in the projection's epilogue (events 4..5), the
+// normalisation in a second pass (events 6..7).  The statistics go to the
+// workspace.
 int output_projection(const void* O, const void* W_O, const void* b_O, void* out, const void* x_q, int M, int D,
-                      int HV, mha::DType dt, hipStream_t s, const LnSpec* ln, hipEvent_t const* ev) {
+                      int HV, mha::DType dt, hipStream_t s, const LnSpec* ln, char* ws, const LnLayout* lnl,
+                      hipEvent_t const* ev) {
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
   mha::GemmProblem p{O, W_O, b_O, out, M, D, HV, HV, D};
   hipError_t e;
-  if (ln && ln_fused(D)) {
+  if (ln) {
     p.residual = x_q;
     p.gamma = ln->gamma;
     p.beta = ln->beta;
     p.eps = ln->eps;
-    e = mha::launch_gemm_ln(p, dt, s, evt(4), evt(5));
+    p.stats = reinterpret_cast<float2*>(ws + lnl->stats_off);
+    e = mha::launch_gemm_ln(p, dt, s, evt(4), evt(5), evt(6), evt(7));
     if (e != hipSuccess) return hip_fail(e, "output projection + normalisation launch");
     return MHA_OK;
   }
@@ -213,10 +226,6 @@ int output_projection(const void* O, const void* W_O, const void* b_O, void* out
   go.count = 1;
   e = mha::launch_gemm_mfma(go, dt, s, evt(4), evt(5));
   if (e != hipSuccess) return hip_fail(e, "output projection launch");
-  if (ln) {
-    e = mha::launch_residual_ln(out, x_q, ln->gamma, ln->beta, ln->eps, M, D, dt, s, evt(6), evt(7));
-    if (e != hipSuccess) return hip_fail(e, "normalisation launch");
-  }
   return MHA_OK;
 }
 
@@ -243,11 +252,8 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     return fail(MHA_ERR_UNSUPPORTED, "the projection path supports d_k == d_v == %d (got %d, %d)",
                 mha::kMfmaHeadDim, d_k, d_v);
   if (D % 8 != 0) return fail(MHA_ERR_UNSUPPORTED, "D must be a multiple of 8 (got %d)", D);
-  if (ln) {
-    if (!std::isfinite(ln->eps) || ln->eps < 0.0f)
-      return fail(MHA_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
-    if (D > kLnMaxD) return fail(MHA_ERR_UNSUPPORTED, "layer normalisation supports D <= %d (got %d)", kLnMaxD, D);
-  }
+  if (ln && (!std::isfinite(ln->eps) || ln->eps < 0.0f))
+    return fail(MHA_ERR_INVALID_ARG, "ln_eps must be finite and >= 0");
   if (B == 0 || Nq == 0) return MHA_OK;  // nothing to write
   if (!x_q || !W_Q || !W_K || !W_V || !W_O || !out)
     return fail(MHA_ERR_INVALID_ARG, "x_q, W_Q, W_K, W_V, W_O and out must be non-null");
@@ -263,10 +269,12 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   ProjLayout L;
   proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L);
-  if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  const LnLayout LN = ln_layout(L, B, Nq, D);
+  const size_t need = ln ? LN.total : L.total;
+  if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  if (workspace_bytes < need)
+    return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   const int64_t nqb = (Nq + 63) / 64;
   if (nqb * H * B > kMaxBlocks || int64_t(B) * std::max(Nq, Nk) > (int64_t(1) << 31) / 64)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -314,7 +322,7 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     pa.scale = scale;
     hipError_t e = mha::launch_proj_attn(pa, dt, s, evt(0), evt(1));
     if (e != hipSuccess) return hip_fail(e, "fused projection/attention launch");
-    return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ev);
+    return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ws, &LN, ev);
   }
 
   // 1. Q, K, V projections in one launch; outputs row-major [B*N, H*d].
@@ -358,7 +366,7 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   if (e != hipSuccess) return hip_fail(e, "attention launch");
 
   // 3. Output projection (and the residual connection and normalisation).
-  return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ev);
+  return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ws, &LN, ev);
 }
 
 }  // namespace
@@ -409,7 +417,11 @@ int mha_proj_ln_forward_timed(const void* x_q, const void* x_kv, const void* W_Q
                            reinterpret_cast<hipEvent_t const*>(events), plan, &ln);
 }
 
-int mha_proj_ln_fused(int D) { return ln_fused(D) ? 1 : 0; }
+size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype) {
+  ProjLayout L;
+  if (D < 1 || !proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L)) return 0;
+  return ln_layout(L, B, Nq, D).total;
+}
 
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention) {
   return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;

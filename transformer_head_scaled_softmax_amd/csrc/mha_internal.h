@@ -75,11 +75,17 @@ struct GemmProblem {
   void* c;
   int M, N, K;
   int64_t ldx, ldc;
-  const void* residual;  // launch_gemm_ln only: [M, N], row stride ldc
-  const void* gamma;     // launch_gemm_ln only: nullable (1), [N]
-  const void* beta;      // launch_gemm_ln only: nullable (0), [N]
+  // launch_gemm_ln only:
+  const void* residual;  // [M, N], row stride ldc
+  const void* gamma;     // nullable (1), [N]
+  const void* beta;      // nullable (0), [N]
   float eps;
+  float2* stats;         // [M, ln_stats_stride(N)]: per row and column tile, (sum, centred sum of squares)
 };
+
+// Scratch of launch_gemm_ln: per-row statistics of up to one 64-column tile
+// each (the narrowest tiles).
+__host__ __device__ inline int ln_stats_stride(int N) { return (N + 63) / 64; }
 
 constexpr int kMaxGemmProblems = 3;
 
@@ -117,15 +123,14 @@ hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hip
                             hipEvent_t t1 = nullptr);
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
-// Output projection with the residual connection and layer normalisation in
-// its epilogue: one workgroup owns whole rows.  Requires N <= kLnFusedMaxN.
+// Output projection followed by the residual connection and layer
+// normalisation: the projection's epilogue adds the bias and the residual and
+// leaves per-tile row statistics in p.stats and the rows as fp16 differences
+// from their tile means in p.c; a second kernel merges the statistics and
+// normalises the rows in place.  t0/t1 time the projection, t2/t3 the second
+// kernel.
 hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
-                          hipEvent_t t1 = nullptr);
-// out[m, :] = LayerNorm(out[m, :] + residual[m, :]) * gamma + beta in place,
-// rows of D features (D a multiple of 8), row stride D.
-hipError_t launch_residual_ln(void* out, const void* residual, const void* gamma, const void* beta, float eps,
-                              int M, int D, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
-                              hipEvent_t t1 = nullptr);
+                          hipEvent_t t1 = nullptr, hipEvent_t t2 = nullptr, hipEvent_t t3 = nullptr);
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
 hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
@@ -142,8 +147,7 @@ constexpr int kMfmaHeadDim = 64;
 // one wave per workgroup and one per SIMD of the 256 compute units; a partial
 // state is (reference maximum, sum, 2 pad, 64 accumulators) in fp32.
 constexpr int kDecodeMaxRows = 64;
-// Widest row the fused output-projection + layer-normalisation kernel owns.
-constexpr int kLnFusedMaxN = 512;
+
 constexpr int kDecodeWaves = 256 * 4;
 constexpr int kDecodePartFloats = 68;
 

@@ -53,6 +53,8 @@ class Workload:
     # cache capacity S, ``lens`` the filled slots, Hkv cache heads (None: H).
     decode: bool = False
     Hkv: int | None = None
+    # The sublayer with its residual connection and layer normalisation.
+    ln: bool = False
 
     @property
     def D(self) -> int:
@@ -79,6 +81,13 @@ WORKLOADS = {
                  "(B=32, Nq=64, Nk=80, d_model=1024, h=16, source lengths U{20..80})"),
         Workload("long_causal", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 5,
                  "long-context causal self-attention (B=2, n=8192, h=16, d=64)"),
+        Workload("base_encoder_proj_ln", 64, 8, 64, 64, 64, "bf16", MASK_NONE, (10, 64), True, False, 2,
+                 "Transformer-base encoder self-attention sublayer with its residual connection and "
+                 "layer normalisation (B=64, n=64, d_model=512, h=8, lengths U{10..64})", ln=True),
+        Workload("big_cross_proj_ln", 32, 16, 64, 80, 64, "bf16", MASK_NONE, (20, 80), True, True, 4,
+                 "Transformer-big encoder-decoder cross-attention sublayer with its residual connection "
+                 "and layer normalisation (B=32, Nq=64, Nk=80, d_model=1024, h=16, source lengths "
+                 "U{20..80})", ln=True),
         Workload("long_decode", 16, 16, 1, 8192, 64, "bf16", MASK_CAUSAL, (1024, 8192), False, False, 6,
                  "one decoding step against long key/value caches (B=16, h=16, d=64, one new token, "
                  "cache of 8192 slots filled U{1024..8192})", decode=True),
@@ -135,9 +144,11 @@ def core_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None):
     return {"q": q, "k": k, "v": v, "key_lens": key_lens}
 
 
-def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None):
+def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None, ln=False):
     """x_q [B,Nq,D] (and x_kv [B,Nk,D] when ``cross``) ~ N(0,1); Xavier-uniform
-    W_Q, W_K [H*dk, D], W_V [H*dv, D], W_O [D, H*dv]; key_lens from ``lens``."""
+    W_Q, W_K [H*dk, D], W_V [H*dv, D], W_O [D, H*dv]; key_lens from ``lens``;
+    with ``ln`` the norm's scale ~ U(0.5, 1.5) and shift ~ N(0, 0.5^2), drawn
+    last."""
     g = generator(seed)
     x_q = normal(g, (B, Nq, D), dtype)
     x_kv = normal(g, (B, Nk, D), dtype) if cross else None
@@ -146,8 +157,11 @@ def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None):
     W_V = xavier_uniform(g, H * dv, D, dtype)
     W_O = xavier_uniform(g, D, H * dv, dtype)
     key_lens = key_lengths(g, B, *lens) if lens is not None else None
-    return {"x_q": x_q, "x_kv": x_kv, "W_Q": W_Q, "W_K": W_K, "W_V": W_V, "W_O": W_O,
-            "key_lens": key_lens}
+    out = {"x_q": x_q, "x_kv": x_kv, "W_Q": W_Q, "W_K": W_K, "W_V": W_V, "W_O": W_O, "key_lens": key_lens}
+    if ln:
+        out["ln_gamma"] = round_to(g.uniform(0.5, 1.5, size=D).astype(np.float32), dtype)
+        out["ln_beta"] = round_to((g.standard_normal(D) * 0.5).astype(np.float32), dtype)
+    return out
 
 
 def decode_inputs(B, H, Hkv, Nq, S, dk, dv, dtype, seed, lens=None):
@@ -167,7 +181,7 @@ def workload_inputs(w: Workload, seed: int | None = None):
     if w.decode:
         return decode_inputs(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
     if w.proj:
-        return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens)
+        return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens, w.ln)
     return core_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
 
 
