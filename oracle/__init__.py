@@ -92,8 +92,11 @@ class Oracle:
         lib.oracle_decode.argtypes = [_dp] * 4 + [i] * 8 + [_ip, ctypes.c_double, i]
         lib.oracle_mha_proj_ln.argtypes = ([_dp] * 12 + [ctypes.c_double, _dp] + [i] * 8
                                            + [_ip, ctypes.c_double, i])
+        lib.oracle_attention_lse.argtypes = [_dp, _dp, _dp] + [i] * 6 + [_ip, ctypes.c_double, i]
+        lib.oracle_attention_backward.argtypes = [_dp] * 7 + [i] * 7 + [_ip, ctypes.c_double, i]
         for f in (lib.oracle_attention, lib.oracle_scores, lib.oracle_attention_rows,
-                  lib.oracle_mha_proj, lib.oracle_decode, lib.oracle_mha_proj_ln):
+                  lib.oracle_mha_proj, lib.oracle_decode, lib.oracle_mha_proj_ln,
+                  lib.oracle_attention_lse, lib.oracle_attention_backward):
             f.restype = ctypes.c_int
         self._lib = lib
 
@@ -151,6 +154,43 @@ class Oracle:
                                              nthreads or default_threads())
         self._check(st, "oracle_attention_rows")
         return out
+
+    # -- training: row statistics and gradients ----------------------------------
+    def attention_lse(self, q, k, mask_kind: int = MASK_NONE, key_lens=None, scale=None,
+                      nthreads: int | None = None):
+        """lse [B,H,Nq]: natural log of the softmax denominator of each row over its
+        visible keys (-inf for a row with none)."""
+        q, k = _f64(q), _f64(k)
+        B, H, Nq, dk = q.shape
+        Nk = k.shape[2]
+        if scale is None:
+            scale = 1.0 / np.sqrt(dk)
+        lens, lens_p = _lens(key_lens, B)
+        lse = np.empty((B, H, Nq), np.float64)
+        st = self._lib.oracle_attention_lse(_ptr(q), _ptr(k), _ptr(lse), B, H, Nq, Nk, dk, int(mask_kind),
+                                            lens_p, float(scale), nthreads or default_threads())
+        self._check(st, "oracle_attention_lse")
+        return lse
+
+    def attention_backward(self, q, k, v, dout, mask_kind: int = MASK_NONE, key_lens=None, scale=None,
+                           nthreads: int | None = None):
+        """(dq, dk, dv): gradients of sum(dout * attention(q, k, v))."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        B, H, Nq, dk = q.shape
+        Nk, dv = k.shape[2], v.shape[3]
+        if dout.shape != (B, H, Nq, dv):
+            raise ValueError("dout shape")
+        if scale is None:
+            scale = 1.0 / np.sqrt(dk)
+        lens, lens_p = _lens(key_lens, B)
+        gq = np.empty_like(q)
+        gk = np.empty_like(k)
+        gv = np.empty_like(v)
+        st = self._lib.oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(gq), _ptr(gk),
+                                                 _ptr(gv), B, H, Nq, Nk, dk, dv, int(mask_kind), lens_p,
+                                                 float(scale), nthreads or default_threads())
+        self._check(st, "oracle_attention_backward")
+        return gq, gk, gv
 
     # -- multi-head attention with projections ---------------------------------
     def mha_proj(self, x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None,
@@ -261,3 +301,11 @@ def decode(*args, **kwargs):
 
 def mha_proj_ln(*args, **kwargs):
     return get().mha_proj_ln(*args, **kwargs)
+
+
+def attention_lse(*args, **kwargs):
+    return get().attention_lse(*args, **kwargs)
+
+
+def attention_backward(*args, **kwargs):
+    return get().attention_backward(*args, **kwargs)

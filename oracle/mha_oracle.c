@@ -515,3 +515,119 @@ int oracle_mha_proj_ln(const double *x_q, const double *x_kv, const double *W_Q,
     free(z);
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Training: the row statistics of the forward pass and the backward pass.    */
+/*
+ * [TP] "Training (Teacher Forcing + Masking)": the pages' main use of the path is
+ * parallel training, in which gradients flow back through every layer; [AD]
+ * "One forward pass covers the whole sequence".  The pages give no gradient
+ * formulas; these are the derivatives of the forward definition above,
+ * written out: with P the softmax weights of a row (0 at masked keys) and dO
+ * the gradient of a scalar loss with respect to the output rows,
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - D_i),   D_i = sum_j P_ij dP_ij = dO_i . out_i
+ *   dQ_i  = scale sum_j dS_ij k_j
+ *   dK_j  = scale sum_i dS_ij q_i
+ * (the chain rule through out = P V, the softmax Jacobian
+ * diag(P) - P P^T, and s = scale q.k).  Masked keys have P = 0, so they get no
+ * gradient, and a row with no visible key contributes nothing.
+ *
+ * oracle_attention_lse: lse [B,H,Nq] = log sum_j exp(scale q_i.k_j) over the
+ * visible keys (natural logarithm; -inf for a row with no visible key), the
+ * row statistic from which the backward pass recomputes P = exp(s - lse).
+ */
+struct lse_ctx {
+    const double *q, *k;
+    double *lse;
+    int H, Nq, Nk, dk, mask_kind;
+    const int32_t *key_lens;
+    double scale;
+};
+
+static void lse_unit(void *vctx, long unit, double *scratch) {
+    (void)scratch;
+    struct lse_ctx *c = (struct lse_ctx *)vctx;
+    int b = (int)(unit / c->H);
+    int L = key_length(c->key_lens, b, c->Nk);
+    for (int i = 0; i < c->Nq; ++i) {
+        const double *qi = c->q + (unit * c->Nq + i) * (long)c->dk;
+        double m = -INFINITY;
+        for (int j = 0; j < c->Nk; ++j)
+            if (key_visible(i, j, L, c->mask_kind)) {
+                double s = scaled_score(qi, c->k + (unit * c->Nk + j) * (long)c->dk, c->dk, c->scale);
+                if (s > m) m = s;
+            }
+        double z = 0.0;
+        for (int j = 0; j < c->Nk; ++j)
+            if (key_visible(i, j, L, c->mask_kind))
+                z += exp(scaled_score(qi, c->k + (unit * c->Nk + j) * (long)c->dk, c->dk, c->scale) - m);
+        c->lse[unit * c->Nq + i] = (m == -INFINITY) ? -INFINITY : m + log(z);
+    }
+}
+
+int oracle_attention_lse(const double *q, const double *k, double *lse, int B, int H, int Nq, int Nk, int dk,
+                         int mask_kind, const int32_t *key_lens, double scale, int nthreads) {
+    int st = check_dims(B, H, Nq, Nk, dk, 1, mask_kind);
+    if (st) return st;
+    if (!q || !k || !lse) return ORACLE_EINVAL;
+    struct lse_ctx ctx = {q, k, lse, H, Nq, Nk, dk, mask_kind, key_lens, scale};
+    return parallel_for((long)B * H, nthreads, 0, lse_unit, &ctx);
+}
+
+/* Gradients of a scalar loss with respect to q, k, v, given dout = dLoss/dout,
+ * per (b, h) on per-head tensors as in oracle_attention. */
+struct bwd_ctx {
+    const double *q, *k, *v, *dout;
+    double *dq, *dk, *dv;
+    int H, Nq, Nk, dkd, dvd, mask_kind;
+    const int32_t *key_lens;
+    double scale;
+};
+
+static void bwd_unit(void *vctx, long unit, double *scratch) {
+    struct bwd_ctx *c = (struct bwd_ctx *)vctx;
+    int b = (int)(unit / c->H);
+    int L = key_length(c->key_lens, b, c->Nk);
+    const int Nq = c->Nq, Nk = c->Nk, dkd = c->dkd, dvd = c->dvd;
+    const double *q = c->q + unit * (long)Nq * dkd, *k = c->k + unit * (long)Nk * dkd;
+    const double *v = c->v + unit * (long)Nk * dvd, *dout = c->dout + unit * (long)Nq * dvd;
+    double *dq = c->dq + unit * (long)Nq * dkd, *dk = c->dk + unit * (long)Nk * dkd;
+    double *dv = c->dv + unit * (long)Nk * dvd;
+    double *w = scratch;             /* Nk weights of the current row */
+    double *out = scratch + Nk;      /* dvd outputs of the current row */
+    for (long x = 0; x < (long)Nq * dkd; ++x) dq[x] = 0.0;
+    for (long x = 0; x < (long)Nk * dkd; ++x) dk[x] = 0.0;
+    for (long x = 0; x < (long)Nk * dvd; ++x) dv[x] = 0.0;
+    for (int i = 0; i < Nq; ++i) {
+        /* forward for row i: weights P_i. and out_i */
+        attend_row(q + (long)i * dkd, k, dkd, v, dvd, i, Nk, L, c->mask_kind, dkd, dvd, c->scale, out, w);
+        double D = 0.0;
+        for (int e = 0; e < dvd; ++e) D += dout[(long)i * dvd + e] * out[e];
+        for (int j = 0; j < Nk; ++j) {
+            if (!key_visible(i, j, L, c->mask_kind)) continue;
+            const double p = w[j];
+            double dp = 0.0;
+            for (int e = 0; e < dvd; ++e) {
+                dv[(long)j * dvd + e] += p * dout[(long)i * dvd + e];
+                dp += dout[(long)i * dvd + e] * v[(long)j * dvd + e];
+            }
+            const double ds = p * (dp - D);
+            for (int e = 0; e < dkd; ++e) {
+                dq[(long)i * dkd + e] += c->scale * ds * k[(long)j * dkd + e];
+                dk[(long)j * dkd + e] += c->scale * ds * q[(long)i * dkd + e];
+            }
+        }
+    }
+}
+
+int oracle_attention_backward(const double *q, const double *k, const double *v, const double *dout, double *dq,
+                              double *dk, double *dv, int B, int H, int Nq, int Nk, int dkd, int dvd,
+                              int mask_kind, const int32_t *key_lens, double scale, int nthreads) {
+    int st = check_dims(B, H, Nq, Nk, dkd, dvd, mask_kind);
+    if (st) return st;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORACLE_EINVAL;
+    struct bwd_ctx ctx = {q, k, v, dout, dq, dk, dv, H, Nq, Nk, dkd, dvd, mask_kind, key_lens, scale};
+    return parallel_for((long)B * H, nthreads, (long)Nk + dvd + 1, bwd_unit, &ctx);
+}

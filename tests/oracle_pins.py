@@ -632,6 +632,115 @@ def pin_ln_shift_invariance(orc):
     return fails
 
 
+# --------------------------------------------------------------------------
+# Training: row statistics and gradients.
+
+def pin_lse_consistent_with_weights(orc):
+    """exp(s_ij - lse_i) reproduces the softmax weights the forward pass uses, for
+    padded and causal rows; one visible key gives lse = its score; a row with no
+    visible key gives -inf."""
+    fails = []
+    for mask in (NONE, CAUSAL):
+        q, k, v, lens = _random_case(221 + mask, Nq=12, Nk=12 if mask else 17, lo=0)
+        _, w = orc.attention(q, k, v, mask_kind=mask, key_lens=lens, return_weights=True, nthreads=2)
+        s = orc.scores(q, k, mask_kind=mask, key_lens=lens)
+        lse = orc.attention_lse(q, k, mask_kind=mask, key_lens=lens, nthreads=2)
+        with np.errstate(invalid="ignore"):
+            p = np.where(np.isfinite(s), np.exp(s - lse[..., None]), 0.0)
+        p = np.nan_to_num(p)
+        _close(fails, f"exp(s - lse) == weights (mask={mask})", p, w, 1e-13)
+        empty = lens == 0
+        if np.any(empty) and not np.all(np.isneginf(lse[empty])):
+            fails.append("empty rows not -inf")
+    q, k, _, _ = _random_case(225, Nq=3, Nk=3)
+    lse = orc.attention_lse(q, k, mask_kind=CAUSAL, nthreads=1)
+    s = orc.scores(q, k, mask_kind=CAUSAL)
+    _close(fails, "single visible key", lse[:, :, 0], s[:, :, 0, 0], 1e-14)
+    return fails
+
+
+def _fd_loss(orc, q, k, v, dout, mask, lens, scale):
+    return float(np.sum(dout * orc.attention(q, k, v, mask_kind=mask, key_lens=lens, scale=scale, nthreads=1)))
+
+
+def pin_backward_finite_differences(orc):
+    """The gradients of L = sum(dout * out) match central finite differences of
+    the forward oracle (step 1e-5, fp64) at sampled entries of q, k and v, for
+    padded cross-shaped and causal inputs -- a check by a different method."""
+    fails = []
+    g = _rng(231)
+    for mask, Nq, Nk in ((NONE, 5, 7), (CAUSAL, 6, 6)):
+        B, H, d, dv = 2, 2, 4, 3
+        q = g.standard_normal((B, H, Nq, d))
+        k = g.standard_normal((B, H, Nk, d))
+        v = g.standard_normal((B, H, Nk, dv))
+        dout = g.standard_normal((B, H, Nq, dv))
+        lens = np.array([Nk, Nk - 2], np.int32)
+        scale = 0.7
+        gq, gk, gv = orc.attention_backward(q, k, v, dout, mask_kind=mask, key_lens=lens, scale=scale, nthreads=1)
+        h = 1e-5
+        for name, arr, grad in (("q", q, gq), ("k", k, gk), ("v", v, gv)):
+            for _ in range(12):
+                idx = tuple(int(g.integers(0, n)) for n in arr.shape)
+                a1, a2 = arr.copy(), arr.copy()
+                a1[idx] += h
+                a2[idx] -= h
+                args1 = {"q": q, "k": k, "v": v}
+                args2 = dict(args1)
+                args1[name], args2[name] = a1, a2
+                fd = (_fd_loss(orc, args1["q"], args1["k"], args1["v"], dout, mask, lens, scale)
+                      - _fd_loss(orc, args2["q"], args2["k"], args2["v"], dout, mask, lens, scale)) / (2 * h)
+                if abs(fd - grad[idx]) > 1e-7 * (1 + abs(fd)):
+                    fails.append(f"d{name}{idx} (mask={mask}): analytic {grad[idx]:.9g} vs fd {fd:.9g}")
+    return fails
+
+
+def pin_backward_invariants(orc):
+    """Softmax is unchanged by adding one vector to every key, so the key
+    gradients of a row's visible keys sum to zero; padded keys get exactly zero
+    gradient; the gradients are linear in dout."""
+    fails = []
+    for mask, Nq, Nk in ((NONE, 9, 13), (CAUSAL, 11, 11)):
+        q, k, v, lens = _random_case(241 + mask, Nq=Nq, Nk=Nk)
+        dout = _rng(242).standard_normal(v.shape[:2] + (Nq, v.shape[3]))
+        gq, gk, gv = orc.attention_backward(q, k, v, dout, mask_kind=mask, key_lens=lens, nthreads=2)
+        _close(fails, f"sum of key gradients (mask={mask})", gk.sum(axis=2), np.zeros(gk.sum(axis=2).shape), 1e-12)
+        for b, L in enumerate(lens):
+            if np.any(gk[b, :, L:] != 0.0) or np.any(gv[b, :, L:] != 0.0):
+                fails.append(f"padded keys got gradient (mask={mask}, b={b})")
+        g2 = orc.attention_backward(q, k, v, -2.5 * dout, mask_kind=mask, key_lens=lens, nthreads=2)
+        for name, a, b2 in zip("qkv", (gq, gk, gv), g2):
+            _close(fails, f"linearity d{name} (mask={mask})", b2, -2.5 * a, 1e-12)
+    return fails
+
+
+def pin_backward_selection(orc):
+    """One-hot attention (each query selects one key with weight 1 up to e^-40):
+    the value gradient is dout gathered onto the selected keys, and the query and
+    key gradients vanish (the weights do not move)."""
+    fails = []
+    g = _rng(251)
+    B, H, Nq, Nk, d = 1, 2, 6, 8, 16
+    scale = 1.0
+    q = np.zeros((B, H, Nq, d))
+    k = np.zeros((B, H, Nk, d))
+    v = g.standard_normal((B, H, Nk, 5))
+    dout = g.standard_normal((B, H, Nq, 5))
+    want_dv = np.zeros_like(v)
+    for h in range(H):
+        for j in range(Nk):
+            k[0, h, j, j] = 40.0
+        for i in range(Nq):
+            t = (3 * i + h) % Nk
+            q[0, h, i, t] = 1.0
+            want_dv[0, h, t] += dout[0, h, i]
+    gq, gk, gv = orc.attention_backward(q, k, v, dout, scale=scale, nthreads=1)
+    _close(fails, "selection dv", gv, want_dv, 1e-12)
+    _close(fails, "selection dq", gq, np.zeros_like(gq), 1e-12)
+    _close(fails, "selection dk", gk, np.zeros_like(gk), 1e-12)
+    return fails
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_worked_example_projection,
@@ -658,6 +767,10 @@ ALL_PINS = [
     pin_ln_rows_standardised,
     pin_ln_affine,
     pin_ln_shift_invariance,
+    pin_lse_consistent_with_weights,
+    pin_backward_finite_differences,
+    pin_backward_invariants,
+    pin_backward_selection,
 ]
 
 

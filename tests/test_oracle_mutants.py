@@ -55,6 +55,18 @@ MUTANTS = [
     ("norm scale and shift swapped", "const double g = gamma ? gamma[c] : 1.0, b = beta ? beta[c] : 0.0;",
      "const double b = gamma ? gamma[c] : 1.0, g = beta ? beta[c] : 0.0;"),
     ("residual connection dropped", "z[c] = x_q[m * D + c] + out[m * D + c];", "z[c] = out[m * D + c];"),
+    ("lse without the maximum", "c->lse[unit * c->Nq + i] = (m == -INFINITY) ? -INFINITY : m + log(z);",
+     "c->lse[unit * c->Nq + i] = (m == -INFINITY) ? -INFINITY : log(z);"),
+    ("backward softmax term dropped", "const double ds = p * (dp - D);", "const double ds = p * dp;"),
+    ("backward softmax sign", "const double ds = p * (dp - D);", "const double ds = p * (D - dp);"),
+    ("backward dq without the scale", "dq[(long)i * dkd + e] += c->scale * ds * k[(long)j * dkd + e];",
+     "dq[(long)i * dkd + e] += ds * k[(long)j * dkd + e];"),
+    ("backward dk from keys", "dk[(long)j * dkd + e] += c->scale * ds * q[(long)i * dkd + e];",
+     "dk[(long)j * dkd + e] += c->scale * ds * k[(long)j * dkd + e];"),
+    ("backward dv without the weight", "dv[(long)j * dvd + e] += p * dout[(long)i * dvd + e];",
+     "dv[(long)j * dvd + e] += dout[(long)i * dvd + e];"),
+    ("backward D from the values", "for (int e = 0; e < dvd; ++e) D += dout[(long)i * dvd + e] * out[e];",
+     "for (int e = 0; e < dvd; ++e) D += dout[(long)i * dvd + e] * v[e];"),
 ]
 
 
