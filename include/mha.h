@@ -1,6 +1,6 @@
 /*
- * mha.h -- C ABI of libmha, multi-head scaled dot-product attention (forward)
- * for AMD Instinct MI355X (gfx950).
+ * mha.h -- C ABI of libmha, multi-head scaled dot-product attention (forward
+ * and backward) for AMD Instinct MI355X (gfx950).
  *
  * The operation ("Attention Is All You Need" as explained on the pages cited
  * below; trishampatil.com = [TP], aicassindra.com = [AC], alexdo.xyz = [AD],
@@ -158,6 +158,71 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            int D, int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
                            float scale, int dtype, void* workspace, size_t workspace_bytes,
                            void* stream, void* const* events, int plan);
+
+/*
+ * Training ([TP] "Training (Teacher Forcing + Masking)": one parallel forward
+ * pass over the whole target sequence, then gradients back through it; [AD]
+ * "One forward pass covers the whole sequence").  The pages give no gradient
+ * formulas; the backward pass computes the exact derivatives of the
+ * mha_forward definition for a scalar loss whose gradient with respect to
+ * `out` is `dout`:
+ *
+ *   P_ij  = weight of key j in row i (0 for masked keys)
+ *   dv_j  = sum_i P_ij dout_i                  dP_ij = dout_i . v_j
+ *   dS_ij = P_ij (dP_ij - D_i),  D_i = dout_i . out_i
+ *   dq_i  = scale sum_j dS_ij k_j              dk_j  = scale sum_i dS_ij q_i
+ *
+ * Masked keys (padding, the future under the causal mask) receive exactly
+ * zero gradient, and a row with no visible key contributes nothing.
+ *
+ * mha_forward_lse -- mha_forward that also writes the row statistic the
+ * backward pass needs:
+ *
+ *   lse [B, H, Nq] fp32   ln(sum over visible j of exp(scale q_i . k_j));
+ *                         -inf for a row with no visible key
+ *
+ * lse must be non-null and 4-byte aligned (MHA_ERR_INVALID_ARG otherwise) and
+ * must not overlap the other tensors.  Supported types and sizes as for
+ * mha_forward.
+ */
+int mha_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq,
+                    int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                    void* stream);
+
+/*
+ * mha_backward -- gradients of mha_forward with respect to q, k and v.
+ *
+ *   q, k, v, key_lens, mask_kind, scale   as passed to the forward call
+ *   out  [B, H, Nq, d_v]   the forward output
+ *   lse  [B, H, Nq] fp32   the forward's row statistic (mha_forward_lse)
+ *   dout [B, H, Nq, d_v]   gradient of the loss with respect to out
+ *   dq   [B, H, Nq, d_k]   written
+ *   dk   [B, H, Nk, d_k]   written (zero rows for padded keys)
+ *   dv   [B, H, Nk, d_v]   written (zero rows for padded keys)
+ *
+ * The weights P are recomputed from q, k and lse tile by tile; no Nq x Nk
+ * matrix is stored.  Supported: MHA_BF16 and MHA_F16 with d_k == d_v == 64
+ * (MHA_F32 returns MHA_ERR_UNSUPPORTED); tensors 16-byte aligned, lse 4-byte
+ * aligned; outputs must not overlap inputs or each other; Nq and Nk below
+ * 2^24.  Pointers of a side with zero rows may be NULL.  `workspace`: device
+ * memory of at least mha_backward_workspace_bytes(...) bytes, 256-byte
+ * aligned, owned by the caller, contents scratch (it holds D); calls sharing a
+ * workspace must not run concurrently.  Two kernels run in stream order (dq,
+ * which also forms D; then dk and dv).  Returns MHA_OK or a negative status.
+ */
+size_t mha_backward_workspace_bytes(int B, int H, int Nq, int Nk, int d_k, int d_v, int dtype);
+
+int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind,
+                 const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* mha_backward_timed -- as mha_backward, plus 4 events (see the timed variants
+ * above): events[0..1] time the dq kernel, events[2..3] the dk/dv kernel. */
+int mha_backward_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k,
+                       int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* events);
 
 /*
  * mha_proj_ln_forward -- the attention sublayer with its residual connection and

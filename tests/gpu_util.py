@@ -9,6 +9,15 @@ Tolerances (stated for the whole suite):
   rounding unit relative to magnitude (bf16 2^-8, f16 2^-11): rounding a value
   of magnitude |ref| to the output type alone can cost u * |ref|, which the
   flat bound covers only below |ref| ~ 4 (bf16).
+  gradients (bf16 / f16): |g - ref| <= 2e-2 + 2u * A element by element, where
+  A is the sum of the magnitudes of the terms whose sum is g (grad_bounds).
+  Each term carries at most a relative error of about u: the weights P and
+  dS = P (dP - D) are rounded to the input type (u/2) before their products,
+  and P is recomputed from the forward's row statistic, itself a sum of
+  rounded weights (u/2); D uses the rounded forward output, which A covers
+  through |D|_i = sum_c |dout_ic out_ic|; the rounded result adds u/2 |g|
+  <= u/2 A.  A flat bound fails when the terms are large and cancel (scale
+  ~ 1 makes the weights peaked and dP of size ~ sqrt(d)).
 """
 from __future__ import annotations
 
@@ -74,6 +83,33 @@ def assert_close_scaled(got: np.ndarray, ref: np.ndarray, dtype: str, what: str 
         return 0.0
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     bound = TOL_LOWP_ABS + ROUNDING_UNIT[dtype] * np.abs(ref)
+    ratio = float(np.max(np.abs(got - ref) / bound))
+    assert ratio <= 1.0, f"{what}: error reaches {ratio:.3g} x the bound (max abs err {np.max(np.abs(got - ref)):.3g})"
+    return ratio
+
+
+def grad_bounds(q, k, v, dout, P, out, scale):
+    """Magnitude sums (A_dq, A_dk, A_dv) of the gradient terms; see the module
+    docstring.  All arguments fp64 numpy arrays of the oracle's shapes."""
+    q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
+    dP = dout @ np.swapaxes(v, -1, -2)                          # [B,H,Nq,Nk]
+    dabs = np.sum(np.abs(dout * out), axis=-1, keepdims=True)   # [B,H,Nq,1]
+    M = P * (np.abs(dP) + dabs)
+    a = abs(scale)
+    A_dv = np.swapaxes(P, -1, -2) @ np.abs(dout)
+    A_dk = a * (np.swapaxes(M, -1, -2) @ np.abs(q))
+    A_dq = a * (M @ np.abs(k))
+    return A_dq, A_dk, A_dv
+
+
+def assert_close_grad(got: np.ndarray, ref: np.ndarray, A: np.ndarray, dtype: str, what: str = "") -> float:
+    """Element-wise |got - ref| <= 2e-2 + 2u * A (see the module docstring); returns
+    the largest ratio of error to bound."""
+    assert got.shape == ref.shape == A.shape, (got.shape, ref.shape, A.shape)
+    if got.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    bound = TOL_LOWP_ABS + 2.0 * ROUNDING_UNIT[dtype] * A
     ratio = float(np.max(np.abs(got - ref) / bound))
     assert ratio <= 1.0, f"{what}: error reaches {ratio:.3g} x the bound (max abs err {np.max(np.abs(got - ref)):.3g})"
     return ratio

@@ -344,3 +344,123 @@ def test_proj_ln_workspace_checked(lib):
     assert need > lib.mha_proj_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
     assert proj_ln(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
     assert "needed" in lib.mha_last_error().decode()
+
+
+# --------------------------------------------------------------------------
+# Training: the forward row statistic and the backward pass.
+
+def fwd_lse(lib, q=P, k=P, v=P, out=P, lse=P, B=2, H=3, Nq=5, Nk=5, dk=64, dv=64, mask=0, lens=None,
+            scale=0.125, dtype=mb.BF16):
+    return lib.mha_forward_lse(q, k, v, out, lse, B, H, Nq, Nk, dk, dv, mask, lens, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), mb.ERR_INVALID_ARG),
+    (dict(lse=P + 2), mb.ERR_INVALID_ARG),
+    (dict(mask=1, Nq=4, Nk=5), mb.ERR_INVALID_ARG),
+    (dict(dk=32, dv=32), mb.ERR_UNSUPPORTED),
+    (dict(q=None), mb.ERR_INVALID_ARG),
+])
+def test_forward_lse_rejects(lib, kw, status):
+    assert fwd_lse(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+def test_forward_lse_empty_is_ok(lib):
+    assert fwd_lse(lib, Nq=0, lse=None) == mb.OK
+    assert fwd_lse(lib, B=0, lse=None) == mb.OK
+
+
+def bwd(lib, q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, Nq=5, Nk=7, d_k=64, d_v=64,
+        mask=0, lens=None, scale=0.125, dtype=mb.BF16, ws=P, ws_bytes=1 << 20):
+    return lib.mha_backward(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, mask, lens, scale,
+                            dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), mb.ERR_INVALID_ARG),
+    (dict(Nk=-1), mb.ERR_INVALID_ARG),
+    (dict(d_k=0), mb.ERR_INVALID_ARG),
+    (dict(mask=2), mb.ERR_INVALID_ARG),
+    (dict(mask=1), mb.ERR_INVALID_ARG),              # causal needs Nq == Nk
+    (dict(dtype=7), mb.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mb.ERR_INVALID_ARG),
+    (dict(dtype=mb.F32), mb.ERR_UNSUPPORTED),
+    (dict(d_k=128, d_v=128), mb.ERR_UNSUPPORTED),
+    (dict(d_v=32), mb.ERR_UNSUPPORTED),
+    (dict(q=None), mb.ERR_INVALID_ARG),
+    (dict(out=None), mb.ERR_INVALID_ARG),
+    (dict(dout=None), mb.ERR_INVALID_ARG),
+    (dict(lse=None), mb.ERR_INVALID_ARG),
+    (dict(dq=None), mb.ERR_INVALID_ARG),
+    (dict(k=None), mb.ERR_INVALID_ARG),
+    (dict(v=None), mb.ERR_INVALID_ARG),
+    (dict(dk=None), mb.ERR_INVALID_ARG),
+    (dict(dv=None), mb.ERR_INVALID_ARG),
+    (dict(dq=P + 8), mb.ERR_INVALID_ARG),
+    (dict(dout=P + 2), mb.ERR_INVALID_ARG),
+    (dict(lse=P + 2), mb.ERR_INVALID_ARG),
+    (dict(lens=P + 2), mb.ERR_INVALID_ARG),
+    (dict(ws=None), mb.ERR_WORKSPACE),
+    (dict(ws=P + 16), mb.ERR_WORKSPACE),
+    (dict(ws_bytes=255), mb.ERR_WORKSPACE),
+    (dict(Nq=1 << 24, Nk=1 << 24, ws_bytes=1 << 40), mb.ERR_UNSUPPORTED),
+])
+def test_backward_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0, Nk=0),
+                                dict(B=0, q=None, k=None, v=None, out=None, dout=None, lse=None, dq=None,
+                                     dk=None, dv=None, ws=None)])
+def test_backward_empty_is_ok(lib, kw):
+    assert bwd(lib, **kw) == mb.OK
+
+
+_ONE_SIDED_SCRIPT = r"""
+import ctypes, sys
+hip = ctypes.CDLL("libamdhip64.so")
+n = ctypes.c_int(0)
+hip.hipGetDeviceCount(ctypes.byref(n))
+if n.value != 0:
+    print("SKIP device present"); sys.exit(0)
+sys.path.insert(0, sys.argv[1])
+from transformer_head_scaled_softmax_amd import _binding as mb
+lib = mb.load()
+P = 0x100000
+# Nq == 0: no query-side tensor and no workspace (dk, dv are zeros).
+st = lib.mha_backward(None, P, P, None, None, None, None, P, P, 2, 3, 0, 7, 64, 64, 0, None, 0.125, mb.BF16,
+                      None, 0, None)
+print("STATUS", st, lib.mha_last_error().decode())
+# Nk == 0: no key-side tensor (dq is zeros).
+st = lib.mha_backward(P, None, None, P, P, P, P, None, None, 2, 3, 5, 0, 64, 64, 0, None, 0.125, mb.BF16,
+                      P, 1 << 20, None)
+print("STATUS", st, lib.mha_last_error().decode())
+"""
+
+
+def test_backward_one_sided_problems_need_only_that_side():
+    """Pointers of a side with zero rows may be NULL: such calls pass validation and
+    fail only at the launch, for want of a device.  Runs in a child process that
+    first confirms no device is visible (so nothing is launched with fake pointers)."""
+    res = subprocess.run([sys.executable, "-c", _ONE_SIDED_SCRIPT, str(ROOT)], capture_output=True,
+                         text=True, timeout=120, env={"HIP_VISIBLE_DEVICES": "-1",
+                                                      "PATH": "/usr/bin:/bin",
+                                                      "LD_LIBRARY_PATH": "/opt/rocm/lib"})
+    if "SKIP" in res.stdout:
+        pytest.skip("a device is visible")
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.count(f"STATUS {mb.ERR_HIP}") == 2, res.stdout + res.stderr
+
+
+def test_backward_workspace_bytes(lib):
+    # D_i per row, fp32 [B, H, Nq], rounded up to 256 bytes
+    assert lib.mha_backward_workspace_bytes(2, 16, 8192, 8192, 64, 64, mb.BF16) == 2 * 16 * 8192 * 4
+    assert lib.mha_backward_workspace_bytes(3, 5, 7, 9, 64, 64, mb.F16) == _r256(3 * 5 * 7 * 4)
+    assert lib.mha_backward_workspace_bytes(3, 5, 0, 9, 64, 64, mb.BF16) == 0
+    assert lib.mha_backward_workspace_bytes(-1, 5, 7, 9, 64, 64, mb.BF16) == 0
+    assert lib.mha_backward_workspace_bytes(3, 5, 7, 9, 64, 64, 9) == 0
+    need = lib.mha_backward_workspace_bytes(2, 3, 5, 7, 64, 64, mb.BF16)
+    assert bwd(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+    assert "needed" in lib.mha_last_error().decode()

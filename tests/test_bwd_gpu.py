@@ -1,0 +1,229 @@
+"""GPU parity of the training path: the forward row statistic (mha_forward_lse)
+and the gradients (mha_backward) against the fp64 oracle on the same seeded
+inputs, through the C ABI.
+
+The GPU backward takes the GPU forward's own out and lse, as a training step
+would; the oracle computes the gradients from q, k, v and dout alone, so every
+rounding of the GPU path (forward output, row statistic, the weights and dS
+rounded to the input type for the matrix cores, the rounded gradients) counts
+against the tolerance.
+
+Tolerances (derivation in gpu_util):
+  lse: |lse - ref| <= 4e-3 (bf16), 1e-3 (f16), 1e-5 * max(1, |ref|) (fp32);
+       -inf exactly for a row with no visible key.
+  gradients (bf16/f16): |g - ref| <= 2e-2 + 2u * A element by element, A the
+       sum of the magnitudes of the terms that make up each gradient element.
+  masking: gradients of padded keys are exactly zero.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close_grad, grad_bounds, lens_dev, to_dev, to_host
+from transformer_head_scaled_softmax_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mha = pytest.importorskip("transformer_head_scaled_softmax_amd")
+
+CAUSAL, NONE = mha.MASK_CAUSAL, mha.MASK_NONE
+LSE_TOL = {"bf16": 4e-3, "f16": 1e-3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mha.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_train(inp, dtype, mask, scale=None):
+    """Forward with lse, then backward, on the device; returns host arrays."""
+    q, k, v, dout = (to_dev(inp[n], dtype) for n in ("q", "k", "v", "dout"))
+    lens = lens_dev(inp["key_lens"])
+    out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=lens, scale=scale)
+    dq, dk, dv = mha.backward(q, k, v, out, dout, lse, mask_kind=mask, key_lens=lens, scale=scale)
+    torch.cuda.synchronize()
+    return {"out": to_host(out), "lse": lse.cpu().numpy().astype(np.float64), "dq": to_host(dq),
+            "dk": to_host(dk), "dv": to_host(dv)}
+
+
+def check_lse(got, ref, dtype, what):
+    assert got.shape == ref.shape
+    ninf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ninf), f"{what}: -inf rows differ"
+    g, r = got[~ninf], ref[~ninf]
+    if g.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(g)), f"{what}: non-finite lse"
+    err = np.abs(g - r)
+    if dtype == "f32":
+        bound = 1e-5 * np.maximum(1.0, np.abs(r))
+        ratio = float(np.max(err / bound))
+    else:
+        ratio = float(np.max(err) / LSE_TOL[dtype])
+    assert ratio <= 1.0, f"{what}: lse error {np.max(err):.3g} ({ratio:.3g} x the bound)"
+    return ratio
+
+
+def compare_grads(got, inp, dtype, kw, what):
+    """Gradients against the oracle at the suite's gradient tolerance; returns the
+    error-to-bound ratios."""
+    ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], **kw)
+    out, P = oracle.attention(inp["q"], inp["k"], inp["v"], return_weights=True, **kw)
+    scale = kw.get("scale")
+    scale = 1.0 / np.sqrt(inp["q"].shape[-1]) if scale is None else scale
+    A = grad_bounds(inp["q"], inp["k"], inp["v"], inp["dout"], P, out, scale)
+    return {n: assert_close_grad(got[n], r, a, dtype, f"{n} {what}")
+            for n, r, a in zip(("dq", "dk", "dv"), ref, A)}
+
+
+def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override=None):
+    inp = synth.train_inputs(B, H, Nq, Nk, 64, 64, dtype, seed, lens)
+    if lens_override is not None:
+        inp["key_lens"] = np.asarray(lens_override, np.int32)
+    what = f"B{B} H{H} Nq{Nq} Nk{Nk} {dtype} mask{mask} lens{inp['key_lens']} scale{scale}"
+    got = gpu_train(inp, dtype, mask, scale)
+    kw = dict(mask_kind=mask, key_lens=inp["key_lens"], scale=scale)
+    check_lse(got["lse"], oracle.attention_lse(inp["q"], inp["k"], **kw), dtype, what)
+    ratios = compare_grads(got, inp, dtype, kw, what)
+    # Padded keys receive exactly zero gradient.
+    if inp["key_lens"] is not None:
+        for b, L in enumerate(np.clip(inp["key_lens"], 0, Nk)):
+            assert not np.any(got["dk"][b, :, L:]), f"dk of padded keys {what}"
+            assert not np.any(got["dv"][b, :, L:]), f"dv of padded keys {what}"
+    return got, ratios
+
+
+# ---------------------------------------------------------------------------
+# The row statistic.
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("B,H,Nq,Nk,mask,lens", [
+    (2, 3, 64, 64, NONE, None),
+    (2, 2, 150, 150, CAUSAL, (20, 150)),
+    (3, 2, 37, 101, NONE, (1, 101)),
+    (1, 2, 300, 300, CAUSAL, None),
+])
+def test_forward_lse_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
+    inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, dtype, 11, lens)
+    q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
+    kl = lens_dev(inp["key_lens"])
+    out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=kl)
+    plain = mha.forward(q, k, v, mask_kind=mask, key_lens=kl)
+    torch.cuda.synchronize()
+    # The statistic is an extra output: the attention output is unchanged.
+    assert torch.equal(out, plain)
+    ref = oracle.attention_lse(inp["q"], inp["k"], mask_kind=mask, key_lens=inp["key_lens"])
+    check_lse(lse.cpu().numpy().astype(np.float64), ref, dtype, f"lse B{B} H{H} Nq{Nq} Nk{Nk} {dtype}")
+
+
+def test_forward_lse_rows_without_keys_are_minus_inf():
+    inp = synth.core_inputs(3, 2, 70, 70, 64, 64, "bf16", 12)
+    lens = np.array([0, 5, 70], np.int32)
+    q, k, v = (to_dev(inp[n], "bf16") for n in ("q", "k", "v"))
+    out, lse = mha.forward_lse(q, k, v, mask_kind=NONE, key_lens=lens_dev(lens))
+    torch.cuda.synchronize()
+    got = lse.cpu().numpy()
+    assert np.all(np.isneginf(got[0])) and np.all(np.isfinite(got[1:]))
+    ref = oracle.attention_lse(inp["q"], inp["k"], key_lens=lens)
+    check_lse(got.astype(np.float64), ref, "bf16", "lse with an empty sequence")
+
+
+# ---------------------------------------------------------------------------
+# Gradients.
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,H,Nq,Nk,mask,lens", [
+    (2, 3, 64, 64, NONE, None),              # one tile each way
+    (2, 2, 64, 64, CAUSAL, (10, 64)),        # the decoder shape, padded
+    (2, 2, 150, 150, CAUSAL, (20, 150)),     # several tiles, ragged tail, padding
+    (3, 2, 37, 101, NONE, (1, 101)),         # cross-attention, padded, Nq < Nk
+    (2, 2, 200, 64, NONE, (30, 64)),         # cross-attention, Nq > Nk
+    (1, 2, 300, 300, CAUSAL, None),          # long blocks (four waves) with a ragged tail
+    (1, 1, 1, 1, NONE, None),                # one query, one key
+    (1, 1, 33, 33, CAUSAL, None),            # one row past a 32-row block
+])
+def test_backward_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
+    check_train(B, H, Nq, Nk, dtype, mask, lens, seed=13)
+
+
+@pytest.mark.parametrize("scale", [0.125, 1.0, -0.3, 0.0])
+def test_backward_scale_argument(scale):
+    check_train(2, 2, 96, 96, "bf16", CAUSAL, (40, 96), seed=14, scale=scale)
+
+
+def test_backward_empty_sequences_and_clamped_lengths():
+    # key length 0 (no visible key: zero gradients), clamped -3 -> 0, 500 -> Nk
+    got, _ = check_train(4, 2, 80, 80, "bf16", NONE, None, seed=15, lens_override=[0, 37, -3, 500])
+    for b in (0, 2):
+        assert not np.any(got["dq"][b]) and not np.any(got["dk"][b]) and not np.any(got["dv"][b])
+        assert np.all(np.isneginf(got["lse"][b]))
+
+
+def test_backward_one_sided_problems():
+    # Nq == 0: every key gets zero gradient; Nk == 0: every query does.
+    inp = synth.train_inputs(2, 3, 45, 70, 64, 64, "bf16", 17)
+    k, v = to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
+    q0 = torch.empty(2, 3, 0, 64, device="cuda", dtype=torch.bfloat16)
+    lse0 = torch.empty(2, 3, 0, device="cuda", dtype=torch.float32)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    mha.backward(q0, k, v, q0, q0, lse0, dk=dk, dv=dv)
+    q, dout = to_dev(inp["q"], "bf16"), to_dev(inp["dout"], "bf16")
+    k0 = torch.empty(2, 3, 0, 64, device="cuda", dtype=torch.bfloat16)
+    out, lse = mha.forward_lse(q, k0, k0)
+    dq = torch.full_like(q, 7.0)
+    mha.backward(q, k0, k0, out, dout, lse, dq=dq)
+    torch.cuda.synchronize()
+    assert not torch.any(dk) and not torch.any(dv) and not torch.any(dq) and not torch.any(out)
+    assert bool(torch.all(torch.isneginf(lse)))
+
+
+def test_backward_is_deterministic():
+    inp = synth.train_inputs(2, 4, 300, 300, 64, 64, "bf16", 16, (100, 300))
+    a = gpu_train(inp, "bf16", CAUSAL)
+    b = gpu_train(inp, "bf16", CAUSAL)
+    for n in ("dq", "dk", "dv", "lse"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_base_decoder_causal_bwd_full():
+    w = synth.WORKLOADS["base_decoder_causal_bwd"]
+    inp = synth.workload_inputs(w)
+    got = gpu_train(inp, w.dtype, w.mask)
+    compare_grads(got, inp, w.dtype, dict(mask_kind=w.mask, key_lens=inp["key_lens"]), w.name)
+
+
+def test_long_causal_bwd_full_size():
+    """The long-context workload at full size (B=2, n=8192, h=16) in the launch
+    configuration the benchmark times: four (b, h) slices against the oracle element
+    by element, and properties that hold exactly on every slice:
+    sum_j dv_j = sum_i dout_i (each weight row sums to 1) and sum_j dk_j = 0 up to
+    the rounding of out in D (each dS row sums to 0)."""
+    w = synth.WORKLOADS["long_causal_bwd"]
+    inp = synth.workload_inputs(w)
+    got = gpu_train(inp, w.dtype, w.mask)
+    for n in ("dq", "dk", "dv"):
+        assert np.all(np.isfinite(got[n])), n
+    sdv = got["dv"].sum(axis=2)
+    sdo = inp["dout"].astype(np.float64).sum(axis=2)
+    # |sum of 8192 rounded terms - exact| stays far below 0.05 * sqrt(8192) ~ 4.5
+    assert np.max(np.abs(sdv - sdo)) <= 0.05 * np.sqrt(w.Nq), np.max(np.abs(sdv - sdo))
+    assert np.max(np.abs(got["dk"].sum(axis=2))) <= 0.05 * np.sqrt(w.Nk)
+    # Four slices against the oracle: the gradients in one call (a thread per
+    # slice), the weights for the bound one slice at a time (512 MiB each in fp64).
+    picks = ((0, 0), (0, 9), (1, 5), (1, 15))
+    st = {n: np.stack([inp[n][b, h] for b, h in picks])[None] for n in ("q", "k", "v", "dout")}
+    ref = oracle.attention_backward(st["q"], st["k"], st["v"], st["dout"], mask_kind=w.mask)
+    scale = 1.0 / np.sqrt(w.d)
+    for s, (b, h) in enumerate(picks):
+        sl = {n: st[n][:, s:s + 1] for n in st}
+        out, P = oracle.attention(sl["q"], sl["k"], sl["v"], mask_kind=w.mask, return_weights=True)
+        A = grad_bounds(sl["q"], sl["k"], sl["v"], sl["dout"], P, out, scale)
+        del P
+        r = [assert_close_grad(got[n][b:b + 1, h:h + 1], ref[i][:, s:s + 1], A[i], w.dtype,
+                               f"{n} {w.name} slice ({b},{h})") for i, n in enumerate(("dq", "dk", "dv"))]
+        print(f"slice ({b},{h}) error/bound dq {r[0]:.3f} dk {r[1]:.3f} dv {r[2]:.3f}", flush=True)

@@ -1,4 +1,4 @@
-"""MI355X-native multi-head scaled dot-product attention (forward).
+"""MI355X-native multi-head scaled dot-product attention (forward and backward).
 
 Thin PyTorch-facing wrappers over libmha's C ABI (include/mha.h).  PyTorch only
 provides device memory and the current HIP stream; the computation is the
@@ -13,6 +13,8 @@ library's HIP kernels.  Functions raise ``MhaError`` on a non-zero status and
         LayerNorm(x_q + proj_forward(...)) -> out [B,Nq,D]
     decode_forward(q, k_cache, v_cache, cache_lens=None, mask_kind=MASK_CAUSAL, ...)
         q [B,H,Nq,d_k], k_cache [B,H_kv,S,d_k], v_cache [B,H_kv,S,d_v] -> out [B,H,Nq,d_v]
+    forward_lse(q, k, v, ...) -> (out, lse [B,H,Nq] fp32)
+    backward(q, k, v, out, dout, lse, ...) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ import math
 from ._binding import (BF16, EXPORTS, F16, F32, MASK_CAUSAL, MASK_NONE, PLAN_AUTO, PLAN_FUSED, PLAN_UNFUSED,
                        MhaError, check, load)
 
-__all__ = ["forward", "proj_forward", "proj_ln_forward", "proj_workspace_bytes", "decode_forward",
+__all__ = ["forward", "forward_lse", "backward", "backward_workspace_bytes", "proj_forward", "proj_ln_forward", "proj_workspace_bytes", "decode_forward",
            "decode_workspace_bytes",
            "decode_split", "MASK_NONE", "MASK_CAUSAL", "PLAN_AUTO", "PLAN_UNFUSED", "PLAN_FUSED", "MhaError",
            "load", "EXPORTS"]
@@ -199,3 +201,75 @@ def decode_forward(q, k_cache, v_cache, cache_lens=None, mask_kind: int = MASK_C
         st = lib.mha_decode_forward_timed(*args, arr)
     check(lib, st)
     return out
+
+
+def forward_lse(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None,
+                out=None, lse=None, stream=None):
+    """Attention per head plus the row statistic lse [B,H,Nq] (fp32) the backward
+    pass needs; see mha_forward_lse in include/mha.h.  Returns (out, lse)."""
+    import torch
+    B, H, Nq, dk = q.shape
+    Nk, dv = k.shape[2], v.shape[3]
+    if k.shape != (B, H, Nk, dk) or v.shape != (B, H, Nk, dv):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, Nq):
+        raise ValueError(f"lse must be a float32 tensor of shape ({B}, {H}, {Nq})")
+    lib = load()
+    st = lib.mha_forward_lse(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                             _dev_ptr(lse, "lse"), B, H, Nq, Nk, dk, dv, int(mask_kind), _lens_ptr(key_lens, B),
+                             float(scale), _dtype_code(q), _stream(stream))
+    check(lib, st)
+    return out, lse
+
+
+def backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, dtype_code: int = BF16) -> int:
+    return int(load().mha_backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, dtype_code))
+
+
+def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
+    """Gradients (dq, dk, dv) of attention for output gradient ``dout``; ``out`` and
+    ``lse`` come from forward_lse with the same arguments.  See mha_backward in
+    include/mha.h.  ``events``: None, or 4 hipEvent_t handles (ints) for
+    mha_backward_timed."""
+    import torch
+    B, H, Nq, d_k = q.shape
+    Nk, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, H, Nk, d_k) or v.shape != (B, H, Nk, d_v):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if out.shape != (B, H, Nq, d_v) or dout.shape != (B, H, Nq, d_v):
+        raise ValueError("out and dout must have shape [B, H, Nq, d_v]")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, Nq):
+        raise ValueError(f"lse must be a float32 tensor of shape ({B}, {H}, {Nq})")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out, dout must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    code = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    lib = load()
+    need = int(lib.mha_backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = (_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"), _dev_ptr(dout, "dout"),
+            _dev_ptr(lse, "lse"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, Nq, Nk, d_k,
+            d_v, int(mask_kind), _lens_ptr(key_lens, B), float(scale), code, _dev_ptr(workspace, "workspace"),
+            0 if workspace is None else workspace.numel(), _stream(stream))
+    if events is None:
+        st = lib.mha_backward(*args)
+    else:
+        import ctypes
+        arr = (ctypes.c_void_p * 4)(*events)
+        st = lib.mha_backward_timed(*args, arr)
+    check(lib, st)
+    return dq, dk, dv

@@ -102,6 +102,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int nqb) {
 
   if (valid) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    // Row statistic for the backward pass: ln(sum_j exp(scale q.k_j)).
+    if (a.lse && lane == 0)
+      a.lse[((int64_t)b * a.H + h) * a.Nq + i] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
     float* op = static_cast<float*>(a.out) + b * a.o_sb + h * a.o_sh + (int64_t)i * a.o_sn;
     if (lane < a.dv) op[lane] = acc0 * inv;
     if (lane + 64 < a.dv) op[lane + 64] = acc1 * inv;

@@ -307,6 +307,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
   for (int u = 0; u < QS; ++u) {
     const float ltot = lanes_sum(lsum[u]);
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    // Row statistic for the backward pass: ln(sum_j exp(scale q.k_j)) =
+    // (m_ref + log2(sum)) * ln 2, whatever reference the row ended with.
+    if (a.lse && half == 0 && qvalid[u])
+      a.lse[((int64_t)b * a.H + h) * a.Nq + qi[u]] =
+          ltot > 0.0f ? (m_ref[u] + __builtin_amdgcn_logf(ltot)) * 0.6931471805599453f : -INFINITY;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll

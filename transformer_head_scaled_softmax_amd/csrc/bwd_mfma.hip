@@ -1,0 +1,501 @@
+// bwd_mfma.hip -- gradients of bf16 / fp16 scaled dot-product attention, head
+// size 64, on the gfx950 matrix cores (v_mfma_f32_32x32x16_{bf16,f16}).
+//
+// The pages' use of the path is teacher-forced training, where one forward
+// pass covers the whole sequence and gradients flow back through it
+// ("Training (Teacher Forcing + Masking)", trishampatil.com; "One forward pass
+// covers the whole sequence", alexdo.xyz).  They give no gradient formulas;
+// these are the exact derivatives of the forward definition
+// softmax(scale * Q K^T) V with masked keys at weight 0, for output gradient
+// dO:
+//
+//   P_ij  = exp(scale q_i.k_j - lse_i)  (visible keys; 0 otherwise)
+//   dV_j  = sum_i P_ij dO_i             dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i),         D_i = dO_i . out_i
+//   dQ_i  = scale sum_j dS_ij k_j       dK_j = scale sum_i dS_ij q_i
+//
+// lse_i is the forward pass's row statistic (natural log of the softmax
+// denominator), so P is recomputed tile by tile and never stored.
+//
+// Two kernels, no atomics.  bwd_dq_kernel owns a block of queries and
+// streams the keys (three products per tile: S^T, dP^T, dQ^T); it also forms
+// D_i for its rows and leaves them in a workspace.  bwd_dkdv_kernel owns a
+// block of keys and streams the queries (four products: S, dP, dV^T, dK^T).
+// The products are arranged so that the score-shaped accumulators (S, dP)
+// feed the next MFMA as its B operand straight from registers: a 32x32
+// accumulator holds, in lane n + 32*half, rows 16t + 8(e/4) + 4half + e%4
+// (t = 0, 1; e = 0..7) of column n, and those eight values are the B operand
+// of one 16-deep MFMA step when the A operand is read with the same row order
+// -- which the transposing LDS read ds_read_b64_tr_b16 delivers.
+//
+// MFMA 32x32x16 lane layout (checked on the device): A[m][k] comes from lane
+// m + 32*(k/8), element k%8; B[k][n] from lane n + 32*(k/8), element k%8;
+// C[m][n] lands in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
+#include "mfma_util.h"
+
+namespace mha {
+namespace {
+
+constexpr int kD = kMfmaHeadDim;  // 64
+constexpr int kBT = 64;           // rows per streamed LDS tile
+constexpr int kSS = 72;           // row stride (elements) of the epilogue staging
+constexpr int kDead = (int)0x80000000u;  // beyond any range check: loads return zeros
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Tiles in LDS are dense 128-byte rows whose 16-byte chunks are permuted per
+// row: chunk c of row r sits in slot c ^ dual_swizzle(r).  The permutation
+// keeps both access patterns conflict-free: row operands (16 bytes per lane
+// from 16 consecutive rows: the slots of rows of one parity are all distinct)
+// and the transposing reads (8 bytes per lane from 4 consecutive rows and 4
+// adjacent chunks: rows 4a, 4a+1 and 4a+2, 4a+3 use chunk sets that differ in
+// bit 2).
+__device__ inline int dual_swizzle(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+
+__device__ inline u32x4_t row_read(const uint16_t* tile, int row, int chunk) {
+  return *reinterpret_cast<const u32x4_t*>(&tile[row * kD + ((chunk ^ dual_swizzle(row)) << 3)]);
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4k + q supplies the
+// address of row (r0 + k), features (c0 + 4q .. +3); lane l of the group then
+// receives feature c0 + l of rows r0 .. r0+3.
+__device__ inline u32x2_t tr_read(const uint16_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  lds_s16x4_t* lp = (lds_s16x4_t*)(const __attribute__((address_space(3))) uint16_t*)p;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
+
+// Per-lane offsets of the transposed A operand A[m = feature][k = tile row]
+// for 16-row step t of a 32-row sub-block: rows 16t + 4half + {0..3} (first
+// half of the operand) and 16t + 8 + 4half + {0..3} (second half), features
+// 32cb + (lane & 31).  Offsets are relative to row 16t of the sub-block (the
+// swizzle does not depend on t).
+struct TrOffsets {
+  int off[2][2];  // [lo/hi][cb]
+  __device__ TrOffsets(int lane) {
+    const int half = lane >> 5, k = (lane & 15) >> 2, q = lane & 3, cg = (lane >> 4) & 1;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int row = 8 * hi + 4 * half + k;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int c = cb * 32 + 16 * cg + 4 * q;
+        off[hi][cb] = row * kD + (((c >> 3) ^ dual_swizzle(row)) << 3) + (c & 7);
+      }
+    }
+  }
+};
+
+__device__ inline u32x4_t tr_operand(const uint16_t* tile, const TrOffsets& o, int row16, int cb) {
+  const u32x2_t lo = tr_read(tile + row16 * kD + o.off[0][cb]);
+  const u32x2_t hi = tr_read(tile + row16 * kD + o.off[1][cb]);
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// lse in natural-log units -> the exp2 argument offset; a row with no
+// visible key (lse = -inf) gets +inf so every weight of it is 0.
+__device__ inline float lse_to_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// Stores a 64-feature x 32-row accumulator pair (register (cb, 4g + e) of lane
+// (col, half) = feature 32cb + 8g + 4half + e of row col) times `mul` as
+// 32 rows of the output, through this wave's staging area, 16 bytes per lane.
+template <class Op>
+__device__ inline void store_rows(const f32x16_t (&acc)[2], float mul, uint16_t* stage, uint16_t* out,
+                                  int row0, int nrows, int lane) {
+  const int half = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2_t w;
+      w[0] = Op::pack(acc[cb][4 * g + 0] * mul, acc[cb][4 * g + 1] * mul);
+      w[1] = Op::pack(acc[cb][4 * g + 2] * mul, acc[cb][4 * g + 3] * mul);
+      *reinterpret_cast<u32x2_t*>(&stage[col * kSS + cb * 32 + g * 8 + half * 4]) = w;
+    }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = lane + 64 * i, row = id >> 3, ch = id & 7;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&stage[row * kSS + ch * 8]);
+    if (row0 + row < nrows) *reinterpret_cast<u32x4_t*>(out + (int64_t)(row0 + row) * kD + ch * 8) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a workgroup owns 32*NW queries of one (b, h), one wave per 32 queries.
+// Per 64-key tile a wave computes S^T = K Q^T and dP^T = V dO^T (keys x
+// queries, so each lane holds one query's scores), P^T and dS^T, then
+// dQ^T += K^T dS^T with K^T read transposed from the same LDS tile.
+template <class Op, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a, int nqb) {
+  constexpr int NT = NW * 64;
+  constexpr int QB = NW * 32;
+  constexpr int CH = (kBT * 8) / NT;  // 16-byte chunks of K (and of V) per thread per tile
+  static_assert(CH >= 1, "tile too small for the workgroup");
+  static_assert(NW * 32 * kSS <= 4 * kBT * kD, "staging does not fit");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBT * kD];  // K, V double-buffered
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // longest first under the causal mask
+  const int b = bh / a.H;
+
+  int L = a.Nk;
+  if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
+  const int q0 = qb * QB, qw0 = q0 + wave * 32;
+  const int qi = qw0 + col;
+  const bool qvalid = qi < a.Nq;
+  const int kend = a.causal ? min(L, qi + 1) : L;  // keys this lane's query sees
+  const int kend_blk = a.causal ? min(L, min(q0 + QB, a.Nq)) : L;
+  const int kmin_wave = a.causal ? min(L, qw0 + 1) : L;               // tiles below: no masking
+  const int kmax_wave = a.causal ? min(L, min(qw0 + 32, a.Nq)) : L;   // tiles from here: skip
+  const int ntiles = (max(kend_blk, 0) + kBT - 1) / kBT;
+
+  const int64_t qhead = (int64_t)bh * a.Nq * kD, khead = (int64_t)bh * a.Nk * kD;
+  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint16_t*>(a.q) + qhead, (int64_t)a.Nq * kD * 2);
+  const __amdgpu_buffer_rsrc_t dosrc =
+      make_rsrc(static_cast<const uint16_t*>(a.dout) + qhead, (int64_t)a.Nq * kD * 2);
+  const __amdgpu_buffer_rsrc_t osrc = make_rsrc(static_cast<const uint16_t*>(a.out) + qhead, (int64_t)a.Nq * kD * 2);
+  const int64_t kvbytes = (int64_t)max(kend_blk, 0) * kD * 2;
+  const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(static_cast<const uint16_t*>(a.k) + khead, kvbytes);
+  const __amdgpu_buffer_rsrc_t vsrc = make_rsrc(static_cast<const uint16_t*>(a.v) + khead, kvbytes);
+
+  // This lane's query as B operands (features 16kk + 8half .. +7) of
+  // S^T = K Q^T and dP^T = V dO^T; out only for D.
+  const int qoff = qvalid ? qi * (kD * 2) + half * 16 : kDead;
+  u32x4_t qreg[4], doreg[4];
+  float dpart = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    qreg[kk] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff + kk * 32, 0, 0);
+    doreg[kk] = __builtin_amdgcn_raw_buffer_load_b128(dosrc, qoff + kk * 32, 0, 0);
+    const u32x4_t ov = __builtin_amdgcn_raw_buffer_load_b128(osrc, qoff + kk * 32, 0, 0);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dpart = fmaf(Op::to_float(doreg[kk][w] & 0xffff), Op::to_float(ov[w] & 0xffff), dpart);
+      dpart = fmaf(Op::to_float(doreg[kk][w] >> 16), Op::to_float(ov[w] >> 16), dpart);
+    }
+  }
+  const float Dq = lanes_sum(dpart);  // D_i = dO_i . out_i (both lane halves)
+  float lse2 = INFINITY;
+  if (qvalid) {
+    lse2 = lse_to_log2(a.lse[(int64_t)bh * a.Nq + qi]);
+    if (half == 0) a.dsum[(int64_t)bh * a.Nq + qi] = Dq;
+  }
+  const float c2 = a.scale * kLog2e;
+
+  uint16_t* const kbuf0 = lds;
+  uint16_t* const vbuf0 = lds + 2 * kBT * kD;
+  int goff[CH], spos[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = tid + c * NT, row = idx >> 3, ch = idx & 7;
+    goff[c] = (row * kD + ch * 8) * 2;
+    spos[c] = row * kD + ((ch ^ dual_swizzle(row)) << 3);
+  }
+  u32x4_t kreg[CH], vreg[CH];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(ksrc, goff[c] + t * (kBT * kD * 2), 0, 0);
+      vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, goff[c] + t * (kBT * kD * 2), 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      *reinterpret_cast<u32x4_t*>(&kbuf0[buf * kBT * kD + spos[c]]) = kreg[c];
+      *reinterpret_cast<u32x4_t*>(&vbuf0[buf * kBT * kD + spos[c]]) = vreg[c];
+    }
+  };
+  const TrOffsets tro(lane);
+
+  f32x16_t dq[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[cb][r] = 0.0f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int j0 = t * kBT;
+    const uint16_t* ks = kbuf0 + buf * kBT * kD;
+    const uint16_t* vs = vbuf0 + buf * kBT * kD;
+    load_tile(t + 1);
+
+    if (j0 < kmax_wave) {  // wave-uniform
+      // S^T and dP^T, two 32-key blocks: register (jb, r) of this lane is key
+      // j0 + 32jb + 8(r/4) + 4half + r%4 of query qi.
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[jb][r] = 0.0f;
+          dp[jb][r] = 0.0f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          s[jb] = Op::mma(row_read(ks, jb * 32 + col, 2 * kk + half), qreg[kk], s[jb]);
+          dp[jb] = Op::mma(row_read(vs, jb * 32 + col, 2 * kk + half), doreg[kk], dp[jb]);
+        }
+      }
+      // K^T operands of dQ^T += K^T dS^T: step t4 covers keys 16t4 .. +15.
+      u32x4_t kt[4][2];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) kt[t4][cb] = tr_operand(ks, tro, 16 * t4, cb);
+
+      const bool masking = j0 + kBT > kmin_wave;
+      const int lim = kend - j0 - 4 * half;
+      u32x4_t dsb[4];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int jb = t4 >> 1, r = (t4 & 1) * 8 + 2 * w;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -lse2));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[jb][r + 1], c2, -lse2));
+          if (masking) {
+            const int kr = jb * 32 + (r >> 2) * 8 + (r & 3);
+            p0 = kr >= lim ? 0.0f : p0;
+            p1 = kr + 1 >= lim ? 0.0f : p1;
+          }
+          dsb[t4][w] = Op::pack(p0 * (dp[jb][r] - Dq), p1 * (dp[jb][r + 1] - Dq));
+        }
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) dq[cb] = Op::mma(kt[t4][cb], dsb[t4], dq[cb]);
+    }
+
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ = scale * (dQ^T)^T; rows past Nq are not written.
+  uint16_t* stage = lds + wave * 32 * kSS;
+  store_rows<Op>(dq, a.scale, stage, static_cast<uint16_t*>(a.dq) + qhead, qw0, a.Nq, lane);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: a workgroup owns 32*NW keys of one (b, h), one wave per 32 keys.
+// Query tiles of 64 (Q, dO, lse, D) stream through LDS; per 32-query
+// sub-block a wave computes S = Q K^T and dP = dO V^T (queries x keys, so each
+// lane holds one key's column), P and dS, then dV^T += dO^T P and
+// dK^T += Q^T dS with dO^T and Q^T read transposed from the same tiles.
+template <class Op, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
+  constexpr int NT = NW * 64;
+  constexpr int KB = NW * 32;
+  constexpr int CH = (kBT * 8) / NT;  // 16-byte chunks of Q (and of dO) per thread per tile
+  static_assert(CH >= 1 && NT >= 2 * kBT, "tile too small for the workgroup");
+  static_assert(NW * 32 * kSS <= 4 * kBT * kD, "staging does not fit");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBT * kD];  // Q, dO double-buffered
+  __shared__ __attribute__((aligned(16))) float rowstat[2][2][kBT];   // [buf][lse2 | D][row]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int kb = (int)(blockIdx.x / BH);  // low key blocks first: under the causal mask they see most queries
+  const int b = bh / a.H;
+
+  int L = a.Nk;
+  if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
+  const int k0 = kb * KB, kw0 = k0 + wave * 32;
+  const int kj = kw0 + col;  // this lane's key
+  // Query tiles that see a key of this workgroup: all, or under the causal
+  // mask those from the tile holding query k0; none if every key is padding.
+  const int tfirst = a.causal ? k0 / kBT : 0;
+  const int ntiles_q = (a.Nq + kBT - 1) / kBT;
+  const int tend = k0 < L ? ntiles_q : tfirst;
+  const bool wave_live = kw0 < L;
+  // Masking is needed for the keys past L, and under the causal mask in the
+  // query sub-blocks that reach below the wave's last key.
+  const bool pad_mask = kw0 + 32 > L;
+
+  const int64_t qhead = (int64_t)bh * a.Nq * kD, khead = (int64_t)bh * a.Nk * kD;
+  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint16_t*>(a.q) + qhead, (int64_t)a.Nq * kD * 2);
+  const __amdgpu_buffer_rsrc_t dosrc =
+      make_rsrc(static_cast<const uint16_t*>(a.dout) + qhead, (int64_t)a.Nq * kD * 2);
+  const __amdgpu_buffer_rsrc_t lsrc = make_rsrc(a.lse + (int64_t)bh * a.Nq, (int64_t)a.Nq * 4);
+  const __amdgpu_buffer_rsrc_t dsrc = make_rsrc(a.dsum + (int64_t)bh * a.Nq, (int64_t)a.Nq * 4);
+  const int64_t kvbytes = (int64_t)L * kD * 2;
+  const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(static_cast<const uint16_t*>(a.k) + khead, kvbytes);
+  const __amdgpu_buffer_rsrc_t vsrc = make_rsrc(static_cast<const uint16_t*>(a.v) + khead, kvbytes);
+
+  // This lane's key as B operands (features 16kk + 8half .. +7) of S = Q K^T
+  // and dP = dO V^T; keys at or past L read as zeros.
+  const int koff = kj < L ? kj * (kD * 2) + half * 16 : kDead;
+  u32x4_t kreg[4], vreg[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    kreg[kk] = __builtin_amdgcn_raw_buffer_load_b128(ksrc, koff + kk * 32, 0, 0);
+    vreg[kk] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, koff + kk * 32, 0, 0);
+  }
+  const float c2 = a.scale * kLog2e;
+
+  uint16_t* const qbuf0 = lds;
+  uint16_t* const obuf0 = lds + 2 * kBT * kD;
+  int goff[CH], spos[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int idx = tid + c * NT, row = idx >> 3, ch = idx & 7;
+    goff[c] = (row * kD + ch * 8) * 2;
+    spos[c] = row * kD + ((ch ^ dual_swizzle(row)) << 3);
+  }
+  // Threads 0..63 stage lse (as the exp2 offset), threads 64..127 D.
+  const int srow = tid & (kBT - 1), skind = tid >> 6;
+  u32x4_t qreg[CH], oreg[CH];
+  float sreg = 0.0f;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      qreg[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, goff[c] + t * (kBT * kD * 2), 0, 0);
+      oreg[c] = __builtin_amdgcn_raw_buffer_load_b128(dosrc, goff[c] + t * (kBT * kD * 2), 0, 0);
+    }
+    if (skind < 2)
+      sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(skind ? dsrc : lsrc,
+                                                                           (t * kBT + srow) * 4, 0, 0));
+  };
+  auto store_tile = [&](int t, int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      *reinterpret_cast<u32x4_t*>(&qbuf0[buf * kBT * kD + spos[c]]) = qreg[c];
+      *reinterpret_cast<u32x4_t*>(&obuf0[buf * kBT * kD + spos[c]]) = oreg[c];
+    }
+    if (skind == 0) rowstat[buf][0][srow] = t * kBT + srow < a.Nq ? lse_to_log2(sreg) : INFINITY;
+    if (skind == 1) rowstat[buf][1][srow] = sreg;  // 0 past Nq
+  };
+  const TrOffsets tro(lane);
+
+  f32x16_t dv[2], dk[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dv[cb][r] = 0.0f;
+      dk[cb][r] = 0.0f;
+    }
+
+  if (tfirst < tend) {
+    load_tile(tfirst);
+    store_tile(tfirst, 0);
+  }
+  __syncthreads();
+
+  for (int t = tfirst; t < tend; ++t) {
+    const int buf = (t - tfirst) & 1;
+    const uint16_t* qs = qbuf0 + buf * kBT * kD;
+    const uint16_t* os = obuf0 + buf * kBT * kD;
+    load_tile(t + 1);
+
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int i0 = t * kBT + sb * 32;
+      // Wave-uniform: skip sub-blocks entirely before the wave's first key
+      // (causal) or past Nq.
+      if (wave_live && i0 < a.Nq && (!a.causal || i0 + 32 > kw0)) {
+        const int rb = sb * 32;
+        // S and dP: register r of this lane is query i0 + 8(r/4) + 4half + r%4.
+        f32x16_t s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.0f;
+          dp[r] = 0.0f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          s = Op::mma(row_read(qs, rb + col, 2 * kk + half), kreg[kk], s);
+          dp = Op::mma(row_read(os, rb + col, 2 * kk + half), vreg[kk], dp);
+        }
+        const bool masking = pad_mask || (a.causal && i0 < kw0 + 31);
+        u32x4_t pb[2], dsb[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&rowstat[buf][0][rb + 8 * g + 4 * half]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&rowstat[buf][1][rb + 8 * g + 4 * half]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + e], c2, -lv[e]));
+            if (masking) {
+              const int i = i0 + 8 * g + 4 * half + e;
+              const bool vis = kj < L && (!a.causal || kj <= i);
+              p[e] = vis ? p[e] : 0.0f;
+            }
+            ds[e] = p[e] * (dp[4 * g + e] - dvv[e]);
+          }
+          // Registers 8t .. 8t+7 form the B operand of step t.
+          pb[g >> 1][2 * (g & 1)] = Op::pack(p[0], p[1]);
+          pb[g >> 1][2 * (g & 1) + 1] = Op::pack(p[2], p[3]);
+          dsb[g >> 1][2 * (g & 1)] = Op::pack(ds[0], ds[1]);
+          dsb[g >> 1][2 * (g & 1) + 1] = Op::pack(ds[2], ds[3]);
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            dv[cb] = Op::mma(tr_operand(os, tro, rb + 16 * st, cb), pb[st], dv[cb]);
+            dk[cb] = Op::mma(tr_operand(qs, tro, rb + 16 * st, cb), dsb[st], dk[cb]);
+          }
+      }
+    }
+
+    if (t + 1 < tend) store_tile(t + 1, buf ^ 1);
+    __syncthreads();
+  }
+
+  // dV = (dV^T)^T, dK = scale * (dK^T)^T; padded keys get zeros, rows past Nk
+  // are not written.
+  uint16_t* stage = lds + wave * 32 * kSS;
+  store_rows<Op>(dv, 1.0f, stage, static_cast<uint16_t*>(a.dv) + khead, kw0, a.Nk, lane);
+  __builtin_amdgcn_wave_barrier();
+  store_rows<Op>(dk, a.scale, stage, static_cast<uint16_t*>(a.dk) + khead, kw0, a.Nk, lane);
+}
+
+template <class Op, int NW>
+hipError_t launch_dq(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const int nqb = (a.Nq + NW * 32 - 1) / (NW * 32);
+  const int64_t blocks = (int64_t)nqb * a.B * a.H;
+  if (blocks == 0) return hipSuccess;
+  hipExtLaunchKernelGGL((bwd_dq_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0, t1, 0, a,
+                        nqb);
+  return hipGetLastError();
+}
+
+template <class Op, int NW>
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
+  const int64_t blocks = (int64_t)nkb * a.B * a.H;
+  if (blocks == 0) return hipSuccess;
+  hipExtLaunchKernelGGL((bwd_dkdv_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0, t1, 0,
+                        a, nkb);
+  return hipGetLastError();
+}
+
+template <class Op>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t const* ev) {
+  auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
+  // The dQ kernel writes D, which the dK/dV kernel reads: stream order.
+  hipError_t e = a.Nq > 64 ? launch_dq<Op, 4>(a, stream, evt(0), evt(1)) : launch_dq<Op, 2>(a, stream, evt(0), evt(1));
+  if (e != hipSuccess) return e;
+  return a.Nk > 64 ? launch_dkdv<Op, 4>(a, stream, evt(2), evt(3)) : launch_dkdv<Op, 2>(a, stream, evt(2), evt(3));
+}
+
+}  // namespace
+
+hipError_t launch_bwd_mfma(const BwdArgs& a, DType dt, hipStream_t stream, hipEvent_t const* ev) {
+  return dt == DType::BF16 ? launch_bwd<BF16>(a, stream, ev) : launch_bwd<F16>(a, stream, ev);
+}
+
+}  // namespace mha

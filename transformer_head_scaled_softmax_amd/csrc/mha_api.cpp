@@ -94,7 +94,7 @@ namespace {
 
 int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
                  int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
-                 int dtype, void* stream, hipEvent_t const* ev) {
+                 int dtype, void* stream, hipEvent_t const* ev, float* lse = nullptr, bool want_lse = false) {
   g_last_error.clear();
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
@@ -116,6 +116,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   if (!aligned(q, align) || !aligned(k, align) || !aligned(v, align) || !aligned(out, align))
     return fail(MHA_ERR_INVALID_ARG, "q, k, v, out must be %d-byte aligned", (int)align);
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
+  if (want_lse && (!lse || !aligned(lse, 4))) return fail(MHA_ERR_INVALID_ARG, "lse must be non-null and 4-byte aligned");
   const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 128 : 64);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -149,6 +150,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   a.dv = d_v;
   a.causal = mask_kind == MHA_MASK_CAUSAL;
   a.scale = scale;
+  a.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t t0 = ev ? ev[0] : nullptr, t1 = ev ? ev[1] : nullptr;
   hipError_t e = dtype == MHA_F32 ? mha::launch_attn_f32(a, s, t0, t1)
@@ -173,6 +175,13 @@ int mha_forward_timed(const void* q, const void* k, const void* v, void* out, in
                       int dtype, void* stream, void* const* events) {
   return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype,
                       stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+int mha_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq,
+                    int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                    void* stream) {
+  return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype, stream, nullptr,
+                      lse, true);
 }
 
 size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype) {
@@ -425,6 +434,97 @@ size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k,
 
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention) {
   return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of mha_backward: D_i = dout_i . out_i per row, fp32 [B, H, Nq].
+size_t backward_workspace(int B, int H, int Nq) { return round256(size_t(B) * H * Nq * sizeof(float)); }
+
+int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind,
+                  const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream, hipEvent_t const* ev) {
+  g_last_error.clear();
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
+  if (d_k < 1 || d_v < 1) return fail(MHA_ERR_INVALID_ARG, "d_k, d_v must be >= 1 (got %d, %d)", d_k, d_v);
+  int st = check_common(mask_kind, Nq, Nk, dtype, scale);
+  if (st) return st;
+  if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "the backward pass supports bf16 and f16 only");
+  if (d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim)
+    return fail(MHA_ERR_UNSUPPORTED, "the backward pass supports d_k == d_v == %d (got %d, %d)", mha::kMfmaHeadDim,
+                d_k, d_v);
+  if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return MHA_OK;  // nothing to write
+  if (Nq > 0 && (!q || !out || !dout || !lse || !dq))
+    return fail(MHA_ERR_INVALID_ARG, "q, out, dout, lse and dq must be non-null when Nq > 0");
+  if (Nk > 0 && (!k || !v || !dk || !dv))
+    return fail(MHA_ERR_INVALID_ARG, "k, v, dk and dv must be non-null when Nk > 0");
+  for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned(p, 16)) return fail(MHA_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk, dv must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(MHA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
+  // 32-bit byte offsets within one head, plus the tile read past its end.
+  if ((int64_t(std::max(Nq, Nk)) + 128) * d_k * 2 >= kMaxBufferBytes)
+    return fail(MHA_ERR_UNSUPPORTED, "sequences too long for 32-bit per-head offsets");
+  if ((int64_t(std::max(Nq, Nk)) + 63) / 64 * int64_t(H) * B > kMaxBlocks)
+    return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+  const size_t need = backward_workspace(B, H, Nq);
+  if (need > 0) {
+    if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(MHA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  mha::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = static_cast<float*>(workspace);
+  a.key_lens = key_lens;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.causal = mask_kind == MHA_MASK_CAUSAL;
+  a.scale = scale;
+  hipError_t e = mha::launch_bwd_mfma(a, static_cast<mha::DType>(dtype), static_cast<hipStream_t>(stream), ev);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mha_backward_workspace_bytes(int B, int H, int Nq, int Nk, int d_k, int d_v, int dtype) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d_k < 1 || d_v < 1) return 0;
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  return backward_workspace(B, H, Nq);
+}
+
+int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind,
+                 const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale,
+                       dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mha_backward_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k,
+                       int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* events) {
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale,
+                       dtype, workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
 }  // extern "C"

@@ -34,6 +34,31 @@ struct AttnArgs {
   // cache): query i sits at position L - Nq + i and sees keys j <= L - Nq + i.
   // 0: query i sees keys j <= i (self-attention, Nq == Nk).
   int causal_end;
+  // Optional row statistic for training: lse[(b*H + h)*Nq + i] = natural log
+  // of the softmax denominator of row i over its visible keys (-inf for a row
+  // with none).  nullptr: not written.
+  float* lse;
+};
+
+// Gradients of attention on dense per-head tensors [B, H, N, 64]: q, k, v,
+// out (the forward output), dout (dLoss/dout) and lse (the forward's row
+// statistic, [B, H, Nq]) in; dq, dk, dv out.  dsum is scratch [B, H, Nq] that
+// the dQ kernel fills with D_i = dout_i . out_i for the dK/dV kernel.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;
+  const int32_t* key_lens;  // device int32[B] or nullptr
+  int B, H, Nq, Nk;
+  int causal;
+  float scale;
 };
 
 // One decoding step against a key/value cache, head size 64: q [B, H, Nq, 64]
@@ -133,6 +158,9 @@ hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hi
                           hipEvent_t t1 = nullptr, hipEvent_t t2 = nullptr, hipEvent_t t3 = nullptr);
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
+// Backward pass (bf16/f16, head size 64): the dQ kernel (events ev[0..1]),
+// then the dK/dV kernel (ev[2..3]); ev may be nullptr.
+hipError_t launch_bwd_mfma(const BwdArgs& a, DType dt, hipStream_t stream, hipEvent_t const* ev);
 hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                               hipEvent_t t1 = nullptr, hipEvent_t t2 = nullptr, hipEvent_t t3 = nullptr);
 // Whether launch_proj_attn handles a problem: head size 64, D a multiple of

@@ -17,7 +17,7 @@ pages' generation loop ([AD] "Translation and summarization (encoder-decoder)":
 keys and values of earlier positions are cached, only the new one is computed).
 
 Recipe: ``numpy.random.Generator(PCG64(seed))``; fp32 N(0,1) draws in the order
-(x_q | q), (x_kv | k | k_cache), (v | v_cache), W_Q, W_K, W_V, W_O,
+(x_q | q), (x_kv | k | k_cache), (v | v_cache), dout, W_Q, W_K, W_V, W_O,
 (key_lens | cache_lens); rounding to bf16 is
 round-to-nearest-even; Xavier-uniform weights are U(-a, a) with
 a = sqrt(6 / (fan_in + fan_out)); key lengths are i.i.d. discrete uniform over the
@@ -55,6 +55,9 @@ class Workload:
     Hkv: int | None = None
     # The sublayer with its residual connection and layer normalisation.
     ln: bool = False
+    # Training: the backward pass for an N(0,1) output gradient (after the
+    # forward pass that leaves its row statistic).
+    backward: bool = False
 
     @property
     def D(self) -> int:
@@ -94,6 +97,12 @@ WORKLOADS = {
         Workload("long_decode_gqa", 16, 16, 1, 8192, 64, "bf16", MASK_CAUSAL, (1024, 8192), False, False, 7,
                  "one decoding step with grouped-query attention (B=16, h=16 query heads over 4 cache "
                  "heads, d=64, one new token, cache of 8192 slots filled U{1024..8192})", decode=True, Hkv=4),
+        Workload("long_causal_bwd", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 5,
+                 "backward pass of long-context causal self-attention (B=2, n=8192, h=16, d=64, "
+                 "output gradient N(0,1))", backward=True),
+        Workload("base_decoder_causal_bwd", 64, 8, 64, 64, 64, "bf16", MASK_CAUSAL, (10, 64), False, False, 3,
+                 "backward pass of Transformer-base decoder masked self-attention with key padding "
+                 "(B=64, n=64, h=8, d=64, lengths U{10..64}, output gradient N(0,1))", backward=True),
     ]
 }
 
@@ -144,6 +153,18 @@ def core_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None):
     return {"q": q, "k": k, "v": v, "key_lens": key_lens}
 
 
+def train_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None):
+    """core_inputs plus an output gradient dout [B,H,Nq,dv] ~ N(0,1), drawn after
+    v and before the key lengths."""
+    g = generator(seed)
+    q = normal(g, (B, H, Nq, dk), dtype)
+    k = normal(g, (B, H, Nk, dk), dtype)
+    v = normal(g, (B, H, Nk, dv), dtype)
+    dout = normal(g, (B, H, Nq, dv), dtype)
+    key_lens = key_lengths(g, B, *lens) if lens is not None else None
+    return {"q": q, "k": k, "v": v, "dout": dout, "key_lens": key_lens}
+
+
 def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None, ln=False):
     """x_q [B,Nq,D] (and x_kv [B,Nk,D] when ``cross``) ~ N(0,1); Xavier-uniform
     W_Q, W_K [H*dk, D], W_V [H*dv, D], W_O [D, H*dv]; key_lens from ``lens``;
@@ -182,6 +203,8 @@ def workload_inputs(w: Workload, seed: int | None = None):
         return decode_inputs(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
     if w.proj:
         return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens, w.ln)
+    if w.backward:
+        return train_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
     return core_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
 
 
