@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the multi-head attention forward path on one MI355X.
+"""Benchmark of the multi-head attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -10,6 +10,10 @@ projections, masked scaled dot-product attention per head, head concatenation an
 the output projection, via mha_proj_forward.  Inputs are seeded N(0,1) / Xavier
 draws, resident in HBM before timing; each step reads the next of several
 rotating input sets so that caches cannot hold the batch between steps.
+
+The training workloads (``--workload *_bwd``) time the backward pass instead:
+dq, dk, dv from resident q, k, v, the forward output, its row statistic and an
+N(0,1) output gradient, via mha_backward.
 
 Prints one JSON line: whole-job throughput (algorithmic TFLOP/s), tokens/s, the
 roofline of the dominant kernel (its time measured with HIP events around it on
@@ -42,12 +46,13 @@ KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip", "mfma_util.h"],
                   "qkv_attention": ["proj_attn.hip", "mfma_util.h"],
                   "out_projection": ["gemm_mfma.hip", "mfma_util.h"], "attention_f32": ["attn_f32.hip"],
                   "decode": ["decode_mfma.hip", "mfma_util.h"], "decode_combine": ["decode_mfma.hip", "mfma_util.h"],
-                  "out_projection_ln": ["gemm_mfma.hip", "mfma_util.h"], "ln_rows": ["gemm_mfma.hip", "mfma_util.h"]}
+                  "out_projection_ln": ["gemm_mfma.hip", "mfma_util.h"], "ln_rows": ["gemm_mfma.hip", "mfma_util.h"],
+                  "bwd_dq": ["bwd_mfma.hip", "mfma_util.h"], "bwd_dkdv": ["bwd_mfma.hip", "mfma_util.h"]}
 KERNEL_SYMBOLS = {"qkv_projection": "gemm_mfma_kernel", "attention": "attn_mfma_kernel",
                   "qkv_attention": "proj_attn_kernel", "out_projection": "gemm_mfma_kernel",
                   "attention_f32": "attn_f32_kernel", "decode": "decode_mfma_kernel",
                   "decode_combine": "decode_combine_kernel", "out_projection_ln": "gemm_mfma_kernel",
-                  "ln_rows": "ln_rows_kernel"}
+                  "ln_rows": "ln_rows_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel"}
 
 
 def log(*a):
@@ -104,6 +109,27 @@ def decode_work(w, lens, nsplit):
     if nsplit > 1:
         return {"decode": (f, qo + kv + lb), "decode_combine": (0.0, qo + lb)}
     return {"decode": (f, 2 * qo + kv + lb)}
+
+
+def backward_work(w, lens):
+    """(flops, bytes) per launch of the two backward kernels, and the step's
+    algorithmic FLOPs.  Per visible (query, key) pair the gradients need five
+    products of 2d FLOPs: S (recomputed; the weights are not stored), dP, dV,
+    dQ and dK -- the step's count.  The dQ kernel forms S, dP and dQ (6d), the
+    dK/dV kernel S, dP, dV and dK (8d).  Bytes: the dQ kernel reads q, dout,
+    out, lse and the visible rows of k and v and writes dq and D; the dK/dV
+    kernel reads k, v (visible rows), q, dout, lse and D and writes dk, dv."""
+    es = ES[w.dtype]
+    pairs = visible_counts(w, lens)
+    Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
+    qrow = w.B * w.H * w.Nq * w.d * es
+    krow = w.B * w.H * w.Nk * w.d * es
+    kvis = 2 * int(Ls.sum()) * w.H * w.d * es
+    stat = w.B * w.H * w.Nq * 4
+    lb = 0 if lens is None else 4 * w.B
+    dq = (6.0 * w.d * pairs, 3 * qrow + stat + kvis + qrow + stat + lb)
+    dkdv = (8.0 * w.d * pairs, kvis + 2 * qrow + 2 * stat + 2 * krow + lb)
+    return {"bwd_dq": dq, "bwd_dkdv": dkdv}, 10.0 * w.d * pairs
 
 
 def projection_flops(w):
@@ -231,6 +257,20 @@ def cpu_baseline(w, inp_sets, seconds_target):
                           cache_lens=inp["cache_lens"], nthreads=threads)
             done_flops += 4.0 * w.d * decode_visible(w, inp["cache_lens"])
             sample = "whole batches"
+        elif w.backward and w.Nq * w.Nk > 1 << 22:
+            # one (b, h) slice per thread, stacked as heads of one sequence
+            g = np.random.Generator(np.random.PCG64(100 + n))
+            picks = [(int(g.integers(w.B)), int(g.integers(w.H))) for _ in range(threads)]
+            st = {k_: np.stack([inp[k_][b, h] for b, h in picks])[None] for k_ in ("q", "k", "v", "dout")}
+            oracle.attention_backward(st["q"], st["k"], st["v"], st["dout"], mask_kind=w.mask, nthreads=threads)
+            pairs = (w.Nq * (w.Nq + 1) // 2) if w.mask == 1 else w.Nq * w.Nk
+            done_flops += 10.0 * w.d * pairs * len(picks)
+            sample = f"passes over {len(picks)} (b, h) slices"
+        elif w.backward:
+            oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], mask_kind=w.mask,
+                                      key_lens=inp["key_lens"], nthreads=threads)
+            done_flops += 10.0 * w.d * visible_counts(w, inp["key_lens"])
+            sample = "whole batches"
         elif w.Nq * w.Nk > 1 << 22:
             from transformer_head_scaled_softmax_amd import synth
             rows = synth.sample_rows(w.B, w.H, w.Nq, seed=100 + n, n_random=4)
@@ -302,6 +342,8 @@ def main():
         per_set = (w.B * w.Nq * w.D * 2 + (w.B * w.Nk * w.D if w.cross else 0)) * es
     elif w.decode:
         per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.kv_heads * w.Nk * w.d) * es
+    elif w.backward:  # q, out, dout, dq and k, v, dk, dv (+ lse)
+        per_set = (4 * w.B * w.H * w.Nq * w.d + 4 * w.B * w.H * w.Nk * w.d) * es + 4 * w.B * w.H * w.Nq
     else:
         per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.H * w.Nk * w.d) * es
     nsets = args.sets or int(min(64, max(2, math.ceil((1 << 30) / per_set))))
@@ -320,6 +362,14 @@ def main():
             d = {n_: to_dev(inp[n_]) for n_ in ("q", "k_cache", "v_cache")}
             d["key_lens"] = lens_t
             d["out"] = torch.empty((w.B, w.H, w.Nq, w.d), dtype=tdt, device=dev)
+        elif w.backward:
+            # The forward pass (with its row statistic) runs once here, untimed:
+            # a step is the backward pass over resident q, k, v, out, dout, lse.
+            d = {n_: to_dev(inp[n_]) for n_ in ("q", "k", "v", "dout")}
+            d["key_lens"] = lens_t
+            d["out"], d["lse"] = mha.forward_lse(d["q"], d["k"], d["v"], mask_kind=w.mask, key_lens=lens_t)
+            for n_ in ("q", "k", "v"):
+                d["d" + n_] = torch.empty_like(d[n_])
         else:
             d = {n_: to_dev(inp[n_]) for n_ in ("q", "k", "v")}
             d["key_lens"] = lens_t
@@ -387,6 +437,20 @@ def main():
         stage_events = {"decode": (0, 1)}
         if nsplit > 1:
             stage_events["decode_combine"] = (2, 3)
+        n_events = 4
+    elif w.backward:
+        need = lib.mha_backward_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, w.d, code)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def step(i, sp, events=None):
+            d = dev_sets[i % nsets]
+            lp = None if d["key_lens"] is None else d["key_lens"].data_ptr()
+            argsv = tuple(d[n_].data_ptr() for n_ in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv")) + (
+                w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.mask, lp, scale, code, ws.data_ptr(), need, sp)
+            st = lib.mha_backward(*argsv) if events is None else lib.mha_backward_timed(*argsv, events)
+            if st != 0:
+                raise RuntimeError(lib.mha_last_error().decode())
+        stage_events = {"bwd_dq": (0, 1), "bwd_dkdv": (2, 3)}
         n_events = 4
     else:
         def step(i, sp, events=None):
@@ -473,6 +537,13 @@ def main():
         works = [decode_work(w, L, nsplit) for L in used]
         flops = float(np.mean([sum(f for f, _ in wk.values()) for wk in works]))
         bytes_ = float(np.mean([decode_work(w, L, 1)["decode"][1] for L in used]))  # whole step
+    elif w.backward:
+        works = [backward_work(w, L) for L in used]
+        flops = float(np.mean([f for _, f in works]))
+        # whole step: q, k, v (visible rows), out, dout, lse in; dq, dk, dv out
+        Lm = [np.full(w.B, w.Nk) if L is None else np.clip(L, 0, w.Nk) for L in used]
+        bytes_ = float(np.mean([(4 * w.B * w.H * w.Nq * w.d + 2 * int(L.sum()) * w.H * w.d
+                                 + 2 * w.B * w.H * w.Nk * w.d) * es + 4 * w.B * w.H * w.Nq for L in Lm]))
     else:
         flops = att_f
         bytes_ = float(np.mean([attention_bytes(w, L) for L in used]))
@@ -489,7 +560,9 @@ def main():
                    "input_sets": nsets, "issue": "HIP graph replay",
                    **({"residual_layer_norm": True} if w.ln else {}),
                    **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "waves": nsplit}
-                      if w.decode else {})},
+                      if w.decode else {}),
+                   **({"pass": "backward (dq, dk, dv from q, k, v, out, dout, lse)",
+                       "flops_per_visible_pair": 10 * w.d} if w.backward else {})},
         "tokens_per_s": round(w.B * w.Nq / sec, 1),
         "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 5),
         "hbm_gbps_algorithmic": round(bytes_ / sec / 1e9, 1),
@@ -509,6 +582,9 @@ def main():
     elif w.decode:
         f_ = float(np.mean([wk[dom][0] for wk in works]))
         b_ = float(np.mean([wk[dom][1] for wk in works]))
+    elif w.backward:
+        f_ = float(np.mean([wk[dom][0] for wk, _ in works]))
+        b_ = float(np.mean([wk[dom][1] for wk, _ in works]))
     else:
         f_, b_ = flops, bytes_
     result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom, w.name)
