@@ -31,6 +31,8 @@
 // MFMA 32x32x16 lane layout (checked on the device): A[m][k] comes from lane
 // m + 32*(k/8), element k%8; B[k][n] from lane n + 32*(k/8), element k%8;
 // C[m][n] lands in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
+#include <type_traits>
+
 #include "mfma_util.h"
 
 namespace mha {
@@ -40,7 +42,6 @@ constexpr int kD = kMfmaHeadDim;  // 64
 constexpr int kBT = 64;           // rows per streamed LDS tile
 constexpr int kSS = 72;           // row stride (elements) of the epilogue staging
 constexpr int kDead = (int)0x80000000u;  // beyond any range check: loads return zeros
-constexpr float kLn2 = 0.6931471805599453f;
 
 // Tiles in LDS are dense 128-byte rows whose 16-byte chunks are permuted per
 // row: chunk c of row r sits in slot c ^ dual_swizzle(r).  The permutation
@@ -229,16 +230,21 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a, int nqb) 
     const uint16_t* vs = vbuf0 + buf * kBT * kD;
     load_tile(t + 1);
 
-    if (j0 < kmax_wave) {  // wave-uniform
-      // S^T and dP^T, two 32-key blocks: register (jb, r) of this lane is key
-      // j0 + 32jb + 8(r/4) + 4half + r%4 of query qi.
+    // One tile.  MASK: some key of the tile is invisible to some query of the
+    // wave (diagonal or padded tail); the other tiles take the branch without
+    // the per-element selects.
+    auto tile = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // S^T and dP^T - D, two 32-key blocks: register (jb, r) of this lane is
+      // key j0 + 32jb + 8(r/4) + 4half + r%4 of query qi.  The dP^T
+      // accumulators start at -D, so they end as dP - D.
       f32x16_t s[2], dp[2];
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s[jb][r] = 0.0f;
-          dp[jb][r] = 0.0f;
+          dp[jb][r] = -Dq;
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -246,34 +252,32 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a, int nqb) 
           dp[jb] = Op::mma(row_read(vs, jb * 32 + col, 2 * kk + half), doreg[kk], dp[jb]);
         }
       }
-      // K^T operands of dQ^T += K^T dS^T: step t4 covers keys 16t4 .. +15.
-      u32x4_t kt[4][2];
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) kt[t4][cb] = tr_operand(ks, tro, 16 * t4, cb);
-
-      const bool masking = j0 + kBT > kmin_wave;
       const int lim = kend - j0 - 4 * half;
-      u32x4_t dsb[4];
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < 4; ++t4) {
+        u32x4_t dsb;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int jb = t4 >> 1, r = (t4 & 1) * 8 + 2 * w;
           float p0 = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -lse2));
           float p1 = __builtin_amdgcn_exp2f(fmaf(s[jb][r + 1], c2, -lse2));
-          if (masking) {
+          if (MASK) {
             const int kr = jb * 32 + (r >> 2) * 8 + (r & 3);
             p0 = kr >= lim ? 0.0f : p0;
             p1 = kr + 1 >= lim ? 0.0f : p1;
           }
-          dsb[t4][w] = Op::pack(p0 * (dp[jb][r] - Dq), p1 * (dp[jb][r + 1] - Dq));
+          dsb[w] = Op::pack(p0 * dp[jb][r], p1 * dp[jb][r + 1]);
         }
+        // dQ^T += K^T dS^T for keys 16t4 .. +15, K^T read transposed.
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) dq[cb] = Op::mma(kt[t4][cb], dsb[t4], dq[cb]);
+        for (int cb = 0; cb < 2; ++cb) dq[cb] = Op::mma(tr_operand(ks, tro, 16 * t4, cb), dsb, dq[cb]);
+      }
+    };
+    if (j0 < kmax_wave) {  // wave-uniform
+      if (j0 + kBT > kmin_wave)
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
     }
 
     if (t + 1 < ntiles) store_tile(buf ^ 1);
@@ -318,9 +322,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb
   const int ntiles_q = (a.Nq + kBT - 1) / kBT;
   const int tend = k0 < L ? ntiles_q : tfirst;
   const bool wave_live = kw0 < L;
-  // Masking is needed for the keys past L, and under the causal mask in the
-  // query sub-blocks that reach below the wave's last key.
-  const bool pad_mask = kw0 + 32 > L;
+  const bool pad_mask = kw0 + 32 > L;  // some key of this wave is padding
 
   const int64_t qhead = (int64_t)bh * a.Nq * kD, khead = (int64_t)bh * a.Nk * kD;
   const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint16_t*>(a.q) + qhead, (int64_t)a.Nq * kD * 2);
@@ -352,8 +354,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb
     goff[c] = (row * kD + ch * 8) * 2;
     spos[c] = row * kD + ((ch ^ dual_swizzle(row)) << 3);
   }
-  // Threads 0..63 stage lse (as the exp2 offset), threads 64..127 D.
-  const int srow = tid & (kBT - 1), skind = tid >> 6;
+  // Wave 0 stages lse (as the exp2 offset), wave 1 D (wave-uniform, so the
+  // buffer resource stays scalar).
+  const int srow = tid & (kBT - 1), skind = __builtin_amdgcn_readfirstlane(wave);
   u32x4_t qreg[CH], oreg[CH];
   float sreg = 0.0f;
   auto load_tile = [&](int t) {
@@ -398,49 +401,56 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb
     const uint16_t* os = obuf0 + buf * kBT * kD;
     load_tile(t + 1);
 
+    // One tile of 64 queries as two 32-query sub-blocks.  MASK: some pair of
+    // the tile is invisible (padded keys of this wave, or queries before its
+    // last key under the causal mask); other tiles skip the per-element selects.
+    auto tile = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int i0 = t * kBT + sb * 32;
-      // Wave-uniform: skip sub-blocks entirely before the wave's first key
-      // (causal) or past Nq.
-      if (wave_live && i0 < a.Nq && (!a.causal || i0 + 32 > kw0)) {
-        const int rb = sb * 32;
-        // S and dP: register r of this lane is query i0 + 8(r/4) + 4half + r%4.
+      for (int sb = 0; sb < 2; ++sb) {
+        const int i0 = t * kBT + sb * 32, rb = sb * 32;
+        // Register r of this lane is query i0 + 8(r/4) + 4half + r%4: its exp2
+        // offset, and -D as the start of the dP accumulator (which then ends
+        // as dP - D).
         f32x16_t s, dp;
+        float lv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.0f;
-          dp[r] = 0.0f;
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&rowstat[buf][0][rb + 8 * g + 4 * half]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&rowstat[buf][1][rb + 8 * g + 4 * half]);
+          lv[4 * g + 0] = l4.x;
+          lv[4 * g + 1] = l4.y;
+          lv[4 * g + 2] = l4.z;
+          lv[4 * g + 3] = l4.w;
+          dp[4 * g + 0] = -d4.x;
+          dp[4 * g + 1] = -d4.y;
+          dp[4 * g + 2] = -d4.z;
+          dp[4 * g + 3] = -d4.w;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+        // S = Q K^T and dP = dO V^T (queries x keys).
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           s = Op::mma(row_read(qs, rb + col, 2 * kk + half), kreg[kk], s);
           dp = Op::mma(row_read(os, rb + col, 2 * kk + half), vreg[kk], dp);
         }
-        const bool masking = pad_mask || (a.causal && i0 < kw0 + 31);
         u32x4_t pb[2], dsb[2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 l4 = *reinterpret_cast<const float4*>(&rowstat[buf][0][rb + 8 * g + 4 * half]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&rowstat[buf][1][rb + 8 * g + 4 * half]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-          float p[4], ds[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + e], c2, -lv[e]));
-            if (masking) {
-              const int i = i0 + 8 * g + 4 * half + e;
-              const bool vis = kj < L && (!a.causal || kj <= i);
-              p[e] = vis ? p[e] : 0.0f;
-            }
-            ds[e] = p[e] * (dp[4 * g + e] - dvv[e]);
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lv[r]));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c2, -lv[r + 1]));
+          if (MASK) {
+            const int i = i0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            p0 = (kj < L && (!a.causal || kj <= i)) ? p0 : 0.0f;
+            p1 = (kj < L && (!a.causal || kj <= i + 1)) ? p1 : 0.0f;
           }
-          // Registers 8t .. 8t+7 form the B operand of step t.
-          pb[g >> 1][2 * (g & 1)] = Op::pack(p[0], p[1]);
-          pb[g >> 1][2 * (g & 1) + 1] = Op::pack(p[2], p[3]);
-          dsb[g >> 1][2 * (g & 1)] = Op::pack(ds[0], ds[1]);
-          dsb[g >> 1][2 * (g & 1) + 1] = Op::pack(ds[2], ds[3]);
+          // Registers 8st .. 8st+7 form the B operand of step st.
+          pb[r >> 3][(r & 7) >> 1] = Op::pack(p0, p1);
+          dsb[r >> 3][(r & 7) >> 1] = Op::pack(p0 * dp[r], p1 * dp[r + 1]);
         }
+        // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read
+        // from the same tiles.
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -449,6 +459,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb
             dk[cb] = Op::mma(tr_operand(qs, tro, rb + 16 * st, cb), dsb[st], dk[cb]);
           }
       }
+    };
+    // Wave-uniform: skip tiles entirely before the wave's first key (causal).
+    const int t0q = t * kBT;
+    if (wave_live && (!a.causal || t0q + kBT > kw0)) {
+      if (pad_mask || (a.causal && t0q < kw0 + 31))
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
     }
 
     if (t + 1 < tend) store_tile(t + 1, buf ^ 1);
