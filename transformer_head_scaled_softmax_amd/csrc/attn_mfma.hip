@@ -186,6 +186,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
     if (j0 < kmax_wave) {  // wave-uniform: tiles past all of this wave's rows are skipped
       // S^T = K_tile Q^T: two 32-key blocks; each K operand read serves every
       // query sub-block of the wave.
+      // All eight K operands are read before the first product, so the
+      // products do not wait on LDS one pair at a time.
+      u32x4_t kop[2][4];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          kop[jb][kk] = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kKS + kk * 16 + half * 8]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the eight reads ahead of the products
       f32x16_t s[QS][2];
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
@@ -194,11 +203,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[u][jb][r] = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kKS + kk * 16 + half * 8]);
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int u = 0; u < QS; ++u) s[u][jb] = Op::mma(av, qreg[u][kk], s[u][jb]);
-        }
+          for (int u = 0; u < QS; ++u) s[u][jb] = Op::mma(kop[jb][kk], qreg[u][kk], s[u][jb]);
       }
 
       // V^T operands of O^T += V^T P^T for the whole tile, read once and used
