@@ -247,7 +247,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
         // s[t4/2]); the row sum comes from the packed values with v_dot2.
         float ls = 0.0f;
         auto exponentiate = [&](float mu, bool select_masked) {
-          ls = 0.0f;
+          // Four partial sums (one per register pair of a step) keep the
+          // v_dot2 accumulation chains short.
+          float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
@@ -260,8 +262,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(AttnArgs a, int n
                 p1 = s[u][jb][r + 1] == -INFINITY ? 0.0f : p1;
               }
               pb[t4][w] = Op::pack(p0, p1);
-              ls = Op::sum2(pb[t4][w], ls);
+              lp[w] = Op::sum2(pb[t4][w], lp[w]);
             }
+          ls = (lp[0] + lp[1]) + (lp[2] + lp[3]);
         };
         // Optimistic pass against the current reference.  It is kept unless
         // this query's partial sum is not finite or exceeds kGuard (first tile,

@@ -313,8 +313,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   // P = exp2(s * c2 - mc) for visible keys, 0 for the rest, packed in the
   // order of the P^T operand: 16-key step t4 takes registers 8(t4%2) .. +7 of
   // s[t4/2], i.e. keys 16t4 + 4half + {0..3} and 16t4 + 8 + 4half + {0..3}.
+  // The row sum is kept as four partial sums (one per register pair of a
+  // step), combined as (0 + 1) + (2 + 3) -- the order of the per-head
+  // attention kernel, so the two agree bit for bit on one 64-key tile.
   u32x4_t pb[2 * KB];
-  float ls = 0.0f;
+  float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int t4 = 0; t4 < 2 * KB; ++t4)
 #pragma unroll
@@ -324,9 +327,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
       const float p0 = key < kend ? __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -mc)) : 0.0f;
       const float p1 = key + 1 < kend ? __builtin_amdgcn_exp2f(fmaf(s[jb][r + 1], c2, -mc)) : 0.0f;
       pb[t4][w4] = Op::pack(p0, p1);
-      ls = Op::sum2(pb[t4][w4], ls);
+      lp[w4] = Op::sum2(pb[t4][w4], lp[w4]);
     }
-  const float ltot = lanes_sum(ls);
+  const float ltot = lanes_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
 
   // O^T += V^T P^T.  ds_read_b64_tr_b16: in each group of 16 lanes, lane
   // 4k + q points at key row (k0 + k), features c0 + 4q .. +3, and lane l'
