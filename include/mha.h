@@ -201,10 +201,11 @@ int mha_forward_lse(const void* q, const void* k, const void* v, void* out, floa
  *   dv   [B, H, Nk, d_v]   written (zero rows for padded keys)
  *
  * The weights P are recomputed from q, k and lse tile by tile; no Nq x Nk
- * matrix is stored.  Supported: MHA_BF16 and MHA_F16 with d_k == d_v == 64
- * (MHA_F32 returns MHA_ERR_UNSUPPORTED); tensors 16-byte aligned, lse 4-byte
- * aligned; outputs must not overlap inputs or each other; Nq and Nk below
- * 2^24.  Pointers of a side with zero rows may be NULL.  `workspace`: device
+ * matrix is stored.  Supported types and head sizes as for mha_forward
+ * (MHA_F32 with d_k, d_v <= 128; MHA_BF16 and MHA_F16 with d_k == d_v == 64);
+ * bf16/f16 tensors 16-byte aligned, fp32 tensors and lse 4-byte aligned;
+ * outputs must not overlap inputs or each other; bf16/f16 sequences below
+ * 2^24 rows.  Pointers of a side with zero rows may be NULL.  `workspace`: device
  * memory of at least mha_backward_workspace_bytes(...) bytes, 256-byte
  * aligned, owned by the caller, contents scratch (it holds D); calls sharing a
  * workspace must not run concurrently.  Two kernels run in stream order (dq,

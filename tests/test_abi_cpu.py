@@ -385,7 +385,8 @@ def bwd(lib, q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, Nq
     (dict(mask=1), mb.ERR_INVALID_ARG),              # causal needs Nq == Nk
     (dict(dtype=7), mb.ERR_INVALID_ARG),
     (dict(scale=float("nan")), mb.ERR_INVALID_ARG),
-    (dict(dtype=mb.F32), mb.ERR_UNSUPPORTED),
+    (dict(dtype=mb.F32, d_k=129), mb.ERR_UNSUPPORTED),
+    (dict(dtype=mb.F32, q=P + 2), mb.ERR_INVALID_ARG),
     (dict(d_k=128, d_v=128), mb.ERR_UNSUPPORTED),
     (dict(d_v=32), mb.ERR_UNSUPPORTED),
     (dict(q=None), mb.ERR_INVALID_ARG),

@@ -12,14 +12,15 @@ Tolerances (derivation in gpu_util):
   lse: |lse - ref| <= 4e-3 (bf16), 1e-3 (f16), 1e-5 * max(1, |ref|) (fp32);
        -inf exactly for a row with no visible key.
   gradients (bf16/f16): |g - ref| <= 2e-2 + 2u * A element by element, A the
-       sum of the magnitudes of the terms that make up each gradient element.
+       sum of the magnitudes of the terms that make up each gradient element;
+       (fp32): max |g - ref| / max |ref| <= 1e-5.
   masking: gradients of padded keys are exactly zero.
 """
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close_grad, grad_bounds, lens_dev, to_dev, to_host
+from gpu_util import assert_close, assert_close_grad, grad_bounds, lens_dev, to_dev, to_host
 from transformer_head_scaled_softmax_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +73,8 @@ def compare_grads(got, inp, dtype, kw, what):
     """Gradients against the oracle at the suite's gradient tolerance; returns the
     error-to-bound ratios."""
     ref = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["dout"], **kw)
+    if dtype == "f32":  # relative to the output scale, as for the forward pass
+        return {n: assert_close(got[n], r, "f32", f"{n} {what}") for n, r in zip(("dq", "dk", "dv"), ref)}
     out, P = oracle.attention(inp["q"], inp["k"], inp["v"], return_weights=True, **kw)
     scale = kw.get("scale")
     scale = 1.0 / np.sqrt(inp["q"].shape[-1]) if scale is None else scale
@@ -80,8 +83,8 @@ def compare_grads(got, inp, dtype, kw, what):
             for n, r, a in zip(("dq", "dk", "dv"), ref, A)}
 
 
-def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override=None):
-    inp = synth.train_inputs(B, H, Nq, Nk, 64, 64, dtype, seed, lens)
+def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override=None, dk=64, dv=64):
+    inp = synth.train_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens)
     if lens_override is not None:
         inp["key_lens"] = np.asarray(lens_override, np.int32)
     what = f"B{B} H{H} Nq{Nq} Nk{Nk} {dtype} mask{mask} lens{inp['key_lens']} scale{scale}"
@@ -148,6 +151,17 @@ def test_forward_lse_rows_without_keys_are_minus_inf():
 ])
 def test_backward_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
     check_train(B, H, Nq, Nk, dtype, mask, lens, seed=13)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,mask,lens,dk,dv", [
+    (1, 8, 16, 16, NONE, None, 64, 64),       # the tiny encoder workload's shape
+    (2, 2, 150, 150, CAUSAL, (20, 150), 64, 64),
+    (3, 2, 37, 101, NONE, (1, 101), 32, 80),  # unequal head sizes
+    (1, 2, 70, 70, CAUSAL, None, 128, 128),   # the largest fp32 head size
+    (2, 1, 5, 3, NONE, (0, 3), 7, 5),         # odd sizes, an empty sequence
+])
+def test_backward_f32_matches_oracle(B, H, Nq, Nk, mask, lens, dk, dv):
+    check_train(B, H, Nq, Nk, "f32", mask, lens, seed=18, dk=dk, dv=dv)
 
 
 @pytest.mark.parametrize("scale", [0.125, 1.0, -0.3, 0.0])

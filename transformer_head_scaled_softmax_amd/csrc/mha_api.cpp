@@ -453,23 +453,28 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   if (d_k < 1 || d_v < 1) return fail(MHA_ERR_INVALID_ARG, "d_k, d_v must be >= 1 (got %d, %d)", d_k, d_v);
   int st = check_common(mask_kind, Nq, Nk, dtype, scale);
   if (st) return st;
-  if (dtype == MHA_F32) return fail(MHA_ERR_UNSUPPORTED, "the backward pass supports bf16 and f16 only");
-  if (d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim)
-    return fail(MHA_ERR_UNSUPPORTED, "the backward pass supports d_k == d_v == %d (got %d, %d)", mha::kMfmaHeadDim,
-                d_k, d_v);
+  if (dtype == MHA_F32) {
+    if (d_k > mha::kF32MaxHeadDim || d_v > mha::kF32MaxHeadDim)
+      return fail(MHA_ERR_UNSUPPORTED, "fp32 supports d_k, d_v <= %d (got %d, %d)", mha::kF32MaxHeadDim, d_k, d_v);
+  } else if (d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim) {
+    return fail(MHA_ERR_UNSUPPORTED, "bf16/f16 support d_k == d_v == %d (got %d, %d)", mha::kMfmaHeadDim, d_k, d_v);
+  }
   if (B == 0 || H == 0 || (Nq == 0 && Nk == 0)) return MHA_OK;  // nothing to write
   if (Nq > 0 && (!q || !out || !dout || !lse || !dq))
     return fail(MHA_ERR_INVALID_ARG, "q, out, dout, lse and dq must be non-null when Nq > 0");
   if (Nk > 0 && (!k || !v || !dk || !dv))
     return fail(MHA_ERR_INVALID_ARG, "k, v, dk and dv must be non-null when Nk > 0");
+  const uintptr_t align = dtype == MHA_F32 ? 4 : 16;
   for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
-    if (!aligned(p, 16)) return fail(MHA_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk, dv must be 16-byte aligned");
+    if (!aligned(p, align))
+      return fail(MHA_ERR_INVALID_ARG, "q, k, v, out, dout, dq, dk, dv must be %d-byte aligned", (int)align);
   if (!aligned(lse, 4)) return fail(MHA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   // 32-bit byte offsets within one head, plus the tile read past its end.
-  if ((int64_t(std::max(Nq, Nk)) + 128) * d_k * 2 >= kMaxBufferBytes)
+  if (dtype != MHA_F32 && (int64_t(std::max(Nq, Nk)) + 128) * d_k * 2 >= kMaxBufferBytes)
     return fail(MHA_ERR_UNSUPPORTED, "sequences too long for 32-bit per-head offsets");
-  if ((int64_t(std::max(Nq, Nk)) + 63) / 64 * int64_t(H) * B > kMaxBlocks)
+  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : 64;
+  if ((int64_t(std::max(Nq, Nk)) + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
   const size_t need = backward_workspace(B, H, Nq);
   if (need > 0) {
@@ -496,7 +501,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.Nk = Nk;
   a.causal = mask_kind == MHA_MASK_CAUSAL;
   a.scale = scale;
-  hipError_t e = mha::launch_bwd_mfma(a, static_cast<mha::DType>(dtype), static_cast<hipStream_t>(stream), ev);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == MHA_F32 ? mha::launch_bwd_f32(a, d_k, d_v, s, ev)
+                                  : mha::launch_bwd_mfma(a, static_cast<mha::DType>(dtype), s, ev);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return MHA_OK;
 }

@@ -40,7 +40,7 @@ struct AttnArgs {
   float* lse;
 };
 
-// Gradients of attention on dense per-head tensors [B, H, N, 64]: q, k, v,
+// Gradients of attention on dense per-head tensors [B, H, N, d]: q, k, v,
 // out (the forward output), dout (dLoss/dout) and lse (the forward's row
 // statistic, [B, H, Nq]) in; dq, dk, dv out.  dsum is scratch [B, H, Nq] that
 // the dQ kernel fills with D_i = dout_i . out_i for the dK/dV kernel.
@@ -161,6 +161,8 @@ hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream,
 // Backward pass (bf16/f16, head size 64): the dQ kernel (events ev[0..1]),
 // then the dK/dV kernel (ev[2..3]); ev may be nullptr.
 hipError_t launch_bwd_mfma(const BwdArgs& a, DType dt, hipStream_t stream, hipEvent_t const* ev);
+// The same for fp32 with head sizes dk, dv <= kF32MaxHeadDim (vector ALUs).
+hipError_t launch_bwd_f32(const BwdArgs& a, int dk, int dv, hipStream_t stream, hipEvent_t const* ev);
 hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                               hipEvent_t t1 = nullptr, hipEvent_t t2 = nullptr, hipEvent_t t3 = nullptr);
 // Whether launch_proj_attn handles a problem: head size 64, D a multiple of
