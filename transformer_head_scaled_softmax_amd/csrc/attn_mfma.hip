@@ -361,8 +361,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hip
   // staged K/V tile among 128 queries.
   const bool longq = a.Nq > 64;
   if (dt == DType::BF16)
-    return longq ? launch<BF16, 4, 2>(a, stream, t0, t1) : launch<BF16, 2, 1>(a, stream, t0, t1);
-  return longq ? launch<F16, 4, 2>(a, stream, t0, t1) : launch<F16, 2, 1>(a, stream, t0, t1);
+    return longq ? launch<BF16, 4, 2>(a, stream, t0, t1) : launch<BF16, 1, 1>(a, stream, t0, t1);
+  return longq ? launch<F16, 4, 2>(a, stream, t0, t1) : launch<F16, 1, 1>(a, stream, t0, t1);
 }
 
 }  // namespace mha
