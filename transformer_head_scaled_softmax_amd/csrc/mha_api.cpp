@@ -117,7 +117,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
     return fail(MHA_ERR_INVALID_ARG, "q, k, v, out must be %d-byte aligned", (int)align);
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   if (want_lse && (!lse || !aligned(lse, 4))) return fail(MHA_ERR_INVALID_ARG, "lse must be non-null and 4-byte aligned");
-  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 128 : 64);
+  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 512 : 32);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
   // The matrix-core kernel addresses one (b, h) slice with 32-bit byte offsets.
@@ -634,7 +634,7 @@ int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache,
     return MHA_OK;
   }
 
-  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 128 : 64);
+  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 512 : 32);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
   mha::AttnArgs a{};
