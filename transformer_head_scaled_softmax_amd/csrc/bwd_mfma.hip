@@ -93,6 +93,11 @@ __device__ inline u32x4_t tr_operand(const uint16_t* tile, const TrOffsets& o, i
   return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Tile memory of a workgroup of NW waves: two 64-row tiles of each streamed
+// operand, or the epilogue's staging rows if that is more.
+template <int NW>
+constexpr int kLdsElems = 4 * kBT * kD > NW * 32 * kSS ? 4 * kBT * kD : NW * 32 * kSS;
+
 // lse in natural-log units -> the exp2 argument offset; a row with no
 // visible key (lse = -inf) gets +inf so every weight of it is 0.
 __device__ inline float lse_to_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
@@ -128,13 +133,13 @@ __device__ inline void store_rows(const f32x16_t (&acc)[2], float mul, uint16_t*
 // queries, so each lane holds one query's scores), P^T and dS^T, then
 // dQ^T += K^T dS^T with K^T read transposed from the same LDS tile.
 template <class Op, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a, int nqb) {
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArgs a, int nqb) {
   constexpr int NT = NW * 64;
   constexpr int QB = NW * 32;
   constexpr int CH = (kBT * 8) / NT;  // 16-byte chunks of K (and of V) per thread per tile
   static_assert(CH >= 1, "tile too small for the workgroup");
-  static_assert(NW * 32 * kSS <= 4 * kBT * kD, "staging does not fit");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBT * kD];  // K, V double-buffered
+  // K, V double-buffered; afterwards the epilogue staging (32 x kSS per wave).
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems<NW>];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
@@ -296,13 +301,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdArgs a, int nqb) 
 // lane holds one key's column), P and dS, then dV^T += dO^T P and
 // dK^T += Q^T dS with dO^T and Q^T read transposed from the same tiles.
 template <class Op, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
   constexpr int NT = NW * 64;
   constexpr int KB = NW * 32;
   constexpr int CH = (kBT * 8) / NT;  // 16-byte chunks of Q (and of dO) per thread per tile
   static_assert(CH >= 1 && NT >= 2 * kBT, "tile too small for the workgroup");
-  static_assert(NW * 32 * kSS <= 4 * kBT * kD, "staging does not fit");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kBT * kD];  // Q, dO double-buffered
+  // Q, dO double-buffered; afterwards the epilogue staging (32 x kSS per wave).
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems<NW>];
   __shared__ __attribute__((aligned(16))) float rowstat[2][2][kBT];   // [buf][lse2 | D][row]
 
   const int tid = threadIdx.x;
@@ -505,7 +510,10 @@ template <class Op>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t const* ev) {
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
   // The dQ kernel writes D, which the dK/dV kernel reads: stream order.
-  hipError_t e = a.Nq > 64 ? launch_dq<Op, 4>(a, stream, evt(0), evt(1)) : launch_dq<Op, 2>(a, stream, evt(0), evt(1));
+  // Long sequences: eight waves per dQ workgroup (256 queries share each K/V
+  // tile; 397 vs 407 us at n = 8192), four per dK/dV workgroup (eight were 1%
+  // slower there).
+  hipError_t e = a.Nq > 64 ? launch_dq<Op, 8>(a, stream, evt(0), evt(1)) : launch_dq<Op, 2>(a, stream, evt(0), evt(1));
   if (e != hipSuccess) return e;
   return a.Nk > 64 ? launch_dkdv<Op, 4>(a, stream, evt(2), evt(3)) : launch_dkdv<Op, 2>(a, stream, evt(2), evt(3));
 }
