@@ -190,21 +190,28 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
     for (int m = 0; m < TL::MPT; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[jt][m][r] = 0.0f;
+  // One 64-deep step of every live task of this wave: all operands of the
+  // task's step are read from LDS first, then its products run, so the
+  // products do not wait on the reads one by one.
   auto compute = [&](int buf) {
     const uint16_t* st = lds + buf * TL::STAGE;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int slot = (kk * 2 + half) ^ swz;
+    for (int jt = 0; jt < TL::TPW; ++jt) {
+      if (!tlive[jt]) continue;  // wave-uniform
+      u32x4_t bx[kBK / 16], aw[kBK / 16][TL::MPT];
 #pragma unroll
-      for (int jt = 0; jt < TL::TPW; ++jt) {
-        if (!tlive[jt]) continue;  // wave-uniform
-        const u32x4_t bx = *reinterpret_cast<const u32x4_t*>(&st[(32 * xrow[jt] + col) * kBK + slot * 8]);
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int slot = (kk * 2 + half) ^ swz;
+        bx[kk] = *reinterpret_cast<const u32x4_t*>(&st[(32 * xrow[jt] + col) * kBK + slot * 8]);
 #pragma unroll
-        for (int m = 0; m < TL::MPT; ++m) {
-          const u32x4_t aw = *reinterpret_cast<const u32x4_t*>(&st[(wrow[jt][m] + col) * kBK + slot * 8]);
-          acc[jt][m] = Op::mma(aw, bx, acc[jt][m]);
-        }
+        for (int m = 0; m < TL::MPT; ++m)
+          aw[kk][m] = *reinterpret_cast<const u32x4_t*>(&st[(wrow[jt][m] + col) * kBK + slot * 8]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk)
+#pragma unroll
+        for (int m = 0; m < TL::MPT; ++m) acc[jt][m] = Op::mma(aw[kk][m], bx[kk], acc[jt][m]);
     }
   };
 
