@@ -68,7 +68,7 @@ extern "C" {
 /* status codes */
 #define MHA_OK 0
 #define MHA_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad enum, ... */
-#define MHA_ERR_UNSUPPORTED (-2) /* valid request this build has no kernel for */
+#define MHA_ERR_UNSUPPORTED (-2) /* valid request the library has no kernel for */
 #define MHA_ERR_WORKSPACE (-3)   /* workspace missing, too small or misaligned */
 #define MHA_ERR_HIP (-4)         /* the HIP runtime refused a launch */
 
