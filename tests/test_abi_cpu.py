@@ -78,6 +78,7 @@ def fwd(lib, q=P, k=P, v=P, out=P, B=2, H=3, Nq=5, Nk=5, dk=64, dv=64, mask=0, l
     (dict(q=P + 8), mb.ERR_INVALID_ARG),
     (dict(out=P + 2), mb.ERR_INVALID_ARG),
     (dict(dtype=mb.F32, q=P + 2), mb.ERR_INVALID_ARG),
+    (dict(Nq=64, Nk=(1 << 24) - 128), mb.ERR_UNSUPPORTED),   # one key past the 32-bit offset limit
     (dict(lens=P + 2), mb.ERR_INVALID_ARG),
 ])
 def test_forward_rejects(lib, kw, status):

@@ -408,3 +408,17 @@ def test_graph_replays_match_eager():
         assert torch.equal(out_p, want_p)
         assert torch.equal(out_c, want_c)
         del run_eager_noise
+
+
+def test_longest_key_sequence_at_the_offset_limit():
+    """The most keys one head may have (the kernels address one head with 32-bit
+    byte offsets, including the tile read past its end: (Nk + 128) * 128 bytes
+    < 2^31).  Cross-attention of 64 queries over 16,777,087 keys, a padded tail;
+    sampled rows against the oracle."""
+    Nk = (1 << 24) - 128 - 1
+    lens = np.array([Nk - 5], np.int32)
+    inp = synth.core_inputs(1, 1, 64, Nk, 64, 64, "bf16", seed=21)
+    got = run_core(inp, "bf16", NONE, lens_override=lens)
+    rows = np.array([(0, 0, 0), (0, 0, 31), (0, 0, 32), (0, 0, 63)], np.int32)
+    ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, mask_kind=NONE, key_lens=lens)
+    assert_close(got[0, 0, rows[:, 2]], ref, "bf16", "Nk at the offset limit")
