@@ -160,6 +160,28 @@ int mha_proj_forward_timed(const void* x_q, const void* x_kv, const void* W_Q, c
                            void* stream, void* const* events, int plan);
 
 /*
+ * mha_forward_strided -- mha_forward on strided views, so that layouts such as
+ * the [B, N, H, d] of a projection's output ([TP] "Multi-Head Attention": head
+ * h is a block of d columns of the projected rows) need no copy.  Element
+ * (b, h, n, c) of q lives at q + b*q_strides[0] + h*q_strides[1] +
+ * n*q_strides[2] + c (strides in elements, host arrays of 3, c contiguous);
+ * likewise k and v (n over keys) and out.  lse: NULL, or as for
+ * mha_forward_lse (dense [B, H, Nq] fp32).
+ *
+ * Strides must be >= 0 (zero strides broadcast an input); bf16/f16 strides
+ * must be multiples of 8 elements and the tensors 16-byte aligned (fp32:
+ * 4-byte aligned).  Output rows must not overlap (out strides of a dimension
+ * with more than one entry at least d_v) and out must not overlap the inputs.
+ * bf16/f16 rows of one head, with their stride, must span less than 2^31
+ * bytes (including 128 rows past the end).  Otherwise as mha_forward; with
+ * dense strides it is mha_forward (or mha_forward_lse).
+ */
+int mha_forward_strided(const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+                        const void* v, const int64_t* v_strides, void* out, const int64_t* out_strides, float* lse,
+                        int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
+                        float scale, int dtype, void* stream);
+
+/*
  * Training ([TP] "Training (Teacher Forcing + Masking)": one parallel forward
  * pass over the whole target sequence, then gradients back through it; [AD]
  * "One forward pass covers the whole sequence").  The pages give no gradient

@@ -466,3 +466,32 @@ def test_backward_workspace_bytes(lib):
     need = lib.mha_backward_workspace_bytes(2, 3, 5, 7, 64, 64, mb.BF16)
     assert bwd(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
     assert "needed" in lib.mha_last_error().decode()
+
+
+def fwd_strided(lib, qs=(3 * 5 * 64, 5 * 64, 64), ks=(3 * 5 * 64, 5 * 64, 64), vs=(3 * 5 * 64, 5 * 64, 64),
+                os_=(3 * 5 * 64, 5 * 64, 64), q=P, k=P, v=P, out=P, lse=None, B=2, H=3, Nq=5, Nk=5, dk=64, dv=64,
+                mask=0, dtype=mb.BF16):
+    arr = [None if x is None else (ctypes.c_int64 * 3)(*x) for x in (qs, ks, vs, os_)]
+    return lib.mha_forward_strided(q, arr[0], k, arr[1], v, arr[2], out, arr[3], lse, B, H, Nq, Nk, dk, dv, mask,
+                                   None, 0.125, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), mb.ERR_INVALID_ARG),
+    (dict(os_=None), mb.ERR_INVALID_ARG),
+    (dict(ks=(-64, 64, 64)), mb.ERR_INVALID_ARG),
+    (dict(qs=(960, 320, 68)), mb.ERR_INVALID_ARG),            # bf16 row stride not a multiple of 8
+    (dict(os_=(960, 320, 32)), mb.ERR_INVALID_ARG),           # output rows overlap
+    (dict(os_=(960, 0, 64)), mb.ERR_INVALID_ARG),             # output heads overlap
+    (dict(ks=(0, 0, 1 << 24), Nk=3), mb.ERR_UNSUPPORTED),     # a head spans more than 2^31 bytes
+    (dict(mask=1, Nk=6), mb.ERR_INVALID_ARG),
+    (dict(dtype=mb.BF16, dk=32, dv=32), mb.ERR_UNSUPPORTED),
+])
+def test_forward_strided_rejects(lib, kw, status):
+    assert fwd_strided(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+def test_forward_strided_empty_is_ok(lib):
+    assert fwd_strided(lib, Nq=0) == mb.OK
+    assert fwd_strided(lib, B=0, q=None, out=None) == mb.OK

@@ -422,3 +422,48 @@ def test_longest_key_sequence_at_the_offset_limit():
     rows = np.array([(0, 0, 0), (0, 0, 31), (0, 0, 32), (0, 0, 63)], np.int32)
     ref = oracle.attention_rows(inp["q"], inp["k"], inp["v"], rows, mask_kind=NONE, key_lens=lens)
     assert_close(got[0, 0, rows[:, 2]], ref, "bf16", "Nk at the offset limit")
+
+
+@pytest.mark.parametrize("dtype,mask,Nq,Nk,lens", [
+    ("bf16", CAUSAL, 150, 150, (20, 150)),
+    ("f16", NONE, 37, 101, (1, 101)),
+    ("bf16", NONE, 300, 64, None),
+    ("f32", CAUSAL, 70, 70, (5, 70)),
+])
+def test_strided_views_of_token_major_storage(dtype, mask, Nq, Nk, lens):
+    """q, k, v and out stored token-major [B, N, H, d] (the layout of a projection's
+    output) and passed as [B, H, N, d] views: the same result as the oracle on the
+    logical tensors, and bit-identical to the dense call."""
+    B, H = 2, 3
+    inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, dtype, seed=22, lens=lens)
+    q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
+    qt, kt, vt = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    assert not qt.is_contiguous()
+    out_store = torch.full((B, Nq, H, 64), 7.0, dtype=q.dtype, device="cuda")
+    out = out_store.transpose(1, 2)
+    kl = lens_dev(inp["key_lens"])
+    mha.forward(qt, kt, vt, mask_kind=mask, key_lens=kl, out=out)
+    dense = mha.forward(q, k, v, mask_kind=mask, key_lens=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dense)
+    assert_close(to_host(out), ref_core(inp, mask), dtype, f"strided {dtype} {Nq}x{Nk}")
+
+
+def test_strided_broadcast_key_value_heads():
+    """Zero head strides share one key/value head among all query heads (the
+    multi-query arrangement): the oracle on the repeated tensors."""
+    B, H, Nq, Nk = 2, 4, 96, 130
+    inp = synth.core_inputs(B, 1, Nq, Nk, 64, 64, "bf16", seed=23, lens=(40, 130))
+    q_full = synth.core_inputs(B, H, Nq, Nk, 64, 64, "bf16", seed=24)["q"]
+    q = to_dev(q_full, "bf16")
+    k1, v1 = to_dev(inp["k"], "bf16"), to_dev(inp["v"], "bf16")
+    k = k1.expand(B, H, Nk, 64)
+    v = v1.expand(B, H, Nk, 64)
+    out, lse = mha.forward_lse(q, k, v, mask_kind=NONE, key_lens=lens_dev(inp["key_lens"]))
+    torch.cuda.synchronize()
+    k_rep = np.repeat(inp["k"], H, axis=1)
+    v_rep = np.repeat(inp["v"], H, axis=1)
+    ref = oracle.attention(q_full, k_rep, v_rep, mask_kind=NONE, key_lens=inp["key_lens"])
+    assert_close(to_host(out), ref, "bf16", "broadcast key/value heads")
+    ref_lse = oracle.attention_lse(q_full, k_rep, mask_kind=NONE, key_lens=inp["key_lens"])
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 4e-3

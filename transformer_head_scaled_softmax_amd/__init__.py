@@ -62,9 +62,22 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _strides(t, name):
+    """(device pointer, ctypes int64[3] of the batch, head, row strides) of a
+    [B, H, N, d] view whose last dimension is contiguous."""
+    import ctypes
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.stride(3) != 1 and t.shape[3] > 1:
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+    return t.data_ptr(), (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
 def forward(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None,
             out=None, stream=None):
-    """Attention per head; see mha_forward in include/mha.h."""
+    """Attention per head; see mha_forward in include/mha.h.  Views with other
+    strides (e.g. [B, N, H, d] storage transposed to [B, H, N, d]) go through
+    mha_forward_strided without a copy."""
     import torch
     B, H, Nq, dk = q.shape
     Nk, dv = k.shape[2], v.shape[3]
@@ -77,9 +90,23 @@ def forward(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | N
     if out is None:
         out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=q.device)
     lib = load()
+    if not all(t.is_contiguous() for t in (q, k, v, out)):
+        return _forward_strided(lib, q, k, v, out, None, mask_kind, key_lens, scale, stream)
     st = lib.mha_forward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
                          B, H, Nq, Nk, dk, dv, int(mask_kind), _lens_ptr(key_lens, B), float(scale),
                          _dtype_code(q), _stream(stream))
+    check(lib, st)
+    return out
+
+
+def _forward_strided(lib, q, k, v, out, lse, mask_kind, key_lens, scale, stream):
+    B, H, Nq, dk = q.shape
+    Nk, dv = k.shape[2], v.shape[3]
+    (qp, qs), (kp, ks), (vp, vs), (op, os_) = (_strides(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"),
+                                                                           (out, "out")))
+    st = lib.mha_forward_strided(qp, qs, kp, ks, vp, vs, op, os_, _dev_ptr(lse, "lse"), B, H, Nq, Nk, dk, dv,
+                                 int(mask_kind), _lens_ptr(key_lens, B), float(scale), _dtype_code(q),
+                                 _stream(stream))
     check(lib, st)
     return out
 
@@ -223,6 +250,8 @@ def forward_lse(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float
     if lse.dtype != torch.float32 or lse.shape != (B, H, Nq):
         raise ValueError(f"lse must be a float32 tensor of shape ({B}, {H}, {Nq})")
     lib = load()
+    if not all(t.is_contiguous() for t in (q, k, v, out)):
+        return _forward_strided(lib, q, k, v, out, lse, mask_kind, key_lens, scale, stream), lse
     st = lib.mha_forward_lse(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
                              _dev_ptr(lse, "lse"), B, H, Nq, Nk, dk, dv, int(mask_kind), _lens_ptr(key_lens, B),
                              float(scale), _dtype_code(q), _stream(stream))

@@ -27,7 +27,7 @@ ERR_HIP = -4
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
            "mha_proj_forward_timed", "mha_proj_fused", "mha_proj_ln_forward", "mha_proj_ln_forward_timed",
            "mha_proj_ln_workspace_bytes", "mha_decode_workspace_bytes", "mha_decode_forward",
-           "mha_decode_forward_timed", "mha_decode_split", "mha_forward_lse", "mha_backward_workspace_bytes",
+           "mha_decode_forward_timed", "mha_decode_split", "mha_forward_lse", "mha_forward_strided", "mha_backward_workspace_bytes",
            "mha_backward", "mha_backward_timed", "mha_status_string", "mha_last_error", "mha_version")
 
 
@@ -78,6 +78,9 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_decode_split.restype = i
     lib.mha_forward_lse.argtypes = [vp] * 5 + [i] * 7 + [vp, f, i, vp]
     lib.mha_forward_lse.restype = i
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.mha_forward_strided.argtypes = [vp, i64p, vp, i64p, vp, i64p, vp, i64p, vp] + [i] * 7 + [vp, f, i, vp]
+    lib.mha_forward_strided.restype = i
     lib.mha_backward_workspace_bytes.argtypes = [i] * 7
     lib.mha_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_backward.argtypes = [vp] * 9 + [i] * 7 + [vp, f, i, vp, ctypes.c_size_t, vp]

@@ -92,9 +92,31 @@ extern "C" {
 
 namespace {
 
+// Element strides (batch, head, row) of the four tensors of a per-head call;
+// the feature index is contiguous.
+struct Strides4 {
+  int64_t q[3], k[3], v[3], o[3];
+};
+
+Strides4 dense_strides(int H, int Nq, int Nk, int d_k, int d_v) {
+  Strides4 s;
+  const int64_t qs[3] = {int64_t(H) * Nq * d_k, int64_t(Nq) * d_k, d_k};
+  const int64_t ks[3] = {int64_t(H) * Nk * d_k, int64_t(Nk) * d_k, d_k};
+  const int64_t vs[3] = {int64_t(H) * Nk * d_v, int64_t(Nk) * d_v, d_v};
+  const int64_t os[3] = {int64_t(H) * Nq * d_v, int64_t(Nq) * d_v, d_v};
+  for (int i = 0; i < 3; ++i) {
+    s.q[i] = qs[i];
+    s.k[i] = ks[i];
+    s.v[i] = vs[i];
+    s.o[i] = os[i];
+  }
+  return s;
+}
+
 int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
                  int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
-                 int dtype, void* stream, hipEvent_t const* ev, float* lse = nullptr, bool want_lse = false) {
+                 int dtype, void* stream, hipEvent_t const* ev, float* lse = nullptr, bool want_lse = false,
+                 const Strides4* strides = nullptr) {
   g_last_error.clear();
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
@@ -109,19 +131,33 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
     return fail(MHA_ERR_UNSUPPORTED, "bf16/f16 support d_k == d_v == %d (got %d, %d)",
                 mha::kMfmaHeadDim, d_k, d_v);
   }
+  const Strides4 S = strides ? *strides : dense_strides(H, Nq, Nk, d_k, d_v);
+  const int64_t* all[4] = {S.q, S.k, S.v, S.o};
+  for (const int64_t* t : all)
+    for (int i = 0; i < 3; ++i)
+      if (t[i] < 0) return fail(MHA_ERR_INVALID_ARG, "strides must be >= 0");
   if (B == 0 || H == 0 || Nq == 0) return MHA_OK;  // nothing to write
   if (!q || !out) return fail(MHA_ERR_INVALID_ARG, "q and out must be non-null");
   if (Nk > 0 && (!k || !v)) return fail(MHA_ERR_INVALID_ARG, "k and v must be non-null when Nk > 0");
   const uintptr_t align = dtype == MHA_F32 ? 4 : 16;
   if (!aligned(q, align) || !aligned(k, align) || !aligned(v, align) || !aligned(out, align))
     return fail(MHA_ERR_INVALID_ARG, "q, k, v, out must be %d-byte aligned", (int)align);
+  if (dtype != MHA_F32)
+    for (const int64_t* t : all)
+      for (int i = 0; i < 3; ++i)
+        if (t[i] % 8) return fail(MHA_ERR_INVALID_ARG, "bf16/f16 strides must be multiples of 8 elements");
+  // Output rows must not overlap one another (inputs may share rows).
+  if ((Nq > 1 && S.o[2] < d_v) || (H > 1 && S.o[1] < d_v) || (B > 1 && S.o[0] < d_v))
+    return fail(MHA_ERR_INVALID_ARG, "output strides must separate the output rows");
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   if (want_lse && (!lse || !aligned(lse, 4))) return fail(MHA_ERR_INVALID_ARG, "lse must be non-null and 4-byte aligned");
   const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 512 : 32);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
-  // The matrix-core kernel addresses one (b, h) slice with 32-bit byte offsets.
-  if (dtype != MHA_F32 && (int64_t(Nk) + 128) * d_k * 2 >= kMaxBufferBytes)
+  // The matrix-core kernel addresses one (b, h) slice with 32-bit byte offsets
+  // (row strides included, plus the tiles read past the ends).
+  if (dtype != MHA_F32 && ((int64_t(Nk) + 128) * std::max<int64_t>(std::max(S.k[2], S.v[2]), d_k) * 2 >= kMaxBufferBytes ||
+                           (int64_t(Nq) + 128) * std::max<int64_t>(std::max(S.q[2], S.o[2]), d_k) * 2 >= kMaxBufferBytes))
     return fail(MHA_ERR_UNSUPPORTED, "sequences too long for 32-bit per-head offsets");
 
   mha::AttnArgs a{};
@@ -130,18 +166,18 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   a.v = v;
   a.out = out;
   a.key_lens = key_lens;
-  a.q_sn = d_k;
-  a.q_sh = int64_t(Nq) * d_k;
-  a.q_sb = int64_t(H) * Nq * d_k;
-  a.k_sn = d_k;
-  a.k_sh = int64_t(Nk) * d_k;
-  a.k_sb = int64_t(H) * Nk * d_k;
-  a.v_sn = d_v;
-  a.v_sh = int64_t(Nk) * d_v;
-  a.v_sb = int64_t(H) * Nk * d_v;
-  a.o_sn = d_v;
-  a.o_sh = int64_t(Nq) * d_v;
-  a.o_sb = int64_t(H) * Nq * d_v;
+  a.q_sb = S.q[0];
+  a.q_sh = S.q[1];
+  a.q_sn = S.q[2];
+  a.k_sb = S.k[0];
+  a.k_sh = S.k[1];
+  a.k_sn = S.k[2];
+  a.v_sb = S.v[0];
+  a.v_sh = S.v[1];
+  a.v_sn = S.v[2];
+  a.o_sb = S.o[0];
+  a.o_sh = S.o[1];
+  a.o_sn = S.o[2];
   a.B = B;
   a.H = H;
   a.Nq = Nq;
@@ -182,6 +218,24 @@ int mha_forward_lse(const void* q, const void* k, const void* v, void* out, floa
                     void* stream) {
   return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype, stream, nullptr,
                       lse, true);
+}
+
+int mha_forward_strided(const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+                        const void* v, const int64_t* v_strides, void* out, const int64_t* out_strides, float* lse,
+                        int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens,
+                        float scale, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q_strides || !k_strides || !v_strides || !out_strides)
+    return fail(MHA_ERR_INVALID_ARG, "the four stride arrays must be non-null");
+  Strides4 S;
+  for (int i = 0; i < 3; ++i) {
+    S.q[i] = q_strides[i];
+    S.k[i] = k_strides[i];
+    S.v[i] = v_strides[i];
+    S.o[i] = out_strides[i];
+  }
+  return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype, stream, nullptr,
+                      lse, false, &S);
 }
 
 size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype) {
