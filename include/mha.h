@@ -248,6 +248,35 @@ int mha_backward_timed(const void* q, const void* k, const void* v, const void* 
                        size_t workspace_bytes, void* stream, void* const* events);
 
 /*
+ * Shared key/value heads in training (grouped-query attention, H_kv key/value
+ * heads serving H query heads; [TP] "Limitations of the Original Design"; [ZS]
+ * "Many heads, many subspaces"; [TP] "Training (Teacher Forcing + Masking)").
+ * Query head h reads key/value head h / (H / H_kv); H_kv == H is mha_forward,
+ * H_kv == 1 multi-query attention.  k and v (and dk, dv) are dense
+ * [B, H_kv, Nk, d]; q, out, lse, dout and dq are as in mha_forward_lse and
+ * mha_backward.  1 <= H_kv <= H with H a multiple of H_kv, else
+ * MHA_ERR_INVALID_ARG.
+ *
+ * mha_forward_gqa -- the forward pass; lse may be NULL (not written), else as
+ * for mha_forward_lse.
+ *
+ * mha_backward_gqa -- its gradients: dk and dv of a shared head are the sums,
+ * over the H / H_kv query heads that read it, of the per-head gradients of
+ * mha_backward.  Workspace as mha_backward_workspace_bytes(B, H, ...); the
+ * other requirements as mha_backward.  The dk/dv kernel takes one workgroup
+ * per key block of a shared head and loops over its query heads, so the sums
+ * are formed in registers, in a fixed order, without atomics.
+ */
+int mha_forward_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int H_kv,
+                    int Nq, int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                    void* stream);
+
+int mha_backward_gqa(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk,
+                     int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mha_proj_ln_forward -- the attention sublayer with its residual connection and
  * layer normalisation ([TP] "Residual Connections and Layer Normalization":
  * LayerNorm(x + Sublayer(x)), the normalisation after the residual addition;

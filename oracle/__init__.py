@@ -192,6 +192,35 @@ class Oracle:
         self._check(st, "oracle_attention_backward")
         return gq, gk, gv
 
+    # -- shared key/value heads (grouped-query attention) -----------------------
+    # [TP] "Limitations of the Original Design" and [ZS] "Many heads, many
+    # subspaces": the key/value heads are shared by groups of query heads.  Query
+    # head h reads key/value head h // (H // H_kv).  The forward pass is
+    # per-head attention on the key/value heads repeated to H; a shared head's
+    # gradient is, by the chain rule, the sum of the gradients of its copies.
+    @staticmethod
+    def _group(H: int, Hkv: int) -> int:
+        if Hkv < 1 or H % Hkv:
+            raise ValueError(f"H_kv = {Hkv} does not divide H = {H}")
+        return H // Hkv
+
+    def attention_gqa(self, q, k, v, **kwargs):
+        """q [B,H,Nq,dk]; k [B,H_kv,Nk,dk]; v [B,H_kv,Nk,dv]."""
+        G = self._group(q.shape[1], k.shape[1])
+        return self.attention(q, np.repeat(_f64(k), G, axis=1), np.repeat(_f64(v), G, axis=1), **kwargs)
+
+    def attention_lse_gqa(self, q, k, **kwargs):
+        G = self._group(q.shape[1], k.shape[1])
+        return self.attention_lse(q, np.repeat(_f64(k), G, axis=1), **kwargs)
+
+    def attention_backward_gqa(self, q, k, v, dout, **kwargs):
+        """(dq, dk, dv) with dk, dv of the shared shape [B,H_kv,Nk,d]."""
+        B, Hkv, Nk = k.shape[:3]
+        G = self._group(q.shape[1], Hkv)
+        gq, gk, gv = self.attention_backward(q, np.repeat(_f64(k), G, axis=1), np.repeat(_f64(v), G, axis=1),
+                                             dout, **kwargs)
+        return gq, gk.reshape(B, Hkv, G, Nk, -1).sum(axis=2), gv.reshape(B, Hkv, G, Nk, -1).sum(axis=2)
+
     # -- multi-head attention with projections ---------------------------------
     def mha_proj(self, x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None,
                  b_O=None, mask_kind: int = MASK_NONE, key_lens=None, scale=None,
@@ -309,3 +338,15 @@ def attention_lse(*args, **kwargs):
 
 def attention_backward(*args, **kwargs):
     return get().attention_backward(*args, **kwargs)
+
+
+def attention_gqa(*args, **kwargs):
+    return get().attention_gqa(*args, **kwargs)
+
+
+def attention_lse_gqa(*args, **kwargs):
+    return get().attention_lse_gqa(*args, **kwargs)
+
+
+def attention_backward_gqa(*args, **kwargs):
+    return get().attention_backward_gqa(*args, **kwargs)

@@ -741,6 +741,53 @@ def pin_backward_selection(orc):
     return fails
 
 
+def pin_backward_gqa_finite_differences(orc):
+    """Shared key/value heads: the gradients of L = sum(dout * out) with respect to
+    the shared k and v match central finite differences of the shared-head forward
+    pass (each shared entry moves every query head of its group at once), and the
+    forward pass and the query gradient equal those of explicitly copied heads
+    computed head by head."""
+    fails = []
+    g = _rng(261)
+    B, H, Hkv, Nq, Nk, d, dv = 2, 6, 2, 5, 7, 4, 3
+    q = g.standard_normal((B, H, Nq, d))
+    k = g.standard_normal((B, Hkv, Nk, d))
+    v = g.standard_normal((B, Hkv, Nk, dv))
+    dout = g.standard_normal((B, H, Nq, dv))
+    lens = np.array([Nk, Nk - 3], np.int32)
+    scale = 0.6
+
+    def loss(kk, vv):
+        return float(np.sum(dout * orc.attention_gqa(q, kk, vv, key_lens=lens, scale=scale, nthreads=1)))
+
+    gq, gk, gv = orc.attention_backward_gqa(q, k, v, dout, key_lens=lens, scale=scale, nthreads=1)
+    if gk.shape != k.shape or gv.shape != v.shape or gq.shape != q.shape:
+        return [f"shapes {gq.shape} {gk.shape} {gv.shape}"]
+    h = 1e-5
+    for name, arr, grad in (("k", k, gk), ("v", v, gv)):
+        for _ in range(16):
+            idx = tuple(int(g.integers(0, n)) for n in arr.shape)
+            a1, a2 = arr.copy(), arr.copy()
+            a1[idx] += h
+            a2[idx] -= h
+            f1 = loss(a1, v) if name == "k" else loss(k, a1)
+            f2 = loss(a2, v) if name == "k" else loss(k, a2)
+            fd = (f1 - f2) / (2 * h)
+            if abs(fd - grad[idx]) > 1e-7 * (1 + abs(fd)):
+                fails.append(f"shared d{name}{idx}: analytic {grad[idx]:.9g} vs fd {fd:.9g}")
+    # Head h reads key/value head h // 3: compare with single-head calls.
+    out = orc.attention_gqa(q, k, v, key_lens=lens, scale=scale, nthreads=1)
+    for hh in range(H):
+        sl = slice(hh, hh + 1)
+        kv = slice(hh // 3, hh // 3 + 1)
+        one = orc.attention(q[:, sl], k[:, kv], v[:, kv], key_lens=lens, scale=scale, nthreads=1)
+        _close(fails, f"shared-head forward, head {hh}", out[:, sl], one, 1e-14)
+        dq1 = orc.attention_backward(q[:, sl], k[:, kv], v[:, kv], dout[:, sl], key_lens=lens, scale=scale,
+                                     nthreads=1)[0]
+        _close(fails, f"shared-head dq, head {hh}", gq[:, sl], dq1, 1e-14)
+    return fails
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_worked_example_projection,
@@ -771,6 +818,7 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_invariants,
     pin_backward_selection,
+    pin_backward_gqa_finite_differences,
 ]
 
 

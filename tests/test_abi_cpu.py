@@ -486,6 +486,7 @@ def fwd_strided(lib, qs=(3 * 5 * 64, 5 * 64, 64), ks=(3 * 5 * 64, 5 * 64, 64), v
     (dict(ks=(0, 0, 1 << 24), Nk=3), mb.ERR_UNSUPPORTED),     # a head spans more than 2^31 bytes
     (dict(mask=1, Nk=6), mb.ERR_INVALID_ARG),
     (dict(dtype=mb.BF16, dk=32, dv=32), mb.ERR_UNSUPPORTED),
+    (dict(lse=P + 2), mb.ERR_INVALID_ARG),                    # optional lse, misaligned
 ])
 def test_forward_strided_rejects(lib, kw, status):
     assert fwd_strided(lib, **kw) == status
@@ -495,3 +496,57 @@ def test_forward_strided_rejects(lib, kw, status):
 def test_forward_strided_empty_is_ok(lib):
     assert fwd_strided(lib, Nq=0) == mb.OK
     assert fwd_strided(lib, B=0, q=None, out=None) == mb.OK
+
+
+# --------------------------------------------------------------------------
+# Shared key/value heads in training.
+
+def fwd_gqa(lib, q=P, k=P, v=P, out=P, lse=None, B=2, H=4, Hkv=2, Nq=5, Nk=5, dk=64, dv=64, mask=0,
+            dtype=mb.BF16):
+    return lib.mha_forward_gqa(q, k, v, out, lse, B, H, Hkv, Nq, Nk, dk, dv, mask, None, 0.125, dtype, None)
+
+
+def bwd_gqa(lib, B=2, H=4, Hkv=2, Nq=5, Nk=7, d_k=64, d_v=64, dtype=mb.BF16, ws=P, ws_bytes=1 << 20, **ptrs):
+    p = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P)
+    p.update(ptrs)
+    return lib.mha_backward_gqa(*p.values(), B, H, Hkv, Nq, Nk, d_k, d_v, 0, None, 0.125, dtype, ws, ws_bytes,
+                                None)
+
+
+@pytest.mark.parametrize("Hkv", [0, -1, 3, 5])
+def test_gqa_head_counts_checked(lib, Hkv):
+    """H_kv must divide H (1 <= H_kv <= H)."""
+    assert fwd_gqa(lib, Hkv=Hkv) == mb.ERR_INVALID_ARG
+    assert "H_kv" in lib.mha_last_error().decode()
+    assert bwd_gqa(lib, Hkv=Hkv) == mb.ERR_INVALID_ARG
+    assert "H_kv" in lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=P + 2), mb.ERR_INVALID_ARG),
+    (dict(dk=32, dv=32), mb.ERR_UNSUPPORTED),
+    (dict(mask=1, Nk=6), mb.ERR_INVALID_ARG),
+    (dict(k=None), mb.ERR_INVALID_ARG),
+])
+def test_forward_gqa_rejects(lib, kw, status):
+    assert fwd_gqa(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=None), mb.ERR_INVALID_ARG),
+    (dict(lse=None), mb.ERR_INVALID_ARG),
+    (dict(d_k=32, d_v=32), mb.ERR_UNSUPPORTED),
+    (dict(ws=None), mb.ERR_WORKSPACE),
+    (dict(ws_bytes=255), mb.ERR_WORKSPACE),
+])
+def test_backward_gqa_rejects(lib, kw, status):
+    assert bwd_gqa(lib, **kw) == status
+    assert lib.mha_last_error().decode()
+
+
+def test_gqa_empty_is_ok(lib):
+    assert fwd_gqa(lib, Nq=0) == mb.OK
+    assert fwd_gqa(lib, H=0, Hkv=0) == mb.OK
+    assert bwd_gqa(lib, B=0) == mb.OK
+    assert bwd_gqa(lib, H=0, Hkv=0) == mb.OK

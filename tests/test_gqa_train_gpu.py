@@ -1,0 +1,148 @@
+"""GPU parity of training with shared key/value heads (mha_forward_gqa,
+mha_backward_gqa) against the fp64 oracle, through the C ABI.
+
+The oracle repeats each key/value head over its H / H_kv query heads, runs
+per-head attention and its gradients, and sums the gradients of the copies of a
+shared head (oracle.attention_backward_gqa, pinned by finite differences).
+
+Tolerances: lse and dq as for mha_backward (tests/test_bwd_gpu.py).  A shared
+head's dk, dv is the sum of G = H / H_kv per-head gradients, each within the
+per-head bound 2e-2 + 2u * A_h, so the sum is held to the sum of the bounds,
+G * 2e-2 + 2u * sum_h A_h (fp32: 1e-5 of the largest reference value).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (ROUNDING_UNIT, TOL_LOWP_ABS, assert_close, assert_close_grad, grad_bounds, lens_dev,
+                      to_dev, to_host)
+from transformer_head_scaled_softmax_amd import _binding as mb, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mha = pytest.importorskip("transformer_head_scaled_softmax_amd")
+
+CAUSAL, NONE = mha.MASK_CAUSAL, mha.MASK_NONE
+LSE_TOL = {"bf16": 4e-3, "f16": 1e-3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mha.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_train(inp, dtype, mask):
+    q, k, v, dout = (to_dev(inp[n], dtype) for n in ("q", "k", "v", "dout"))
+    lens = lens_dev(inp["key_lens"])
+    out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=lens)
+    plain = mha.forward(q, k, v, mask_kind=mask, key_lens=lens)
+    dq, dk, dv = mha.backward(q, k, v, out, dout, lse, mask_kind=mask, key_lens=lens)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain), "forward with and without the row statistic differ"
+    assert dk.shape == k.shape and dv.shape == v.shape
+    return {"out": to_host(out), "lse": lse.cpu().numpy().astype(np.float64), "dq": to_host(dq),
+            "dk": to_host(dk), "dv": to_host(dv)}
+
+
+def check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed, lens_override=None):
+    inp = synth.train_inputs(B, H, Nq, Nk, 64, 64, dtype, seed, lens, Hkv=Hkv)
+    if lens_override is not None:
+        inp["key_lens"] = np.asarray(lens_override, np.int32)
+    what = f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} {dtype} mask{mask} lens{inp['key_lens']}"
+    got = gpu_train(inp, dtype, mask)
+    kw = dict(mask_kind=mask, key_lens=inp["key_lens"])
+    G = H // Hkv
+
+    out_ref = oracle.attention_gqa(inp["q"], inp["k"], inp["v"], **kw)
+    lse_ref = oracle.attention_lse_gqa(inp["q"], inp["k"], **kw)
+    assert np.array_equal(np.isneginf(got["lse"]), np.isneginf(lse_ref)), what
+    fin = ~np.isneginf(lse_ref)
+    if dtype == "f32":
+        assert_close(got["out"], out_ref, "f32", f"out {what}")
+        assert np.all(np.abs(got["lse"][fin] - lse_ref[fin]) <= 1e-5 * np.maximum(1.0, np.abs(lse_ref[fin])))
+    else:
+        assert np.max(np.abs(got["out"] - out_ref), initial=0.0) <= TOL_LOWP_ABS, what
+        assert np.max(np.abs(got["lse"][fin] - lse_ref[fin]), initial=0.0) <= LSE_TOL[dtype], what
+
+    ref = oracle.attention_backward_gqa(inp["q"], inp["k"], inp["v"], inp["dout"], **kw)
+    if dtype == "f32":
+        for n, r in zip(("dq", "dk", "dv"), ref):
+            assert_close(got[n], r, "f32", f"{n} {what}")
+    else:
+        kx = np.repeat(inp["k"].astype(np.float64), G, axis=1)
+        vx = np.repeat(inp["v"].astype(np.float64), G, axis=1)
+        out, P = oracle.attention(inp["q"], kx, vx, return_weights=True, **kw)
+        A_dq, A_dk, A_dv = grad_bounds(inp["q"], kx, vx, inp["dout"], P, out, 1.0 / np.sqrt(64))
+        assert_close_grad(got["dq"], ref[0], A_dq, dtype, f"dq {what}")
+        for n, r, A in (("dk", ref[1], A_dk), ("dv", ref[2], A_dv)):
+            A = A.reshape(B, Hkv, G, Nk, -1).sum(axis=2)
+            bound = G * TOL_LOWP_ABS + 2.0 * ROUNDING_UNIT[dtype] * A
+            ratio = float(np.max(np.abs(got[n] - r) / bound, initial=0.0))
+            assert ratio <= 1.0, f"{n} {what}: error reaches {ratio:.3g} x the bound"
+    if inp["key_lens"] is not None:
+        for b, L in enumerate(np.clip(inp["key_lens"], 0, Nk)):
+            assert not np.any(got["dk"][b, :, L:]) and not np.any(got["dv"][b, :, L:]), f"padded keys {what}"
+    return got
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,mask,lens", [
+    (2, 8, 2, 150, 150, CAUSAL, (20, 150)),  # groups of 4, several tiles, ragged tail, padding
+    (2, 6, 1, 64, 200, NONE, (1, 200)),      # multi-query: one key/value head, cross-shaped
+    (3, 4, 2, 37, 101, NONE, None),          # groups of 2, Nq < Nk
+    (1, 6, 3, 300, 300, CAUSAL, None),       # long query blocks, groups of 2
+    (2, 2, 1, 1, 1, NONE, None),             # one query, one key
+])
+def test_gqa_training_matches_oracle(dtype, B, H, Hkv, Nq, Nk, mask, lens):
+    check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed=41)
+
+
+def test_gqa_training_empty_sequences():
+    # key length 0 (no visible key: zero output and gradients), 37, clamped 500 -> Nk
+    got = check_gqa(3, 4, 1, 80, 80, "bf16", NONE, None, seed=42, lens_override=[0, 37, 500])
+    for n in ("out", "dq", "dk", "dv"):
+        assert not np.any(got[n][0]), n
+    assert np.all(np.isneginf(got["lse"][0]))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def test_gqa_with_one_head_per_group_is_mha_backward():
+    """H_kv == H through the shared-head entry points gives the per-head entry
+    points' results bit for bit."""
+    inp = synth.train_inputs(2, 4, 150, 150, 64, 64, "bf16", 43, (60, 150))
+    q, k, v, dout = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "dout"))
+    lens = lens_dev(inp["key_lens"])
+    out, lse = mha.forward_lse(q, k, v, mask_kind=CAUSAL, key_lens=lens)
+    dq, dk, dv = mha.backward(q, k, v, out, dout, lse, mask_kind=CAUSAL, key_lens=lens)
+    lib = mha.load()
+    out2, lse2 = torch.empty_like(out), torch.empty_like(lse)
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    ws = torch.empty(mha.backward_workspace_bytes(2, 4, 150, 150, 64, 64), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    st = lib.mha_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out2), _ptr(lse2), 2, 4, 4, 150, 150, 64, 64, CAUSAL,
+                             _ptr(lens), 0.125, mha.BF16, stream)
+    assert st == mb.OK, lib.mha_last_error()
+    st = lib.mha_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out2), _ptr(dout), _ptr(lse2), _ptr(dq2), _ptr(dk2),
+                              _ptr(dv2), 2, 4, 4, 150, 150, 64, 64, CAUSAL, _ptr(lens), 0.125, mha.BF16, _ptr(ws),
+                              ws.numel(), stream)
+    assert st == mb.OK, lib.mha_last_error()
+    torch.cuda.synchronize()
+    for a, b in ((out, out2), (lse, lse2), (dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b)
+
+
+def test_gqa_backward_is_deterministic():
+    inp = synth.train_inputs(2, 8, 300, 300, 64, 64, "bf16", 44, (100, 300), Hkv=2)
+    a = gpu_train(inp, "bf16", CAUSAL)
+    b = gpu_train(inp, "bf16", CAUSAL)
+    for n in ("dq", "dk", "dv", "lse"):
+        assert np.array_equal(a[n], b[n]), n

@@ -77,11 +77,12 @@ def forward(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | N
             out=None, stream=None):
     """Attention per head; see mha_forward in include/mha.h.  Views with other
     strides (e.g. [B, N, H, d] storage transposed to [B, H, N, d]) go through
-    mha_forward_strided without a copy."""
+    mha_forward_strided without a copy; k, v with H_kv < H heads (shared
+    key/value heads) through mha_forward_gqa."""
     import torch
     B, H, Nq, dk = q.shape
-    Nk, dv = k.shape[2], v.shape[3]
-    if k.shape != (B, H, Nk, dk) or v.shape != (B, H, Nk, dv):
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, Hkv, Nk, dk) or v.shape != (B, Hkv, Nk, dv) or Hkv < 1 or H % Hkv:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
@@ -90,6 +91,12 @@ def forward(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | N
     if out is None:
         out = torch.empty((B, H, Nq, dv), dtype=q.dtype, device=q.device)
     lib = load()
+    if Hkv != H:
+        st = lib.mha_forward_gqa(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"), None,
+                                 B, H, Hkv, Nq, Nk, dk, dv, int(mask_kind), _lens_ptr(key_lens, B), float(scale),
+                                 _dtype_code(q), _stream(stream))
+        check(lib, st)
+        return out
     if not all(t.is_contiguous() for t in (q, k, v, out)):
         return _forward_strided(lib, q, k, v, out, None, mask_kind, key_lens, scale, stream)
     st = lib.mha_forward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
@@ -233,11 +240,13 @@ def decode_forward(q, k_cache, v_cache, cache_lens=None, mask_kind: int = MASK_C
 def forward_lse(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None,
                 out=None, lse=None, stream=None):
     """Attention per head plus the row statistic lse [B,H,Nq] (fp32) the backward
-    pass needs; see mha_forward_lse in include/mha.h.  Returns (out, lse)."""
+    pass needs; see mha_forward_lse in include/mha.h.  k, v may carry fewer
+    heads H_kv dividing H (shared key/value heads, mha_forward_gqa).  Returns
+    (out, lse)."""
     import torch
     B, H, Nq, dk = q.shape
-    Nk, dv = k.shape[2], v.shape[3]
-    if k.shape != (B, H, Nk, dk) or v.shape != (B, H, Nk, dv):
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, Hkv, Nk, dk) or v.shape != (B, Hkv, Nk, dv) or Hkv < 1 or H % Hkv:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
@@ -250,6 +259,14 @@ def forward_lse(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float
     if lse.dtype != torch.float32 or lse.shape != (B, H, Nq):
         raise ValueError(f"lse must be a float32 tensor of shape ({B}, {H}, {Nq})")
     lib = load()
+    if Hkv != H:  # shared key/value heads: dense tensors only
+        if not all(t.is_contiguous() for t in (q, k, v, out)):
+            raise ValueError("shared key/value heads need contiguous q, k, v, out")
+        st = lib.mha_forward_gqa(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
+                                 _dev_ptr(lse, "lse"), B, H, Hkv, Nq, Nk, dk, dv, int(mask_kind),
+                                 _lens_ptr(key_lens, B), float(scale), _dtype_code(q), _stream(stream))
+        check(lib, st)
+        return out, lse
     if not all(t.is_contiguous() for t in (q, k, v, out)):
         return _forward_strided(lib, q, k, v, out, lse, mask_kind, key_lens, scale, stream), lse
     st = lib.mha_forward_lse(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"),
@@ -267,13 +284,16 @@ def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None,
              dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
     """Gradients (dq, dk, dv) of attention for output gradient ``dout``; ``out`` and
     ``lse`` come from forward_lse with the same arguments.  See mha_backward in
-    include/mha.h.  ``events``: None, or 4 hipEvent_t handles (ints) for
+    include/mha.h; k, v with H_kv < H heads go to mha_backward_gqa (dk, dv then
+    sum over the query heads sharing each key/value head).  ``events``: None, or 4 hipEvent_t handles (ints) for
     mha_backward_timed."""
     import torch
     B, H, Nq, d_k = q.shape
-    Nk, d_v = k.shape[2], v.shape[3]
-    if k.shape != (B, H, Nk, d_k) or v.shape != (B, H, Nk, d_v):
+    Hkv, Nk, d_v = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, Hkv, Nk, d_k) or v.shape != (B, Hkv, Nk, d_v) or Hkv < 1 or H % Hkv:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if Hkv != H and events is not None:
+        raise ValueError("events: timing covers mha_backward only (H_kv == H)")
     if out.shape != (B, H, Nq, d_v) or dout.shape != (B, H, Nq, d_v):
         raise ValueError("out and dout must have shape [B, H, Nq, d_v]")
     if lse.dtype != torch.float32 or lse.shape != (B, H, Nq):
@@ -294,7 +314,9 @@ def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None,
             _dev_ptr(lse, "lse"), _dev_ptr(dq, "dq"), _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), B, H, Nq, Nk, d_k,
             d_v, int(mask_kind), _lens_ptr(key_lens, B), float(scale), code, _dev_ptr(workspace, "workspace"),
             0 if workspace is None else workspace.numel(), _stream(stream))
-    if events is None:
+    if Hkv != H:
+        st = lib.mha_backward_gqa(*args[:11], Hkv, *args[11:])  # H_kv follows B, H
+    elif events is None:
         st = lib.mha_backward(*args)
     else:
         import ctypes

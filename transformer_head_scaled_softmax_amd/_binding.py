@@ -27,8 +27,9 @@ ERR_HIP = -4
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
            "mha_proj_forward_timed", "mha_proj_fused", "mha_proj_ln_forward", "mha_proj_ln_forward_timed",
            "mha_proj_ln_workspace_bytes", "mha_decode_workspace_bytes", "mha_decode_forward",
-           "mha_decode_forward_timed", "mha_decode_split", "mha_forward_lse", "mha_forward_strided", "mha_backward_workspace_bytes",
-           "mha_backward", "mha_backward_timed", "mha_status_string", "mha_last_error", "mha_version")
+           "mha_decode_forward_timed", "mha_decode_split", "mha_forward_lse", "mha_forward_strided",
+           "mha_forward_gqa", "mha_backward_workspace_bytes", "mha_backward", "mha_backward_timed",
+           "mha_backward_gqa", "mha_status_string", "mha_last_error", "mha_version")
 
 
 class MhaError(RuntimeError):
@@ -87,6 +88,10 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_backward.restype = i
     lib.mha_backward_timed.argtypes = lib.mha_backward.argtypes + [vp]
     lib.mha_backward_timed.restype = i
+    lib.mha_forward_gqa.argtypes = [vp] * 5 + [i] * 8 + [vp, f, i, vp]
+    lib.mha_forward_gqa.restype = i
+    lib.mha_backward_gqa.argtypes = [vp] * 9 + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]
+    lib.mha_backward_gqa.restype = i
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
     lib.mha_last_error.argtypes = []

@@ -13,7 +13,8 @@
 // per lane for P and dS, then one output feature per lane for dQ; it also
 // writes D_i.  The dK/dV kernel gives each wave one key row (four per
 // workgroup share 64-query tiles of Q, dO, lse and D): one query per lane for P
-// and dS, one feature per lane for dK and dV.
+// and dS, one feature per lane for dK and dV, summed over the query heads that
+// share the key/value head.
 #include "mha_internal.h"
 
 namespace mha {
@@ -55,8 +56,9 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs a, int dk, int 
   const float* qp = static_cast<const float*>(a.q) + ((int64_t)bh * a.Nq + i) * dk;
   const float* op = static_cast<const float*>(a.out) + ((int64_t)bh * a.Nq + i) * dv;
   const float* gp = static_cast<const float*>(a.dout) + ((int64_t)bh * a.Nq + i) * dv;
-  const float* kp = static_cast<const float*>(a.k) + (int64_t)bh * a.Nk * dk;
-  const float* vp = static_cast<const float*>(a.v) + (int64_t)bh * a.Nk * dv;
+  const int64_t kvhead = (int64_t)b * a.Hkv + (bh % a.H) / (a.H / a.Hkv);  // key/value head read
+  const float* kp = static_cast<const float*>(a.k) + kvhead * a.Nk * dk;
+  const float* vp = static_cast<const float*>(a.v) + kvhead * a.Nk * dv;
   // D_i = dO_i . out_i; the wave's query row and dO row go to LDS.
   float dpart = 0.0f;
   for (int c = lane; c < kDm; c += 64) {
@@ -122,8 +124,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int dk, in
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kb = blockIdx.x % nkb;
-  const int bh = blockIdx.x / nkb;
-  const int b = bh / a.H;
+  const int bkv = blockIdx.x / nkb;  // (b, key/value head); its G query heads are streamed in turn
+  const int b = bkv / a.Hkv, G = a.H / a.Hkv;
 
   int L = a.Nk;
   if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
@@ -134,10 +136,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int dk, in
   const int kfirst = kb * kRows;
   const int qstart = kfirst < L ? (a.causal ? kfirst : 0) : a.Nq;
 
-  const float* kp = static_cast<const float*>(a.k) + ((int64_t)bh * a.Nk + j) * dk;
-  const float* vp = static_cast<const float*>(a.v) + ((int64_t)bh * a.Nk + j) * dv;
-  const float* qp = static_cast<const float*>(a.q) + (int64_t)bh * a.Nq * dk;
-  const float* gp = static_cast<const float*>(a.dout) + (int64_t)bh * a.Nq * dv;
+  const float* kp = static_cast<const float*>(a.k) + ((int64_t)bkv * a.Nk + j) * dk;
+  const float* vp = static_cast<const float*>(a.v) + ((int64_t)bkv * a.Nk + j) * dv;
   for (int c = lane; c < kDm; c += 64) {
     kr[wave][c] = live && c < dk ? kp[c] : 0.0f;
     vr[wave][c] = live && c < dv ? vp[c] : 0.0f;
@@ -145,49 +145,54 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int dk, in
   const float c2 = a.scale * kLog2e;
 
   float dv0 = 0.0f, dv1 = 0.0f, dk0 = 0.0f, dk1 = 0.0f;  // features lane, lane + 64
-  for (int i0 = qstart; i0 < a.Nq; i0 += kTile) {
-    __syncthreads();  // previous tile consumed (and kr, vr visible)
-    const int nq = min(kTile, a.Nq - i0);
-    for (int idx = threadIdx.x; idx < kTile * dk; idx += 256) {
-      const int r = idx / dk, c = idx - r * dk;
-      qs[r][c] = r < nq ? qp[(int64_t)(i0 + r) * dk + c] : 0.0f;
-    }
-    for (int idx = threadIdx.x; idx < kTile * dv; idx += 256) {
-      const int r = idx / dv, c = idx - r * dv;
-      gs[r][c] = r < nq ? gp[(int64_t)(i0 + r) * dv + c] : 0.0f;
-    }
-    if (threadIdx.x < kTile) {
-      const int r = threadIdx.x;
-      ls[r] = r < nq ? lse_offset(a.lse[(int64_t)bh * a.Nq + i0 + r]) : INFINITY;
-      ds_[r] = r < nq ? a.dsum[(int64_t)bh * a.Nq + i0 + r] : 0.0f;
-    }
-    __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int64_t bh = (int64_t)b * a.H + (bkv % a.Hkv) * G + g;  // query head of this pass
+    const float* qp = static_cast<const float*>(a.q) + bh * a.Nq * dk;
+    const float* gp = static_cast<const float*>(a.dout) + bh * a.Nq * dv;
+    for (int i0 = qstart; i0 < a.Nq; i0 += kTile) {
+      __syncthreads();  // previous tile consumed (and kr, vr visible)
+      const int nq = min(kTile, a.Nq - i0);
+      for (int idx = threadIdx.x; idx < kTile * dk; idx += 256) {
+        const int r = idx / dk, c = idx - r * dk;
+        qs[r][c] = r < nq ? qp[(int64_t)(i0 + r) * dk + c] : 0.0f;
+      }
+      for (int idx = threadIdx.x; idx < kTile * dv; idx += 256) {
+        const int r = idx / dv, c = idx - r * dv;
+        gs[r][c] = r < nq ? gp[(int64_t)(i0 + r) * dv + c] : 0.0f;
+      }
+      if (threadIdx.x < kTile) {
+        const int r = threadIdx.x;
+        ls[r] = r < nq ? lse_offset(a.lse[(int64_t)bh * a.Nq + i0 + r]) : INFINITY;
+        ds_[r] = r < nq ? a.dsum[(int64_t)bh * a.Nq + i0 + r] : 0.0f;
+      }
+      __syncthreads();
 
-    const int i = i0 + lane;
-    float p = 0.0f, ds = 0.0f;
-    if (live && lane < nq && (!a.causal || j <= i)) {
-      float s = 0.0f, dp = 0.0f;
-      for (int c = 0; c < dk; ++c) s = fmaf(qs[lane][c], kr[wave][c], s);
-      for (int c = 0; c < dv; ++c) dp = fmaf(gs[lane][c], vr[wave][c], dp);
-      p = exp2f(fmaf(s, c2, -ls[lane]));
-      ds = p * (dp - ds_[lane]);
-    }
-    ps[wave][lane] = p;
-    dss[wave][lane] = ds;
-    __syncthreads();
+      const int i = i0 + lane;
+      float p = 0.0f, ds = 0.0f;
+      if (live && lane < nq && (!a.causal || j <= i)) {
+        float s = 0.0f, dp = 0.0f;
+        for (int c = 0; c < dk; ++c) s = fmaf(qs[lane][c], kr[wave][c], s);
+        for (int c = 0; c < dv; ++c) dp = fmaf(gs[lane][c], vr[wave][c], dp);
+        p = exp2f(fmaf(s, c2, -ls[lane]));
+        ds = p * (dp - ds_[lane]);
+      }
+      ps[wave][lane] = p;
+      dss[wave][lane] = ds;
+      __syncthreads();
 
-    for (int u = 0; u < nq; ++u) {
-      const float pu = ps[wave][u], du = dss[wave][u];
-      if (lane < dv) dv0 = fmaf(pu, gs[u][lane], dv0);
-      if (lane + 64 < dv) dv1 = fmaf(pu, gs[u][lane + 64], dv1);
-      if (lane < dk) dk0 = fmaf(du, qs[u][lane], dk0);
-      if (lane + 64 < dk) dk1 = fmaf(du, qs[u][lane + 64], dk1);
+      for (int u = 0; u < nq; ++u) {
+        const float pu = ps[wave][u], du = dss[wave][u];
+        if (lane < dv) dv0 = fmaf(pu, gs[u][lane], dv0);
+        if (lane + 64 < dv) dv1 = fmaf(pu, gs[u][lane + 64], dv1);
+        if (lane < dk) dk0 = fmaf(du, qs[u][lane], dk0);
+        if (lane + 64 < dk) dk1 = fmaf(du, qs[u][lane + 64], dk1);
+      }
     }
   }
 
   if (j < a.Nk) {
-    float* dkp = static_cast<float*>(a.dk) + ((int64_t)bh * a.Nk + j) * dk;
-    float* dvp = static_cast<float*>(a.dv) + ((int64_t)bh * a.Nk + j) * dv;
+    float* dkp = static_cast<float*>(a.dk) + ((int64_t)bkv * a.Nk + j) * dk;
+    float* dvp = static_cast<float*>(a.dv) + ((int64_t)bkv * a.Nk + j) * dv;
     if (lane < dk) dkp[lane] = dk0 * a.scale;
     if (lane + 64 < dk) dkp[lane + 64] = dk1 * a.scale;
     if (lane < dv) dvp[lane] = dv0;
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(BwdArgs a, int dk, in
 hipError_t launch_bwd_f32(const BwdArgs& a, int dk, int dv, hipStream_t stream, hipEvent_t const* ev) {
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
   const int nqb = (a.Nq + kRows - 1) / kRows, nkb = (a.Nk + kRows - 1) / kRows;
-  const int64_t bh = (int64_t)a.B * a.H;
+  const int64_t bh = (int64_t)a.B * a.H, bkv = (int64_t)a.B * a.Hkv;
   // The dQ kernel writes D, which the dK/dV kernel reads: stream order.
   if (nqb * bh > 0) {
     hipExtLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)(nqb * bh)), dim3(256), 0, stream, evt(0), evt(1), 0, a,
@@ -208,8 +213,8 @@ hipError_t launch_bwd_f32(const BwdArgs& a, int dk, int dv, hipStream_t stream, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (nkb * bh > 0) {
-    hipExtLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nkb * bh)), dim3(256), 0, stream, evt(2), evt(3), 0,
+  if (nkb * bkv > 0) {
+    hipExtLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)(nkb * bkv)), dim3(256), 0, stream, evt(2), evt(3), 0,
                           a, dk, dv, nkb);
     return hipGetLastError();
   }

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArg
   const int kmax_wave = a.causal ? min(L, min(qw0 + 32, a.Nq)) : L;   // tiles from here: skip
   const int ntiles = (max(kend_blk, 0) + kBT - 1) / kBT;
 
-  const int64_t qhead = (int64_t)bh * a.Nq * kD, khead = (int64_t)bh * a.Nk * kD;
+  const int kvh = (bh % a.H) / (a.H / a.Hkv);  // key/value head read by this query head
+  const int64_t qhead = (int64_t)bh * a.Nq * kD, khead = ((int64_t)b * a.Hkv + kvh) * a.Nk * kD;
   const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint16_t*>(a.q) + qhead, (int64_t)a.Nq * kD * 2);
   const __amdgpu_buffer_rsrc_t dosrc =
       make_rsrc(static_cast<const uint16_t*>(a.dout) + qhead, (int64_t)a.Nq * kD * 2);
@@ -312,10 +313,12 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int kb = (int)(blockIdx.x / BH);  // low key blocks first: under the causal mask they see most queries
-  const int b = bh / a.H;
+  // One (b, key/value head, key block); the G query heads that share the
+  // key/value head are streamed one after the other.
+  const int BHkv = a.B * a.Hkv, G = a.H / a.Hkv;
+  const int bkv = blockIdx.x % BHkv;
+  const int kb = (int)(blockIdx.x / BHkv);  // low key blocks first: under the causal mask they see most queries
+  const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
 
   int L = a.Nk;
   if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
@@ -325,16 +328,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
   // mask those from the tile holding query k0; none if every key is padding.
   const int tfirst = a.causal ? k0 / kBT : 0;
   const int ntiles_q = (a.Nq + kBT - 1) / kBT;
-  const int tend = k0 < L ? ntiles_q : tfirst;
+  const int nt = k0 < L ? ntiles_q - tfirst : 0;  // tiles per query head
+  const int iend = nt * G;                          // iteration it: head it / nt, tile tfirst + it % nt
   const bool wave_live = kw0 < L;
   const bool pad_mask = kw0 + 32 > L;  // some key of this wave is padding
 
-  const int64_t qhead = (int64_t)bh * a.Nq * kD, khead = (int64_t)bh * a.Nk * kD;
-  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(static_cast<const uint16_t*>(a.q) + qhead, (int64_t)a.Nq * kD * 2);
-  const __amdgpu_buffer_rsrc_t dosrc =
-      make_rsrc(static_cast<const uint16_t*>(a.dout) + qhead, (int64_t)a.Nq * kD * 2);
-  const __amdgpu_buffer_rsrc_t lsrc = make_rsrc(a.lse + (int64_t)bh * a.Nq, (int64_t)a.Nq * 4);
-  const __amdgpu_buffer_rsrc_t dsrc = make_rsrc(a.dsum + (int64_t)bh * a.Nq, (int64_t)a.Nq * 4);
+  // Per-head sources of the streamed side (query head kvh*G + j of batch b).
+  const int64_t khead = ((int64_t)b * a.Hkv + kvh) * a.Nk * kD;
+  auto head_of = [&](int it) { return (int64_t)b * a.H + kvh * G + (nt > 0 ? it / nt : 0); };
+  auto qsrc_of = [&](const void* base, int64_t bhq) {
+    return make_rsrc(static_cast<const uint16_t*>(base) + bhq * a.Nq * kD, (int64_t)a.Nq * kD * 2);
+  };
+  auto ssrc_of = [&](const float* base, int64_t bhq) { return make_rsrc(base + bhq * a.Nq, (int64_t)a.Nq * 4); };
   const int64_t kvbytes = (int64_t)L * kD * 2;
   const __amdgpu_buffer_rsrc_t ksrc = make_rsrc(static_cast<const uint16_t*>(a.k) + khead, kvbytes);
   const __amdgpu_buffer_rsrc_t vsrc = make_rsrc(static_cast<const uint16_t*>(a.v) + khead, kvbytes);
@@ -364,15 +369,20 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
   const int srow = tid & (kBT - 1), skind = __builtin_amdgcn_readfirstlane(wave);
   u32x4_t qreg[CH], oreg[CH];
   float sreg = 0.0f;
-  auto load_tile = [&](int t) {
+  // Iteration it: query head head_of(it), tile tfirst + it % nt; iterations
+  // past the end read nothing (their head's range check ends at Nq rows).
+  auto load_tile = [&](int it) {
+    const int64_t bhq = head_of(it < iend ? it : iend - 1);
+    const int t = it < iend ? tfirst + it % nt : ntiles_q;
+    const __amdgpu_buffer_rsrc_t qsrc = qsrc_of(a.q, bhq), dosrc = qsrc_of(a.dout, bhq);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       qreg[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, goff[c] + t * (kBT * kD * 2), 0, 0);
       oreg[c] = __builtin_amdgcn_raw_buffer_load_b128(dosrc, goff[c] + t * (kBT * kD * 2), 0, 0);
     }
     if (skind < 2)
-      sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(skind ? dsrc : lsrc,
-                                                                           (t * kBT + srow) * 4, 0, 0));
+      sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           skind ? ssrc_of(a.dsum, bhq) : ssrc_of(a.lse, bhq), (t * kBT + srow) * 4, 0, 0));
   };
   auto store_tile = [&](int t, int buf) {
 #pragma unroll
@@ -394,17 +404,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
       dk[cb][r] = 0.0f;
     }
 
-  if (tfirst < tend) {
-    load_tile(tfirst);
+  if (iend > 0) {
+    load_tile(0);
     store_tile(tfirst, 0);
   }
   __syncthreads();
 
-  for (int t = tfirst; t < tend; ++t) {
-    const int buf = (t - tfirst) & 1;
+  for (int it = 0; it < iend; ++it) {
+    const int t = tfirst + it % nt;
+    const int buf = it & 1;
     const uint16_t* qs = qbuf0 + buf * kBT * kD;
     const uint16_t* os = obuf0 + buf * kBT * kD;
-    load_tile(t + 1);
+    load_tile(it + 1);
 
     // One tile of 64 queries as two 32-query sub-blocks.  MASK: some pair of
     // the tile is invisible (padded keys of this wave, or queries before its
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
         tile(std::false_type{});
     }
 
-    if (t + 1 < tend) store_tile(t + 1, buf ^ 1);
+    if (it + 1 < iend) store_tile(tfirst + (it + 1) % nt, buf ^ 1);
     __syncthreads();
   }
 
@@ -499,7 +510,7 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipEve
 template <class Op, int NW>
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
-  const int64_t blocks = (int64_t)nkb * a.B * a.H;
+  const int64_t blocks = (int64_t)nkb * a.B * a.Hkv;
   if (blocks == 0) return hipSuccess;
   hipExtLaunchKernelGGL((bwd_dkdv_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0, t1, 0,
                         a, nkb);

@@ -116,7 +116,7 @@ Strides4 dense_strides(int H, int Nq, int Nk, int d_k, int d_v) {
 int forward_impl(const void* q, const void* k, const void* v, void* out, int B, int H, int Nq,
                  int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
                  int dtype, void* stream, hipEvent_t const* ev, float* lse = nullptr, bool want_lse = false,
-                 const Strides4* strides = nullptr) {
+                 const Strides4* strides = nullptr, int kv_group = 1) {
   g_last_error.clear();
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
@@ -150,7 +150,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   if ((Nq > 1 && S.o[2] < d_v) || (H > 1 && S.o[1] < d_v) || (B > 1 && S.o[0] < d_v))
     return fail(MHA_ERR_INVALID_ARG, "output strides must separate the output rows");
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
-  if (want_lse && (!lse || !aligned(lse, 4))) return fail(MHA_ERR_INVALID_ARG, "lse must be non-null and 4-byte aligned");
+  if ((want_lse && !lse) || !aligned(lse, 4))
+    return fail(MHA_ERR_INVALID_ARG, "lse must be %s4-byte aligned", want_lse ? "non-null and " : "");
   const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 512 : 32);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
@@ -187,6 +188,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   a.causal = mask_kind == MHA_MASK_CAUSAL;
   a.scale = scale;
   a.lse = lse;
+  a.kv_group = kv_group;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t t0 = ev ? ev[0] : nullptr, t1 = ev ? ev[1] : nullptr;
   hipError_t e = dtype == MHA_F32 ? mha::launch_attn_f32(a, s, t0, t1)
@@ -236,6 +238,21 @@ int mha_forward_strided(const void* q, const int64_t* q_strides, const void* k, 
   }
   return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype, stream, nullptr,
                       lse, false, &S);
+}
+
+int mha_forward_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int H_kv,
+                    int Nq, int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                    void* stream) {
+  g_last_error.clear();
+  if (H > 0 && (H_kv < 1 || H_kv > H || H % H_kv))
+    return fail(MHA_ERR_INVALID_ARG, "H_kv must divide H (got H = %d, H_kv = %d)", H, H_kv);
+  Strides4 S = dense_strides(H, Nq, Nk, d_k, d_v);
+  if (H > 0) {
+    S.k[0] = int64_t(H_kv) * Nk * d_k;  // k, v: [B, H_kv, Nk, d]
+    S.v[0] = int64_t(H_kv) * Nk * d_v;
+  }
+  return forward_impl(q, k, v, out, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale, dtype, stream, nullptr,
+                      lse, false, &S, H > 0 ? H / H_kv : 1);
 }
 
 size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, int d_v, int dtype) {
@@ -498,12 +515,14 @@ namespace {
 size_t backward_workspace(int B, int H, int Nq) { return round256(size_t(B) * H * Nq * sizeof(float)); }
 
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind,
-                  const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
-                  void* stream, hipEvent_t const* ev) {
+                  void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v,
+                  int mask_kind, const int32_t* key_lens, float scale, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream, hipEvent_t const* ev) {
   g_last_error.clear();
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 0 (got %d, %d, %d, %d)", B, H, Nq, Nk);
+  if (H > 0 && (H_kv < 1 || H_kv > H || H % H_kv))
+    return fail(MHA_ERR_INVALID_ARG, "H_kv must divide H (got H = %d, H_kv = %d)", H, H_kv);
   if (d_k < 1 || d_v < 1) return fail(MHA_ERR_INVALID_ARG, "d_k, d_v must be >= 1 (got %d, %d)", d_k, d_v);
   int st = check_common(mask_kind, Nq, Nk, dtype, scale);
   if (st) return st;
@@ -551,6 +570,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.key_lens = key_lens;
   a.B = B;
   a.H = H;
+  a.Hkv = H_kv;
   a.Nq = Nq;
   a.Nk = Nk;
   a.causal = mask_kind == MHA_MASK_CAUSAL;
@@ -576,15 +596,23 @@ int mha_backward(const void* q, const void* k, const void* v, const void* out, c
                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind,
                  const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream) {
-  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale,
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale,
                        dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mha_backward_gqa(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk,
+                     int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d_k, d_v, mask_kind, key_lens,
+                       scale, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 int mha_backward_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k,
                        int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream, void* const* events) {
-  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale,
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H, Nq, Nk, d_k, d_v, mask_kind, key_lens, scale,
                        dtype, workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 

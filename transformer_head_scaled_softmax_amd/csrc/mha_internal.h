@@ -40,7 +40,8 @@ struct AttnArgs {
   float* lse;
 };
 
-// Gradients of attention on dense per-head tensors [B, H, N, d]: q, k, v,
+// Gradients of attention on dense per-head tensors [B, H, N, d] (k, v:
+// [B, Hkv, N, d]): q, k, v,
 // out (the forward output), dout (dLoss/dout) and lse (the forward's row
 // statistic, [B, H, Nq]) in; dq, dk, dv out.  dsum is scratch [B, H, Nq] that
 // the dQ kernel fills with D_i = dout_i . out_i for the dK/dV kernel.
@@ -59,6 +60,10 @@ struct BwdArgs {
   int B, H, Nq, Nk;
   int causal;
   float scale;
+  // Key/value heads: k, v, dk, dv are [B, Hkv, Nk, d]; query head h uses
+  // key/value head h / (H / Hkv) (Hkv == H: one each), and the gradients of a
+  // shared key/value head sum over its query heads.
+  int Hkv;
 };
 
 // One decoding step against a key/value cache, head size 64: q [B, H, Nq, 64]

@@ -153,13 +153,15 @@ def core_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None):
     return {"q": q, "k": k, "v": v, "key_lens": key_lens}
 
 
-def train_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None):
+def train_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None, Hkv=None):
     """core_inputs plus an output gradient dout [B,H,Nq,dv] ~ N(0,1), drawn after
-    v and before the key lengths."""
+    v and before the key lengths.  ``Hkv``: k and v carry that many (shared)
+    heads instead of H."""
     g = generator(seed)
+    Hkv = H if Hkv is None else Hkv
     q = normal(g, (B, H, Nq, dk), dtype)
-    k = normal(g, (B, H, Nk, dk), dtype)
-    v = normal(g, (B, H, Nk, dv), dtype)
+    k = normal(g, (B, Hkv, Nk, dk), dtype)
+    v = normal(g, (B, Hkv, Nk, dv), dtype)
     dout = normal(g, (B, H, Nq, dv), dtype)
     key_lens = key_lengths(g, B, *lens) if lens is not None else None
     return {"q": q, "k": k, "v": v, "dout": dout, "key_lens": key_lens}
