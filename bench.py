@@ -13,7 +13,8 @@ rotating input sets so that caches cannot hold the batch between steps.
 
 The training workloads (``--workload *_bwd``) time the backward pass instead:
 dq, dk, dv from resident q, k, v, the forward output, its row statistic and an
-N(0,1) output gradient, via mha_backward.
+N(0,1) output gradient, via mha_backward (mha_backward_gqa when the key/value
+heads are shared).
 
 Prints one JSON line: whole-job throughput (algorithmic TFLOP/s), tokens/s, the
 roofline of the dominant kernel (its time measured with HIP events around it on
@@ -118,13 +119,14 @@ def backward_work(w, lens):
     dQ and dK -- the step's count.  The dQ kernel forms S, dP and dQ (6d), the
     dK/dV kernel S, dP, dV and dK (8d).  Bytes: the dQ kernel reads q, dout,
     out, lse and the visible rows of k and v and writes dq and D; the dK/dV
-    kernel reads k, v (visible rows), q, dout, lse and D and writes dk, dv."""
+    kernel reads k, v (visible rows), q, dout, lse and D and writes dk, dv.
+    Shared key/value heads count once."""
     es = ES[w.dtype]
     pairs = visible_counts(w, lens)
     Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
     qrow = w.B * w.H * w.Nq * w.d * es
-    krow = w.B * w.H * w.Nk * w.d * es
-    kvis = 2 * int(Ls.sum()) * w.H * w.d * es
+    krow = w.B * w.kv_heads * w.Nk * w.d * es
+    kvis = 2 * int(Ls.sum()) * w.kv_heads * w.d * es
     stat = w.B * w.H * w.Nq * 4
     lb = 0 if lens is None else 4 * w.B
     dq = (6.0 * w.d * pairs, 3 * qrow + stat + kvis + qrow + stat + lb)
@@ -261,7 +263,9 @@ def cpu_baseline(w, inp_sets, seconds_target):
             # one (b, h) slice per thread, stacked as heads of one sequence
             g = np.random.Generator(np.random.PCG64(100 + n))
             picks = [(int(g.integers(w.B)), int(g.integers(w.H))) for _ in range(threads)]
-            st = {k_: np.stack([inp[k_][b, h] for b, h in picks])[None] for k_ in ("q", "k", "v", "dout")}
+            G = w.H // w.kv_heads  # query head h reads key/value head h // G
+            st = {k_: np.stack([inp[k_][b, h // G if k_ in ("k", "v") else h] for b, h in picks])[None]
+                  for k_ in ("q", "k", "v", "dout")}
             oracle.attention_backward(st["q"], st["k"], st["v"], st["dout"], mask_kind=w.mask, nthreads=threads)
             pairs = (w.Nq * (w.Nq + 1) // 2) if w.mask == 1 else w.Nq * w.Nk
             done_flops += 10.0 * w.d * pairs * len(picks)
@@ -343,7 +347,7 @@ def main():
     elif w.decode:
         per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.kv_heads * w.Nk * w.d) * es
     elif w.backward:  # q, out, dout, dq and k, v, dk, dv (+ lse)
-        per_set = (4 * w.B * w.H * w.Nq * w.d + 4 * w.B * w.H * w.Nk * w.d) * es + 4 * w.B * w.H * w.Nq
+        per_set = (4 * w.B * w.H * w.Nq * w.d + 4 * w.B * w.kv_heads * w.Nk * w.d) * es + 4 * w.B * w.H * w.Nq
     else:
         per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.H * w.Nk * w.d) * es
     nsets = args.sets or int(min(64, max(2, math.ceil((1 << 30) / per_set))))
@@ -445,9 +449,14 @@ def main():
         def step(i, sp, events=None):
             d = dev_sets[i % nsets]
             lp = None if d["key_lens"] is None else d["key_lens"].data_ptr()
-            argsv = tuple(d[n_].data_ptr() for n_ in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv")) + (
-                w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.mask, lp, scale, code, ws.data_ptr(), need, sp)
-            st = lib.mha_backward(*argsv) if events is None else lib.mha_backward_timed(*argsv, events)
+            ptrs = tuple(d[n_].data_ptr() for n_ in ("q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"))
+            tail = (w.Nq, w.Nk, w.d, w.d, w.mask, lp, scale, code, ws.data_ptr(), need, sp)
+            if w.Hkv is not None:  # shared key/value heads
+                argsv = ptrs + (w.B, w.H, w.Hkv) + tail
+                st = lib.mha_backward_gqa(*argsv) if events is None else lib.mha_backward_gqa_timed(*argsv, events)
+            else:
+                argsv = ptrs + (w.B, w.H) + tail
+                st = lib.mha_backward(*argsv) if events is None else lib.mha_backward_timed(*argsv, events)
             if st != 0:
                 raise RuntimeError(lib.mha_last_error().decode())
         stage_events = {"bwd_dq": (0, 1), "bwd_dkdv": (2, 3)}
@@ -562,7 +571,8 @@ def main():
                    **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "waves": nsplit}
                       if w.decode else {}),
                    **({"pass": "backward (dq, dk, dv from q, k, v, out, dout, lse)",
-                       "flops_per_visible_pair": 10 * w.d} if w.backward else {})},
+                       "flops_per_visible_pair": 10 * w.d} if w.backward else {}),
+                   **({"H_kv": w.kv_heads} if w.backward and w.Hkv is not None else {})},
         "tokens_per_s": round(w.B * w.Nq / sec, 1),
         "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 5),
         "hbm_gbps_algorithmic": round(bytes_ / sec / 1e9, 1),

@@ -276,6 +276,13 @@ int mha_backward_gqa(const void* q, const void* k, const void* v, const void* ou
                      int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* mha_backward_gqa_timed -- as mha_backward_gqa, plus 4 events (as for
+ * mha_backward_timed). */
+int mha_backward_gqa_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk,
+                           int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 /*
  * mha_proj_ln_forward -- the attention sublayer with its residual connection and
  * layer normalisation ([TP] "Residual Connections and Layer Normalization":

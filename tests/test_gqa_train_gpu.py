@@ -146,3 +146,43 @@ def test_gqa_backward_is_deterministic():
     b = gpu_train(inp, "bf16", CAUSAL)
     for n in ("dq", "dk", "dv", "lse"):
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_long_causal_gqa_bwd_full_size():
+    """The long-context grouped-query workload at full size (B=2, n=8192, 16 query
+    heads over 4 key/value heads) in the launch configuration the benchmark times:
+    two whole key/value-head groups (eight query heads) against the oracle element
+    by element, and on every shared head sum_j dv_j = sum of dout over its group's
+    rows (each weight row sums to 1) and sum_j dk_j = 0 up to the rounding of out
+    in D (each dS row sums to 0)."""
+    w = synth.WORKLOADS["long_causal_gqa_bwd"]
+    inp = synth.workload_inputs(w)
+    G = w.H // w.Hkv
+    got = gpu_train(inp, w.dtype, w.mask)
+    for n in ("dq", "dk", "dv"):
+        assert np.all(np.isfinite(got[n])), n
+    sdv = got["dv"].sum(axis=2)
+    sdo = inp["dout"].astype(np.float64).reshape(w.B, w.Hkv, G, w.Nq, w.d).sum(axis=(2, 3))
+    assert np.max(np.abs(sdv - sdo)) <= 0.05 * np.sqrt(G * w.Nq), np.max(np.abs(sdv - sdo))
+    assert np.max(np.abs(got["dk"].sum(axis=2))) <= 0.05 * np.sqrt(G * w.Nk)
+    scale = 1.0 / np.sqrt(w.d)
+    for b, g in ((0, 1), (1, 3)):
+        heads = range(g * G, (g + 1) * G)
+        st = {"q": inp["q"][b:b + 1, g * G:(g + 1) * G], "dout": inp["dout"][b:b + 1, g * G:(g + 1) * G],
+              "k": inp["k"][b:b + 1, g:g + 1], "v": inp["v"][b:b + 1, g:g + 1]}
+        ref = oracle.attention_backward_gqa(st["q"], st["k"], st["v"], st["dout"], mask_kind=w.mask)
+        A_dk = np.zeros((1, 1, w.Nk, w.d))
+        A_dv = np.zeros((1, 1, w.Nk, w.d))
+        for s, h in enumerate(heads):  # the weights for the bound, one slice at a time (512 MiB in fp64)
+            sl = {n: st[n][:, s:s + 1] for n in ("q", "dout")}
+            out, P = oracle.attention(sl["q"], st["k"], st["v"], mask_kind=w.mask, return_weights=True)
+            A = grad_bounds(sl["q"], st["k"], st["v"], sl["dout"], P, out, scale)
+            del P
+            assert_close_grad(got["dq"][b:b + 1, h:h + 1], ref[0][:, s:s + 1], A[0], w.dtype, f"dq slice ({b},{h})")
+            A_dk += A[1]
+            A_dv += A[2]
+        for n, r, A in (("dk", ref[1], A_dk), ("dv", ref[2], A_dv)):
+            bound = G * TOL_LOWP_ABS + 2.0 * ROUNDING_UNIT[w.dtype] * A
+            ratio = float(np.max(np.abs(got[n][b:b + 1, g:g + 1] - r) / bound))
+            print(f"group ({b},{g}) {n} error/bound {ratio:.3f}", flush=True)
+            assert ratio <= 1.0, f"{n} {w.name} group ({b},{g}): {ratio:.3g} x the bound"

@@ -285,15 +285,13 @@ def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None,
     """Gradients (dq, dk, dv) of attention for output gradient ``dout``; ``out`` and
     ``lse`` come from forward_lse with the same arguments.  See mha_backward in
     include/mha.h; k, v with H_kv < H heads go to mha_backward_gqa (dk, dv then
-    sum over the query heads sharing each key/value head).  ``events``: None, or 4 hipEvent_t handles (ints) for
-    mha_backward_timed."""
+    sum over the query heads sharing each key/value head).  ``events``: None, or
+    4 hipEvent_t handles (ints) for the timed variants."""
     import torch
     B, H, Nq, d_k = q.shape
     Hkv, Nk, d_v = k.shape[1], k.shape[2], v.shape[3]
     if k.shape != (B, Hkv, Nk, d_k) or v.shape != (B, Hkv, Nk, d_v) or Hkv < 1 or H % Hkv:
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
-    if Hkv != H and events is not None:
-        raise ValueError("events: timing covers mha_backward only (H_kv == H)")
     if out.shape != (B, H, Nq, d_v) or dout.shape != (B, H, Nq, d_v):
         raise ValueError("out and dout must have shape [B, H, Nq, d_v]")
     if lse.dtype != torch.float32 or lse.shape != (B, H, Nq):
@@ -315,7 +313,12 @@ def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None,
             d_v, int(mask_kind), _lens_ptr(key_lens, B), float(scale), code, _dev_ptr(workspace, "workspace"),
             0 if workspace is None else workspace.numel(), _stream(stream))
     if Hkv != H:
-        st = lib.mha_backward_gqa(*args[:11], Hkv, *args[11:])  # H_kv follows B, H
+        gargs = args[:11] + (Hkv,) + args[11:]  # H_kv follows B, H
+        if events is None:
+            st = lib.mha_backward_gqa(*gargs)
+        else:
+            import ctypes
+            st = lib.mha_backward_gqa_timed(*gargs, (ctypes.c_void_p * 4)(*events))
     elif events is None:
         st = lib.mha_backward(*args)
     else:

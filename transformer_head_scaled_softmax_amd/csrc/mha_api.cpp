@@ -608,6 +608,14 @@ int mha_backward_gqa(const void* q, const void* k, const void* v, const void* ou
                        scale, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
+int mha_backward_gqa_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk,
+                           int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  return backward_impl(q, k, v, out, dout, lse, dq, dk, dv, B, H, H_kv, Nq, Nk, d_k, d_v, mask_kind, key_lens,
+                       scale, dtype, workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
 int mha_backward_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k,
                        int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype, void* workspace,

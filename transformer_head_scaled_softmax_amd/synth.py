@@ -103,6 +103,10 @@ WORKLOADS = {
         Workload("base_decoder_causal_bwd", 64, 8, 64, 64, 64, "bf16", MASK_CAUSAL, (10, 64), False, False, 3,
                  "backward pass of Transformer-base decoder masked self-attention with key padding "
                  "(B=64, n=64, h=8, d=64, lengths U{10..64}, output gradient N(0,1))", backward=True),
+        Workload("long_causal_gqa_bwd", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 6,
+                 "backward pass of long-context causal self-attention with grouped-query attention "
+                 "(B=2, n=8192, h=16 query heads over 4 key/value heads, d=64, output gradient N(0,1))",
+                 backward=True, Hkv=4),
     ]
 }
 
@@ -206,7 +210,7 @@ def workload_inputs(w: Workload, seed: int | None = None):
     if w.proj:
         return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens, w.ln)
     if w.backward:
-        return train_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
+        return train_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens, Hkv=w.Hkv)
     return core_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
 
 
