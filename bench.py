@@ -443,7 +443,7 @@ def main():
             stage_events["decode_combine"] = (2, 3)
         n_events = 4
     elif w.backward:
-        need = lib.mha_backward_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, w.d, code)
+        need = lib.mha_backward_gqa_workspace_bytes(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, code)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
         def step(i, sp, events=None):

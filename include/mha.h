@@ -262,11 +262,18 @@ int mha_backward_timed(const void* q, const void* k, const void* v, const void* 
  *
  * mha_backward_gqa -- its gradients: dk and dv of a shared head are the sums,
  * over the H / H_kv query heads that read it, of the per-head gradients of
- * mha_backward.  Workspace as mha_backward_workspace_bytes(B, H, ...); the
- * other requirements as mha_backward.  The dk/dv kernel takes one workgroup
- * per key block of a shared head and loops over its query heads, so the sums
- * are formed in registers, in a fixed order, without atomics.
+ * mha_backward.  `workspace`: at least mha_backward_gqa_workspace_bytes(...)
+ * bytes (0 when H_kv does not divide H), 256-byte aligned, scratch, not shared
+ * by concurrent calls; the other requirements as mha_backward.  A dk/dv
+ * workgroup owns a key block of one shared head and loops over the query heads
+ * that read it, so the sums form in registers in a fixed order, without
+ * atomics.  When that leaves too few workgroups to fill the chip (bf16/f16),
+ * the group's query heads are split into equal runs whose fp32 sums go to the
+ * workspace and a third kernel adds them in order; results are deterministic
+ * either way.
  */
+size_t mha_backward_gqa_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v, int dtype);
+
 int mha_forward_gqa(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int H_kv,
                     int Nq, int Nk, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
                     void* stream);
@@ -277,7 +284,8 @@ int mha_backward_gqa(const void* q, const void* k, const void* v, const void* ou
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* mha_backward_gqa_timed -- as mha_backward_gqa, plus 4 events (as for
- * mha_backward_timed). */
+ * mha_backward_timed; events[2..3] span the dk/dv kernel and the kernel that
+ * adds the runs, when there is one). */
 int mha_backward_gqa_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
                            const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk,
                            int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,

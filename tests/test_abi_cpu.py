@@ -550,3 +550,22 @@ def test_gqa_empty_is_ok(lib):
     assert fwd_gqa(lib, H=0, Hkv=0) == mb.OK
     assert bwd_gqa(lib, B=0) == mb.OK
     assert bwd_gqa(lib, H=0, Hkv=0) == mb.OK
+
+
+def test_backward_gqa_workspace_bytes(lib):
+    # D per row; plus, when the dK/dV pass splits each head group into runs,
+    # two fp32 [runs][B*H_kv][Nk][64] buffers of the runs' sums.
+    assert lib.mha_backward_gqa_workspace_bytes(32, 16, 8, 1024, 1024, 64, 64, mb.BF16) == 32 * 16 * 1024 * 4
+    assert lib.mha_backward_gqa_workspace_bytes(32, 16, 4, 1024, 1024, 64, 64, mb.BF16) == (
+        32 * 16 * 1024 * 4 + 2 * 2 * 32 * 4 * 1024 * 64 * 4)
+    assert lib.mha_backward_gqa_workspace_bytes(2, 16, 4, 8192, 8192, 64, 64, mb.BF16) == (
+        2 * 16 * 8192 * 4 + 2 * 4 * 2 * 4 * 8192 * 64 * 4)
+    assert lib.mha_backward_gqa_workspace_bytes(2, 16, 16, 8192, 8192, 64, 64, mb.BF16) == \
+        lib.mha_backward_workspace_bytes(2, 16, 8192, 8192, 64, 64, mb.BF16)
+    # fp32 never splits; no queries: nothing to split
+    assert lib.mha_backward_gqa_workspace_bytes(2, 16, 4, 8192, 8192, 64, 64, mb.F32) == 2 * 16 * 8192 * 4
+    assert lib.mha_backward_gqa_workspace_bytes(2, 16, 4, 0, 8192, 64, 64, mb.BF16) == 0
+    for Hkv in (0, 3, 17):
+        assert lib.mha_backward_gqa_workspace_bytes(2, 16, Hkv, 64, 64, 64, 64, mb.BF16) == 0
+    need = lib.mha_backward_gqa_workspace_bytes(2, 4, 2, 5, 7, 64, 64, mb.BF16)
+    assert bwd_gqa(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE

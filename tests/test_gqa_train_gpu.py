@@ -148,41 +148,84 @@ def test_gqa_backward_is_deterministic():
         assert np.array_equal(a[n], b[n]), n
 
 
-def test_long_causal_gqa_bwd_full_size():
-    """The long-context grouped-query workload at full size (B=2, n=8192, 16 query
-    heads over 4 key/value heads) in the launch configuration the benchmark times:
-    two whole key/value-head groups (eight query heads) against the oracle element
-    by element, and on every shared head sum_j dv_j = sum of dout over its group's
-    rows (each weight row sums to 1) and sum_j dk_j = 0 up to the rounding of out
-    in D (each dS row sums to 0)."""
-    w = synth.WORKLOADS["long_causal_gqa_bwd"]
-    inp = synth.workload_inputs(w)
-    G = w.H // w.Hkv
-    got = gpu_train(inp, w.dtype, w.mask)
+def _r256(n):
+    return (n + 255) // 256 * 256
+
+
+def split_runs(B, H, Hkv, Nq, Nk):
+    """Number of runs the dK/dV pass splits each head group into, read off the
+    workspace size (D, then two fp32 [runs][B*Hkv][Nk][64] buffers)."""
+    extra = mha.backward_workspace_bytes(B, H, Nq, Nk, 64, 64, mha.BF16, H_kv=Hkv) - _r256(B * H * Nq * 4)
+    return 1 if extra == 0 else extra // (2 * B * Hkv * Nk * 64 * 4)
+
+
+def check_sampled_groups(inp, got, Hkv, mask, dtype, picks):
+    """Whole key/value-head groups (b, g) against the oracle element by element,
+    and on every shared head sum_j dv_j = sum of dout over the group's rows (each
+    weight row sums to 1) and sum_j dk_j = 0 up to the rounding of out in D (each
+    dS row sums to 0)."""
+    B, H, Nq, d = inp["q"].shape
+    Nk = inp["k"].shape[2]
+    G = H // Hkv
     for n in ("dq", "dk", "dv"):
         assert np.all(np.isfinite(got[n])), n
-    sdv = got["dv"].sum(axis=2)
-    sdo = inp["dout"].astype(np.float64).reshape(w.B, w.Hkv, G, w.Nq, w.d).sum(axis=(2, 3))
-    assert np.max(np.abs(sdv - sdo)) <= 0.05 * np.sqrt(G * w.Nq), np.max(np.abs(sdv - sdo))
-    assert np.max(np.abs(got["dk"].sum(axis=2))) <= 0.05 * np.sqrt(G * w.Nk)
-    scale = 1.0 / np.sqrt(w.d)
-    for b, g in ((0, 1), (1, 3)):
-        heads = range(g * G, (g + 1) * G)
+    if inp["key_lens"] is None:
+        sdv = got["dv"].sum(axis=2)
+        sdo = inp["dout"].astype(np.float64).reshape(B, Hkv, G, Nq, d).sum(axis=(2, 3))
+        assert np.max(np.abs(sdv - sdo)) <= 0.05 * np.sqrt(G * Nq), np.max(np.abs(sdv - sdo))
+        assert np.max(np.abs(got["dk"].sum(axis=2))) <= 0.05 * np.sqrt(G * Nk)
+    scale = 1.0 / np.sqrt(d)
+    for b, g in picks:
+        lens = None if inp["key_lens"] is None else inp["key_lens"][b:b + 1]
         st = {"q": inp["q"][b:b + 1, g * G:(g + 1) * G], "dout": inp["dout"][b:b + 1, g * G:(g + 1) * G],
               "k": inp["k"][b:b + 1, g:g + 1], "v": inp["v"][b:b + 1, g:g + 1]}
-        ref = oracle.attention_backward_gqa(st["q"], st["k"], st["v"], st["dout"], mask_kind=w.mask)
-        A_dk = np.zeros((1, 1, w.Nk, w.d))
-        A_dv = np.zeros((1, 1, w.Nk, w.d))
-        for s, h in enumerate(heads):  # the weights for the bound, one slice at a time (512 MiB in fp64)
+        ref = oracle.attention_backward_gqa(st["q"], st["k"], st["v"], st["dout"], mask_kind=mask, key_lens=lens)
+        A_dk = np.zeros((1, 1, Nk, d))
+        A_dv = np.zeros((1, 1, Nk, d))
+        for s in range(G):  # the weights for the bound, one slice at a time
+            h = g * G + s
             sl = {n: st[n][:, s:s + 1] for n in ("q", "dout")}
-            out, P = oracle.attention(sl["q"], st["k"], st["v"], mask_kind=w.mask, return_weights=True)
+            out, P = oracle.attention(sl["q"], st["k"], st["v"], mask_kind=mask, key_lens=lens, return_weights=True)
             A = grad_bounds(sl["q"], st["k"], st["v"], sl["dout"], P, out, scale)
             del P
-            assert_close_grad(got["dq"][b:b + 1, h:h + 1], ref[0][:, s:s + 1], A[0], w.dtype, f"dq slice ({b},{h})")
+            assert_close_grad(got["dq"][b:b + 1, h:h + 1], ref[0][:, s:s + 1], A[0], dtype, f"dq slice ({b},{h})")
             A_dk += A[1]
             A_dv += A[2]
         for n, r, A in (("dk", ref[1], A_dk), ("dv", ref[2], A_dv)):
-            bound = G * TOL_LOWP_ABS + 2.0 * ROUNDING_UNIT[w.dtype] * A
+            bound = G * TOL_LOWP_ABS + 2.0 * ROUNDING_UNIT[dtype] * A
             ratio = float(np.max(np.abs(got[n][b:b + 1, g:g + 1] - r) / bound))
             print(f"group ({b},{g}) {n} error/bound {ratio:.3f}", flush=True)
-            assert ratio <= 1.0, f"{n} {w.name} group ({b},{g}): {ratio:.3g} x the bound"
+            assert ratio <= 1.0, f"{n} group ({b},{g}): {ratio:.3g} x the bound"
+
+
+def test_long_causal_gqa_bwd_full_size():
+    """The long-context grouped-query workload at full size (B=2, n=8192, 16 query
+    heads over 4 key/value heads) in the launch configuration the benchmark times
+    (each group's four query heads in runs of one): two whole groups against the
+    oracle, and the exact sums on every shared head."""
+    w = synth.WORKLOADS["long_causal_gqa_bwd"]
+    assert split_runs(w.B, w.H, w.Hkv, w.Nq, w.Nk) == 4
+    inp = synth.workload_inputs(w)
+    got = gpu_train(inp, w.dtype, w.mask)
+    check_sampled_groups(inp, got, w.Hkv, w.mask, w.dtype, ((0, 1), (1, 3)))
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,mask,lens,runs", [
+    (32, 16, 8, 1024, CAUSAL, None, 1),        # enough key blocks: one run, sums in registers
+    (32, 16, 8, 1024, NONE, (100, 1024), 1),   # the same, unmasked with key padding
+    (32, 16, 4, 1024, CAUSAL, (500, 1024), 2), # runs of two query heads
+    (4, 8, 2, 512, CAUSAL, (60, 512), 4),      # few key blocks: one run per query head
+    (8, 12, 2, 320, NONE, None, 6),            # groups of six, ragged key blocks
+])
+def test_gqa_runs_match_oracle(B, H, Hkv, N, mask, lens, runs):
+    """Both ways the dK/dV pass sums a shared head's gradients -- in registers over
+    the whole group, or over runs of query heads added by a second kernel -- on
+    sampled whole groups against the oracle."""
+    assert split_runs(B, H, Hkv, N, N) == runs
+    inp = synth.train_inputs(B, H, N, N, 64, 64, "bf16", 45, lens, Hkv=Hkv)
+    got = gpu_train(inp, "bf16", mask)
+    picks = ((0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2))
+    check_sampled_groups(inp, got, Hkv, mask, "bf16", picks)
+    if lens is not None:
+        for b, L in enumerate(np.clip(inp["key_lens"], 0, N)):
+            assert not np.any(got["dk"][b, :, L:]) and not np.any(got["dv"][b, :, L:]), b

@@ -276,8 +276,9 @@ def forward_lse(q, k, v, mask_kind: int = MASK_NONE, key_lens=None, scale: float
     return out, lse
 
 
-def backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, dtype_code: int = BF16) -> int:
-    return int(load().mha_backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, dtype_code))
+def backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, dtype_code: int = BF16, H_kv=None) -> int:
+    H_kv = H if H_kv is None else H_kv
+    return int(load().mha_backward_gqa_workspace_bytes(B, H, H_kv, Nq, Nk, d_k, d_v, dtype_code))
 
 
 def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None,
@@ -305,7 +306,7 @@ def backward(q, k, v, out, dout, lse, mask_kind: int = MASK_NONE, key_lens=None,
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     lib = load()
-    need = int(lib.mha_backward_workspace_bytes(B, H, Nq, Nk, d_k, d_v, code))
+    need = int(lib.mha_backward_gqa_workspace_bytes(B, H, Hkv, Nq, Nk, d_k, d_v, code))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     args = (_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(out, "out"), _dev_ptr(dout, "dout"),

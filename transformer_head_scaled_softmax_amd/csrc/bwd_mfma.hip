@@ -38,6 +38,8 @@
 namespace mha {
 namespace {
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kD = kMfmaHeadDim;  // 64
 constexpr int kBT = 64;           // rows per streamed LDS tile
 constexpr int kSS = 72;           // row stride (elements) of the epilogue staging
@@ -313,11 +315,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
-  // One (b, key/value head, key block); the G query heads that share the
-  // key/value head are streamed one after the other.
-  const int BHkv = a.B * a.Hkv, G = a.H / a.Hkv;
-  const int bkv = blockIdx.x % BHkv;
-  const int kb = (int)(blockIdx.x / BHkv);  // low key blocks first: under the causal mask they see most queries
+  // One (b, key/value head, run of query heads, key block); the GP query heads
+  // of the run, which share the key/value head, are streamed one after the
+  // other.
+  const int BHkv = a.B * a.Hkv, G = a.H / a.Hkv, GP = G / a.parts;
+  const int unit = blockIdx.x % (BHkv * a.parts);
+  const int kb = (int)(blockIdx.x / (BHkv * a.parts));  // low key blocks first: under the causal mask they see most queries
+  const int bkv = unit % BHkv, run = unit / BHkv;
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
 
   int L = a.Nk;
@@ -329,13 +333,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
   const int tfirst = a.causal ? k0 / kBT : 0;
   const int ntiles_q = (a.Nq + kBT - 1) / kBT;
   const int nt = k0 < L ? ntiles_q - tfirst : 0;  // tiles per query head
-  const int iend = nt * G;                          // iteration it: head it / nt, tile tfirst + it % nt
+  const int iend = nt * GP;                         // iteration it: head it / nt of the run, tile tfirst + it % nt
   const bool wave_live = kw0 < L;
   const bool pad_mask = kw0 + 32 > L;  // some key of this wave is padding
 
-  // Per-head sources of the streamed side (query head kvh*G + j of batch b).
+  // Per-head sources of the streamed side (query head kvh*G + run*GP + j of batch b).
   const int64_t khead = ((int64_t)b * a.Hkv + kvh) * a.Nk * kD;
-  auto head_of = [&](int it) { return (int64_t)b * a.H + kvh * G + (nt > 0 ? it / nt : 0); };
+  auto head_of = [&](int it) { return (int64_t)b * a.H + kvh * G + run * GP + (nt > 0 ? it / nt : 0); };
   auto qsrc_of = [&](const void* base, int64_t bhq) {
     return make_rsrc(static_cast<const uint16_t*>(base) + bhq * a.Nq * kD, (int64_t)a.Nq * kD * 2);
   };
@@ -489,12 +493,62 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
     __syncthreads();
   }
 
+  if (a.parts > 1) {
+    // This run's fp32 sums, rows [key][64] (dK unscaled); 16 bytes per lane:
+    // registers 4g .. 4g+3 of block cb are features cb*32 + 8g + 4*half + 0..3.
+    const int64_t per = (int64_t)BHkv * a.Nk * kD;  // elements of one run of one tensor
+    float* pk = a.part + ((int64_t)run * BHkv + bkv) * a.Nk * kD + (int64_t)kj * kD + 4 * half;
+    float* pv = pk + (int64_t)a.parts * per;
+    if (kj < a.Nk) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t wk, wv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            wk[e] = dk[cb][4 * g + e];
+            wv[e] = dv[cb][4 * g + e];
+          }
+          *reinterpret_cast<f32x4_t*>(pk + cb * 32 + 8 * g) = wk;
+          *reinterpret_cast<f32x4_t*>(pv + cb * 32 + 8 * g) = wv;
+        }
+    }
+    return;
+  }
+
   // dV = (dV^T)^T, dK = scale * (dK^T)^T; padded keys get zeros, rows past Nk
   // are not written.
   uint16_t* stage = lds + wave * 32 * kSS;
   store_rows<Op>(dv, 1.0f, stage, static_cast<uint16_t*>(a.dv) + khead, kw0, a.Nk, lane);
   __builtin_amdgcn_wave_barrier();
   store_rows<Op>(dk, a.scale, stage, static_cast<uint16_t*>(a.dk) + khead, kw0, a.Nk, lane);
+}
+
+// dK, dV of shared key/value heads from the runs' fp32 sums: element by
+// element, runs added in order (deterministic), dK scaled, rounded once.  One
+// thread per 8 features of a row of dK or dV.
+template <class Op>
+__global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a, int64_t chunks) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= 2 * chunks) return;
+  const int t = id >= chunks;  // 0: dK, 1: dV
+  const int64_t c = id - t * chunks;
+  const int64_t per = chunks * 8;  // elements of one run of one tensor
+  const float* src = a.part + (int64_t)t * a.parts * per + c * 8;
+  f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(src);
+  f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(src + 4);
+  for (int p = 1; p < a.parts; ++p) {
+    s0 += *reinterpret_cast<const f32x4_t*>(src + p * per);
+    s1 += *reinterpret_cast<const f32x4_t*>(src + p * per + 4);
+  }
+  const float mul = t ? 1.0f : a.scale;
+  u32x4_t w;
+  w[0] = Op::pack(s0[0] * mul, s0[1] * mul);
+  w[1] = Op::pack(s0[2] * mul, s0[3] * mul);
+  w[2] = Op::pack(s1[0] * mul, s1[1] * mul);
+  w[3] = Op::pack(s1[2] * mul, s1[3] * mul);
+  *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(t ? a.dv : a.dk) + c * 8) = w;
 }
 
 template <class Op, int NW>
@@ -507,13 +561,22 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipEve
   return hipGetLastError();
 }
 
+// The dK/dV kernel and, for split head groups, the combining kernel; t0 and t1
+// span both.
 template <class Op, int NW>
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  static_assert(NW * 32 == 128 || NW * 32 == 64, "key block size");
   const int nkb = (a.Nk + NW * 32 - 1) / (NW * 32);
-  const int64_t blocks = (int64_t)nkb * a.B * a.Hkv;
+  const int64_t blocks = (int64_t)nkb * a.B * a.Hkv * a.parts;
   if (blocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((bwd_dkdv_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0, t1, 0,
-                        a, nkb);
+  const bool split = a.parts > 1;
+  hipExtLaunchKernelGGL((bwd_dkdv_kernel<Op, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0,
+                        split ? nullptr : t1, 0, a, nkb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  const int64_t chunks = (int64_t)a.B * a.Hkv * a.Nk * (kD / 8);
+  hipExtLaunchKernelGGL(bwd_combine_kernel<Op>, dim3((unsigned)((2 * chunks + 255) / 256)), dim3(256), 0, stream,
+                        nullptr, t1, 0, a, chunks);
   return hipGetLastError();
 }
 
@@ -526,7 +589,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t const* ev
   // slower there).
   hipError_t e = a.Nq > 64 ? launch_dq<Op, 8>(a, stream, evt(0), evt(1)) : launch_dq<Op, 2>(a, stream, evt(0), evt(1));
   if (e != hipSuccess) return e;
-  return a.Nk > 64 ? launch_dkdv<Op, 4>(a, stream, evt(2), evt(3)) : launch_dkdv<Op, 2>(a, stream, evt(2), evt(3));
+  return bwd_dkdv_keys_per_block(a.Nk) == 128 ? launch_dkdv<Op, 4>(a, stream, evt(2), evt(3))
+                                              : launch_dkdv<Op, 2>(a, stream, evt(2), evt(3));
 }
 
 }  // namespace

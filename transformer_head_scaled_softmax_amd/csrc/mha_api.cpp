@@ -511,8 +511,19 @@ int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_atte
 
 namespace {
 
-// Workspace of mha_backward: D_i = dout_i . out_i per row, fp32 [B, H, Nq].
-size_t backward_workspace(int B, int H, int Nq) { return round256(size_t(B) * H * Nq * sizeof(float)); }
+// Workspace of the backward pass: D_i = dout_i . out_i per row, fp32
+// [B, H, Nq]; then, when the dK/dV pass splits the query heads of each shared
+// key/value head into runs (bf16/f16), the runs' fp32 sums of dK and dV,
+// [2][parts][B*H_kv][Nk][64].
+size_t backward_dsum_bytes(int B, int H, int Nq) { return round256(size_t(B) * H * Nq * sizeof(float)); }
+int backward_parts(int B, int H, int H_kv, int Nq, int Nk, int dtype) {
+  return dtype == MHA_F32 || Nq == 0 ? 1 : mha::bwd_head_parts(B, H, H_kv, Nk);
+}
+size_t backward_workspace(int B, int H, int H_kv, int Nq, int Nk, int dtype) {
+  const int P = backward_parts(B, H, H_kv, Nq, Nk, dtype);
+  const size_t part = P > 1 ? round256(size_t(2) * P * B * H_kv * Nk * mha::kMfmaHeadDim * sizeof(float)) : 0;
+  return backward_dsum_bytes(B, H, Nq) + part;
+}
 
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v,
@@ -547,9 +558,10 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   if (dtype != MHA_F32 && (int64_t(std::max(Nq, Nk)) + 128) * d_k * 2 >= kMaxBufferBytes)
     return fail(MHA_ERR_UNSUPPORTED, "sequences too long for 32-bit per-head offsets");
   const int64_t rows_per_block = dtype == MHA_F32 ? 4 : 64;
-  if ((int64_t(std::max(Nq, Nk)) + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
+  if ((int64_t(std::max(Nq, Nk)) + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks ||
+      int64_t(B) * H_kv * Nk / 16 > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
-  const size_t need = backward_workspace(B, H, Nq);
+  const size_t need = backward_workspace(B, H, H_kv, Nq, Nk, dtype);
   if (need > 0) {
     if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -567,6 +579,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   a.dk = dk;
   a.dv = dv;
   a.dsum = static_cast<float*>(workspace);
+  a.parts = backward_parts(B, H, H_kv, Nq, Nk, dtype);
+  a.part = a.parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_dsum_bytes(B, H, Nq))
+                       : nullptr;
   a.key_lens = key_lens;
   a.B = B;
   a.H = H;
@@ -589,7 +604,14 @@ extern "C" {
 size_t mha_backward_workspace_bytes(int B, int H, int Nq, int Nk, int d_k, int d_v, int dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d_k < 1 || d_v < 1) return 0;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
-  return backward_workspace(B, H, Nq);
+  return backward_workspace(B, H, H, Nq, Nk, dtype);
+}
+
+size_t mha_backward_gqa_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v, int dtype) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d_k < 1 || d_v < 1) return 0;
+  if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  if (H > 0 && (H_kv < 1 || H_kv > H || H % H_kv)) return 0;
+  return backward_workspace(B, H, H > 0 ? H_kv : 1, Nq, Nk, dtype);
 }
 
 int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,

@@ -64,7 +64,34 @@ struct BwdArgs {
   // key/value head h / (H / Hkv) (Hkv == H: one each), and the gradients of a
   // shared key/value head sum over its query heads.
   int Hkv;
+  // bf16/f16 only: the query heads of a key/value head are split into `parts`
+  // equal runs (bwd_head_parts); with parts > 1 each run's dK/dV workgroups
+  // leave fp32 sums in `part` ([2][parts][B*Hkv][Nk][64]: dK unscaled, then
+  // dV) and a combining kernel adds the runs in order.
+  int parts;
+  float* part;
 };
+
+// How many runs the dK/dV pass splits each group of H / Hkv query heads into
+// (bf16/f16, head size 64): the fewest (a divisor of the group size) that give
+// at least kBwdMinBlocks workgroups -- one workgroup per key block of one
+// key/value head alone can leave the chip with one round of workgroups whose
+// lengths differ by the causal mask.  A pure function of the sizes, so the
+// workspace query and the launch agree.
+constexpr int kBwdMinBlocks = 2048;
+inline int bwd_dkdv_keys_per_block(int Nk) { return Nk > 64 ? 128 : 64; }
+inline int bwd_head_parts(int B, int H, int Hkv, int Nk) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nk <= 0 || H % Hkv) return 1;
+  const int G = H / Hkv;
+  const int kpb = bwd_dkdv_keys_per_block(Nk);
+  const int64_t units = int64_t(B) * Hkv * ((Nk + kpb - 1) / kpb);
+  int P = 1;
+  while (P < G && units * P < kBwdMinBlocks) {
+    ++P;
+    while (G % P) ++P;
+  }
+  return P;
+}
 
 // One decoding step against a key/value cache, head size 64: q [B, H, Nq, 64]
 // (the Nq newest positions), caches k, v [B, Hkv, S, 64], out [B, H, Nq, 64].
