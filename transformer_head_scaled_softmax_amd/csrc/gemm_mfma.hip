@@ -445,7 +445,11 @@ hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEven
 // CU), eight waves per CU beat four, 128 x 128 tiles win once they give at
 // least one and a half rounds of the chip, and below that the shape that
 // still gives every CU a workgroup wins (within 5% of the best in every case
-// measured).
+// measured).  When 128 x 64 tiles make exactly one round (the output
+// projections of the sentence-length layers: 4096 x 512 and 2048 x 1024), eight
+// waves per workgroup hide more latency than four with a second workgroup that
+// never comes (4096 x 512 x 512: 6.3-6.5 vs 6.8-6.9 us; with the residual and
+// norm statistics 8.9-9.0 vs 9.4-9.7 us; 2048 x 1024 x 1024: unchanged).
 int tiles(const GemmBatch& g, int tm, int tn) {
   int n = 0;
   for (int i = 0; i < g.count; ++i) n += ((g.p[i].M + tm - 1) / tm) * ((g.p[i].N + tn - 1) / tn);
@@ -455,7 +459,9 @@ int tiles(const GemmBatch& g, int tm, int tn) {
 template <class Op>
 hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (tiles(g, 128, 128) >= 384) return launch<Op, 128, 128, 2, 4, 2, 2>(g, stream, t0, t1);  // 64 KiB, 8 waves
-  if (tiles(g, 128, 64) >= 256) return launch<Op, 128, 64, 2, 2, 2, 2>(g, stream, t0, t1);    // 48 KiB
+  const int t64 = tiles(g, 128, 64);
+  if (t64 == 256) return launch<Op, 128, 64, 4, 2, 2, 1>(g, stream, t0, t1);  // one round: 8 waves
+  if (t64 >= 256) return launch<Op, 128, 64, 2, 2, 2, 2>(g, stream, t0, t1);                 // 48 KiB
   return launch<Op, 64, 64, 2, 2, 2, 2>(g, stream, t0, t1);                                    // 32 KiB
 }
 
@@ -470,6 +476,9 @@ hipError_t launch_ln(const GemmProblem& p, hipStream_t stream, hipEvent_t t0, hi
   if (tiles(g, 128, 128) >= 384) {
     e = launch<Op, 128, 128, 2, 4, 2, 2, true>(g, stream, t0, t1);
     tn = 128;
+  } else if (tiles(g, 128, 64) == 256) {
+    e = launch<Op, 128, 64, 4, 2, 2, 1, true>(g, stream, t0, t1);
+    tn = 64;
   } else if (tiles(g, 128, 64) >= 256) {
     e = launch<Op, 128, 64, 2, 2, 2, 2, true>(g, stream, t0, t1);
     tn = 64;
