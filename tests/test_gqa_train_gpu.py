@@ -229,3 +229,44 @@ def test_gqa_runs_match_oracle(B, H, Hkv, N, mask, lens, runs):
     if lens is not None:
         for b, L in enumerate(np.clip(inp["key_lens"], 0, N)):
             assert not np.any(got["dk"][b, :, L:]) and not np.any(got["dv"][b, :, L:]), b
+
+
+def test_gqa_training_step_graph_replays_match_eager():
+    """Forward and backward with shared heads -- including the run-splitting dK/dV
+    pass and its combining kernel -- captured in one HIP graph: every replay,
+    with eager work and synchronisations in between, reproduces the eager
+    results bit for bit."""
+    B, H, Hkv, N = 2, 8, 2, 300
+    assert split_runs(B, H, Hkv, N, N) > 1
+    inp = synth.train_inputs(B, H, N, N, 64, 64, "bf16", 46, (100, N), Hkv=Hkv)
+    q, k, v, dout = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "dout"))
+    lens = lens_dev(inp["key_lens"])
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(mha.backward_workspace_bytes(B, H, N, N, 64, 64, H_kv=Hkv), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mha.forward_lse(q, k, v, mask_kind=CAUSAL, key_lens=lens, out=out, lse=lse)
+        mha.backward(q, k, v, out, dout, lse, mask_kind=CAUSAL, key_lens=lens, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (out, lse, dq, dk, dv)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for _ in range(4):
+        for t in (out, lse, dq, dk, dv, ws):
+            t.zero_()
+        noise = torch.ones(1 << 20, device="cuda").cumsum(0)  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, w in zip((out, lse, dq, dk, dv), want):
+            assert torch.equal(t, w)
+        del noise
