@@ -21,6 +21,11 @@
 // streams the keys (three products per tile: S^T, dP^T, dQ^T); it also forms
 // D_i for its rows and leaves them in a workspace.  bwd_dkdv_kernel owns a
 // block of keys and streams the queries (four products: S, dP, dV^T, dK^T).
+// With key/value heads shared by G query heads ("Limitations of the Original
+// Design", trishampatil.com) a dK/dV workgroup streams the queries of a run of
+// G / parts query heads one head after the other, so a shared head's gradient
+// sums in its accumulators; with more than one run the runs' fp32 sums go to
+// the workspace and bwd_combine_kernel adds them in order.
 // The products are arranged so that the score-shaped accumulators (S, dP)
 // feed the next MFMA as its B operand straight from registers: a 32x32
 // accumulator holds, in lane n + 32*half, rows 16t + 8(e/4) + 4half + e%4
@@ -298,7 +303,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArg
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: a workgroup owns 32*NW keys of one (b, h), one wave per 32 keys.
+// dK, dV: a workgroup owns 32*NW keys of one (b, key/value head), one wave
+// per 32 keys, for one run of query heads.
 // Query tiles of 64 (Q, dO, lse, D) stream through LDS; per 32-query
 // sub-block a wave computes S = Q K^T and dP = dO V^T (queries x keys, so each
 // lane holds one key's column), P and dS, then dV^T += dO^T P and
