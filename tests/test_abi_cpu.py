@@ -569,3 +569,22 @@ def test_backward_gqa_workspace_bytes(lib):
         assert lib.mha_backward_gqa_workspace_bytes(2, 16, Hkv, 64, 64, 64, 64, mb.BF16) == 0
     need = lib.mha_backward_gqa_workspace_bytes(2, 4, 2, 5, 7, 64, 64, mb.BF16)
     assert bwd_gqa(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+
+
+def test_python_binding_checks_shared_head_shapes():
+    """The binding rejects key/value head counts that do not divide the query
+    heads, and mismatched k/v heads, before any device call."""
+    torch = pytest.importorskip("torch")
+    import transformer_head_scaled_softmax_amd as mha
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k3 = torch.zeros(1, 3, 8, 64, dtype=torch.bfloat16)
+    k2 = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    k1 = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    for fn in (mha.forward, mha.forward_lse):
+        with pytest.raises(ValueError):
+            fn(q, k3, k3)
+        with pytest.raises(ValueError):
+            fn(q, k2, k1)  # k and v must have the same heads
+    lse = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        mha.backward(q, k3, k3, q, q, lse)
