@@ -135,8 +135,8 @@ def backward_work(w, lens):
 
 
 def projection_flops(w):
-    D, HD = w.D, w.H * w.d
-    qkv = 2.0 * w.B * (w.Nq * D * HD + 2 * w.Nk * D * HD)
+    D, HD, HKV = w.D, w.H * w.d, w.kv_heads * w.d  # HKV: width of the (shared) K and V projections
+    qkv = 2.0 * w.B * (w.Nq * D * HD + 2 * w.Nk * D * HKV)
     out = 2.0 * w.B * w.Nq * HD * D
     return qkv, out
 
@@ -145,9 +145,9 @@ def proj_path_bytes(w, lens):
     """Inputs + weights + output of the whole projection path (the norm's scale
     and shift with it; x_q, its residual, is read once)."""
     es = ES[w.dtype]
-    D, HD = w.D, w.H * w.d
+    D, HD, HKV = w.D, w.H * w.d, w.kv_heads * w.d
     x = w.B * w.Nq * D + (w.B * w.Nk * D if w.cross else 0)
-    weights = 3 * HD * D + D * HD + (2 * D if w.ln else 0)
+    weights = (HD + 2 * HKV) * D + D * HD + (2 * D if w.ln else 0)
     return (x + weights + w.B * w.Nq * D) * es + (0 if lens is None else 4 * w.B)
 
 
@@ -157,12 +157,12 @@ def stage_work(w, lens):
     kernel (whose bytes are x, the three input weights, the head outputs it
     writes and the key lengths)."""
     es = ES[w.dtype]
-    D, HD = w.D, w.H * w.d
+    D, HD, HKV = w.D, w.H * w.d, w.kv_heads * w.d
     qkv_f, out_f = projection_flops(w)
     x_bytes = (w.B * w.Nq * D + (w.B * w.Nk * D if w.cross else 0)) * es
-    qkv_b = x_bytes + 3 * HD * D * es + (w.B * w.Nq * HD + 2 * w.B * w.Nk * HD) * es
+    qkv_b = x_bytes + (HD + 2 * HKV) * D * es + (w.B * w.Nq * HD + 2 * w.B * w.Nk * HKV) * es
     out_b = (w.B * w.Nq * HD + D * HD + w.B * w.Nq * D) * es
-    fused_b = x_bytes + 3 * HD * D * es + w.B * w.Nq * HD * es + (0 if lens is None else 4 * w.B)
+    fused_b = x_bytes + (HD + 2 * HKV) * D * es + w.B * w.Nq * HD * es + (0 if lens is None else 4 * w.B)
     rows = w.B * w.Nq * D * es
     return {"qkv_projection": (qkv_f, qkv_b),
             "attention": (attention_flops(w, lens), attention_bytes(w, lens)),
@@ -244,13 +244,17 @@ def cpu_baseline(w, inp_sets, seconds_target):
     done_flops, t0, n = 0.0, time.perf_counter(), 0
     while True:
         inp = inp_sets[n % len(inp_sets)]
-        if w.proj and w.ln:
-            oracle.mha_proj_ln(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
-                               H=w.H, gamma=inp["ln_gamma"], beta=inp["ln_beta"], eps=1e-5,
-                               mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
-        elif w.proj:
-            oracle.mha_proj(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
-                            H=w.H, mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
+        if w.proj:
+            if w.ln:
+                oracle.mha_proj_ln(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
+                                   H=w.H, gamma=inp["ln_gamma"], beta=inp["ln_beta"], eps=1e-5,
+                                   mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
+            elif w.Hkv is not None:
+                oracle.mha_proj_gqa(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
+                                    H=w.H, H_kv=w.Hkv, mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
+            else:
+                oracle.mha_proj(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"],
+                                H=w.H, mask_kind=w.mask, key_lens=inp["key_lens"], nthreads=threads)
             qkv_f, out_f = projection_flops(w)
             done_flops += qkv_f + out_f + attention_flops(w, inp["key_lens"])
             sample = "whole batches"
@@ -390,8 +394,12 @@ def main():
     if w.proj:
         wts = synth.workload_inputs(w)  # seed of the workload: the model weights
         W = {n_: to_dev(wts[n_]) for n_ in ("W_Q", "W_K", "W_V", "W_O") + (("ln_gamma", "ln_beta") if w.ln else ())}
-        need = (lib.mha_proj_ln_workspace_bytes if w.ln else lib.mha_proj_workspace_bytes)(
-            w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, code)
+        gqa = w.Hkv is not None and w.Hkv != w.H  # shared key/value projections
+        if gqa:
+            need = lib.mha_proj_gqa_workspace_bytes(w.B, w.Nq, w.Nk, w.D, w.H, w.Hkv, w.d, w.d, code)
+        else:
+            need = (lib.mha_proj_ln_workspace_bytes if w.ln else lib.mha_proj_workspace_bytes)(
+                w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, code)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
         def step(i, sp, events=None):
@@ -406,6 +414,10 @@ def main():
                          d["out"].data_ptr(), *tail)
                 st = (lib.mha_proj_ln_forward(*argsv) if events is None
                       else lib.mha_proj_ln_forward_timed(*argsv, events, 0))
+            elif gqa:
+                argsv = (*head, d["out"].data_ptr(), *tail[:5], w.Hkv, *tail[5:])
+                st = (lib.mha_proj_forward_gqa(*argsv) if events is None
+                      else lib.mha_proj_forward_gqa_timed(*argsv, events))
             else:
                 argsv = (*head, d["out"].data_ptr(), *tail)
                 st = (lib.mha_proj_forward(*argsv) if events is None
@@ -572,7 +584,7 @@ def main():
                       if w.decode else {}),
                    **({"pass": "backward (dq, dk, dv from q, k, v, out, dout, lse)",
                        "flops_per_visible_pair": 10 * w.d} if w.backward else {}),
-                   **({"H_kv": w.kv_heads} if w.backward and w.Hkv is not None else {})},
+                   **({"H_kv": w.kv_heads} if (w.backward or w.proj) and w.Hkv is not None else {})},
         "tokens_per_s": round(w.B * w.Nq / sec, 1),
         "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 5),
         "hbm_gbps_algorithmic": round(bytes_ / sec / 1e9, 1),

@@ -130,6 +130,38 @@ int mha_proj_forward(const void* x_q, const void* x_kv, const void* W_Q, const v
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mha_proj_forward_gqa -- mha_proj_forward with the key and value projections
+ * shared by groups of query heads ([TP] "Limitations of the Original Design":
+ * multi-query and grouped-query attention keep a query projection per head and
+ * share the key/value projections; [ZS] "Many heads, many subspaces").  W_K is
+ * [H_kv*d_k, D], W_V [H_kv*d_v, D], b_K, b_V [H_kv*d] (nullable); query head h
+ * attends with key/value head h / (H / H_kv), so each run of H / H_kv
+ * consecutive query heads shares one.  Everything else as mha_proj_forward;
+ * H_kv == H is mha_proj_forward (same plan, same results), H_kv == 1
+ * multi-query attention.  1 <= H_kv <= H with H a multiple of H_kv, else
+ * MHA_ERR_INVALID_ARG.  The plan is mha_proj_forward's for the same sizes
+ * (mha_proj_fused): fused, each query head's workgroup projects its group's K
+ * and V itself; unfused, the projections write K and V once per key/value
+ * head and the attention kernel reads them for the whole group.  `workspace`:
+ * at least mha_proj_gqa_workspace_bytes(...) bytes (0 for invalid sizes).
+ */
+size_t mha_proj_gqa_workspace_bytes(int B, int Nq, int Nk, int D, int H, int H_kv, int d_k, int d_v, int dtype);
+
+int mha_proj_forward_gqa(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K, const void* W_V,
+                         const void* W_O, const void* b_Q, const void* b_K, const void* b_V, const void* b_O,
+                         void* out, int B, int Nq, int Nk, int D, int H, int H_kv, int d_k, int d_v, int mask_kind,
+                         const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* mha_proj_forward_gqa_timed -- as mha_proj_forward_gqa, plus 6 events as for
+ * mha_proj_forward_timed (whose plan is MHA_PLAN_AUTO). */
+int mha_proj_forward_gqa_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                               const void* W_V, const void* W_O, const void* b_Q, const void* b_K, const void* b_V,
+                               const void* b_O, void* out, int B, int Nq, int Nk, int D, int H, int H_kv, int d_k,
+                               int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                               void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
  * Timed variants, for profiling.  Same arguments, validation and results as the
  * entry point they extend, plus `events`: caller-created hipEvent_t handles
  * (hipEventCreate; the caller owns them) that receive the start and end

@@ -246,6 +246,25 @@ class Oracle:
         self._check(st, "oracle_mha_proj")
         return out
 
+    def mha_proj_gqa(self, x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, H_kv: int, b_Q=None, b_K=None, b_V=None,
+                     b_O=None, **kwargs):
+        """mha_proj with the key and value projections shared by groups of query
+        heads ([TP] "Limitations of the Original Design"): W_K [H_kv*dk, D],
+        W_V [H_kv*dv, D], b_K, b_V [H_kv*d] or None; query head h uses key/value
+        head h // (H // H_kv).  Computed as mha_proj with each shared block of
+        rows repeated for its group, which is the same function."""
+        G = self._group(H, H_kv)
+
+        def rep(w):
+            if w is None:
+                return None
+            w = _f64(w)
+            rows = w.shape[0] // H_kv
+            return np.repeat(w.reshape((H_kv, rows) + w.shape[1:]), G, axis=0).reshape((H * rows,) + w.shape[1:])
+
+        return self.mha_proj(x_q, x_kv, W_Q, rep(W_K), rep(W_V), W_O, H, b_Q=b_Q, b_K=rep(b_K), b_V=rep(b_V),
+                             b_O=b_O, **kwargs)
+
     def mha_proj_ln(self, x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None,
                     b_O=None, gamma=None, beta=None, eps: float = 1e-5, mask_kind: int = MASK_NONE,
                     key_lens=None, scale=None, nthreads: int | None = None):
@@ -350,3 +369,7 @@ def attention_lse_gqa(*args, **kwargs):
 
 def attention_backward_gqa(*args, **kwargs):
     return get().attention_backward_gqa(*args, **kwargs)
+
+
+def mha_proj_gqa(*args, **kwargs):
+    return get().mha_proj_gqa(*args, **kwargs)

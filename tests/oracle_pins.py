@@ -788,6 +788,45 @@ def pin_backward_gqa_finite_differences(orc):
     return fails
 
 
+def pin_projection_shared_heads(orc):
+    """Shared key/value projections (H = 6 query heads over H_kv = 2, groups of
+    three): with W_Q = W_K = 0 every query head averages the visible rows of its
+    group's value head, out = sum_h mean_{j<L}(x_kv_j W_V[g(h)]^T + b_V[g(h)])
+    W_O[:, h]^T + b_O with g(h) = h // 3 (closed form); and with random weights
+    the result equals per-head projections by plain matrix products fed to the
+    per-head attention oracle."""
+    fails = []
+    g = _rng(271)
+    B, Nq, Nk, D, H, Hkv, dk, dv = 2, 5, 7, 12, 6, 2, 4, 3
+    G = H // Hkv
+    x_q = g.standard_normal((B, Nq, D))
+    x_kv = g.standard_normal((B, Nk, D))
+    W_V = g.standard_normal((Hkv * dv, D))
+    W_O = g.standard_normal((D, H * dv))
+    b_V, b_O = g.standard_normal(Hkv * dv), g.standard_normal(D)
+    lens = np.array([7, 3], np.int32)
+    out = orc.mha_proj_gqa(x_q, x_kv, np.zeros((H * dk, D)), np.zeros((Hkv * dk, D)), W_V, W_O, H=H, H_kv=Hkv,
+                           b_Q=g.standard_normal(H * dk), b_K=g.standard_normal(Hkv * dk), b_V=b_V, b_O=b_O,
+                           key_lens=lens, nthreads=1)
+    want = np.tile(b_O, (B, Nq, 1))
+    for b in range(B):
+        for h in range(H):
+            kv = h // G
+            v = x_kv[b, :lens[b]] @ W_V[kv * dv:(kv + 1) * dv].T + b_V[kv * dv:(kv + 1) * dv]
+            want[b] += (v.mean(axis=0) @ W_O[:, h * dv:(h + 1) * dv].T)[None, :]
+    _close(fails, "shared-head uniform closed form", out, want, 1e-12)
+
+    W_Q, W_K = g.standard_normal((H * dk, D)), g.standard_normal((Hkv * dk, D))
+    out = orc.mha_proj_gqa(x_q, None, W_Q, W_K, W_V, W_O, H=H, H_kv=Hkv, mask_kind=CAUSAL, nthreads=1)
+    q = np.stack([x_q @ W_Q[h * dk:(h + 1) * dk].T for h in range(H)], axis=1)
+    k = np.stack([x_q @ W_K[(h // G) * dk:(h // G + 1) * dk].T for h in range(H)], axis=1)
+    v = np.stack([x_q @ W_V[(h // G) * dv:(h // G + 1) * dv].T for h in range(H)], axis=1)
+    heads = orc.attention(q, k, v, mask_kind=CAUSAL, nthreads=1)             # [B, H, Nq, dv]
+    want = np.concatenate([heads[:, h] for h in range(H)], axis=-1) @ W_O.T  # head-major concatenation
+    _close(fails, "shared-head projections through per-head attention", out, want, 1e-11)
+    return fails
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_worked_example_projection,
@@ -819,6 +858,7 @@ ALL_PINS = [
     pin_backward_invariants,
     pin_backward_selection,
     pin_backward_gqa_finite_differences,
+    pin_projection_shared_heads,
 ]
 
 

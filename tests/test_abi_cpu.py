@@ -588,3 +588,28 @@ def test_python_binding_checks_shared_head_shapes():
     lse = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         mha.backward(q, k3, k3, q, q, lse)
+
+
+def proj_gqa(lib, H=4, Hkv=2, ws_bytes=1 << 24, **kw):
+    a = dict(B=2, Nq=4, Nk=6, D=64, d_k=64, d_v=64, mask=0, dtype=mb.BF16)
+    a.update(kw)
+    return lib.mha_proj_forward_gqa(P, P, P, P, P, P, None, None, None, None, P, a["B"], a["Nq"], a["Nk"], a["D"],
+                                    H, Hkv, a["d_k"], a["d_v"], a["mask"], None, 0.125, a["dtype"], P, ws_bytes,
+                                    None)
+
+
+@pytest.mark.parametrize("Hkv", [0, -2, 3, 8])
+def test_proj_gqa_head_counts_checked(lib, Hkv):
+    assert proj_gqa(lib, Hkv=Hkv) == mb.ERR_INVALID_ARG
+    assert "H_kv" in lib.mha_last_error().decode()
+    assert lib.mha_proj_gqa_workspace_bytes(2, 4, 6, 64, 4, Hkv, 64, 64, mb.BF16) == 0
+
+
+def test_proj_gqa_workspace(lib):
+    # Q and O [B*Nq, H*64], K and V [B*Nk, H_kv*64], each rounded up to 256 bytes
+    assert lib.mha_proj_gqa_workspace_bytes(64, 64, 64, 512, 8, 2, 64, 64, mb.BF16) == (
+        2 * 64 * 64 * 8 * 64 * 2 + 2 * 64 * 64 * 2 * 64 * 2)
+    need = lib.mha_proj_gqa_workspace_bytes(2, 4, 6, 64, 4, 2, 64, 64, mb.BF16)
+    assert proj_gqa(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
+    assert proj_gqa(lib, d_k=32, d_v=32) == mb.ERR_UNSUPPORTED
+    assert proj_gqa(lib, B=0) == mb.OK

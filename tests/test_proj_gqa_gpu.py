@@ -1,0 +1,92 @@
+"""GPU parity of the projection path with shared key/value projections
+(mha_proj_forward_gqa) against the fp64 oracle (oracle.mha_proj_gqa, pinned by
+a closed form and by per-head projections), through the C ABI.  Tolerance as
+for mha_proj_forward (bf16/f16: 2e-2 absolute on the output)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, lens_dev, to_dev, to_host
+from transformer_head_scaled_softmax_amd import _binding as mb, synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mha = pytest.importorskip("transformer_head_scaled_softmax_amd")
+
+CAUSAL, NONE = mha.MASK_CAUSAL, mha.MASK_NONE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mha.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(inp, H, Hkv, dtype, mask, biases=None):
+    d = {n: to_dev(inp[n], dtype) for n in ("x_q", "x_kv", "W_Q", "W_K", "W_V", "W_O")}
+    b = {n: to_dev(x, dtype) for n, x in (biases or {}).items()}
+    out = mha.proj_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=H, H_kv=Hkv,
+                           mask_kind=mask, key_lens=lens_dev(inp["key_lens"]), **b)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,Nq,Nk,D,H,Hkv,cross,mask", [
+    (2, 5, 5, 128, 2, 1, False, CAUSAL),      # multi-query, tiny
+    (3, 17, 33, 256, 4, 2, True, NONE),       # cross-attention, groups of two
+    (2, 70, 70, 512, 8, 2, False, NONE),      # several key tiles, groups of four
+    (1, 130, 130, 384, 6, 3, False, CAUSAL),  # causal, ragged tail
+    (4, 64, 80, 1024, 16, 4, True, NONE),     # the big cross shape with four key/value heads
+])
+def test_proj_gqa_matches_oracle(dtype, B, Nq, Nk, D, H, Hkv, cross, mask):
+    inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed=B * 10 + Nq + H, cross=cross, Hkv=Hkv)
+    g = synth.generator(D + Nq + Hkv)
+    inp["key_lens"] = g.integers(1, Nk + 1, size=B).astype(np.int32)
+    biases = {n: synth.round_to(synth.normal(g, (size,), dtype) * np.float32(0.5), dtype)
+              for n, size in (("b_Q", H * 64), ("b_K", Hkv * 64), ("b_V", Hkv * 64), ("b_O", D))}
+    got = run(inp, H, Hkv, dtype, mask, biases)
+    ref = oracle.mha_proj_gqa(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"], H=H,
+                              H_kv=Hkv, mask_kind=mask, key_lens=inp["key_lens"], **biases)
+    assert_close(got, ref, dtype, f"proj gqa B{B} Nq{Nq} Nk{Nk} D{D} H{H} Hkv{Hkv}")
+
+
+def test_base_encoder_proj_gqa_full():
+    """The grouped-query workload, in the launch configuration the benchmark times."""
+    w = synth.WORKLOADS["base_encoder_proj_gqa"]
+    inp = synth.workload_inputs(w)
+    got = run(inp, w.H, w.Hkv, w.dtype, w.mask)
+    ref = oracle.mha_proj_gqa(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"], H=w.H,
+                              H_kv=w.Hkv, mask_kind=w.mask, key_lens=inp["key_lens"])
+    assert_close(got, ref, w.dtype, w.name)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@pytest.mark.parametrize("cross", [False, True])
+def test_proj_gqa_with_one_head_per_group_is_proj_forward(cross):
+    """H_kv == H through the shared-head entry point gives mha_proj_forward's
+    results bit for bit (the same plan)."""
+    B, N, D, H = 8, 64, 512, 8
+    inp = synth.proj_inputs(B, N, N, D, H, 64, 64, "bf16", seed=47, cross=cross, lens=(10, N))
+    d = {n: to_dev(inp[n], "bf16") for n in ("x_q", "x_kv", "W_Q", "W_K", "W_V", "W_O")}
+    lens = lens_dev(inp["key_lens"])
+    want = mha.proj_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=H, key_lens=lens)
+    lib = mha.load()
+    need = lib.mha_proj_gqa_workspace_bytes(B, N, N, D, H, H, 64, 64, mb.BF16)
+    assert need == lib.mha_proj_workspace_bytes(B, N, N, D, H, 64, 64, mb.BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(want)
+    st = lib.mha_proj_forward_gqa(_p(d["x_q"]), _p(d["x_kv"]), _p(d["W_Q"]), _p(d["W_K"]), _p(d["W_V"]),
+                                  _p(d["W_O"]), None, None, None, None, _p(out), B, N, N, D, H, H, 64, 64, NONE,
+                                  _p(lens), 0.125, mb.BF16, _p(ws), need, torch.cuda.current_stream().cuda_stream)
+    assert st == mb.OK, lib.mha_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)

@@ -124,24 +124,33 @@ def proj_workspace_bytes(B, Nq, Nk, D, H, d_k, d_v, dtype_code: int = BF16) -> i
 
 def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=None, b_O=None,
                  mask_kind: int = MASK_NONE, key_lens=None, scale: float | None = None, out=None,
-                 workspace=None, stream=None, plan: int | None = None):
+                 workspace=None, stream=None, plan: int | None = None, H_kv: int | None = None):
     """Multi-head attention with projections; see mha_proj_forward in include/mha.h.
 
     Weights are [out_features, in_features] (nn.Linear layout).  ``plan``
     (PLAN_UNFUSED / PLAN_FUSED) forces a kernel plan through
-    mha_proj_forward_timed; None lets the library choose."""
+    mha_proj_forward_timed; None lets the library choose.  ``H_kv``: key/value
+    heads shared by groups of query heads (W_K, W_V with H_kv*d rows), through
+    mha_proj_forward_gqa."""
     import torch
     B, Nq, D = x_q.shape
     Nk = Nq if x_kv is None else x_kv.shape[1]
     dk = W_Q.shape[0] // H
-    dv = W_V.shape[0] // H
+    dv = W_O.shape[1] // H
+    gqa = H_kv is not None and H_kv != H
+    if H_kv is None:
+        H_kv = H
+    if H_kv < 1 or H % H_kv or W_K.shape[0] != H_kv * dk or W_V.shape[0] != H_kv * dv:
+        raise ValueError(f"W_K {tuple(W_K.shape)}, W_V {tuple(W_V.shape)} do not fit H = {H}, H_kv = {H_kv}")
+    if gqa and plan is not None:
+        raise ValueError("plan: shared key/value heads take mha_proj_forward's plan for the sizes")
     if scale is None:
         scale = 1.0 / math.sqrt(dk)
     code = _dtype_code(x_q)
     if out is None:
         out = torch.empty((B, Nq, D), dtype=x_q.dtype, device=x_q.device)
     lib = load()
-    need = int(lib.mha_proj_workspace_bytes(B, Nq, Nk, D, H, dk, dv, code))
+    need = int(lib.mha_proj_gqa_workspace_bytes(B, Nq, Nk, D, H, H_kv, dk, dv, code))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_q.device)
     ptrs = [_dev_ptr(t, n) for t, n in ((x_q, "x_q"), (x_kv, "x_kv"), (W_Q, "W_Q"), (W_K, "W_K"),
@@ -149,7 +158,9 @@ def proj_forward(x_q, x_kv, W_Q, W_K, W_V, W_O, H: int, b_Q=None, b_K=None, b_V=
                                         (b_V, "b_V"), (b_O, "b_O"), (out, "out"))]
     args = (*ptrs, B, Nq, Nk, D, H, dk, dv, int(mask_kind), _lens_ptr(key_lens, B), float(scale), code,
             _dev_ptr(workspace, "workspace"), workspace.numel(), _stream(stream))
-    if plan is None:
+    if gqa:
+        st = lib.mha_proj_forward_gqa(*ptrs, B, Nq, Nk, D, H, H_kv, *args[16:])
+    elif plan is None:
         st = lib.mha_proj_forward(*args)
     else:
         st = lib.mha_proj_forward_timed(*args, None, int(plan))

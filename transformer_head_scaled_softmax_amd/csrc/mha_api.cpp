@@ -54,13 +54,16 @@ struct ProjLayout {
   size_t q_off, k_off, v_off, o_off, total;
 };
 
-bool proj_layout(int B, int Nq, int Nk, int H, int d_k, int d_v, int dtype, ProjLayout* L) {
+// H_kv key/value heads (H_kv == H: one per query head; 0 means H).
+bool proj_layout(int B, int Nq, int Nk, int H, int d_k, int d_v, int dtype, ProjLayout* L, int H_kv = 0) {
+  if (H_kv == 0) H_kv = H;
   if (B < 0 || Nq < 0 || Nk < 0 || H < 1 || d_k < 1 || d_v < 1) return false;
+  if (H_kv < 1 || H_kv > H || H % H_kv) return false;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return false;
   const size_t es = elem_size(dtype);
   const size_t q = round256(size_t(B) * Nq * H * d_k * es);
-  const size_t k = round256(size_t(B) * Nk * H * d_k * es);
-  const size_t v = round256(size_t(B) * Nk * H * d_v * es);
+  const size_t k = round256(size_t(B) * Nk * H_kv * d_k * es);
+  const size_t v = round256(size_t(B) * Nk * H_kv * d_v * es);
   const size_t o = round256(size_t(B) * Nq * H * d_v * es);
   L->q_off = 0;
   L->k_off = q;
@@ -316,9 +319,12 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
                       const void* b_V, const void* b_O, void* out, int B, int Nq, int Nk, int D,
                       int H, int d_k, int d_v, int mask_kind, const int32_t* key_lens, float scale,
                       int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                      hipEvent_t const* ev, int plan, const LnSpec* ln) {
+                      hipEvent_t const* ev, int plan, const LnSpec* ln, int H_kv = 0) {
   g_last_error.clear();
   if (plan < MHA_PLAN_AUTO || plan > MHA_PLAN_FUSED) return fail(MHA_ERR_INVALID_ARG, "unknown plan %d", plan);
+  if (H_kv == 0) H_kv = H;
+  if (H >= 1 && (H_kv < 1 || H_kv > H || H % H_kv))
+    return fail(MHA_ERR_INVALID_ARG, "H_kv must divide H (got H = %d, H_kv = %d)", H, H_kv);
   if (B < 0 || Nq < 0 || Nk < 0)
     return fail(MHA_ERR_INVALID_ARG, "B, Nq, Nk must be >= 0 (got %d, %d, %d)", B, Nq, Nk);
   if (D < 1 || H < 1 || d_k < 1 || d_v < 1)
@@ -348,7 +354,7 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   }
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   ProjLayout L;
-  proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L);
+  proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L, H_kv);
   const LnLayout LN = ln_layout(L, B, Nq, D);
   const size_t need = ln ? LN.total : L.total;
   if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -371,6 +377,7 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   void* Vw = ws + L.v_off;
   void* Ow = ws + L.o_off;
   const int HK = H * d_k, HV = H * d_v;
+  const int HKk = H_kv * d_k, HVk = H_kv * d_v;  // widths of the projected K and V rows
   hipStream_t s = static_cast<hipStream_t>(stream);
   const mha::DType dt = static_cast<mha::DType>(dtype);
 
@@ -400,6 +407,7 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
     pa.H = H;
     pa.causal = mask_kind == MHA_MASK_CAUSAL;
     pa.scale = scale;
+    pa.kv_group = H / H_kv;
     hipError_t e = mha::launch_proj_attn(pa, dt, s, evt(0), evt(1));
     if (e != hipSuccess) return hip_fail(e, "fused projection/attention launch");
     return output_projection(Ow, W_O, b_O, out, x_q, B * Nq, D, HV, dt, s, ln, ws, &LN, ev);
@@ -408,8 +416,8 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   // 1. Q, K, V projections in one launch; outputs row-major [B*N, H*d].
   mha::GemmBatch g{};
   g.p[0] = {x_q, W_Q, b_Q, Qw, B * Nq, HK, D, D, HK};
-  g.p[1] = {xkv, W_K, b_K, Kw, B * Nk, HK, D, D, HK};
-  g.p[2] = {xkv, W_V, b_V, Vw, B * Nk, HV, D, D, HV};
+  g.p[1] = {xkv, W_K, b_K, Kw, B * Nk, HKk, D, D, HKk};
+  g.p[2] = {xkv, W_V, b_V, Vw, B * Nk, HVk, D, D, HVk};
   g.count = 3;
   hipError_t e = mha::launch_gemm_mfma(g, dt, s, evt(0), evt(1));
   if (e != hipSuccess) return hip_fail(e, "Q/K/V projection launch");
@@ -425,12 +433,13 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
   a.q_sn = HK;
   a.q_sh = d_k;
   a.q_sb = int64_t(Nq) * HK;
-  a.k_sn = HK;
+  a.k_sn = HKk;
   a.k_sh = d_k;
-  a.k_sb = int64_t(Nk) * HK;
-  a.v_sn = HV;
+  a.k_sb = int64_t(Nk) * HKk;
+  a.v_sn = HVk;
   a.v_sh = d_v;
-  a.v_sb = int64_t(Nk) * HV;
+  a.v_sb = int64_t(Nk) * HVk;
+  a.kv_group = H / H_kv;  // query head h reads key/value head h / (H / H_kv)
   a.o_sn = HV;
   a.o_sh = d_v;
   a.o_sb = int64_t(Nq) * HV;
@@ -505,6 +514,40 @@ size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k,
 
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention) {
   return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;
+}
+
+size_t mha_proj_gqa_workspace_bytes(int B, int Nq, int Nk, int D, int H, int H_kv, int d_k, int d_v, int dtype) {
+  ProjLayout L;
+  if (D < 1 || H_kv < 1 || !proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L, H_kv)) return 0;
+  return L.total;
+}
+
+int mha_proj_forward_gqa(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K, const void* W_V,
+                         const void* W_O, const void* b_Q, const void* b_K, const void* b_V, const void* b_O,
+                         void* out, int B, int Nq, int Nk, int D, int H, int H_kv, int d_k, int d_v, int mask_kind,
+                         const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (H_kv < 1) {
+    g_last_error.clear();
+    return fail(MHA_ERR_INVALID_ARG, "H_kv must divide H (got H = %d, H_kv = %d)", H, H_kv);
+  }
+  return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H, d_k, d_v,
+                           mask_kind, key_lens, scale, dtype, workspace, workspace_bytes, stream, nullptr,
+                           MHA_PLAN_AUTO, nullptr, H_kv);
+}
+
+int mha_proj_forward_gqa_timed(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K,
+                               const void* W_V, const void* W_O, const void* b_Q, const void* b_K, const void* b_V,
+                               const void* b_O, void* out, int B, int Nq, int Nk, int D, int H, int H_kv, int d_k,
+                               int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype,
+                               void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  if (H_kv < 1) {
+    g_last_error.clear();
+    return fail(MHA_ERR_INVALID_ARG, "H_kv must divide H (got H = %d, H_kv = %d)", H, H_kv);
+  }
+  return proj_forward_impl(x_q, x_kv, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O, out, B, Nq, Nk, D, H, d_k, d_v,
+                           mask_kind, key_lens, scale, dtype, workspace, workspace_bytes, stream,
+                           reinterpret_cast<hipEvent_t const*>(events), MHA_PLAN_AUTO, nullptr, H_kv);
 }
 
 }  // extern "C"

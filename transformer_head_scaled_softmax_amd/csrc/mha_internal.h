@@ -168,6 +168,9 @@ struct ProjAttnArgs {
   int B, Nq, Nk, D, H;
   int causal;
   float scale;
+  // Query heads per key/value head (0 or 1: one each): W_K, W_V, b_K, b_V hold
+  // H / kv_group heads and head h uses head h / kv_group of them.
+  int kv_group;
 };
 
 // Launchers return hipSuccess or the launch error; they validate nothing

@@ -87,10 +87,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   // ---- Projection phase: C^T[f][t] = sum_k W[f][k] x[t][k].
   const __amdgpu_buffer_rsrc_t xqsrc = make_rsrc(a.xq, (int64_t)a.B * Nq * D * 2);
   const __amdgpu_buffer_rsrc_t xkvsrc = make_rsrc(a.xkv, (int64_t)a.B * Nk * D * 2);
-  const int64_t hoff = (int64_t)h * kD * D;
+  // Head h projects K and V with the rows of its key/value head (shared by
+  // kv_group consecutive query heads; recomputed by each of them).
+  const int kvh = a.kv_group > 1 ? h / a.kv_group : h;
+  const int64_t hoff = (int64_t)h * kD * D, kvoff = (int64_t)kvh * kD * D;
   const __amdgpu_buffer_rsrc_t wsrc0 = make_rsrc(static_cast<const uint16_t*>(a.wq) + hoff, (int64_t)kD * D * 2);
-  const __amdgpu_buffer_rsrc_t wsrc1 = make_rsrc(static_cast<const uint16_t*>(a.wk) + hoff, (int64_t)kD * D * 2);
-  const __amdgpu_buffer_rsrc_t wsrc2 = make_rsrc(static_cast<const uint16_t*>(a.wv) + hoff, (int64_t)kD * D * 2);
+  const __amdgpu_buffer_rsrc_t wsrc1 = make_rsrc(static_cast<const uint16_t*>(a.wk) + kvoff, (int64_t)kD * D * 2);
+  const __amdgpu_buffer_rsrc_t wsrc2 = make_rsrc(static_cast<const uint16_t*>(a.wv) + kvoff, (int64_t)kD * D * 2);
 
   // Load i of this wave fills 1 KiB chunk c = wave + NW*i of a stage: rows
   // 8c .. 8c+7, lane l at row 8c + l/8, slot l%8, which holds global chunk
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
         float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias[mat]) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bb[e] = Op::to_float(bias[mat][h * kD + f0 + e]);
+          for (int e = 0; e < 4; ++e) bb[e] = Op::to_float(bias[mat][(mat == 0 ? h : kvh) * kD + f0 + e]);
         }
         u32x2_t v = {0u, 0u};
         if (valid) {

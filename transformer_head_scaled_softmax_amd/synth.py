@@ -103,6 +103,9 @@ WORKLOADS = {
         Workload("base_decoder_causal_bwd", 64, 8, 64, 64, 64, "bf16", MASK_CAUSAL, (10, 64), False, False, 3,
                  "backward pass of Transformer-base decoder masked self-attention with key padding "
                  "(B=64, n=64, h=8, d=64, lengths U{10..64}, output gradient N(0,1))", backward=True),
+        Workload("base_encoder_proj_gqa", 64, 8, 64, 64, 64, "bf16", MASK_NONE, (10, 64), True, False, 8,
+                 "Transformer-base encoder self-attention with grouped-query projections (B=64, n=64, "
+                 "d_model=512, 8 query heads over 2 key/value heads, d=64, lengths U{10..64})", Hkv=2),
         Workload("long_causal_gqa_bwd", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 6,
                  "backward pass of long-context causal self-attention with grouped-query attention "
                  "(B=2, n=8192, h=16 query heads over 4 key/value heads, d=64, output gradient N(0,1))",
@@ -171,17 +174,18 @@ def train_inputs(B, H, Nq, Nk, dk, dv, dtype, seed, lens=None, Hkv=None):
     return {"q": q, "k": k, "v": v, "dout": dout, "key_lens": key_lens}
 
 
-def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None, ln=False):
+def proj_inputs(B, Nq, Nk, D, H, dk, dv, dtype, seed, cross, lens=None, ln=False, Hkv=None):
     """x_q [B,Nq,D] (and x_kv [B,Nk,D] when ``cross``) ~ N(0,1); Xavier-uniform
     W_Q, W_K [H*dk, D], W_V [H*dv, D], W_O [D, H*dv]; key_lens from ``lens``;
     with ``ln`` the norm's scale ~ U(0.5, 1.5) and shift ~ N(0, 0.5^2), drawn
-    last."""
+    last.  ``Hkv``: W_K and W_V have Hkv*d rows (shared key/value heads)."""
     g = generator(seed)
+    Hkv = H if Hkv is None else Hkv
     x_q = normal(g, (B, Nq, D), dtype)
     x_kv = normal(g, (B, Nk, D), dtype) if cross else None
     W_Q = xavier_uniform(g, H * dk, D, dtype)
-    W_K = xavier_uniform(g, H * dk, D, dtype)
-    W_V = xavier_uniform(g, H * dv, D, dtype)
+    W_K = xavier_uniform(g, Hkv * dk, D, dtype)
+    W_V = xavier_uniform(g, Hkv * dv, D, dtype)
     W_O = xavier_uniform(g, D, H * dv, dtype)
     key_lens = key_lengths(g, B, *lens) if lens is not None else None
     out = {"x_q": x_q, "x_kv": x_kv, "W_Q": W_Q, "W_K": W_K, "W_V": W_V, "W_O": W_O, "key_lens": key_lens}
@@ -208,7 +212,7 @@ def workload_inputs(w: Workload, seed: int | None = None):
     if w.decode:
         return decode_inputs(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
     if w.proj:
-        return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens, w.ln)
+        return proj_inputs(w.B, w.Nq, w.Nk, w.D, w.H, w.d, w.d, w.dtype, seed, w.cross, w.lens, w.ln, Hkv=w.Hkv)
     if w.backward:
         return train_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens, Hkv=w.Hkv)
     return core_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.dtype, seed, w.lens)
