@@ -270,3 +270,24 @@ def test_gqa_training_step_graph_replays_match_eager():
         for t, w in zip((out, lse, dq, dk, dv), want):
             assert torch.equal(t, w)
         del noise
+
+
+def test_gqa_one_sided_problems():
+    """Shared heads with no queries (every shared key gets zero gradient) and with
+    no keys (zero output, lse -inf, zero query gradient)."""
+    B, H, Hkv = 2, 6, 2
+    k = to_dev(synth.train_inputs(B, H, 4, 70, 64, 64, "bf16", 48, Hkv=Hkv)["k"], "bf16")
+    q0 = torch.empty(B, H, 0, 64, device="cuda", dtype=torch.bfloat16)
+    lse0 = torch.empty(B, H, 0, device="cuda", dtype=torch.float32)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    mha.backward(q0, k, k, q0, q0, lse0, dk=dk, dv=dv)
+    inp = synth.train_inputs(B, H, 45, 1, 64, 64, "bf16", 49, Hkv=Hkv)
+    q, dout = to_dev(inp["q"], "bf16"), to_dev(inp["dout"], "bf16")
+    k0 = torch.empty(B, Hkv, 0, 64, device="cuda", dtype=torch.bfloat16)
+    out, lse = mha.forward_lse(q, k0, k0)
+    dq = torch.full_like(q, 7.0)
+    mha.backward(q, k0, k0, out, dout, lse, dq=dq)
+    torch.cuda.synchronize()
+    assert not torch.any(dk) and not torch.any(dv) and not torch.any(dq) and not torch.any(out)
+    assert bool(torch.all(torch.isneginf(lse)))
