@@ -76,6 +76,9 @@ WORKLOADS = {
         Workload("base_encoder_proj", 64, 8, 64, 64, 64, "bf16", MASK_NONE, (10, 64), True, False, 2,
                  "Transformer-base encoder self-attention with projections and key padding "
                  "(B=64, n=64, d_model=512, h=8, lengths U{10..64})"),
+        Workload("base_encoder_proj_b384", 384, 8, 64, 64, 64, "bf16", MASK_NONE, (10, 64), True, False, 12,
+                 "the base encoder layer at about the pages' batch of 25k tokens (B=384, n=64, d_model=512, "
+                 "h=8, lengths U{10..64})"),
         Workload("base_decoder_causal", 64, 8, 64, 64, 64, "bf16", MASK_CAUSAL, (10, 64), False, False, 3,
                  "Transformer-base decoder masked self-attention with key padding "
                  "(B=64, n=64, h=8, d=64, lengths U{10..64})"),
