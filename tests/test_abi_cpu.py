@@ -613,3 +613,12 @@ def test_proj_gqa_workspace(lib):
     assert proj_gqa(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
     assert proj_gqa(lib, d_k=32, d_v=32) == mb.ERR_UNSUPPORTED
     assert proj_gqa(lib, B=0) == mb.OK
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with a message and status 2
+    before touching a device."""
+    res = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                         timeout=300, cwd=str(ROOT))
+    assert res.returncode == 2, res.stderr
+    assert "one GPU" in res.stdout
