@@ -48,12 +48,14 @@ KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip", "mfma_util.h"],
                   "out_projection": ["gemm_mfma.hip", "mfma_util.h"], "attention_f32": ["attn_f32.hip"],
                   "decode": ["decode_mfma.hip", "mfma_util.h"], "decode_combine": ["decode_mfma.hip", "mfma_util.h"],
                   "out_projection_ln": ["gemm_mfma.hip", "mfma_util.h"], "ln_rows": ["gemm_mfma.hip", "mfma_util.h"],
-                  "bwd_dq": ["bwd_mfma.hip", "mfma_util.h"], "bwd_dkdv": ["bwd_mfma.hip", "mfma_util.h"]}
+                  "bwd_dq": ["bwd_mfma.hip", "mfma_util.h"], "bwd_dkdv": ["bwd_mfma.hip", "mfma_util.h"],
+                  "bwd_fused": ["bwd_mfma.hip", "mfma_util.h"]}
 KERNEL_SYMBOLS = {"qkv_projection": "gemm_mfma_kernel", "attention": "attn_mfma_kernel",
                   "qkv_attention": "proj_attn_kernel", "out_projection": "gemm_mfma_kernel",
                   "attention_f32": "attn_f32_kernel", "decode": "decode_mfma_kernel",
                   "decode_combine": "decode_combine_kernel", "out_projection_ln": "gemm_mfma_kernel",
-                  "ln_rows": "ln_rows_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel"}
+                  "ln_rows": "ln_rows_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                  "bwd_fused": "bwd_short_kernel"}
 
 
 def log(*a):
@@ -120,7 +122,8 @@ def backward_work(w, lens):
     dK/dV kernel S, dP, dV and dK (8d).  Bytes: the dQ kernel reads q, dout,
     out, lse and the visible rows of k and v and writes dq and D; the dK/dV
     kernel reads k, v (visible rows), q, dout, lse and D and writes dk, dv.
-    Shared key/value heads count once."""
+    Shared key/value heads count once.  The single-launch kernel of short
+    problems does both parts' products (14d) and keeps D on chip."""
     es = ES[w.dtype]
     pairs = visible_counts(w, lens)
     Ls = np.full(w.B, w.Nk) if lens is None else np.clip(lens, 0, w.Nk)
@@ -131,7 +134,9 @@ def backward_work(w, lens):
     lb = 0 if lens is None else 4 * w.B
     dq = (6.0 * w.d * pairs, 3 * qrow + stat + kvis + qrow + stat + lb)
     dkdv = (8.0 * w.d * pairs, kvis + 2 * qrow + 2 * stat + 2 * krow + lb)
-    return {"bwd_dq": dq, "bwd_dkdv": dkdv}, 10.0 * w.d * pairs
+    # one launch for both parts (sentence-length problems): D stays on chip
+    fused = (14.0 * w.d * pairs, 3 * qrow + stat + kvis + qrow + 2 * krow + lb)
+    return {"bwd_dq": dq, "bwd_dkdv": dkdv, "bwd_fused": fused}, 10.0 * w.d * pairs
 
 
 def projection_flops(w):
@@ -471,7 +476,10 @@ def main():
                 st = lib.mha_backward(*argsv) if events is None else lib.mha_backward_timed(*argsv, events)
             if st != 0:
                 raise RuntimeError(lib.mha_last_error().decode())
-        stage_events = {"bwd_dq": (0, 1), "bwd_dkdv": (2, 3)}
+        if lib.mha_backward_single_launch(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, code):
+            stage_events = {"bwd_fused": (0, 1)}
+        else:
+            stage_events = {"bwd_dq": (0, 1), "bwd_dkdv": (2, 3)}
         n_events = 4
     else:
         def step(i, sp, events=None):

@@ -267,13 +267,24 @@ int mha_forward_lse(const void* q, const void* k, const void* v, void* out, floa
  */
 size_t mha_backward_workspace_bytes(int B, int H, int Nq, int Nk, int d_k, int d_v, int dtype);
 
+/*
+ * mha_backward_single_launch -- 1 when a backward call with these sizes
+ * (bf16/f16, d_k == d_v == 64, at most 64 queries and 64 keys, H_kv == H) runs
+ * as one kernel, whose workgroup per (b, h) forms dq and then, from D kept in
+ * LDS, dk and dv; 0 otherwise (two kernels).  A pure function of the sizes;
+ * both plans give the same results bit for bit.
+ */
+int mha_backward_single_launch(int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v, int dtype);
+
 int mha_backward(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k, int d_v, int mask_kind,
                  const int32_t* key_lens, float scale, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream);
 
 /* mha_backward_timed -- as mha_backward, plus 4 events (see the timed variants
- * above): events[0..1] time the dq kernel, events[2..3] the dk/dv kernel. */
+ * above): events[0..1] time the dq kernel, events[2..3] the dk/dv kernel; when
+ * mha_backward_single_launch is 1 for the sizes, events[0..1] time the one
+ * kernel and events[2..3] are left untouched. */
 int mha_backward_timed(const void* q, const void* k, const void* v, const void* out, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d_k,
                        int d_v, int mask_kind, const int32_t* key_lens, float scale, int dtype, void* workspace,

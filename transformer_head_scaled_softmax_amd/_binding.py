@@ -30,7 +30,8 @@ EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_
            "mha_decode_forward_timed", "mha_decode_split", "mha_forward_lse", "mha_forward_strided",
            "mha_forward_gqa", "mha_backward_workspace_bytes", "mha_backward", "mha_backward_timed",
            "mha_backward_gqa", "mha_backward_gqa_timed", "mha_backward_gqa_workspace_bytes", "mha_proj_forward_gqa",
-           "mha_proj_forward_gqa_timed", "mha_proj_gqa_workspace_bytes", "mha_status_string", "mha_last_error", "mha_version")
+           "mha_proj_forward_gqa_timed", "mha_proj_gqa_workspace_bytes", "mha_backward_single_launch",
+           "mha_status_string", "mha_last_error", "mha_version")
 
 
 class MhaError(RuntimeError):
@@ -99,6 +100,8 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_backward_gqa_workspace_bytes.restype = ctypes.c_size_t
     lib.mha_proj_gqa_workspace_bytes.argtypes = [i] * 9
     lib.mha_proj_gqa_workspace_bytes.restype = ctypes.c_size_t
+    lib.mha_backward_single_launch.argtypes = [i] * 8
+    lib.mha_backward_single_launch.restype = i
     lib.mha_proj_forward_gqa.argtypes = [vp] * 11 + [i] * 9 + [vp, f, i, vp, ctypes.c_size_t, vp]
     lib.mha_proj_forward_gqa.restype = i
     lib.mha_proj_forward_gqa_timed.argtypes = lib.mha_proj_forward_gqa.argtypes + [vp]

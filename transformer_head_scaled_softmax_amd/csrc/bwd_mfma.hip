@@ -139,8 +139,8 @@ __device__ inline void store_rows(const f32x16_t (&acc)[2], float mul, uint16_t*
 // Per 64-key tile a wave computes S^T = K Q^T and dP^T = V dO^T (keys x
 // queries, so each lane holds one query's scores), P^T and dS^T, then
 // dQ^T += K^T dS^T with K^T read transposed from the same LDS tile.
-template <class Op, int NW>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArgs a, int nqb) {
+template <class Op, int NW, bool FUSED>
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int nqb, int block, float* dsh) {
   constexpr int NT = NW * 64;
   constexpr int QB = NW * 32;
   constexpr int CH = (kBT * 8) / NT;  // 16-byte chunks of K (and of V) per thread per tile
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArg
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // longest first under the causal mask
+  const int bh = block % BH;
+  const int qb = nqb - 1 - (int)(block / BH);  // longest first under the causal mask
   const int b = bh / a.H;
 
   int L = a.Nk;
@@ -196,7 +196,12 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArg
   float lse2 = INFINITY;
   if (qvalid) {
     lse2 = lse_to_log2(a.lse[(int64_t)bh * a.Nq + qi]);
-    if (half == 0) a.dsum[(int64_t)bh * a.Nq + qi] = Dq;
+    if (half == 0) {
+      if (FUSED)
+        dsh[qi - q0] = Dq;  // for the dK/dV part of the same workgroup
+      else
+        a.dsum[(int64_t)bh * a.Nq + qi] = Dq;
+    }
   }
   const float c2 = a.scale * kLog2e;
 
@@ -302,6 +307,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArg
   store_rows<Op>(dq, a.scale, stage, static_cast<uint16_t*>(a.dq) + qhead, qw0, a.Nq, lane);
 }
 
+template <class Op, int NW>
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArgs a, int nqb) {
+  bwd_dq_body<Op, NW, false>(a, nqb, blockIdx.x, nullptr);
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV: a workgroup owns 32*NW keys of one (b, key/value head), one wave
 // per 32 keys, for one run of query heads.
@@ -309,8 +319,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dq_kernel(BwdArg
 // sub-block a wave computes S = Q K^T and dP = dO V^T (queries x keys, so each
 // lane holds one key's column), P and dS, then dV^T += dO^T P and
 // dK^T += Q^T dS with dO^T and Q^T read transposed from the same tiles.
-template <class Op, int NW>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
+template <class Op, int NW, bool FUSED>
+__device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& a, int nkb, int block, const float* dsh) {
   constexpr int NT = NW * 64;
   constexpr int KB = NW * 32;
   constexpr int CH = (kBT * 8) / NT;  // 16-byte chunks of Q (and of dO) per thread per tile
@@ -325,8 +335,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
   // of the run, which share the key/value head, are streamed one after the
   // other.
   const int BHkv = a.B * a.Hkv, G = a.H / a.Hkv, GP = G / a.parts;
-  const int unit = blockIdx.x % (BHkv * a.parts);
-  const int kb = (int)(blockIdx.x / (BHkv * a.parts));  // low key blocks first: under the causal mask they see most queries
+  const int unit = block % (BHkv * a.parts);
+  const int kb = (int)(block / (BHkv * a.parts));  // low key blocks first: under the causal mask they see most queries
   const int bkv = unit % BHkv, run = unit / BHkv;
   const int b = bkv / a.Hkv, kvh = bkv % a.Hkv;
 
@@ -390,7 +400,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
       qreg[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, goff[c] + t * (kBT * kD * 2), 0, 0);
       oreg[c] = __builtin_amdgcn_raw_buffer_load_b128(dosrc, goff[c] + t * (kBT * kD * 2), 0, 0);
     }
-    if (skind < 2)
+    if (FUSED && skind == 1)
+      sreg = t * kBT + srow < a.Nq ? dsh[t * kBT + srow] : 0.0f;  // D from this workgroup's dQ part
+    else if (skind < 2)
       sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                            skind ? ssrc_of(a.dsum, bhq) : ssrc_of(a.lse, bhq), (t * kBT + srow) * 4, 0, 0));
   };
@@ -531,6 +543,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdA
   store_rows<Op>(dk, a.scale, stage, static_cast<uint16_t*>(a.dk) + khead, kw0, a.Nk, lane);
 }
 
+template <class Op, int NW>
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, int nkb) {
+  bwd_dkdv_body<Op, NW, false>(a, nkb, blockIdx.x, nullptr);
+}
+
+// Sentence-length problems (at most 64 queries and 64 keys per head, one
+// key/value head per query head): both parts in one launch, one workgroup per
+// (b, h) -- the dQ part, then, after a barrier, the dK/dV part, which takes D
+// from LDS (written by the dQ part of the same workgroup) rather than from the
+// workspace.  Same arithmetic as the two kernels, one launch fewer.
+template <class Op>
+__global__ __launch_bounds__(128, 2) void bwd_short_kernel(BwdArgs a) {
+  __shared__ float dsh[kBT];
+  bwd_dq_body<Op, 2, true>(a, 1, blockIdx.x, dsh);
+  __syncthreads();
+  bwd_dkdv_body<Op, 2, true>(a, 1, blockIdx.x, dsh);
+}
+
 // dK, dV of shared key/value heads from the runs' fp32 sums: element by
 // element, runs added in order (deterministic), dK scaled, rounded once.  One
 // thread per 8 features of a row of dK or dV.
@@ -589,6 +619,12 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream, hipEvent_t t0, hipE
 template <class Op>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t const* ev) {
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
+  if (bwd_single_launch(a.H, a.Hkv, a.Nq, a.Nk)) {
+    const int64_t blocks = (int64_t)a.B * a.H;
+    if (blocks == 0) return hipSuccess;
+    hipExtLaunchKernelGGL(bwd_short_kernel<Op>, dim3((unsigned)blocks), dim3(128), 0, stream, evt(0), evt(1), 0, a);
+    return hipGetLastError();
+  }
   // The dQ kernel writes D, which the dK/dV kernel reads: stream order.
   // Long sequences: eight waves per dQ workgroup (256 queries share each K/V
   // tile; 397 vs 407 us at n = 8192), four per dK/dV workgroup (eight were 1%

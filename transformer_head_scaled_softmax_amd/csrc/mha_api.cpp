@@ -650,6 +650,12 @@ size_t mha_backward_workspace_bytes(int B, int H, int Nq, int Nk, int d_k, int d
   return backward_workspace(B, H, H, Nq, Nk, dtype);
 }
 
+int mha_backward_single_launch(int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v, int dtype) {
+  if (B < 1 || H < 1 || d_k != mha::kMfmaHeadDim || d_v != mha::kMfmaHeadDim) return 0;
+  if (dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  return mha::bwd_single_launch(H, H_kv, Nq, Nk) ? 1 : 0;
+}
+
 size_t mha_backward_gqa_workspace_bytes(int B, int H, int H_kv, int Nq, int Nk, int d_k, int d_v, int dtype) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d_k < 1 || d_v < 1) return 0;
   if (dtype != MHA_F32 && dtype != MHA_BF16 && dtype != MHA_F16) return 0;

@@ -79,6 +79,12 @@ struct BwdArgs {
 // lengths differ by the causal mask.  A pure function of the sizes, so the
 // workspace query and the launch agree.
 constexpr int kBwdMinBlocks = 2048;
+// Whether the bf16/f16 backward pass runs as one launch (both parts in one
+// workgroup per (b, h)): at most 64 queries and 64 keys, one key/value head
+// per query head.
+inline bool bwd_single_launch(int H, int Hkv, int Nq, int Nk) {
+  return Hkv == H && Nq >= 1 && Nk >= 1 && Nq <= 64 && Nk <= 64;
+}
 inline int bwd_dkdv_keys_per_block(int Nk) { return Nk > 64 ? 128 : 64; }
 inline int bwd_head_parts(int B, int H, int Hkv, int Nk) {
   if (B <= 0 || H <= 0 || Hkv <= 0 || Nk <= 0 || H % Hkv) return 1;
@@ -194,7 +200,8 @@ hipError_t launch_gemm_ln(const GemmProblem& p, DType dt, hipStream_t stream, hi
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
 // Backward pass (bf16/f16, head size 64): the dQ kernel (events ev[0..1]),
-// then the dK/dV kernel (ev[2..3]); ev may be nullptr.
+// then the dK/dV kernel (ev[2..3]); or, when bwd_single_launch, one kernel
+// (ev[0..1]); ev may be nullptr.
 hipError_t launch_bwd_mfma(const BwdArgs& a, DType dt, hipStream_t stream, hipEvent_t const* ev);
 // The same for fp32 with head sizes dk, dv <= kF32MaxHeadDim (vector ALUs).
 hipError_t launch_bwd_f32(const BwdArgs& a, int dk, int dv, hipStream_t stream, hipEvent_t const* ev);
