@@ -622,3 +622,15 @@ def test_bench_refuses_more_than_one_gpu():
                          timeout=300, cwd=str(ROOT))
     assert res.returncode == 2, res.stderr
     assert "one GPU" in res.stdout
+
+
+def test_backward_single_launch_rule(lib):
+    """One launch for bf16/f16 problems of at most 64 queries and 64 keys with one
+    key/value head per query head; two kernels otherwise."""
+    assert lib.mha_backward_single_launch(64, 8, 8, 64, 64, 64, 64, mb.BF16) == 1
+    assert lib.mha_backward_single_launch(2, 3, 3, 1, 64, 64, 64, mb.F16) == 1
+    assert lib.mha_backward_single_launch(64, 8, 8, 65, 64, 64, 64, mb.BF16) == 0
+    assert lib.mha_backward_single_launch(64, 8, 8, 64, 65, 64, 64, mb.BF16) == 0
+    assert lib.mha_backward_single_launch(64, 8, 2, 64, 64, 64, 64, mb.BF16) == 0  # shared heads
+    assert lib.mha_backward_single_launch(64, 8, 8, 0, 64, 64, 64, mb.BF16) == 0
+    assert lib.mha_backward_single_launch(64, 8, 8, 64, 64, 64, 64, mb.F32) == 0

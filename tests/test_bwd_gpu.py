@@ -243,17 +243,18 @@ def test_long_causal_bwd_full_size():
         print(f"slice ({b},{h}) error/bound dq {r[0]:.3f} dk {r[1]:.3f} dv {r[2]:.3f}", flush=True)
 
 
-def test_training_step_graph_replays_match_eager():
+@pytest.mark.parametrize("N", [300, 64])  # two backward kernels; the single launch
+def test_training_step_graph_replays_match_eager(N):
     """The forward with its row statistic and the backward pass captured in one HIP
     graph: every replay, with eager work and synchronisations in between,
     reproduces the eager results bit for bit."""
-    inp = synth.train_inputs(2, 4, 300, 300, 64, 64, "bf16", 19, (100, 300))
+    inp = synth.train_inputs(2, 4, N, N, 64, 64, "bf16", 19, (N // 3, N))
     q, k, v, dout = (to_dev(inp[n], "bf16") for n in ("q", "k", "v", "dout"))
     lens = lens_dev(inp["key_lens"])
     out = torch.empty_like(q)
-    lse = torch.empty((2, 4, 300), dtype=torch.float32, device="cuda")
+    lse = torch.empty((2, 4, N), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(mha.backward_workspace_bytes(2, 4, 300, 300, 64, 64), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mha.backward_workspace_bytes(2, 4, N, N, 64, 64), dtype=torch.uint8, device="cuda")
 
     def run():
         mha.forward_lse(q, k, v, mask_kind=CAUSAL, key_lens=lens, out=out, lse=lse)
