@@ -4,12 +4,14 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch of synthetic input.  The
-default workload is the Transformer-base encoder self-attention with projections
-and key padding (B=64, n=64, d_model=512, h=8, lengths U{10..64}): Q/K/V
-projections, masked scaled dot-product attention per head, head concatenation and
-the output projection, via mha_proj_forward.  Inputs are seeded N(0,1) / Xavier
-draws, resident in HBM before timing; each step reads the next of several
-rotating input sets so that caches cannot hold the batch between steps.
+default workload is the long-context causal self-attention where the n^2 term
+dominates (B=2, n=8192, h=16, d=64, bf16, via mha_forward) -- the largest of the
+five configurations that fit one GPU.  The same run also times the other four
+(tiny fp32 encoder, base encoder with projections, base decoder with causal
+mask, big cross-attention with projections) on the GPU only and reports them
+under "configs".  Inputs are seeded N(0,1) / Xavier draws, resident in HBM
+before timing; each step reads the next of several rotating input sets so that
+caches cannot hold the batch between steps.
 
 The training workloads (``--workload *_bwd``) time the backward pass instead:
 dq, dk, dv from resident q, k, v, the forward output, its row statistic and an
@@ -18,7 +20,8 @@ heads are shared).
 
 Prints one JSON line: whole-job throughput (algorithmic TFLOP/s), tokens/s, the
 roofline of the dominant kernel (its time measured with HIP events around it on
-the launch stream) and the fp64 oracle timed on the host as a CPU baseline.
+the launch stream) and the fp64 oracle timed on the host as a CPU baseline
+(headline workload only).
 """
 from __future__ import annotations
 
@@ -41,6 +44,9 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA bf16/f
 PEAK_HBM_GBPS = 8000.0
 ES = {"bf16": 2, "f16": 2, "f32": 4}
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+# The five configurations of the benchmark; the headline is the largest that fits one GPU.
+CONFIGS = ("tiny_encoder_f32", "base_encoder_proj", "base_decoder_causal", "big_cross_proj", "long_causal")
+HEADLINE = "long_causal"
 CSRC = ROOT / "transformer_head_scaled_softmax_amd" / "csrc"
 KERNEL_SOURCES = {"qkv_projection": ["gemm_mfma.hip", "mfma_util.h"],
                   "attention": ["attn_mfma.hip", "mfma_util.h"],
@@ -241,9 +247,30 @@ def roofline(kind_flops, kind_bytes, seconds, dtype, kernel_key, workload):
             "kernel": kernel_key, "algorithmic_flops": kind_flops, "algorithmic_bytes": kind_bytes}
 
 
+def host_cpu() -> dict:
+    """The host's logical CPU count, the CPUs this process may run on, and the
+    CPU model name."""
+    import os
+    model = None
+    try:
+        for line in pathlib.Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"host_logical_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model}
+
+
 def cpu_baseline(w, inp_sets, seconds_target):
     """Time the fp64 oracle on whole batches of the same workload (long sequences:
-    sampled rows) until about ``seconds_target`` seconds of CPU work."""
+    sampled rows) until about ``seconds_target`` seconds of CPU work.  ``cores``
+    is the number of threads the oracle ran on: every CPU this process may use,
+    at most 16 (the CPU share of one GPU on the test machines)."""
     import oracle
     threads = oracle.default_threads()
     done_flops, t0, n = 0.0, time.perf_counter(), 0
@@ -302,46 +329,29 @@ def cpu_baseline(w, inp_sets, seconds_target):
         el = time.perf_counter() - t0
         if el >= seconds_target:
             break
-    return {"value": round(done_flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": f"{n} {sample} of {w.name}, fp64, {el:.1f} s",
-            "tokens_per_s": round(n * w.B * w.Nq / el, 1) if sample == "whole batches" else None}
+    rate = done_flops / el
+    res = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "sample": f"{n} {sample} of {w.name}, fp64, {el:.1f} s",
+           "tokens_per_s": round(n * w.B * w.Nq / el, 1) if sample == "whole batches" else None,
+           **host_cpu()}
+    if sample != "whole batches":
+        # the whole step at the sampled rate, labelled as an extrapolation
+        full = (backward_work(w, None)[1] if w.backward else attention_flops(w, None))
+        res["extrapolated_full_step_s"] = round(full / rate, 1)
+        res["tokens_per_s_extrapolated"] = round(w.B * w.Nq / (full / rate), 3)
+    return res
 
 
-def main():
-    from transformer_head_scaled_softmax_amd import synth
-
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="base_encoder_proj", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for >= 1 GiB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 256 MiB device copy (for HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-
+def measure(w, steps: int, warmup: int, sets: int = 0):
+    """Run ``warmup`` untimed steps of workload ``w``, then time ``steps`` steps
+    (graph replay) and the same steps through the timed entry points (per-kernel
+    dispatch times).  Returns the result line (without the CPU baseline) and the
+    host copies of the first input sets."""
     import torch
     import transformer_head_scaled_softmax_amd as mha
+    from transformer_head_scaled_softmax_amd import synth
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        n = 256 << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
-        return
-
-    w = synth.WORKLOADS[args.workload]
     lib = mha.load()
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
     es = ES[w.dtype]
@@ -359,7 +369,7 @@ def main():
         per_set = (4 * w.B * w.H * w.Nq * w.d + 4 * w.B * w.kv_heads * w.Nk * w.d) * es + 4 * w.B * w.H * w.Nq
     else:
         per_set = (2 * w.B * w.H * w.Nq * w.d + 2 * w.B * w.H * w.Nk * w.d) * es
-    nsets = args.sets or int(min(64, max(2, math.ceil((1 << 30) / per_set))))
+    nsets = sets or int(min(64, max(2, math.ceil((1 << 30) / per_set))))
     log(f"[bench] workload {w.name}: {w.description}; {nsets} rotating input sets "
         f"({per_set * nsets / 2**20:.0f} MiB)")
     host_sets, dev_sets = [], []
@@ -428,7 +438,7 @@ def main():
                 st = (lib.mha_proj_forward(*argsv) if events is None
                       else lib.mha_proj_forward_timed(*argsv, events, 0))
             if st != 0:
-                raise RuntimeError(lib.mha_last_error().decode())
+                raise RuntimeError(lib.mha_last_error_message().decode())
         # Kernel -> (start, end) event indices of mha_proj_forward_timed.
         if lib.mha_proj_fused(w.B, w.Nq, w.Nk, w.D, w.d, w.d, 0 if w.cross else 1):
             stage_events = {"qkv_attention": (0, 1), "out_projection": (4, 5)}
@@ -454,7 +464,7 @@ def main():
             st = (lib.mha_decode_forward(*argsv) if events is None
                   else lib.mha_decode_forward_timed(*argsv, events))
             if st != 0:
-                raise RuntimeError(lib.mha_last_error().decode())
+                raise RuntimeError(lib.mha_last_error_message().decode())
         stage_events = {"decode": (0, 1)}
         if nsplit > 1:
             stage_events["decode_combine"] = (2, 3)
@@ -475,7 +485,7 @@ def main():
                 argsv = ptrs + (w.B, w.H) + tail
                 st = lib.mha_backward(*argsv) if events is None else lib.mha_backward_timed(*argsv, events)
             if st != 0:
-                raise RuntimeError(lib.mha_last_error().decode())
+                raise RuntimeError(lib.mha_last_error_message().decode())
         if lib.mha_backward_single_launch(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, w.d, code):
             stage_events = {"bwd_fused": (0, 1)}
         else:
@@ -489,22 +499,22 @@ def main():
                      w.B, w.H, w.Nq, w.Nk, w.d, w.d, w.mask, lp, scale, code, sp)
             st = lib.mha_forward(*argsv) if events is None else lib.mha_forward_timed(*argsv, events)
             if st != 0:
-                raise RuntimeError(lib.mha_last_error().decode())
+                raise RuntimeError(lib.mha_last_error_message().decode())
         stage_events = {("attention_f32" if w.dtype == "f32" else "attention"): (0, 1)}
         n_events = 2
 
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     t0 = time.perf_counter()
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, sp)
     torch.cuda.synchronize()
-    host_us_per_step = (time.perf_counter() - t0) / max(1, args.warmup) * 1e6
+    host_us_per_step = (time.perf_counter() - t0) / max(1, warmup) * 1e6
 
     # Timed region 1 (the reported throughput): the K steps replayed from HIP
     # graphs, as a serving loop would issue them, so host launch overhead does
     # not stall the GPU.  One graph holds one step per input set.
-    K = args.steps
+    K = steps
     G = min(nsets, K)
     cap = torch.cuda.Stream()
 
@@ -516,7 +526,7 @@ def main():
         with torch.cuda.graph(g, stream=cap):
             csp = ctypes.c_void_p(cap.cuda_stream)
             for i in range(n):
-                step(args.warmup + i, csp)
+                step(warmup + i, csp)
         return g
 
     g_full = capture(G)
@@ -546,7 +556,7 @@ def main():
                  for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
-        step(args.warmup + i, sp, ev_arrays[i])
+        step(warmup + i, sp, ev_arrays[i])
     torch.cuda.synchronize()
     per = {n_: [] for n_ in stage_events}
     for evs in ev_arrays:
@@ -556,7 +566,7 @@ def main():
     last_end = max(b_ for _, b_ in stage_events.values())  # some events may stay unrecorded
     eager_ms_step = hip.elapsed_ms(ev_arrays[0][0], ev_arrays[-1][last_end]) / K
 
-    used = [lens_list[(args.warmup + i) % nsets] for i in range(K)]
+    used = [lens_list[(warmup + i) % nsets] for i in range(K)]
     att_f = float(np.mean([attention_flops(w, L) for L in used]))
     if w.proj:
         qkv_f, out_f = projection_flops(w)
@@ -579,7 +589,7 @@ def main():
     sec = ms_step / 1e3
     result = {
         "metric": METRIC, "value": round(flops / sec / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "steps": K, "warmup": warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) activations, Xavier-uniform weights, uniform key lengths)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d_k": w.d,
@@ -619,15 +629,70 @@ def main():
         f_, b_ = flops, bytes_
     result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom, w.name)
 
+    return result, host_sets
+
+
+def main():
+    from transformer_head_scaled_softmax_amd import synth
+
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time only --workload (by default a run of one of the five configurations also "
+                         "times the other four, GPU only)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import transformer_head_scaled_softmax_amd as mha
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    result, host_sets = measure(w, args.steps, args.warmup, args.sets)
     if not args.no_cpu_baseline:
-        log(f"[bench] GPU done: {ms_step * 1e3:.2f} us/step; timing the fp64 oracle "
+        log(f"[bench] GPU done: {result['ms_per_step'] * 1e3:.2f} us/step; timing the fp64 oracle "
             f"for ~{args.cpu_seconds:.0f} s")
         result["cpu_baseline"] = cpu_baseline(w, [h for h in host_sets if "x_q" in h or "q" in h],
                                               args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    del host_sets
+    if not args.no_other_configs and w.name in CONFIGS:
+        # The other configurations, GPU only, same step definition and timing.
+        others = {}
+        for name in CONFIGS:
+            if name == w.name:
+                continue
+            torch.cuda.empty_cache()
+            r, _ = measure(synth.WORKLOADS[name], args.steps, min(args.warmup, 20), 0)
+            others[name] = {k: r[k] for k in ("ms_per_step", "value", "unit", "tokens_per_s",
+                                              "hbm_gbps_algorithmic", "dtype", "kernel_ms")}
+            others[name]["roofline"] = {k: r["roofline"][k] for k in ("kernel", "bound", "achieved", "peak",
+                                                                       "unit", "frac")}
+        result["configs"] = others
     print(json.dumps(result), flush=True)
-
 
 if __name__ == "__main__":
     main()

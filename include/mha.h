@@ -35,7 +35,7 @@
  *     stream).  Argument errors are detected on the host before any HIP call
  *     and return a negative status with nothing launched; launch failures
  *     return MHA_ERR_HIP.  Faults inside kernels surface at the caller's next
- *     synchronisation.  mha_last_error() gives a message for the last failure
+ *     synchronisation.  mha_last_error_message() gives a message for the last failure
  *     on the calling thread.
  *   - Entry points keep no state between calls and may be called from several
  *     threads at once.
@@ -466,8 +466,13 @@ int mha_decode_split(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v, in
 /* Static description of a status code; never NULL. */
 const char* mha_status_string(int status);
 
-/* Message for the last failed call on the calling thread ("" if none);
- * valid until that thread's next call into the library. */
+/* Message for the last failed call on the calling thread ("" if none): the
+ * argument that was rejected, the workspace size that was needed, or the HIP
+ * runtime's text for MHA_ERR_HIP.  The string is thread-local and stays valid
+ * until that thread's next call into the library. */
+const char* mha_last_error_message(void);
+
+/* Same as mha_last_error_message (the name earlier versions exported). */
 const char* mha_last_error(void);
 
 /* Library ABI version (major * 10000 + minor * 100 + patch). */

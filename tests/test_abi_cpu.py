@@ -5,6 +5,7 @@ Pointers here are fake, aligned addresses that are never dereferenced: every cal
 below fails validation first.  Nothing in this file launches a kernel.
 """
 import ctypes
+import os
 import pathlib
 import re
 import subprocess
@@ -21,7 +22,9 @@ P = 0x100000  # fake, 256-byte aligned device address (never dereferenced)
 
 @pytest.fixture(scope="module")
 def lib():
-    return mb.load()
+    # MHA_TEST_LIB: another build of the same ABI (the sanitized CPU build of
+    # the host layer, tests/test_sanitize_cpu.py); default: libmha.so.
+    return mb.load(os.environ.get("MHA_TEST_LIB") or None)
 
 
 def declared_functions():
@@ -83,13 +86,15 @@ def fwd(lib, q=P, k=P, v=P, out=P, B=2, H=3, Nq=5, Nk=5, dk=64, dv=64, mask=0, l
 ])
 def test_forward_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
+    # the earlier name is an alias of the same thread-local message
+    assert lib.mha_last_error().decode() == lib.mha_last_error_message().decode()
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0), dict(B=0, q=None, out=None)])
 def test_forward_empty_problems_are_ok_without_launch(lib, kw):
     assert fwd(lib, **kw) == mb.OK
-    assert lib.mha_last_error().decode() == ""
+    assert lib.mha_last_error_message().decode() == ""
 
 
 def test_workspace_bytes(lib):
@@ -134,13 +139,13 @@ def proj(lib, x_q=P, x_kv=P, W_Q=P, W_K=P, W_V=P, W_O=P, out=P, B=2, Nq=4, Nk=6,
 ])
 def test_proj_rejects(lib, kw, status):
     assert proj(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 def test_proj_workspace_exact_size_passes_validation_check(lib):
     need = lib.mha_proj_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
     assert proj(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
-    assert "needed" in lib.mha_last_error().decode()
+    assert "needed" in lib.mha_last_error_message().decode()
 
 
 def test_proj_empty_is_ok(lib):
@@ -178,13 +183,13 @@ def test_last_error_is_per_thread(lib):
     seen = {}
 
     def other():
-        seen["msg"] = lib.mha_last_error().decode()
+        seen["msg"] = lib.mha_last_error_message().decode()
 
     t = threading.Thread(target=other)
     t.start()
     t.join()
     assert seen["msg"] == ""
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 _NO_DEVICE_SCRIPT = r"""
@@ -199,7 +204,7 @@ from transformer_head_scaled_softmax_amd import _binding as mb
 lib = mb.load()
 P = 0x100000
 st = lib.mha_forward(P, P, P, P, 1, 1, 4, 4, 64, 64, 0, None, 0.125, mb.BF16, None)
-print("STATUS", st, lib.mha_last_error().decode())
+print("STATUS", st, lib.mha_last_error_message().decode())
 """
 
 
@@ -249,7 +254,7 @@ def dec(lib, q=P, k=P, v=P, out=P, B=2, H=4, Hkv=2, Nq=1, S=300, dk=64, dv=64, m
 ])
 def test_decode_rejects(lib, kw, status):
     assert dec(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 def test_decode_workspace_checked(lib):
@@ -258,13 +263,13 @@ def test_decode_workspace_checked(lib):
     assert dec(lib, ws=None) == mb.ERR_WORKSPACE
     assert dec(lib, ws=P + 16) == mb.ERR_WORKSPACE
     assert dec(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
-    assert "needed" in lib.mha_last_error().decode()
+    assert "needed" in lib.mha_last_error_message().decode()
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(B=0, q=None, out=None)])
 def test_decode_empty_is_ok(lib, kw):
     assert dec(lib, **kw) == mb.OK
-    assert lib.mha_last_error().decode() == ""
+    assert lib.mha_last_error_message().decode() == ""
 
 
 @pytest.mark.parametrize("args,waves", [
@@ -322,7 +327,7 @@ def proj_ln(lib, x_q=P, x_kv=P, W=(P, P, P, P), biases=(None, None, None, None),
 ])
 def test_proj_ln_rejects(lib, kw, status):
     assert proj_ln(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 def test_proj_ln_empty_is_ok(lib):
@@ -344,7 +349,7 @@ def test_proj_ln_workspace_checked(lib):
     need = lib.mha_proj_ln_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
     assert need > lib.mha_proj_workspace_bytes(2, 4, 6, 64, 1, 64, 64, mb.BF16)
     assert proj_ln(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
-    assert "needed" in lib.mha_last_error().decode()
+    assert "needed" in lib.mha_last_error_message().decode()
 
 
 # --------------------------------------------------------------------------
@@ -364,7 +369,7 @@ def fwd_lse(lib, q=P, k=P, v=P, out=P, lse=P, B=2, H=3, Nq=5, Nk=5, dk=64, dv=64
 ])
 def test_forward_lse_rejects(lib, kw, status):
     assert fwd_lse(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 def test_forward_lse_empty_is_ok(lib):
@@ -410,7 +415,7 @@ def bwd(lib, q=P, k=P, v=P, out=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, Nq
 ])
 def test_backward_rejects(lib, kw, status):
     assert bwd(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Nq=0, Nk=0),
@@ -434,11 +439,11 @@ P = 0x100000
 # Nq == 0: no query-side tensor and no workspace (dk, dv are zeros).
 st = lib.mha_backward(None, P, P, None, None, None, None, P, P, 2, 3, 0, 7, 64, 64, 0, None, 0.125, mb.BF16,
                       None, 0, None)
-print("STATUS", st, lib.mha_last_error().decode())
+print("STATUS", st, lib.mha_last_error_message().decode())
 # Nk == 0: no key-side tensor (dq is zeros).
 st = lib.mha_backward(P, None, None, P, P, P, P, None, None, 2, 3, 5, 0, 64, 64, 0, None, 0.125, mb.BF16,
                       P, 1 << 20, None)
-print("STATUS", st, lib.mha_last_error().decode())
+print("STATUS", st, lib.mha_last_error_message().decode())
 """
 
 
@@ -465,7 +470,7 @@ def test_backward_workspace_bytes(lib):
     assert lib.mha_backward_workspace_bytes(3, 5, 7, 9, 64, 64, 9) == 0
     need = lib.mha_backward_workspace_bytes(2, 3, 5, 7, 64, 64, mb.BF16)
     assert bwd(lib, ws_bytes=need - 1) == mb.ERR_WORKSPACE
-    assert "needed" in lib.mha_last_error().decode()
+    assert "needed" in lib.mha_last_error_message().decode()
 
 
 def fwd_strided(lib, qs=(3 * 5 * 64, 5 * 64, 64), ks=(3 * 5 * 64, 5 * 64, 64), vs=(3 * 5 * 64, 5 * 64, 64),
@@ -490,7 +495,7 @@ def fwd_strided(lib, qs=(3 * 5 * 64, 5 * 64, 64), ks=(3 * 5 * 64, 5 * 64, 64), v
 ])
 def test_forward_strided_rejects(lib, kw, status):
     assert fwd_strided(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 def test_forward_strided_empty_is_ok(lib):
@@ -517,9 +522,9 @@ def bwd_gqa(lib, B=2, H=4, Hkv=2, Nq=5, Nk=7, d_k=64, d_v=64, dtype=mb.BF16, ws=
 def test_gqa_head_counts_checked(lib, Hkv):
     """H_kv must divide H (1 <= H_kv <= H)."""
     assert fwd_gqa(lib, Hkv=Hkv) == mb.ERR_INVALID_ARG
-    assert "H_kv" in lib.mha_last_error().decode()
+    assert "H_kv" in lib.mha_last_error_message().decode()
     assert bwd_gqa(lib, Hkv=Hkv) == mb.ERR_INVALID_ARG
-    assert "H_kv" in lib.mha_last_error().decode()
+    assert "H_kv" in lib.mha_last_error_message().decode()
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -530,7 +535,7 @@ def test_gqa_head_counts_checked(lib, Hkv):
 ])
 def test_forward_gqa_rejects(lib, kw, status):
     assert fwd_gqa(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -542,7 +547,7 @@ def test_forward_gqa_rejects(lib, kw, status):
 ])
 def test_backward_gqa_rejects(lib, kw, status):
     assert bwd_gqa(lib, **kw) == status
-    assert lib.mha_last_error().decode()
+    assert lib.mha_last_error_message().decode()
 
 
 def test_gqa_empty_is_ok(lib):
@@ -601,7 +606,7 @@ def proj_gqa(lib, H=4, Hkv=2, ws_bytes=1 << 24, **kw):
 @pytest.mark.parametrize("Hkv", [0, -2, 3, 8])
 def test_proj_gqa_head_counts_checked(lib, Hkv):
     assert proj_gqa(lib, Hkv=Hkv) == mb.ERR_INVALID_ARG
-    assert "H_kv" in lib.mha_last_error().decode()
+    assert "H_kv" in lib.mha_last_error_message().decode()
     assert lib.mha_proj_gqa_workspace_bytes(2, 4, 6, 64, 4, Hkv, 64, 64, mb.BF16) == 0
 
 

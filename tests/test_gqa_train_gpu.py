@@ -130,11 +130,11 @@ def test_gqa_with_one_head_per_group_is_mha_backward():
     stream = torch.cuda.current_stream().cuda_stream
     st = lib.mha_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out2), _ptr(lse2), 2, 4, 4, 150, 150, 64, 64, CAUSAL,
                              _ptr(lens), 0.125, mha.BF16, stream)
-    assert st == mb.OK, lib.mha_last_error()
+    assert st == mb.OK, lib.mha_last_error_message()
     st = lib.mha_backward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out2), _ptr(dout), _ptr(lse2), _ptr(dq2), _ptr(dk2),
                               _ptr(dv2), 2, 4, 4, 150, 150, 64, 64, CAUSAL, _ptr(lens), 0.125, mha.BF16, _ptr(ws),
                               ws.numel(), stream)
-    assert st == mb.OK, lib.mha_last_error()
+    assert st == mb.OK, lib.mha_last_error_message()
     torch.cuda.synchronize()
     for a, b in ((out, out2), (lse, lse2), (dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(a, b)

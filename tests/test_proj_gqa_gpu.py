@@ -87,6 +87,6 @@ def test_proj_gqa_with_one_head_per_group_is_proj_forward(cross):
     st = lib.mha_proj_forward_gqa(_p(d["x_q"]), _p(d["x_kv"]), _p(d["W_Q"]), _p(d["W_K"]), _p(d["W_V"]),
                                   _p(d["W_O"]), None, None, None, None, _p(out), B, N, N, D, H, H, 64, 64, NONE,
                                   _p(lens), 0.125, mb.BF16, _p(ws), need, torch.cuda.current_stream().cuda_stream)
-    assert st == mb.OK, lib.mha_last_error()
+    assert st == mb.OK, lib.mha_last_error_message()
     torch.cuda.synchronize()
     assert torch.equal(out, want)

@@ -31,7 +31,7 @@ EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_
            "mha_forward_gqa", "mha_backward_workspace_bytes", "mha_backward", "mha_backward_timed",
            "mha_backward_gqa", "mha_backward_gqa_timed", "mha_backward_gqa_workspace_bytes", "mha_proj_forward_gqa",
            "mha_proj_forward_gqa_timed", "mha_proj_gqa_workspace_bytes", "mha_backward_single_launch",
-           "mha_status_string", "mha_last_error", "mha_version")
+           "mha_status_string", "mha_last_error_message", "mha_last_error", "mha_version")
 
 
 class MhaError(RuntimeError):
@@ -108,6 +108,8 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_proj_forward_gqa_timed.restype = i
     lib.mha_status_string.argtypes = [i]
     lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_last_error_message.argtypes = []
+    lib.mha_last_error_message.restype = ctypes.c_char_p
     lib.mha_last_error.argtypes = []
     lib.mha_last_error.restype = ctypes.c_char_p
     lib.mha_version.argtypes = []
@@ -119,5 +121,5 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
 
 def check(lib: ctypes.CDLL, status: int) -> None:
     if status != OK:
-        detail = lib.mha_last_error().decode() or lib.mha_status_string(status).decode()
+        detail = lib.mha_last_error_message().decode() or lib.mha_status_string(status).decode()
         raise MhaError(status, detail)

@@ -10,6 +10,8 @@
 // under the causal mask -- "Why Masking Is Required", trishampatil.com; "Two
 // masks, not one", alexdo.xyz) get weight exactly 0 and padded rows are never
 // read.
+#include <hip/hip_ext.h>
+
 #include "mha_internal.h"
 
 namespace mha {

@@ -15,6 +15,8 @@
 // workgroup share 64-query tiles of Q, dO, lse and D): one query per lane for P
 // and dS, one feature per lane for dK and dV, summed over the query heads that
 // share the key/value head.
+#include <hip/hip_ext.h>
+
 #include "mha_internal.h"
 
 namespace mha {

@@ -7,6 +7,8 @@
 // C[m][n] lands in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "mha_internal.h"
 
 namespace mha {

@@ -87,13 +87,6 @@ LnLayout ln_layout(const ProjLayout& P, int B, int Nq, int D) {
   return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
 
 // Element strides (batch, head, row) of the four tensors of a per-head call;
 // the feature index is contiguous.
@@ -876,6 +869,8 @@ const char* mha_status_string(int status) {
     default: return "unknown status";
   }
 }
+
+const char* mha_last_error_message(void) { return g_last_error.c_str(); }
 
 const char* mha_last_error(void) { return g_last_error.c_str(); }
 

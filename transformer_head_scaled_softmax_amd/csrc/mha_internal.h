@@ -2,7 +2,6 @@
 // dispatch (mha_api.cpp) and the kernel files.  Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -210,7 +209,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream,
 // Whether launch_proj_attn handles a problem: head size 64, D a multiple of
 // 64, and self-attention with Nq == Nk <= 128 or cross-attention with
 // Nq <= 64, Nk <= 128.
-bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v);
+inline bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v) {
+  if (D < 64 || D % 64 != 0 || d_k != 64 || d_v != 64 || Nq < 1 || Nk < 1) return false;
+  return self ? (Nq == Nk && Nq <= 128) : (Nq <= 64 && Nk <= 128);
+}
 
 // Limits the launchers rely on.
 constexpr int kF32MaxHeadDim = 128;

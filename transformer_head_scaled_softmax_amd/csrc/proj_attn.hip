@@ -430,11 +430,6 @@ hipError_t launch_sized(const ProjAttnArgs& a, hipStream_t stream, hipEvent_t t0
 
 }  // namespace
 
-bool proj_attn_supported(bool self, int Nq, int Nk, int D, int d_k, int d_v) {
-  if (D < kBK || D % kBK != 0 || d_k != kD || d_v != kD || Nq < 1 || Nk < 1) return false;
-  return self ? (Nq == Nk && Nq <= 128) : (Nq <= 64 && Nk <= 128);
-}
-
 hipError_t launch_proj_attn(const ProjAttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   return dt == DType::BF16 ? launch_sized<BF16>(a, stream, t0, t1) : launch_sized<F16>(a, stream, t0, t1);
 }

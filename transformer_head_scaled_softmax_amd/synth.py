@@ -235,3 +235,37 @@ def sample_rows(B: int, H: int, N: int, seed: int, n_random: int = 64):
             for i in sorted(set(fixed) | set(int(x) for x in extra)):
                 rows.append((b, h, i))
     return np.array(rows, dtype=np.int32)
+
+
+def plant_score_outliers(q: np.ndarray, k: np.ndarray, slots, jump: float, scale: float, dtype: str,
+                         seed: int) -> None:
+    """Give later keys scores far above the earlier ones, in place.
+
+    Every query row gets a common direction: q_i += a_i * sqrt(d) * u with u a
+    seeded unit vector and a_i ~ U(0.5, 1.5), so t_i = q_i . u lies near
+    a_i * sqrt(d) (mostly in [2, 14] for d = 64).  Key slot ``slots[m]`` (of
+    every sequence and head; an index along axis 2 of k) becomes
+    beta_m * u with beta_m = sign(scale) * jump * 2^m / (2 |scale|), so a query
+    with t_i >= 2 sees the scaled score scale * q_i . k jump by at least
+    ``jump`` (natural-log units) at each planted slot, over the previous
+    planted slot and far over the unplanted keys.  The last slot is paired
+    with the slot after it, given beta + sign(scale) / (8 |scale|), so the two
+    largest scores of a row differ by about t_i / 8 and neither weight is 0 or
+    1.  The arrays are rounded to ``dtype`` again afterwards.  Input
+    construction only: nothing here evaluates attention.
+    """
+    g = generator(seed)
+    d = q.shape[-1]
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    a = g.uniform(0.5, 1.5, size=q.shape[:-1] + (1,))
+    q[...] = round_to((q + a * math.sqrt(d) * u).astype(np.float32), dtype)
+    sgn = 1.0 if scale >= 0 else -1.0
+    beta0 = jump / (2.0 * abs(scale))
+    slots = list(slots)
+    for m, j in enumerate(slots):
+        k[:, :, j, :] = round_to((sgn * beta0 * 2.0 ** m * u).astype(np.float32), dtype)
+    last = slots[-1]
+    if last + 1 < k.shape[2]:
+        beta = beta0 * 2.0 ** (len(slots) - 1) + 1.0 / (8.0 * abs(scale))
+        k[:, :, last + 1, :] = round_to((sgn * beta * u).astype(np.float32), dtype)
