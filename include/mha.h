@@ -351,9 +351,12 @@ int mha_backward_gqa_timed(const void* q, const void* k, const void* v, const vo
  * Supported: as mha_proj_forward.  The residual addition and the row
  * statistics run in the epilogue of the output projection (each output tile
  * keeps its share of every row's statistics in fp32 and the rows as fp16
- * differences from its own mean, in `out`); one more light kernel merges the
- * statistics and normalises the rows in place.  Returns MHA_OK or a negative
- * status.
+ * differences from its own mean, scaled by a power of two that keeps them
+ * inside fp16's range, in `out`); one more light kernel merges the
+ * statistics and normalises the rows in place.  Range: the statistics are
+ * fp32 sums of squares about each tile's mean, so rows whose features differ
+ * from that mean by more than ~1e18 overflow them.  Returns MHA_OK or a
+ * negative status.
  */
 int mha_proj_ln_forward(const void* x_q, const void* x_kv, const void* W_Q, const void* W_K, const void* W_V,
                         const void* W_O, const void* b_Q, const void* b_K, const void* b_V, const void* b_O,

@@ -38,14 +38,23 @@ def _norm_params(D, seed, affine=True):
 
 
 def check(B, Nq, Nk, D, H, cross, mask, dtype="bf16", seed=1, biases=False, affine=True, eps=1e-5, plan=None,
-          lens=(1, None)):
+          lens=(1, None), x_scale=1.0, b_O=None):
+    """``x_scale`` multiplies the inputs x_q, x_kv (then rounded again);
+    ``b_O`` = (mean, std) draws the output projection's bias N(mean, std^2)
+    per feature, which moves every residual row by that much."""
     lo, hi = lens
     inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed, cross, (lo, hi or (Nk if cross else Nq)))
+    if x_scale != 1.0:
+        for n in ("x_q", "x_kv"):
+            if inp[n] is not None:
+                inp[n] = synth.round_to((inp[n] * x_scale).astype(np.float32), dtype)
     g = synth.generator(seed + 1000)
     bs = {}
     if biases:
         for n, size in (("b_Q", H * 64), ("b_K", H * 64), ("b_V", H * 64), ("b_O", D)):
             bs[n] = synth.round_to((g.standard_normal(size) * 0.1).astype(np.float32), dtype)
+    if b_O is not None:
+        bs["b_O"] = synth.round_to((b_O[0] + b_O[1] * g.standard_normal(D)).astype(np.float32), dtype)
     gamma, beta = _norm_params(D, seed + 2000, affine)
     d = {n: to_dev(inp[n], dtype) for n in ("x_q", "x_kv", "W_Q", "W_K", "W_V", "W_O")}
     out = mha.proj_ln_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=H,
@@ -121,3 +130,21 @@ def test_without_scale_and_shift_and_large_eps():
     check(3, 50, 50, 512, 8, False, NONE, seed=90, affine=False)
     check(3, 50, 50, 1024, 16, False, NONE, seed=91, affine=False, eps=0.25)
     check(3, 50, 50, 512, 8, False, CAUSAL, seed=92, eps=0.25)
+
+
+@pytest.mark.parametrize("dtype,mean,std", [("bf16", 3e5, 1e5), ("bf16", -2e6, 4e5), ("f16", 2e4, 1e4)])
+@pytest.mark.parametrize("D,H", [(512, 8), (1024, 16)])
+def test_rows_of_large_spread(dtype, mean, std, D, H):
+    """Residual rows that differ from their tile means by far more than fp16's
+    largest value (bf16: ~1e5-1e6): the stored differences are scaled into
+    fp16's range, so the rows still normalise to the oracle's values."""
+    check(4, 64, 64, D, H, False, NONE, dtype=dtype, seed=D + int(std), b_O=(mean, std))
+
+
+@pytest.mark.parametrize("x_scale", [1e-5, 1e-6])
+def test_rows_of_tiny_spread(x_scale):
+    """bf16 rows whose features differ by ~1e-5-1e-6 (below fp16's normal
+    range), normalised with eps = 0 so the outputs are of unit size: the
+    differences are scaled up into fp16's normal range before they are stored."""
+    check(4, 64, 64, 512, 8, False, NONE, seed=31, x_scale=x_scale, eps=0.0)
+    check(4, 64, 80, 512, 8, True, NONE, seed=32, x_scale=x_scale, eps=0.0, affine=False)

@@ -56,9 +56,11 @@ struct TileMap {
 // two steps.  In the projection's epilogue each tile reduces its part of every
 // row -- the sum and the sum of squares about the tile's own mean, fp32, from
 // the values in registers -- and stores them, with the row values as
-// differences from the tile mean in fp16 (in place in the output rows: 2
-// bytes with 11 significant bits, so this intermediate rounding is 2^-12
-// relative to the row's spread rather than bf16's 2^-9 of its size).  A
+// differences from the tile mean in fp16, scaled by a power of two derived
+// from that sum of squares (in place in the output rows: 2 bytes with 11
+// significant bits, so this intermediate rounding is 2^-12 relative to the
+// row's spread rather than bf16's 2^-9 of its size, and the scale keeps any
+// spread inside fp16's range).  A
 // second kernel then merges each row's parts (the pairwise update of Chan,
 // Golub and LeVeque for means and centred sums of squares) and normalises the
 // row in place.  The kernel boundary is what makes every tile's stores visible
@@ -66,6 +68,21 @@ struct TileMap {
 // release (an L2 write-back) in every workgroup and an acquire (an L2
 // invalidate) in every merging one, which measured several times slower.
 //
+// The exponent k of the power of two a tile's stored differences are divided
+// by, read from the bits of their fp32 sum of squares s2 (so the epilogue and
+// the normalisation pass derive the same k from the same stored value).  With
+// e = floor(log2 s2), every difference is below sqrt(s2) < 2^(k + 14), so the
+// scaled values stay within +-2^14 (fp16's largest finite value is 65504),
+// while a typical one, sqrt(s2 / 64), stays near 2^11 -- far above fp16's
+// subnormals whatever the row's magnitude.  Clamped so that 2^k is a normal
+// fp32 value; the limit left is the fp32 sum of squares itself (differences
+// above ~1e18 overflow it).
+__device__ inline int ln_tile_exponent(float s2) {
+  const int e = (int)((__float_as_uint(s2) >> 23) & 0xffu) - 127;
+  return min(100, max(-100, ((e + 1) >> 1) - 13));
+}
+__device__ inline float ln_pow2(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
 // ln_tile_stats: register 4gq + e of acc[mb][nb] holds row wm*WM + 32mb + col
 // of the tile and column wn*WN + 32nb + 8gq + 4half + e; a row's partial sums
 // are combined over the lane halves, then over the WGN waves sharing the row
@@ -149,16 +166,21 @@ __device__ inline void ln_tile_stats(f32x16_t (&acc)[MB][NB], const GemmProblem&
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red2[wn * TM + rbase + 32 * mb] = s2[mb];
   __syncthreads();
-  if (wn == 0 && half == 0) {
-    const int stride = ln_stats_stride(N);
+  const int stride = ln_stats_stride(N);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + wm * WM + 32 * mb + col;
-      float t = 0.0f;
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + wm * WM + 32 * mb + col;
+    float t = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WGN; ++w) t += red2[w * TM + rbase + 32 * mb];
-      if (m < M) P.stats[(int64_t)m * stride + tcol] = float2{sum[mb], t};
-    }
+    for (int w = 0; w < WGN; ++w) t += red2[w * TM + rbase + 32 * mb];
+    if (wn == 0 && half == 0 && m < M) P.stats[(int64_t)m * stride + tcol] = float2{sum[mb], t};
+    // The differences leave as fp16 scaled by 2^-k (ln_tile_exponent of the
+    // stored sum of squares), which keeps them inside fp16's range.
+    const float sc = ln_pow2(-ln_tile_exponent(t));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] *= sc;
   }
 }
 
@@ -188,9 +210,11 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(GemmProblem P, int tn) {
   const uint16_t* bet = static_cast<const uint16_t*>(P.beta);
   uint16_t* row = static_cast<uint16_t*>(P.c) + m * P.ldc;
   for (int f0 = lane * 8; f0 < N; f0 += 512) {  // N is a multiple of 8: chunks are whole
-    const u32x4_t z = *reinterpret_cast<const u32x4_t*>(row + f0);  // fp16 differences from the tile mean
+    const u32x4_t z = *reinterpret_cast<const u32x4_t*>(row + f0);  // scaled fp16 differences from the tile mean
     const int jt = f0 / tn;
-    const float shift = st[jt].x / (float)min(tn, N - jt * tn) - mean;  // (stored + mean_t) - mean
+    const float2 stj = st[jt];
+    const float unscale = ln_pow2(ln_tile_exponent(stj.y));
+    const float shift = stj.x / (float)min(tn, N - jt * tn) - mean;  // (stored + mean_t) - mean
     u32x4_t gv = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
     if (gam) gv = *reinterpret_cast<const u32x4_t*>(gam + f0);
     if (bet) bv = *reinterpret_cast<const u32x4_t*>(bet + f0);
@@ -204,7 +228,7 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(GemmProblem P, int tn) {
                        bs = (uint16_t)(bv[i] >> (16 * e));
         const float gf = gam ? Op::to_float(gs) : 1.0f;
         const float bf = bet ? Op::to_float(bs) : 0.0f;
-        v[e] = fmaf((F16::to_float(zs) + shift) * rstd, gf, bf);
+        v[e] = fmaf(fmaf(F16::to_float(zs), unscale, shift) * rstd, gf, bf);
       }
       y[i] = Op::pack(v[0], v[1]);
     }
