@@ -457,6 +457,31 @@ int mha_decode_forward_timed(const void* q, const void* k_cache, const void* v_c
                              void* const* events);
 
 /*
+ * mha_decode_forward_noalloc -- mha_decode_forward without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, and harnesses that forbid hipMalloc.  The call itself
+ * allocates nothing.  The scratch the decoding kernels need (the partial
+ * softmax states and the wave spans of caches cut between workers, sized as
+ * mha_decode_workspace_bytes reports) comes from an array of 16 MiB
+ * (16777216 bytes) compiled into the library, one per GPU, held from the
+ * library's first use on that GPU until the process ends; its address is
+ * looked up once per device, on the first call with that device current.
+ * Steps whose mha_decode_workspace_bytes exceeds 16 MiB are rejected with
+ * MHA_ERR_UNSUPPORTED before anything is launched (at one new token per
+ * sequence and H_kv == H that is above ~60,000 caches; use
+ * mha_decode_forward with a workspace for those).  Nothing in the array
+ * needs to start at zero: each call writes every state it reads.  All calls
+ * on one GPU share that GPU's array, so calls that may overlap on one GPU
+ * (different streams, or different threads without ordering) race and must
+ * be serialised by the caller.  Arguments, validation, kernels and results
+ * are otherwise those of mha_decode_forward; plans without the split kernel
+ * (mha_decode_split == 0) use no scratch.
+ */
+int mha_decode_forward_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                               int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                               float scale, int dtype, void* stream);
+
+/*
  * mha_decode_split -- how mha_decode_forward runs these sizes: the number of
  * workers (one wave each) the filled cache slots are shared out over by the
  * decoding kernel (bf16/f16, d_k == d_v == 64, at most 64 query rows

@@ -22,4 +22,6 @@ hipError_t launch_decode_mfma(const DecodeArgs&, DType, hipStream_t, hipEvent_t,
   return hipErrorNoDevice;
 }
 
+hipError_t decode_scratch(void**) { return hipErrorNoDevice; }
+
 }  // namespace mha

@@ -639,3 +639,20 @@ def test_backward_single_launch_rule(lib):
     assert lib.mha_backward_single_launch(64, 8, 2, 64, 64, 64, 64, mb.BF16) == 0  # shared heads
     assert lib.mha_backward_single_launch(64, 8, 8, 0, 64, 64, 64, mb.BF16) == 0
     assert lib.mha_backward_single_launch(64, 8, 8, 64, 64, 64, 64, mb.F32) == 0
+
+
+def test_decode_noalloc_rejects_steps_above_its_scratch(lib):
+    """mha_decode_forward_noalloc takes its scratch from a 16 MiB array: a step
+    whose decoding workspace is larger is refused before anything runs (no
+    device needed), and the message names both sizes."""
+    B, H, Hkv, Nq, S = 1000, 64, 1, 1, 1  # (1000 caches + 1024 waves) x 64 rows x 272 B > 16 MiB
+    need = lib.mha_decode_workspace_bytes(B, H, Hkv, Nq, S, 64, 64, mb.BF16)
+    assert need > 16 << 20
+    st = lib.mha_decode_forward_noalloc(P, P, P, P, B, H, Hkv, Nq, S, 64, 64, mb.MASK_CAUSAL, None, 0.125,
+                                        mb.BF16, None)
+    assert st == mb.ERR_UNSUPPORTED
+    msg = lib.mha_last_error_message().decode()
+    assert str(need) in msg and str(16 << 20) in msg
+    # argument errors come first, as for mha_decode_forward
+    assert lib.mha_decode_forward_noalloc(P, P, P, P, 2, 3, 2, 1, 8, 64, 64, 0, None, 0.125, mb.BF16,
+                                          None) == mb.ERR_INVALID_ARG

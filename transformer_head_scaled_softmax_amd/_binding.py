@@ -27,7 +27,7 @@ ERR_HIP = -4
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
            "mha_proj_forward_timed", "mha_proj_fused", "mha_proj_ln_forward", "mha_proj_ln_forward_timed",
            "mha_proj_ln_workspace_bytes", "mha_decode_workspace_bytes", "mha_decode_forward",
-           "mha_decode_forward_timed", "mha_decode_split", "mha_forward_lse", "mha_forward_strided",
+           "mha_decode_forward_timed", "mha_decode_forward_noalloc", "mha_decode_split", "mha_forward_lse", "mha_forward_strided",
            "mha_forward_gqa", "mha_backward_workspace_bytes", "mha_backward", "mha_backward_timed",
            "mha_backward_gqa", "mha_backward_gqa_timed", "mha_backward_gqa_workspace_bytes", "mha_proj_forward_gqa",
            "mha_proj_forward_gqa_timed", "mha_proj_gqa_workspace_bytes", "mha_backward_single_launch",
@@ -77,6 +77,8 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_decode_forward.restype = i
     lib.mha_decode_forward_timed.argtypes = lib.mha_decode_forward.argtypes + [vp]
     lib.mha_decode_forward_timed.restype = i
+    lib.mha_decode_forward_noalloc.argtypes = [vp] * 4 + [i] * 8 + [vp, f, i, vp]
+    lib.mha_decode_forward_noalloc.restype = i
     lib.mha_decode_split.argtypes = [i] * 8
     lib.mha_decode_split.restype = i
     lib.mha_forward_lse.argtypes = [vp] * 5 + [i] * 7 + [vp, f, i, vp]

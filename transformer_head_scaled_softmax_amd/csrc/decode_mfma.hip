@@ -31,7 +31,18 @@
 // kernel that merges the pieces of each cut cache.
 //
 // MFMA 32x32x16 lane layout: see mfma_util.h.
+#include <atomic>
+#include <mutex>
+
 #include "mfma_util.h"
+
+// Device memory of mha_decode_forward_noalloc: the partial softmax states and
+// the per-cache wave spans that the allocation-free entry point would
+// otherwise take from a caller's workspace.  Every GPU the library runs on
+// holds its own copy for the life of the process.  In host code the name
+// stands for a host-side shadow, not a device address: the launch uses the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[mha::kDecodeScratchBytes];
 
 namespace mha {
 namespace {
@@ -466,7 +477,31 @@ hipError_t launch_rows(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, h
   return R <= 32 ? launch<Op, 2, 1>(a, stream, t0, t1, t2, t3) : launch<Op, 2, 2>(a, stream, t0, t1, t2, t3);
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      // Once per device, with that device current: its copy's address.
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1,
                               hipEvent_t t2, hipEvent_t t3) {

@@ -729,7 +729,7 @@ int check_decode_sizes(int B, int H, int H_kv, int Nq, int S, int d_k, int d_v) 
 int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
                         int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
                         float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                        hipEvent_t const* ev) {
+                        hipEvent_t const* ev, bool builtin_scratch = false) {
   g_last_error.clear();
   int st = check_decode_sizes(B, H, H_kv, Nq, S, d_k, d_v);
   if (st) return st;
@@ -763,6 +763,17 @@ int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache,
   if (plan.split_kernel) {
     if (int64_t(B) * H * Nq / 4 > kMaxBlocks || int64_t(B) * H_kv + plan.waves > (int64_t(1) << 31) / 64)
       return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (builtin_scratch) {
+      // mha_decode_forward_noalloc: the library's own per-device array.
+      if (plan.workspace > mha::kDecodeScratchBytes)
+        return fail(MHA_ERR_UNSUPPORTED,
+                    "this step needs %zu bytes of scratch; the built-in scratch holds %zu "
+                    "(call mha_decode_forward with a workspace)",
+                    plan.workspace, mha::kDecodeScratchBytes);
+      hipError_t e = mha::decode_scratch(&workspace);
+      if (e != hipSuccess) return hip_fail(e, "scratch address lookup");
+      workspace_bytes = mha::kDecodeScratchBytes;
+    }
     if (!workspace) return fail(MHA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.workspace);
     if (!aligned(workspace, 256)) return fail(MHA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < plan.workspace)
@@ -841,6 +852,13 @@ int mha_decode_forward(const void* q, const void* k_cache, const void* v_cache, 
                        float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_forward_impl(q, k_cache, v_cache, out, B, H, H_kv, Nq, S, d_k, d_v, mask_kind, cache_lens, scale,
                              dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mha_decode_forward_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,
+                               int H_kv, int Nq, int S, int d_k, int d_v, int mask_kind, const int32_t* cache_lens,
+                               float scale, int dtype, void* stream) {
+  return decode_forward_impl(q, k_cache, v_cache, out, B, H, H_kv, Nq, S, d_k, d_v, mask_kind, cache_lens, scale,
+                             dtype, nullptr, 0, stream, nullptr, true);
 }
 
 int mha_decode_forward_timed(const void* q, const void* k_cache, const void* v_cache, void* out, int B, int H,

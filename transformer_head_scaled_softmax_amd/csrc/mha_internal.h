@@ -225,4 +225,11 @@ constexpr int kDecodeMaxRows = 64;
 constexpr int kDecodeWaves = 256 * 4;
 constexpr int kDecodePartFloats = 68;
 
+// Built-in device memory of the decoding kernels for callers that cannot
+// allocate (mha_decode_forward_noalloc): one array of this many bytes per GPU.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+// The current device's copy of that array (its address is looked up once per
+// device); hipSuccess or the runtime's error.
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace mha
