@@ -125,7 +125,7 @@ def test_causal_square_edges(dtype, n):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("nq,nk", [(1, 1), (1, 129), (7, 64), (64, 80), (65, 63), (130, 17),
-                                   (33, 300), (200, 129), (128, 1)])
+                                   (33, 300), (17, 500), (64, 257), (200, 129), (128, 1)])
 def test_cross_shapes(dtype, nq, nk):
     g = synth.generator(2000 + nq * 7 + nk)
     lens = [nk, int(g.integers(1, nk + 1)), 0]
@@ -173,11 +173,12 @@ def test_empty_key_set_gives_zeros():
 # Masking is bit-exact.
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n,mask", [(64, NONE), (64, CAUSAL), (300, NONE), (300, CAUSAL)])
-def test_padded_slots_never_reach_the_output(dtype, n, mask):
+@pytest.mark.parametrize("nq,n,mask", [(64, 64, NONE), (64, 64, CAUSAL), (300, 300, NONE), (300, 300, CAUSAL),
+                                       (40, 200, NONE)])
+def test_padded_slots_never_reach_the_output(dtype, nq, n, mask):
     """Whatever sits in padded key/value rows j >= key_lens[b] -- huge finite values
     or NaN -- leaves every output bit unchanged."""
-    inp = synth.core_inputs(3, 2, n, n, 64, 64, dtype, seed=10 + n)
+    inp = synth.core_inputs(3, 2, nq, n, 64, 64, dtype, seed=10 + n)
     inp["key_lens"] = np.array([n, n // 2 + 3, 1], np.int32)
     clean = run_core(inp, dtype, mask)
     big = 3.0e38
@@ -191,13 +192,14 @@ def test_padded_slots_never_reach_the_output(dtype, n, mask):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_future_tokens_never_change_earlier_outputs(dtype):
-    n = 300
+@pytest.mark.parametrize("n,cuts", [(300, (0, 31, 63, 64, 130, 298)), (64, (0, 17, 31, 32, 40, 62)),
+                                    (50, (0, 31, 33, 48))])
+def test_future_tokens_never_change_earlier_outputs(dtype, n, cuts):
     inp = synth.core_inputs(2, 2, n, n, 64, 64, dtype, seed=11)
     inp["key_lens"] = None
     base = run_core(inp, dtype, CAUSAL)
     g = synth.generator(12)
-    for i0 in (0, 31, 63, 64, 130, 298):
+    for i0 in cuts:
         pert = {n_: inp[n_].copy() for n_ in ("q", "k", "v")}
         for t in pert.values():
             t[:, :, i0 + 1:] = synth.round_to(g.standard_normal(t[:, :, i0 + 1:].shape) * 30.0, dtype)

@@ -35,6 +35,8 @@
 // reference, rescale its accumulators and exponentiate the tile again.  Row
 // sums come from the packed P values with v_dot2, i.e. from exactly the
 // rounded values the P*V product multiplies.
+#include <type_traits>
+
 #include "mfma_util.h"
 
 namespace mha {
@@ -353,6 +355,295 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
   }
 }
 
+// One wave per workgroup: 32 queries of one (b, h), for query blocks of at
+// most 64 rows (sentence-length self-attention, cross-attention from short
+// query sequences).  The arithmetic is step for step that of attn_mfma_kernel
+// with one 32-query sub-block.  What differs is the memory traffic, which is
+// what bounds a wave that is alone on its SIMD for the whole of a short
+// launch: it is arranged so that a wave waits for memory once.
+//   * The queries and the first tile of keys and values are requested
+//     together with the key length, over the keys the wave can see whatever
+//     the length is (up to its last query under the causal mask, else all
+//     Nk).  Key rows past the length are masked after the products; value
+//     rows past the wave's last visible key are zeroed in the registers once
+//     the length has arrived, so whatever those rows hold never reaches the
+//     output.  Decoding against a cache is the exception: slots past the
+//     filled length are never read there, so its loads wait for the length.
+//   * K needs no LDS: each lane loads its operands of S^T = K Q^T straight
+//     from memory in the MFMA layout (features 16kk + 8half .. +7 of key
+//     32jb + col).  V goes through LDS for the transposing operand reads.
+//   * Later tiles are requested one tile ahead, bounded by the length.
+//   * The output is staged through LDS and leaves as whole 128-byte rows
+//     (rows written in 8-byte pieces from the registers take several times
+//     longer to complete).
+template <class Op>
+__global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a, int nqb) {
+  // One value tile; after the key loop it stages the output rows.
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kBN * kD];
+  static_assert(32 * kKS <= kBN * kD, "output staging exceeds the tile memory");
+  const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+
+  // Longest query blocks first: under the causal mask later blocks see more keys.
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+  const int b = bh / a.H, h = bh % a.H;
+  const int kvh = a.kv_group > 1 ? h / a.kv_group : h;
+  const int q0 = qb * 32;
+  const int qi = q0 + col;
+  const bool qvalid = qi < a.Nq;
+
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_sb + kvh * a.v_sh;
+
+  // This lane's query as the B operand of S^T = K Q^T; a negative scale is
+  // folded in by negating q (exact).
+  const float c2 = fabsf(a.scale) * kLog2e;
+  const __amdgpu_buffer_rsrc_t qsrc = make_rsrc(qbase, ((int64_t)(a.Nq - 1) * a.q_sn + kD) * 2);
+  u32x4_t qreg[4];
+  {
+    const int qoff = qvalid ? (int)(qi * a.q_sn * 2) + half * 16 : kDeadOffset;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qreg[kk] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff + kk * 32, 0, 0);
+  }
+  // Rows of the first tile requested before the length is known: those the
+  // wave may see whatever the length is.  A cache (mask anchored at its
+  // filled end) is read only below its length, which is fetched first there
+  // (scalar work only, so that every path issues the same vector loads).
+  int krows0 = a.causal ? min(a.Nk, min(q0 + 32, a.Nq)) : a.Nk;
+  if (a.causal_end) {
+    const int L0 = a.key_lens ? min(max(a.key_lens[b], 0), a.Nk) : a.Nk;
+    krows0 = a.causal ? min(L0, min(q0 + 32, a.Nq) + L0 - a.Nq) : L0;
+  }
+  __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kbase, krows0 > 0 ? ((int64_t)(krows0 - 1) * a.k_sn + kD) * 2 : 0);
+  __amdgpu_buffer_rsrc_t vsrc = make_rsrc(vbase, krows0 > 0 ? ((int64_t)(krows0 - 1) * a.v_sn + kD) * 2 : 0);
+  auto load_k = [&](int t, u32x4_t (&kop)[2][4]) {
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kop[jb][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+            ksrc, (int)(((t * kBN + jb * 32 + col) * a.k_sn + kk * 16 + half * 8) * 2), 0, 0);
+  };
+  // V through LDS: each lane moves 8 16-byte chunks of a tile (rows of 128
+  // bytes whose chunks are XOR-swizzled by bit 1 of the row, the layout of
+  // the transposing reads).  Chunk c of a lane is row lane/8 + 8c, chunk
+  // lane%8; the swizzle bit is the same for all eight.
+  const int vrow = lane >> 3, vch = lane & 7;
+  const int voff = (int)((vrow * a.v_sn + vch * 8) * 2), vstep = (int)(8 * a.v_sn * 2);
+  const int vpos = vrow * kD + ((vch ^ (((vrow >> 1) & 1) << 2)) << 3);
+  const int vtile = (int)(kBN * a.v_sn * 2);
+  u32x4_t vreg[8];
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, voff + c * vstep + t * vtile, 0, 0);
+  };
+  auto store_v = [&]() {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4_t*>(&vs[vpos + c * 8 * kD]) = vreg[c];
+  };
+
+  u32x4_t kop[2][4];
+  load_k(0, kop);
+  load_v(0);
+
+  int L = a.Nk;
+  if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
+  const int coff = a.causal_end ? L - a.Nq : 0;  // causal: query i sees keys j <= i + coff
+  const int kend = a.causal ? min(L, qi + 1 + coff) : L;                     // keys this query sees
+  const int kend_blk = a.causal ? min(L, min(q0 + 32, a.Nq) + coff) : L;     // keys the wave needs
+  const int kmin = a.causal ? min(L, q0 + 1 + coff) : L;                     // tiles below: no mask
+  const int ntiles = (max(kend_blk, 0) + kBN - 1) / kBN;
+  // From here on, loads stop at the wave's last visible key; a tile past it
+  // loads nothing (its rows are all beyond the range) and returns zeros.
+  ksrc = make_rsrc(kbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.k_sn + kD) * 2 : 0);
+  vsrc = make_rsrc(vbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.v_sn + kD) * 2 : 0);
+  // V^T operands through ds_read_b64_tr_b16 (see attn_mfma_kernel).
+  const int tr_k = (lane & 15) >> 2, tr_q = lane & 3, tr_cg = (lane >> 4) & 1;
+  const int tr_row = 4 * half + tr_k;
+  int tr_col[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int cidx = cb * 32 + 16 * tr_cg + 4 * tr_q;
+    tr_col[cb] = ((((cidx >> 3) ^ (((tr_k >> 1) & 1) << 2))) << 3) + (cidx & 7);
+  }
+  auto vread = [&](int row, int cb) -> u32x2_t {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    lds_s16x4_t* p = (lds_s16x4_t*)(const __attribute__((address_space(3))) uint16_t*)&vs[row * kD + tr_col[cb]];
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+  };
+
+  if (a.scale < 0.0f) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qreg[kk] ^= 0x80008000u;
+  }
+  // Masked keys give exp2(-inf) = 0 by themselves unless the scale is 0.
+  const bool zero_scale = c2 == 0.0f;
+
+  f32x16_t o[2];
+  float m_ref = -INFINITY, lsum = 0.0f;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
+
+  // Per tile: the scores and their softmax while the tile's values are still
+  // in flight, then the values through LDS (one buffer: a wave's LDS accesses
+  // are carried out in order, so the previous tile's reads come first) and
+  // the products with P.
+  auto tile = [&](int t, auto prefetch) {
+    constexpr bool more = decltype(prefetch)::value;
+    const int j0 = t * kBN;
+
+    // S^T = K_tile Q^T: two 32-key blocks.
+    f32x16_t s[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[jb][r] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) s[jb] = Op::mma(kop[jb][kk], qreg[kk], s[jb]);
+    }
+    // The next tile's keys land in the operand registers just consumed.
+    if constexpr (more) load_k(t + 1, kop);
+    // Register (jb, r) holds key j0 + 32jb + 8(r/4) + 4half + r%4; invisible
+    // keys -- padding, the future, and whatever the rows past the length hold
+    // -- become -inf.
+    if (j0 + kBN > kmin) {
+      const int lim = kend - j0 - 4 * half;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (jb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[jb][r] = -INFINITY;
+    }
+
+    // Softmax as in attn_mfma_kernel: P = exp2(s * c2 - m_ref) packed in the
+    // P^T operand order, row sums from the packed values in four v_dot2
+    // chains; the optimistic pass against the reference is skipped while no
+    // query of the wave has one (its first tile).
+    u32x4_t pb[4];
+    float ls = 0.0f;
+    auto exponentiate = [&](float mu, bool select_masked) {
+      float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int jb = t4 >> 1, r = (t4 & 1) * 8 + 2 * w;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[jb][r], c2, -mu));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[jb][r + 1], c2, -mu));
+          if (select_masked) {
+            p0 = s[jb][r] == -INFINITY ? 0.0f : p0;
+            p1 = s[jb][r + 1] == -INFINITY ? 0.0f : p1;
+          }
+          pb[t4][w] = Op::pack(p0, p1);
+          lp[w] = Op::sum2(pb[t4][w], lp[w]);
+        }
+      ls = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+    };
+    bool need = true;
+    if (!__all(m_ref == -INFINITY)) {
+      exponentiate(m_ref, false);
+      need = lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f;
+    }
+    if (__any(need)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+      mx = lanes_max(mx);
+      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+      const float m_new = need ? fmaxf(m_ref, mt) : m_ref;
+      const float alpha = (need && m_new != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      lsum *= alpha;
+      // Before the first tile the accumulators hold nothing to rescale.
+      if (t > 0) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+      }
+      m_ref = m_new;
+      const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+      if (zero_scale)
+        exponentiate(mu, true);
+      else
+        exponentiate(mu, false);
+    }
+    lsum += ls;
+
+    // Value rows of the first tile that were requested before the length was
+    // known and lie past the wave's last visible key become zeros.
+    if (t == 0 && kend_blk < min(krows0, kBN)) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (vrow + 8 * c >= kend_blk) vreg[c] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    store_v();
+    if constexpr (more) load_v(t + 1);
+    // V^T operands of the tile: step t4 supplies keys 16t4 + 4half + {0..3}
+    // and 16t4 + 8 + 4half + {0..3} of this lane's feature row.
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      u32x4_t vop[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const u32x2_t lo = vread(16 * t4 + tr_row, cb);
+        const u32x2_t hi = vread(16 * t4 + 8 + tr_row, cb);
+        vop[cb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) o[cb] = Op::mma(vop[cb], pb[t4], o[cb]);
+    }
+  };
+  // The steady state prefetches unconditionally and the last tile not at all,
+  // so that every path into a tile has the same loads in flight (the
+  // compiler's memory-wait counts are taken over all paths).
+  for (int t = 0; t + 1 < ntiles; ++t) tile(t, std::true_type{});
+  if (ntiles > 0) tile(ntiles - 1, std::false_type{});
+
+  // Register (cb, 4g + e) of this lane is feature 32cb + 8g + 4half + e of
+  // query qi; the rows are staged in the value tile memory (its last reads
+  // come first in LDS order) and copied out 16 bytes per lane.
+  const float ltot = lanes_sum(lsum);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (a.lse && half == 0 && qvalid)
+    a.lse[((int64_t)b * a.H + h) * a.Nq + qi] =
+        ltot > 0.0f ? (m_ref + __builtin_amdgcn_logf(ltot)) * 0.6931471805599453f : -INFINITY;
+  uint16_t* stage = vs;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2_t w;
+      w[0] = Op::pack(o[cb][4 * g + 0] * inv, o[cb][4 * g + 1] * inv);
+      w[1] = Op::pack(o[cb][4 * g + 2] * inv, o[cb][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(&stage[col * kKS + cb * 32 + g * 8 + half * 4]) = w;
+    }
+  __builtin_amdgcn_wave_barrier();
+  // Range-checked stores: rows past the last query get an offset beyond the
+  // range and are dropped, with no branch around the LDS reads.
+  uint16_t* obase = static_cast<uint16_t*>(a.out) + b * a.o_sb + h * a.o_sh;
+  const __amdgpu_buffer_rsrc_t osrc = make_rsrc(obase, ((int64_t)(a.Nq - 1) * a.o_sn + kD) * 2);
+  u32x4_t ov[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = lane + 64 * i, row = id >> 3, ch = id & 7;
+    ov[i] = *reinterpret_cast<const u32x4_t*>(&stage[row * kKS + ch * 8]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = lane + 64 * i, row = id >> 3, ch = id & 7;
+    const int q = q0 + row;
+    const int off = q < a.Nq ? (int)(q * a.o_sn * 2) + ch * 16 : kDeadOffset;
+    __builtin_amdgcn_raw_buffer_store_b128(ov[i], osrc, off, 0, 0);
+  }
+}
+
 template <class Op, int NW, int QS>
 hipError_t launch(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   constexpr int QB = NW * 32 * QS;
@@ -361,6 +652,15 @@ hipError_t launch(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent
   if (blocks == 0) return hipSuccess;
   hipExtLaunchKernelGGL((attn_mfma_kernel<Op, NW, QS>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, t0,
                         t1, 0, a, nqb);
+  return hipGetLastError();
+}
+
+template <class Op>
+hipError_t launch_short(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  const int nqb = (a.Nq + 31) / 32;
+  const int64_t blocks = (int64_t)nqb * a.H * a.B;
+  if (blocks == 0) return hipSuccess;
+  hipExtLaunchKernelGGL((attn_short_kernel<Op>), dim3((unsigned)blocks), dim3(64), 0, stream, t0, t1, 0, a, nqb);
   return hipGetLastError();
 }
 
@@ -374,8 +674,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hip
   // 282 vs 297 us on the long causal workload).
   const bool longq = a.Nq > 64;
   if (dt == DType::BF16)
-    return longq ? launch<BF16, 8, 2>(a, stream, t0, t1) : launch<BF16, 1, 1>(a, stream, t0, t1);
-  return longq ? launch<F16, 8, 2>(a, stream, t0, t1) : launch<F16, 1, 1>(a, stream, t0, t1);
+    return longq ? launch<BF16, 8, 2>(a, stream, t0, t1) : launch_short<BF16>(a, stream, t0, t1);
+  return longq ? launch<F16, 8, 2>(a, stream, t0, t1) : launch_short<F16>(a, stream, t0, t1);
 }
 
 }  // namespace mha
