@@ -376,14 +376,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
 //   * The output is staged through LDS and leaves as whole 128-byte rows
 //     (rows written in 8-byte pieces from the registers take several times
 //     longer to complete).
-template <class Op>
-__global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a, int nqb) {
+template <class Op, bool kCacheEnd>
+__global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a) {
   // One value tile; after the key loop it stages the output rows.
   __shared__ __attribute__((aligned(16))) uint16_t vs[kBN * kD];
   static_assert(32 * kKS <= kBN * kD, "output staging exceeds the tile memory");
   const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
 
   // Longest query blocks first: under the causal mask later blocks see more keys.
+  const int nqb = (a.Nq + 31) >> 5;
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int qb = nqb - 1 - (int)(blockIdx.x / BH);
@@ -392,6 +393,12 @@ __global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a, int nqb) 
   const int q0 = qb * 32;
   const int qi = q0 + col;
   const bool qvalid = qi < a.Nq;
+
+  // The key length is requested before anything else, so that it heads the
+  // memory queues, as a vector load (range 0 without lengths: no access) so
+  // that it is waited for only where it is used.
+  const __amdgpu_buffer_rsrc_t lsrc = make_rsrc(a.key_lens, a.key_lens ? (int64_t)a.B * 4 : 0);
+  const int lraw = (int)__builtin_amdgcn_raw_buffer_load_b32(lsrc, b * 4, 0, 0);
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_sb + kvh * a.k_sh;
@@ -407,24 +414,23 @@ __global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a, int nqb) 
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qreg[kk] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff + kk * 32, 0, 0);
   }
-  // Rows of the first tile requested before the length is known: those the
-  // wave may see whatever the length is.  A cache (mask anchored at its
-  // filled end) is read only below its length, which is fetched first there
-  // (scalar work only, so that every path issues the same vector loads).
-  int krows0 = a.causal ? min(a.Nk, min(q0 + 32, a.Nq)) : a.Nk;
-  if (a.causal_end) {
-    const int L0 = a.key_lens ? min(max(a.key_lens[b], 0), a.Nk) : a.Nk;
-    krows0 = a.causal ? min(L0, min(q0 + 32, a.Nq) + L0 - a.Nq) : L0;
-  }
-  __amdgpu_buffer_rsrc_t ksrc = make_rsrc(kbase, krows0 > 0 ? ((int64_t)(krows0 - 1) * a.k_sn + kD) * 2 : 0);
-  __amdgpu_buffer_rsrc_t vsrc = make_rsrc(vbase, krows0 > 0 ? ((int64_t)(krows0 - 1) * a.v_sn + kD) * 2 : 0);
+  // Key and value loads are range-checked: rows at or past the range read
+  // as zeros and touch no memory.
+  __amdgpu_buffer_rsrc_t ksrc, vsrc;
+  auto set_range = [&](int rows) {
+    ksrc = make_rsrc(kbase, rows > 0 ? ((int64_t)(rows - 1) * a.k_sn + kD) * 2 : 0);
+    vsrc = make_rsrc(vbase, rows > 0 ? ((int64_t)(rows - 1) * a.v_sn + kD) * 2 : 0);
+  };
+  // Keys 32jb .. 32jb + 31 of tile t, straight into the operand registers.
+  auto load_k_block = [&](int t, int jb, u32x4_t (&kb)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      kb[kk] = __builtin_amdgcn_raw_buffer_load_b128(
+          ksrc, (int)(((t * kBN + jb * 32 + col) * a.k_sn + kk * 16 + half * 8) * 2), 0, 0);
+  };
   auto load_k = [&](int t, u32x4_t (&kop)[2][4]) {
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kop[jb][kk] = __builtin_amdgcn_raw_buffer_load_b128(
-            ksrc, (int)(((t * kBN + jb * 32 + col) * a.k_sn + kk * 16 + half * 8) * 2), 0, 0);
+    load_k_block(t, 0, kop[0]);
+    load_k_block(t, 1, kop[1]);
   };
   // V through LDS: each lane moves 8 16-byte chunks of a tile (rows of 128
   // bytes whose chunks are XOR-swizzled by bit 1 of the row, the layout of
@@ -435,30 +441,48 @@ __global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a, int nqb) 
   const int vpos = vrow * kD + ((vch ^ (((vrow >> 1) & 1) << 2)) << 3);
   const int vtile = (int)(kBN * a.v_sn * 2);
   u32x4_t vreg[8];
-  auto load_v = [&](int t) {
+  // Rows 32i .. 32i + 31 of tile t are chunks 4i .. 4i + 3.
+  auto load_v_block = [&](int t, int i) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, voff + c * vstep + t * vtile, 0, 0);
+    for (int c = 4 * i; c < 4 * i + 4; ++c)
+      vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, voff + c * vstep + t * vtile, 0, 0);
+  };
+  auto load_v = [&](int t) {
+    load_v_block(t, 0);
+    load_v_block(t, 1);
   };
   auto store_v = [&]() {
 #pragma unroll
     for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4_t*>(&vs[vpos + c * 8 * kD]) = vreg[c];
   };
 
+  // The first 32 rows of the first tile are requested before the length is
+  // known, up to the last key the wave may see whatever the length is (the
+  // key length decides only the rest).  A cache (mask anchored at its
+  // filled end) is read only below its length: there everything waits for it.
+  const int krows0 = a.causal ? min(a.Nk, min(q0 + 32, a.Nq)) : a.Nk;
   u32x4_t kop[2][4];
-  load_k(0, kop);
-  load_v(0);
+  if constexpr (!kCacheEnd) {
+    set_range(krows0);
+    load_k_block(0, 0, kop[0]);
+    load_v_block(0, 0);
+  }
+  const int L = a.key_lens ? min(max(__builtin_amdgcn_readfirstlane(lraw), 0), a.Nk) : a.Nk;
 
-  int L = a.Nk;
-  if (a.key_lens) L = min(max(a.key_lens[b], 0), a.Nk);
-  const int coff = a.causal_end ? L - a.Nq : 0;  // causal: query i sees keys j <= i + coff
+  const int coff = kCacheEnd ? L - a.Nq : 0;  // causal: query i sees keys j <= i + coff
   const int kend = a.causal ? min(L, qi + 1 + coff) : L;                     // keys this query sees
   const int kend_blk = a.causal ? min(L, min(q0 + 32, a.Nq) + coff) : L;     // keys the wave needs
   const int kmin = a.causal ? min(L, q0 + 1 + coff) : L;                     // tiles below: no mask
   const int ntiles = (max(kend_blk, 0) + kBN - 1) / kBN;
   // From here on, loads stop at the wave's last visible key; a tile past it
   // loads nothing (its rows are all beyond the range) and returns zeros.
-  ksrc = make_rsrc(kbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.k_sn + kD) * 2 : 0);
-  vsrc = make_rsrc(vbase, kend_blk > 0 ? ((int64_t)(kend_blk - 1) * a.v_sn + kD) * 2 : 0);
+  set_range(kend_blk);
+  if constexpr (kCacheEnd) {
+    load_k_block(0, 0, kop[0]);
+    load_v_block(0, 0);
+  }
+  load_k_block(0, 1, kop[1]);
+  load_v_block(0, 1);
   // V^T operands through ds_read_b64_tr_b16 (see attn_mfma_kernel).
   const int tr_k = (lane & 15) >> 2, tr_q = lane & 3, tr_cg = (lane >> 4) & 1;
   const int tr_row = 4 * half + tr_k;
@@ -578,9 +602,9 @@ __global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a, int nqb) 
 
     // Value rows of the first tile that were requested before the length was
     // known and lie past the wave's last visible key become zeros.
-    if (t == 0 && kend_blk < min(krows0, kBN)) {
+    if (!kCacheEnd && t == 0 && kend_blk < min(krows0, 32)) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 4; ++c)
         if (vrow + 8 * c >= kend_blk) vreg[c] = u32x4_t{0u, 0u, 0u, 0u};
     }
     store_v();
@@ -660,7 +684,10 @@ hipError_t launch_short(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hi
   const int nqb = (a.Nq + 31) / 32;
   const int64_t blocks = (int64_t)nqb * a.H * a.B;
   if (blocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((attn_short_kernel<Op>), dim3((unsigned)blocks), dim3(64), 0, stream, t0, t1, 0, a, nqb);
+  if (a.causal_end)
+    hipExtLaunchKernelGGL((attn_short_kernel<Op, true>), dim3((unsigned)blocks), dim3(64), 0, stream, t0, t1, 0, a);
+  else
+    hipExtLaunchKernelGGL((attn_short_kernel<Op, false>), dim3((unsigned)blocks), dim3(64), 0, stream, t0, t1, 0, a);
   return hipGetLastError();
 }
 
