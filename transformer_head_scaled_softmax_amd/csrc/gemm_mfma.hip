@@ -473,7 +473,11 @@ hipError_t launch(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEven
 // projections of the sentence-length layers: 4096 x 512 and 2048 x 1024), eight
 // waves per workgroup hide more latency than four with a second workgroup that
 // never comes (4096 x 512 x 512: 6.3-6.5 vs 6.8-6.9 us; with the residual and
-// norm statistics 8.9-9.0 vs 9.4-9.7 us; 2048 x 1024 x 1024: unchanged).
+// norm statistics 8.9-9.0 vs 9.4-9.7 us; 2048 x 1024 x 1024: unchanged), and
+// with no second workgroup to share the CU a third stage costs nothing and
+// keeps one more step of loads in flight (2048 x 1024 x 1024: 11.5 -> 9.3 us;
+// 4096 x 512 x 512 with the norm statistics: 8.8-9.2 -> 8.0-8.1 us; without
+// them unchanged at 6.5-7.0 us; four stages: no better than three).
 int tiles(const GemmBatch& g, int tm, int tn) {
   int n = 0;
   for (int i = 0; i < g.count; ++i) n += ((g.p[i].M + tm - 1) / tm) * ((g.p[i].N + tn - 1) / tn);
@@ -484,7 +488,7 @@ template <class Op>
 hipError_t launch_sized(const GemmBatch& g, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (tiles(g, 128, 128) >= 384) return launch<Op, 128, 128, 2, 4, 2, 2>(g, stream, t0, t1);  // 64 KiB, 8 waves
   const int t64 = tiles(g, 128, 64);
-  if (t64 == 256) return launch<Op, 128, 64, 4, 2, 2, 1>(g, stream, t0, t1);  // one round: 8 waves
+  if (t64 == 256) return launch<Op, 128, 64, 4, 2, 3, 1>(g, stream, t0, t1);  // one round: 8 waves, 72 KiB
   if (t64 >= 256) return launch<Op, 128, 64, 2, 2, 2, 2>(g, stream, t0, t1);                 // 48 KiB
   return launch<Op, 64, 64, 2, 2, 2, 2>(g, stream, t0, t1);                                    // 32 KiB
 }
@@ -501,7 +505,7 @@ hipError_t launch_ln(const GemmProblem& p, hipStream_t stream, hipEvent_t t0, hi
     e = launch<Op, 128, 128, 2, 4, 2, 2, true>(g, stream, t0, t1);
     tn = 128;
   } else if (tiles(g, 128, 64) == 256) {
-    e = launch<Op, 128, 64, 4, 2, 2, 1, true>(g, stream, t0, t1);
+    e = launch<Op, 128, 64, 4, 2, 3, 1, true>(g, stream, t0, t1);
     tn = 64;
   } else if (tiles(g, 128, 64) >= 256) {
     e = launch<Op, 128, 64, 2, 2, 2, 2, true>(g, stream, t0, t1);

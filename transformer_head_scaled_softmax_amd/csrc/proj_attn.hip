@@ -241,8 +241,6 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   uint16_t* kt_ = lds + TL::XQ * kD;
   uint16_t* vt = kt_ + TL::KR * kD;
   const uint32_t qsign = a.scale < 0.0f ? 0x80008000u : 0u;
-  const uint16_t* bias[3] = {static_cast<const uint16_t*>(a.bq), static_cast<const uint16_t*>(a.bk),
-                             static_cast<const uint16_t*>(a.bv)};
 #pragma unroll
   for (int jt = 0; jt < TL::TPW; ++jt) {
     if (!tlive[jt]) continue;
@@ -253,14 +251,17 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
       const int np = mat == 0 ? NPQ : NPK, nvalid = mat == 0 ? Nq : Nk;
       const int t = 32 * tblk[jt] + col;  // tile row
       const bool valid = t % np < nvalid && b0 + t / np < a.B;
+      // A select, not a table indexed by mat (which would live in scratch
+      // memory when mat depends on the wave's task).
+      const uint16_t* bias = static_cast<const uint16_t*>(mat == 0 ? a.bq : (mat == 1 ? a.bk : a.bv));
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         // Registers 4jj .. 4jj+3: features f0 .. f0+3 of tile row t.
         const int f0 = 32 * tfh[jt][m] + 8 * jj + 4 * half;
         float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (bias[mat]) {
+        if (bias) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bb[e] = Op::to_float(bias[mat][(mat == 0 ? h : kvh) * kD + f0 + e]);
+          for (int e = 0; e < 4; ++e) bb[e] = Op::to_float(bias[(mat == 0 ? h : kvh) * kD + f0 + e]);
         }
         u32x2_t v = {0u, 0u};
         if (valid) {
