@@ -191,6 +191,25 @@ def test_padded_slots_never_reach_the_output(dtype, nq, n, mask):
         assert np.array_equal(got, clean), f"poison {poison} changed the output"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("nq,nk,mask,lens", [(65, 63, NONE, (63, 1, 40)), (100, 100, CAUSAL, (100, 37, 70)),
+                                             (130, 200, NONE, (200, 150, 129))])
+def test_stale_tile_memory_never_reaches_the_output(dtype, nq, nk, mask, lens):
+    """A launch over all-NaN keys and values first leaves NaN in every compute
+    unit's tile memory; a call whose last key tile is partial must still match
+    the clean result bit for bit (rows past the key end read as zeros)."""
+    import torch
+    nan = torch.full((64, 16, 128, 64), float("nan"), dtype=torch.bfloat16 if dtype == "bf16" else torch.float16,
+                     device="cuda")
+    inp = synth.core_inputs(3, 2, nq, nk, 64, 64, dtype, seed=nq + nk)
+    inp["key_lens"] = np.array(lens, np.int32)
+    clean = run_core(inp, dtype, mask)
+    mha.forward(nan, nan, nan)  # 1024 workgroups: every compute unit holds NaN tiles
+    got = run_core(inp, dtype, mask)
+    assert np.array_equal(got, clean)
+    assert_close(got, ref_core(inp, mask), dtype, f"stale-tile case Nq{nq} Nk{nk}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("n,cuts", [(300, (0, 31, 63, 64, 130, 298)), (64, (0, 17, 31, 32, 40, 62)),
                                     (50, (0, 31, 33, 48))])

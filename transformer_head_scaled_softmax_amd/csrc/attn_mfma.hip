@@ -52,18 +52,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
   constexpr int NT = NW * 64;
   constexpr int QW = 32 * QS;         // queries per wave: QS sub-blocks of 32
   constexpr int QB = NW * QW;         // queries per workgroup
-  constexpr int CH = (kBN * 8) / NT;  // 16-byte chunks of K (and of V) per thread per tile
-  static_assert(CH >= 1, "tile too small for the workgroup");
+  static_assert(NW == 8, "one 1 KiB group of K and one of V per wave per tile");
 
   // K and V tiles, double-buffered; after the key loop the same memory stages
   // the output rows (32 rows of kKS elements per wave).
-  constexpr int kTiles = 2 * kBN * kKS + 2 * kBN * kD;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kTiles > NW * 32 * kKS ? kTiles : NW * 32 * kKS];
-  uint16_t (*ks)[kBN * kKS] = reinterpret_cast<uint16_t (*)[kBN * kKS]>(lds);
-  uint16_t (*vs)[kBN * kD] = reinterpret_cast<uint16_t (*)[kBN * kD]>(lds + 2 * kBN * kKS);
+  constexpr int kTiles = 4 * kBN * kD;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kTiles > NW * 32 * kKS ? kTiles : NW * 32 * kKS];
+  uint16_t (*ks)[kBN * kD] = reinterpret_cast<uint16_t (*)[kBN * kD]>(lds);
+  uint16_t (*vs)[kBN * kD] = reinterpret_cast<uint16_t (*)[kBN * kD]>(lds + 2 * kBN * kD);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: wave-uniform branches
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
 
   // Longest query blocks first: under the causal mask later blocks see more keys.
   const int BH = a.B * a.H;
@@ -116,37 +116,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
       qreg[u][kk] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff + kk * 32, 0, 0) ^ qsign;
   }
 
-  // Staging: each thread moves CH 16-byte chunks of the K tile and of the V
-  // tile.  K rows keep a padded stride (conflict-free 16-byte operand reads);
-  // V rows are dense 128-byte rows whose chunks are XOR-swizzled by bit 1 of
-  // the row, which makes the transposing operand reads below conflict-free.
-  int koff[CH], voff[CH], kpos[CH], vpos[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int idx = tid + c * NT, row = idx >> 3, ch = idx & 7;
-    koff[c] = (int)((row * a.k_sn + ch * 8) * 2);
-    voff[c] = (int)((row * a.v_sn + ch * 8) * 2);
-    kpos[c] = row * kKS + ch * 8;
-    vpos[c] = row * kD + ((ch ^ (((row >> 1) & 1) << 2)) << 3);
-  }
+  // Tiles go straight from memory into LDS (buffer loads with an LDS
+  // destination): wave w moves rows 8w .. 8w+7 of the K tile and of the V
+  // tile, one 16-byte chunk per lane, lane l landing at byte 16l of the
+  // wave's 1 KiB group.  Both tiles are dense 128-byte rows whose chunks are
+  // XOR-swizzled, so lane l fetches the global chunk that belongs in its
+  // slot: for K the operand swizzle of the row (conflict-free 16-byte
+  // operand reads), for V bit 1 of the row (conflict-free transposing reads).
+  const int grow = 8 * wave + (lane >> 3), gslot = lane & 7;
+  const int koff = (int)((grow * a.k_sn + ((gslot ^ operand_swizzle(grow)) << 3)) * 2);
+  const int voff = (int)((grow * a.v_sn + ((gslot ^ (((grow >> 1) & 1) << 2)) << 3)) * 2);
   const int ktile = (int)(kBN * a.k_sn * 2), vtile = (int)(kBN * a.v_sn * 2);
   // Tiles at or past the workgroup's key end fall outside the range check, so
-  // the prefetch issued after the last tile reads nothing.
-  u32x4_t kreg[CH], vreg[CH];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(ksrc, koff[c] + t * ktile, 0, 0);
-      vreg[c] = __builtin_amdgcn_raw_buffer_load_b128(vsrc, voff[c] + t * vtile, 0, 0);
-    }
+  // the prefetch issued during the last tile reads nothing.
+  auto issue_tile = [&](int t, int buf) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, MHA_LDS(&ks[buf][wave * 512]), 16, koff + t * ktile, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrc, MHA_LDS(&vs[buf][wave * 512]), 16, voff + t * vtile, 0, 0, 0);
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      *reinterpret_cast<u32x4_t*>(&ks[buf][kpos[c]]) = kreg[c];
-      *reinterpret_cast<u32x4_t*>(&vs[buf][vpos[c]]) = vreg[c];
-    }
-  };
+  const int kswz = operand_swizzle(col);  // = operand_swizzle(32jb + col)
 
   // V^T operand of O^T += V^T P^T through ds_read_b64_tr_b16.  In each group of
   // 16 lanes the instruction hands lane l element l%4 of the 4-element runs read
@@ -181,15 +168,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
       for (int r = 0; r < 16; ++r) o[u][cb][r] = 0.0f;
   }
 
-  load_tile(0);
-  store_tile(0);
+  issue_tile(0, 0);
+  wait_vmcnt<0>();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int j0 = t * kBN;
-    load_tile(t + 1);
 
+    if (j0 >= kmax_wave) issue_tile(t + 1, buf ^ 1);
     if (j0 < kmax_wave) {  // wave-uniform: tiles past all of this wave's rows are skipped
       // S^T = K_tile Q^T: two 32-key blocks; each K operand read serves every
       // query sub-block of the wave.
@@ -200,7 +187,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          kop[jb][kk] = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kKS + kk * 16 + half * 8]);
+          kop[jb][kk] = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kD + (((2 * kk + half) ^ kswz) << 3)]);
       __builtin_amdgcn_sched_barrier(0);  // keep the eight reads ahead of the products
       f32x16_t s[QS][2];
 #pragma unroll
@@ -227,6 +214,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
           const u32x2_t hi = vread(buf, 16 * t4 + 8 + tr_row, cb);
           vop[t4][cb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
+      // The next tile's loads go out after this tile's last LDS reads.
+      issue_tile(t + 1, buf ^ 1);
 
       // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4;
       // invisible keys become -inf (only diagonal and tail tiles have any).
@@ -316,8 +305,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
       }
     }
 
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+    wait_vmcnt<0>();
+    stage_barrier();
   }
 
   // Epilogue through LDS so the output rows leave as whole 128-byte segments:
