@@ -639,6 +639,9 @@ def test_backward_single_launch_rule(lib):
     assert lib.mha_backward_single_launch(64, 8, 2, 64, 64, 64, 64, mb.BF16) == 0  # shared heads
     assert lib.mha_backward_single_launch(64, 8, 8, 0, 64, 64, 64, mb.BF16) == 0
     assert lib.mha_backward_single_launch(64, 8, 8, 64, 64, 64, 64, mb.F32) == 0
+    # the non-square, padded gradient parity shapes run the single launch
+    assert lib.mha_backward_single_launch(3, 2, 2, 37, 50, 64, 64, mb.BF16) == 1
+    assert lib.mha_backward_single_launch(2, 2, 2, 50, 20, 64, 64, mb.F16) == 1
 
 
 def test_decode_noalloc_rejects_steps_above_its_scratch(lib):

@@ -148,9 +148,12 @@ def test_forward_lse_rows_without_keys_are_minus_inf():
     (1, 2, 300, 300, CAUSAL, None),          # long blocks (four waves) with a ragged tail
     (1, 1, 1, 1, NONE, None),                # one query, one key
     (1, 1, 33, 33, CAUSAL, None),            # one row past a 32-row block
+    (3, 2, 37, 50, NONE, (1, 50)),           # single launch: Nq < Nk, padded
+    (2, 2, 50, 20, NONE, (5, 20)),           # single launch: Nq > Nk, padded
 ])
 def test_backward_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
     check_train(B, H, Nq, Nk, dtype, mask, lens, seed=13)
+
 
 
 @pytest.mark.parametrize("B,H,Nq,Nk,mask,lens,dk,dv", [
