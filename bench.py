@@ -344,11 +344,13 @@ def cpu_baseline(w, inp_sets, seconds_target):
     return res
 
 
-def measure(w, steps: int, warmup: int, sets: int = 0):
+def measure(w, steps: int, warmup: int, sets: int = 0, plan: str = "auto"):
     """Run ``warmup`` untimed steps of workload ``w``, then time ``steps`` steps
     (graph replay, then plain stream launches) and the same steps through the
-    timed entry points (per-kernel dispatch times).  Returns the result line (without the CPU baseline) and the
-    host copies of the first input sets."""
+    timed entry points (per-kernel dispatch times).  ``plan`` forces the kernel
+    plan of a projection workload (auto, unfused, fused; the grouped-query entry
+    points take none).  Returns the result line (without the CPU baseline) and
+    the host copies of the first input sets."""
     import torch
     import transformer_head_scaled_softmax_amd as mha
     from transformer_head_scaled_softmax_amd import synth
@@ -412,6 +414,9 @@ def measure(w, steps: int, warmup: int, sets: int = 0):
         wts = synth.workload_inputs(w)  # seed of the workload: the model weights
         W = {n_: to_dev(wts[n_]) for n_ in ("W_Q", "W_K", "W_V", "W_O") + (("ln_gamma", "ln_beta") if w.ln else ())}
         gqa = w.Hkv is not None and w.Hkv != w.H  # shared key/value projections
+        plan_code = {"auto": 0, "unfused": 1, "fused": 2}[plan]
+        if plan_code and gqa:
+            raise SystemExit("--plan: the grouped-query projection entry points choose their own plan")
         if gqa:
             need = lib.mha_proj_gqa_workspace_bytes(w.B, w.Nq, w.Nk, w.D, w.H, w.Hkv, w.d, w.d, code)
         else:
@@ -429,20 +434,23 @@ def measure(w, steps: int, warmup: int, sets: int = 0):
             if w.ln:
                 argsv = (*head, W["ln_gamma"].data_ptr(), W["ln_beta"].data_ptr(), ctypes.c_float(1e-5),
                          d["out"].data_ptr(), *tail)
-                st = (lib.mha_proj_ln_forward(*argsv) if events is None
-                      else lib.mha_proj_ln_forward_timed(*argsv, events, 0))
+                st = (lib.mha_proj_ln_forward(*argsv) if events is None and not plan_code
+                      else lib.mha_proj_ln_forward_timed(*argsv, events, plan_code))
             elif gqa:
                 argsv = (*head, d["out"].data_ptr(), *tail[:5], w.Hkv, *tail[5:])
                 st = (lib.mha_proj_forward_gqa(*argsv) if events is None
                       else lib.mha_proj_forward_gqa_timed(*argsv, events))
             else:
                 argsv = (*head, d["out"].data_ptr(), *tail)
-                st = (lib.mha_proj_forward(*argsv) if events is None
-                      else lib.mha_proj_forward_timed(*argsv, events, 0))
+                st = (lib.mha_proj_forward(*argsv) if events is None and not plan_code
+                      else lib.mha_proj_forward_timed(*argsv, events, plan_code))
             if st != 0:
                 raise RuntimeError(lib.mha_last_error_message().decode())
         # Kernel -> (start, end) event indices of mha_proj_forward_timed.
-        if lib.mha_proj_fused(w.B, w.Nq, w.Nk, w.D, w.d, w.d, 0 if w.cross else 1):
+        fused = lib.mha_proj_fused(w.B, w.Nq, w.Nk, w.D, w.d, w.d, 0 if w.cross else 1)
+        if plan == "fused" and not fused:
+            raise SystemExit("--plan fused: the fused kernel does not take these sizes")
+        if fused and plan != "unfused":
             stage_events = {"qkv_attention": (0, 1), "out_projection": (4, 5)}
         else:
             stage_events = {"qkv_projection": (0, 1), "attention": (2, 3), "out_projection": (4, 5)}
@@ -617,6 +625,7 @@ def measure(w, steps: int, warmup: int, sets: int = 0):
                    "mask": "causal" if w.mask == 1 else "none",
                    "key_lens": None if w.lens is None else f"U{{{w.lens[0]}..{w.lens[1]}}}",
                    "input_sets": nsets, "issue": issue,
+                   **({"plan": plan} if w.proj and plan != "auto" else {}),
                    **({"residual_layer_norm": True} if w.ln else {}),
                    **({"decode": True, "H_kv": w.kv_heads, "cache_slots": w.Nk, "waves": nsplit}
                       if w.decode else {}),
@@ -649,7 +658,8 @@ def measure(w, steps: int, warmup: int, sets: int = 0):
         b_ = float(np.mean([wk[dom][1] for wk, _ in works]))
     else:
         f_, b_ = flops, bytes_
-    result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom, w.name)
+    result["roofline"] = roofline(f_, b_, avg[dom] / 1e3, w.dtype, dom,
+                                  w.name + ("" if plan == "auto" else "_" + plan))
 
     return result, host_sets
 
@@ -663,6 +673,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough for >= 1 GiB)")
+    ap.add_argument("--plan", default="auto", choices=("auto", "unfused", "fused"),
+                    help="kernel plan of a projection workload (default: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
@@ -692,7 +704,7 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
-    result, host_sets = measure(w, args.steps, args.warmup, args.sets)
+    result, host_sets = measure(w, args.steps, args.warmup, args.sets, args.plan)
     if not args.no_cpu_baseline:
         log(f"[bench] GPU done: {result['ms_per_step'] * 1e3:.2f} us/step; timing the fp64 oracle "
             f"for ~{args.cpu_seconds:.0f} s")
