@@ -79,8 +79,13 @@ def compare_grads(got, inp, dtype, kw, what):
     scale = kw.get("scale")
     scale = 1.0 / np.sqrt(inp["q"].shape[-1]) if scale is None else scale
     A = grad_bounds(inp["q"], inp["k"], inp["v"], inp["dout"], P, out, scale)
-    return {n: assert_close_grad(got[n], r, a, dtype, f"{n} {what}")
-            for n, r, a in zip(("dq", "dk", "dv"), ref, A)}
+    res = {n: assert_close_grad(got[n], r, a, dtype, f"{n} {what}")
+           for n, r, a in zip(("dq", "dk", "dv"), ref, A)}
+    # the flat figures beside the element-wise bound, for the record
+    for n, r in zip(("dq", "dk", "dv"), ref):
+        print(f"{what} {n}: max abs error {np.max(np.abs(got[n] - r)):.3g}, max |ref| {np.max(np.abs(r)):.3g}",
+              flush=True)
+    return res
 
 
 def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override=None, dk=64, dv=64):
@@ -244,6 +249,10 @@ def test_long_causal_bwd_full_size():
         r = [assert_close_grad(got[n][b:b + 1, h:h + 1], ref[i][:, s:s + 1], A[i], w.dtype,
                                f"{n} {w.name} slice ({b},{h})") for i, n in enumerate(("dq", "dk", "dv"))]
         print(f"slice ({b},{h}) error/bound dq {r[0]:.3f} dk {r[1]:.3f} dv {r[2]:.3f}", flush=True)
+        for i, n in enumerate(("dq", "dk", "dv")):
+            err = np.max(np.abs(got[n][b:b + 1, h:h + 1] - ref[i][:, s:s + 1]))
+            print(f"slice ({b},{h}) {n}: max abs error {err:.3g}, max |ref| {np.max(np.abs(ref[i][:, s:s + 1])):.3g}",
+                  flush=True)
 
 
 @pytest.mark.parametrize("N", [300, 64])  # two backward kernels; the single launch
