@@ -9,16 +9,18 @@
 // streamed through LDS in tiles of 64 and the row softmax is carried as a
 // running maximum and sum (an exact rearrangement of the same result).
 //
-// Work split.  A workgroup owns 32*NW*QS consecutive queries of one (b, h);
-// each wave owns 32*QS of them, as QS sub-blocks of 32 that share every K
-// operand read.  Per key tile a wave computes the TRANSPOSED scores
-// S^T (64 keys x 32 queries) = K_tile * Q^T, so that each lane ends up holding
-// 32 scores of one query (lanes l and l+32 share a query and split its keys).
-// That layout is exactly the B operand of the second product
-// O^T (64 features x 32 queries) += V^T * P^T, so the probabilities P go from
-// the score accumulators to the second MFMA without touching LDS.  V is
-// stored transposed in LDS when the tile is staged so both MFMA operands read
-// contiguous 8-byte or 16-byte runs.
+// Two kernels.  attn_mfma_kernel (more than 64 queries) gives a workgroup 512
+// consecutive queries of one (b, h): eight waves of 64, each as two sub-blocks
+// of 32 that share every K operand read.  attn_short_kernel (at most 64
+// queries) gives one wave 32 queries and arranges its memory traffic so that
+// it waits for memory once.  In both, per key tile a wave computes the
+// TRANSPOSED scores S^T (64 keys x 32 queries) = K_tile * Q^T, so that each
+// lane ends up holding 32 scores of one query (lanes l and l+32 share a query
+// and split its keys).  That layout is exactly the B operand of the second
+// product O^T (64 features x 32 queries) += V^T * P^T, so the probabilities P
+// go from the score accumulators to the second MFMA without touching LDS.  V
+// stays row-major in LDS and its V^T operands are read with the transposing
+// ds_read_b64_tr_b16.
 //
 // MFMA 32x32x16 lane layout (checked on the device): A[m][k] comes from lane
 // m + 32*(k/8), element k%8; B[k][n] from lane n + 32*(k/8), element k%8;
