@@ -272,12 +272,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
         // mostly a single tile) skips it then, which halves its softmax work
         // (7.95 vs 8.2 us on the base decoder workload).  Long sequences keep
         // the branch-free loop (the check cost 3% there).
-        bool need = true;
+        // The common path asks only whether any lane's partial sum failed the
+        // guard (one compare and a wave vote); which queries must rescale --
+        // lanes l and l + 32 hold one query and decide together -- is worked
+        // out only on the rare path.
+        bool ran = false, any_need = true;
         if (QS > 1 || !__all(m_ref[u] == -INFINITY)) {
           exponentiate(m_ref[u], false);
-          need = lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f;
+          ran = true;
+          any_need = __any(!(ls <= Op::kGuard));
         }
-        if (__any(need)) {
+        if (any_need) {
+          const bool need = ran ? lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f : true;
           float mx = -INFINITY;
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb)
@@ -559,12 +565,14 @@ __global__ __launch_bounds__(64, 2) void attn_short_kernel(AttnArgs a) {
         }
       ls = (lp[0] + lp[1]) + (lp[2] + lp[3]);
     };
-    bool need = true;
+    bool ran = false, any_need = true;  // as in attn_mfma_kernel
     if (!__all(m_ref == -INFINITY)) {
       exponentiate(m_ref, false);
-      need = lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f;
+      ran = true;
+      any_need = __any(!(ls <= Op::kGuard));
     }
-    if (__any(need)) {
+    if (any_need) {
+      const bool need = ran ? lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f : true;
       float mx = -INFINITY;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
