@@ -65,23 +65,32 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a, int nqb) {
 
   for (int j0 = 0; j0 < kend_blk; j0 += kTile) {
     __syncthreads();  // previous tile fully consumed (and qs visible)
-    for (int idx = threadIdx.x; idx < kTile * a.dk; idx += 256) {
-      const int r = idx / a.dk, c = idx - r * a.dk, j = j0 + r;
-      ks[r][c] = j < kend_blk ? kp[(int64_t)j * a.k_sn + c] : 0.0f;
-    }
-    for (int idx = threadIdx.x; idx < kTile * a.dv; idx += 256) {
-      const int r = idx / a.dv, c = idx - r * a.dv, j = j0 + r;
-      vs[r][c] = j < kend_blk ? vp[(int64_t)j * a.v_sn + c] : 0.0f;
-    }
+    // Only the tile's rows below the workgroup's key end are loaded (wave w
+    // takes rows w, w + 4, ..., a lane per column): scores are formed only for
+    // visible keys and the weighted sum runs over the loaded rows, so the
+    // other rows are never read.
+    const int nrows = min(kTile, kend_blk - j0);
+    for (int r = wave; r < nrows; r += kRows)
+      for (int c = lane; c < a.dk; c += 64) ks[r][c] = kp[(int64_t)(j0 + r) * a.k_sn + c];
+    for (int r = wave; r < nrows; r += kRows)
+      for (int c = lane; c < a.dv; c += 64) vs[r][c] = vp[(int64_t)(j0 + r) * a.v_sn + c];
     __syncthreads();
 
     const int j = j0 + lane;
     const bool vis = j < kend;
     float s = -INFINITY;
     if (vis) {
-      float dot = 0.0f;
-      for (int c = 0; c < a.dk; ++c) dot = fmaf(qs[wave][c], ks[lane][c], dot);
-      s = dot * c2;
+      // Four partial sums, so the products do not wait on one another.
+      float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+      int c = 0;
+      for (; c + 4 <= a.dk; c += 4) {
+        d0 = fmaf(qs[wave][c], ks[lane][c], d0);
+        d1 = fmaf(qs[wave][c + 1], ks[lane][c + 1], d1);
+        d2 = fmaf(qs[wave][c + 2], ks[lane][c + 2], d2);
+        d3 = fmaf(qs[wave][c + 3], ks[lane][c + 3], d3);
+      }
+      for (; c < a.dk; ++c) d0 = fmaf(qs[wave][c], ks[lane][c], d0);
+      s = ((d0 + d1) + (d2 + d3)) * c2;
     }
     const float m_new = fmaxf(m, wave_max(s));
     const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m - m_new);
