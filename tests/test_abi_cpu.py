@@ -273,13 +273,13 @@ def test_decode_empty_is_ok(lib, kw):
 
 
 @pytest.mark.parametrize("args,waves", [
-    ((16, 16, 16, 1, 8192, 64, 64, mb.BF16), 1024),   # one wave per SIMD of the 256 CUs
-    ((64, 8, 8, 1, 100, 64, 64, mb.BF16), 1024),
-    ((1, 8, 1, 4, 4096, 64, 64, mb.F16), 1024),       # multi-query, 32 rows
-    ((2, 64, 1, 1, 1000, 64, 64, mb.BF16), 1024),     # 64 rows share the single cache head
+    ((16, 16, 16, 1, 8192, 64, 64, mb.BF16), 768),    # three waves on each of the 256 CUs
+    ((64, 8, 8, 1, 100, 64, 64, mb.BF16), 768),
+    ((1, 8, 1, 4, 4096, 64, 64, mb.F16), 768),       # multi-query, 32 rows
+    ((2, 64, 1, 1, 1000, 64, 64, mb.BF16), 768),     # 64 rows share the single cache head
     ((2, 64, 1, 2, 1000, 64, 64, mb.BF16), 0),        # 128 rows: attention kernels
     ((2, 8, 8, 1, 1000, 64, 64, mb.F32), 0),          # fp32: attention kernels
-    ((2, 8, 8, 1, 0, 64, 64, mb.BF16), 1024),         # empty caches
+    ((2, 8, 8, 1, 0, 64, 64, mb.BF16), 768),         # empty caches
     ((2, 8, 3, 1, 100, 64, 64, mb.BF16), 0),          # invalid head split
 ])
 def test_decode_split_plan(lib, args, waves):
@@ -293,11 +293,11 @@ def _r256(n):
 def test_decode_workspace_bytes(lib):
     # one partial state (68 fp32) per (cache + wave) and row, then an int2 span per cache
     assert lib.mha_decode_workspace_bytes(16, 16, 16, 1, 8192, 64, 64, mb.BF16) == \
-        _r256((256 + 1024) * 1 * 68 * 4) + _r256(256 * 8)
+        _r256((256 + 768) * 1 * 68 * 4) + _r256(256 * 8)
     assert lib.mha_decode_workspace_bytes(1, 8, 1, 4, 4096, 64, 64, mb.F16) == \
-        _r256((1 + 1024) * 32 * 68 * 4) + _r256(8)
+        _r256((1 + 768) * 32 * 68 * 4) + _r256(8)
     assert lib.mha_decode_workspace_bytes(2, 64, 1, 1, 1000, 64, 64, mb.BF16) == \
-        _r256((2 + 1024) * 64 * 68 * 4) + _r256(16)
+        _r256((2 + 768) * 64 * 68 * 4) + _r256(16)
     assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, mb.F32) == 0
     assert lib.mha_decode_workspace_bytes(2, 8, 3, 1, 1000, 64, 64, mb.BF16) == 0
     assert lib.mha_decode_workspace_bytes(2, 8, 8, 1, 1000, 64, 64, 9) == 0
@@ -648,7 +648,7 @@ def test_decode_noalloc_rejects_steps_above_its_scratch(lib):
     """mha_decode_forward_noalloc takes its scratch from a 16 MiB array: a step
     whose decoding workspace is larger is refused before anything runs (no
     device needed), and the message names both sizes."""
-    B, H, Hkv, Nq, S = 1000, 64, 1, 1, 1  # (1000 caches + 1024 waves) x 64 rows x 272 B > 16 MiB
+    B, H, Hkv, Nq, S = 1000, 64, 1, 1, 1  # (1000 caches + 768 waves) x 64 rows x 272 B > 16 MiB
     need = lib.mha_decode_workspace_bytes(B, H, Hkv, Nq, S, 64, 64, mb.BF16)
     assert need > 16 << 20
     st = lib.mha_decode_forward_noalloc(P, P, P, P, B, H, Hkv, Nq, S, 64, 64, mb.MASK_CAUSAL, None, 0.125,

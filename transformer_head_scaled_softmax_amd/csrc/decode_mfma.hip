@@ -17,18 +17,18 @@
 // and query row, so it is bound by HBM bandwidth.  Caches of one batch have
 // unequal fill lengths, so the work is balanced on the device: the filled
 // slots of all caches, laid end to end, are cut into equal ranges, one per
-// wave (each workgroup is one wave, one per SIMD).  A wave's range
-// falls into pieces at cache boundaries.  For each piece the wave takes all
-// R = (H / Hkv) * Nq query rows that read that cache head -- so every cache
-// byte is read once whatever the group size -- and streams the piece's slots
-// in 32-slot blocks through a ring of LDS stages filled by direct-to-LDS
-// buffer loads.  Per block it computes the transposed scores S^T (32 slots x
-// 32 rows) = K Q^T, turns them into probabilities in registers and adds
-// V^T P^T into its O^T accumulators: the register layouts of the prefill
-// attention kernel, with a 32-slot block instead of a 64-key tile.  A piece
-// that is a whole cache writes its normalised rows; the other pieces leave
-// their softmax state (reference maximum, sum, accumulators) for a second
-// kernel that merges the pieces of each cut cache.
+// wave (each workgroup is one wave, three per compute unit, so at most one
+// per SIMD).  A wave's range falls into pieces at cache boundaries.  For each
+// piece the wave takes all R = (H / Hkv) * Nq query rows that read that cache
+// head -- so every cache byte is read once whatever the group size -- and
+// streams the piece's slots in 32-slot blocks through a ring of LDS stages
+// filled by direct-to-LDS buffer loads.  Per block it computes the transposed
+// scores S^T (32 slots x 32 rows) = K Q^T, turns them into probabilities in
+// registers and adds V^T P^T into its O^T accumulators: the register layouts
+// of the prefill attention kernel, with a 32-slot block instead of a 64-key
+// tile.  A piece that is a whole cache writes its normalised rows; the other
+// pieces leave their softmax state (reference maximum, sum, accumulators) for
+// a second kernel that merges the pieces of each cut cache.
 //
 // MFMA 32x32x16 lane layout: see mfma_util.h.
 #include <atomic>
