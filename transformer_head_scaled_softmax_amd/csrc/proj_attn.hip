@@ -18,7 +18,8 @@
 // NPK rows -- for self-attention the x_q rows serve for K and V too.  The
 // projection phase is one GEMM tile (those token rows times the 192 rows
 // W_Q[h], W_K[h], W_V[h]) with the contraction over D streamed through a
-// two-stage pipeline of LDS-direct loads; eight waves (two per SIMD) split it
+// pipeline of LDS-direct loads (three stages for a grid of one round where
+// they fit, else two); eight waves (two per SIMD) split it
 // into equal tasks of 32x32 MFMA blocks.  The Q, K, V tiles then sit in LDS
 // for the attention phase, where each wave takes 32 queries of one sequence
 // and all of that sequence's (at most 128) keys at once, so the softmax is the
@@ -34,7 +35,7 @@ constexpr int kD = kMfmaHeadDim;         // 64
 constexpr int kBK = 64;                  // contraction step
 constexpr int kWRows = 3 * kD;           // W_Q, W_K, W_V rows of one head
 constexpr int kNW = 8;                   // waves (two per SIMD)
-constexpr int kS = 2;                    // pipeline stages
+constexpr int kCUs = 256;                // compute units: a grid of at most this many workgroups is one round
 constexpr int kXcds = 8;
 constexpr uint32_t kDead = 0x80000000u;  // beyond any range check: nothing is read
 
@@ -60,12 +61,16 @@ struct Tile {
   static_assert(NPQ % 32 == 0 && NPK % 32 == 0 && NPQ <= 128 && NPK <= 128, "row padding");
   static_assert(ROWS % (8 * kNW) == 0, "loads must split evenly over the waves");
   static_assert(XQ <= 32 * kNW / 2, "one wave per 32 queries in the attention phase");
-  static_assert((XQ + 2 * KR) * kD <= kS * STAGE, "Q, K, V tiles must fit in the stages");
+  static_assert((XQ + 2 * KR) * kD <= 2 * STAGE, "Q, K, V tiles must fit in the stages");
+  // Three pipeline stages fit a CU's 160 KiB of LDS for every self-attention
+  // tile and for cross-attention over at most 32 keys.
+  static constexpr bool kThreeStages = 3 * STAGE * 2 <= 160 * 1024;
 };
 
-template <class Op, bool SELF, int NPQ, int NPK>
+template <class Op, bool SELF, int NPQ, int NPK, int kS>
 __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, int groups) {
   using TL = Tile<SELF, NPQ, NPK>;
+  static_assert(kS == 2 || (kS == 3 && TL::kThreeStages), "pipeline stages must fit in LDS");
   constexpr int KB = NPK / 32;  // 32-key blocks per sequence
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kS * TL::STAGE];
 
@@ -400,13 +405,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void proj_attn_kernel(ProjAttnArgs a, 
   }
 }
 
+// A grid of at most one round takes a third pipeline stage where it fits: the
+// projection loop waits on operand latency there (base encoder sublayer: 14.6
+// -> 14.1 us).  Larger grids keep two stages, so that two workgroups share a
+// CU (B = 384: 71.3 us with two stages, 75.2 us with three).
 template <class Op, bool SELF, int NPQ, int NPK>
 hipError_t launch(const ProjAttnArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  constexpr int IPW = Tile<SELF, NPQ, NPK>::IPW;
-  const int groups = (a.B + IPW - 1) / IPW;
+  using TL = Tile<SELF, NPQ, NPK>;
+  const int groups = (a.B + TL::IPW - 1) / TL::IPW;
   const int64_t blocks = (int64_t)groups * a.H;
   if (blocks == 0) return hipSuccess;
-  hipExtLaunchKernelGGL((proj_attn_kernel<Op, SELF, NPQ, NPK>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream,
+  if constexpr (TL::kThreeStages) {
+    if (blocks <= kCUs) {
+      hipExtLaunchKernelGGL((proj_attn_kernel<Op, SELF, NPQ, NPK, 3>), dim3((unsigned)blocks), dim3(kNW * 64), 0,
+                            stream, t0, t1, 0, a, groups);
+      return hipGetLastError();
+    }
+  }
+  hipExtLaunchKernelGGL((proj_attn_kernel<Op, SELF, NPQ, NPK, 2>), dim3((unsigned)blocks), dim3(kNW * 64), 0, stream,
                         t0, t1, 0, a, groups);
   return hipGetLastError();
 }
