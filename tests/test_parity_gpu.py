@@ -340,7 +340,11 @@ FUSED_CASES = [  # (B, Nq, Nk, D, H, cross, mask): every row padding, partial la
     (2, 100, 100, 128, 2, False, NONE), (3, 128, 128, 64, 2, False, CAUSAL),
     (3, 1, 5, 64, 2, True, NONE), (5, 20, 40, 128, 2, True, NONE), (3, 32, 64, 64, 2, True, NONE),
     (3, 40, 70, 192, 3, True, NONE), (4, 64, 80, 256, 4, True, NONE), (1, 64, 96, 64, 1, True, NONE),
-    (3, 50, 128, 128, 2, True, NONE), (2, 64, 64, 64, 2, True, CAUSAL)]
+    (3, 50, 128, 128, 2, True, NONE), (2, 64, 64, 64, 2, True, CAUSAL),
+    # grids on both sides of one round of 256 workgroups, where the kernel
+    # switches between three and two pipeline stages: 128 x 2 = 256 (three),
+    # 129 x 2 = 258 (two), and cross-attention over <= 32 keys with 257 (two)
+    (256, 64, 64, 64, 2, False, NONE), (258, 64, 64, 64, 2, False, CAUSAL), (514, 8, 20, 64, 1, True, NONE)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
