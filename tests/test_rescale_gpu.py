@@ -4,8 +4,11 @@ first visible key tile, and with negative scales, against the fp64 oracle.
 The kernels exponentiate each key tile against the row's current reference
 maximum and only take a new reference -- rescaling the running sum and the
 accumulators, then exponentiating the tile again -- when the partial sum
-passes a guard (2^64 for bf16 weights, 2^15 for f16).  N(0,1) data at the
-pages' scale never gets there after the first tile, so these inputs plant
+passes a guard (2^64 for bf16 weights, 2^15 for f16).  The bf16 kernel for
+more than 64 queries first skips that guard after each row's first tile and
+checks the pass at the end (row sums at most 2^100, accumulators finite),
+redoing it with the guard otherwise; the inputs below take both outcomes.
+N(0,1) data at the pages' scale never gets there after the first tile, so these inputs plant
 keys whose scores jump far above everything before them in later tiles
 (synth.plant_score_outliers): at 60 natural-log units (87 in log2) every
 planted tile passes both guards; at 20 (29 in log2) f16 rows rescale while
@@ -94,6 +97,27 @@ def test_attention_late_maximum(shape, scale, jump, dtype):
     # unplanted mean and the last two planted values must both carry weight
     assert np.max(np.abs(ref)) > 0.5
     assert_close(got, ref, dtype, f"{shape} scale {scale} jump {jump} {dtype}")
+
+
+@pytest.mark.parametrize("shape", ["long_causal", "long_cross"])
+@pytest.mark.parametrize("scale", [0.125, -0.125])
+def test_attention_bf16_large_weights_without_rescale(shape, scale):
+    """bf16, more than 64 queries, at the pages' scale: a single planted key
+    in the second tile (slot 70, paired with slot 71) raises a row's scaled
+    score by t_i * 9 / 2 natural-log units, t_i = q_i . u mostly in [4, 12].
+    Measured against each row's first-tile maximum, 13-20% of the rows get a
+    weight above 2^64 (the guard of the streaming softmax) while every row
+    sum stays below 2^90 (largest 2^89.2), so the bf16 kernel keeps its
+    unguarded first pass, with weights far above 2^64, and must still match
+    the oracle."""
+    B, H, Nq, Nk, lens, mask = ATTN_SHAPES[shape]
+    inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, "bf16", _seed(shape, "wide"))
+    synth.plant_score_outliers(inp["q"], inp["k"], [70], 9.0, scale, "bf16", _seed(shape, "wide") + 1)
+    inp["key_lens"] = np.asarray(lens, np.int32)
+    ref = _ref_attention(inp, mask, scale)
+    # the planted key dominates: rows far from the unplanted mean
+    assert np.max(np.abs(ref)) > 0.5
+    assert_close(_run_attention(inp, "bf16", mask, scale), ref, "bf16", f"{shape} scale {scale}")
 
 
 @pytest.mark.parametrize("scale", [-0.5, -2.0])

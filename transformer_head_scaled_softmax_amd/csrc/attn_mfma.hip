@@ -34,9 +34,12 @@
 // only if a query's partial sum is not finite or exceeds a guard (2^64 for
 // bf16 P, 2^15 for f16 P) -- its first visible tile, or a new maximum far above
 // the reference -- does that query take the tile's true maximum as its new
-// reference, rescale its accumulators and exponentiate the tile again.  Row
-// sums come from the packed P values with v_dot2, i.e. from exactly the
-// rounded values the P*V product multiplies.
+// reference, rescale its accumulators and exponentiate the tile again.  With
+// bf16 P (the exponent range of fp32) the long kernel first runs the key loop
+// without that guard after each query's first tile, and keeps the result when
+// every row sum stays at most 2^100 and every accumulator is finite; otherwise
+// the workgroup runs the guarded loop.  Row sums come from the packed P values
+// with v_dot2, i.e. from exactly the rounded values the P*V product multiplies.
 #include <type_traits>
 
 #include "mfma_util.h"
@@ -160,161 +163,197 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
 
   f32x16_t o[QS][2];
   float m_ref[QS], lsum[QS];
+  // One pass over the key tiles.  FAST (bf16 only): once every query of a
+  // sub-block has a reference (its first visible tile), tiles are
+  // exponentiated against it with no guard; the pass is checked at the end.
+  auto key_pass = [&](auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    bool refd[QS];  // wave-uniform: every query of sub-block u has a reference
 #pragma unroll
-  for (int u = 0; u < QS; ++u) {
-    m_ref[u] = -INFINITY;
-    lsum[u] = 0.0f;
+    for (int u = 0; u < QS; ++u) {
+      refd[u] = false;
+      m_ref[u] = -INFINITY;
+      lsum[u] = 0.0f;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[u][cb][r] = 0.0f;
-  }
+        for (int r = 0; r < 16; ++r) o[u][cb][r] = 0.0f;
+    }
 
-  issue_tile(0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
+    issue_tile(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int j0 = t * kBN;
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      const int j0 = t * kBN;
 
-    if (j0 >= kmax_wave) issue_tile(t + 1, buf ^ 1);
-    if (j0 < kmax_wave) {  // wave-uniform: tiles past all of this wave's rows are skipped
-      // S^T = K_tile Q^T: two 32-key blocks; each K operand read serves every
-      // query sub-block of the wave.
-      // All eight K operands are read before the first product, so the
-      // products do not wait on LDS one pair at a time.
-      u32x4_t kop[2][4];
+      if (j0 >= kmax_wave) issue_tile(t + 1, buf ^ 1);
+      if (j0 < kmax_wave) {  // wave-uniform: tiles past all of this wave's rows are skipped
+        // S^T = K_tile Q^T: two 32-key blocks; each K operand read serves every
+        // query sub-block of the wave.
+        // All eight K operands are read before the first product, so the
+        // products do not wait on LDS one pair at a time.
+        u32x4_t kop[2][4];
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          kop[jb][kk] = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kD + (((2 * kk + half) ^ kswz) << 3)]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the eight reads ahead of the products
-      f32x16_t s[QS][2];
+          for (int kk = 0; kk < 4; ++kk)
+            kop[jb][kk] = *reinterpret_cast<const u32x4_t*>(&ks[buf][(jb * 32 + col) * kD + (((2 * kk + half) ^ kswz) << 3)]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the eight reads ahead of the products
+        f32x16_t s[QS][2];
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+        for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-        for (int u = 0; u < QS; ++u)
+          for (int u = 0; u < QS; ++u)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[u][jb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) s[u][jb][r] = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int u = 0; u < QS; ++u) s[u][jb] = Op::mma(kop[jb][kk], qreg[u][kk], s[u][jb]);
-      }
-
-      // V^T operands of O^T += V^T P^T for the whole tile, read once and used
-      // by every query sub-block: step t4 supplies keys 16t4 + 4half + {0..3}
-      // and 16t4 + 8 + 4half + {0..3} of this lane's feature row.
-      u32x4_t vop[4][2];
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const u32x2_t lo = vread(buf, 16 * t4 + tr_row, cb);
-          const u32x2_t hi = vread(buf, 16 * t4 + 8 + tr_row, cb);
-          vop[t4][cb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            for (int u = 0; u < QS; ++u) s[u][jb] = Op::mma(kop[jb][kk], qreg[u][kk], s[u][jb]);
         }
-      // The next tile's loads go out after this tile's last LDS reads.
-      issue_tile(t + 1, buf ^ 1);
 
-      // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4;
-      // invisible keys become -inf (only diagonal and tail tiles have any).
-      if (j0 + kBN > kmin_wave) {
-#pragma unroll
-        for (int u = 0; u < QS; ++u) {
-          const int lim = kend[u] - j0 - 4 * half;
-#pragma unroll
-          for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (jb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[u][jb][r] = -INFINITY;
-        }
-      }
-
-      // Sub-blocks one after the other: softmax, then P V, with no branch
-      // between one sub-block's P V MFMAs and the next one's softmax
-      // arithmetic, so the two can be interleaved.
-#pragma unroll
-      for (int u = 0; u < QS; ++u) {
-        u32x4_t pb[4];
-
-        // P = exp2(s * c2 - m_ref), packed to the MFMA input type in the order
-        // the P^T operand needs (step t4 takes registers 8(t4%2) .. +7 of
-        // s[t4/2]); the row sum comes from the packed values with v_dot2.
-        float ls = 0.0f;
-        auto exponentiate = [&](float mu, bool select_masked) {
-          // Four partial sums (one per register pair of a step) keep the
-          // v_dot2 accumulation chains short.
-          float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const int jb = t4 >> 1, r = (t4 & 1) * 8 + 2 * w;
-              float p0 = __builtin_amdgcn_exp2f(fmaf(s[u][jb][r], c2, -mu));
-              float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][jb][r + 1], c2, -mu));
-              if (select_masked) {
-                p0 = s[u][jb][r] == -INFINITY ? 0.0f : p0;
-                p1 = s[u][jb][r + 1] == -INFINITY ? 0.0f : p1;
-              }
-              pb[t4][w] = Op::pack(p0, p1);
-              lp[w] = Op::sum2(pb[t4][w], lp[w]);
-            }
-          ls = (lp[0] + lp[1]) + (lp[2] + lp[3]);
-        };
-        // Optimistic pass against the current reference.  It is kept unless
-        // this query's partial sum is not finite or exceeds kGuard (a new
-        // maximum far above the reference, or masked keys with no reference
-        // yet).  While no query of the wave has a reference (its first tile)
-        // the pass would always fail; the short-sequence configuration (QS = 1,
-        // mostly a single tile) skips it then, which halves its softmax work
-        // (7.95 vs 8.2 us on the base decoder workload).  Long sequences keep
-        // the branch-free loop (the check cost 3% there).
-        // The common path asks only whether any lane's partial sum failed the
-        // guard (one compare and a wave vote); which queries must rescale --
-        // lanes l and l + 32 hold one query and decide together -- is worked
-        // out only on the rare path.
-        bool ran = false, any_need = true;
-        if (QS > 1 || !__all(m_ref[u] == -INFINITY)) {
-          exponentiate(m_ref[u], false);
-          ran = true;
-          any_need = __any(!(ls <= Op::kGuard));
-        }
-        if (any_need) {
-          const bool need = ran ? lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f : true;
-          float mx = -INFINITY;
-#pragma unroll
-          for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][jb][r]);
-          mx = lanes_max(mx);
-          const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
-          // Queries that passed keep their reference, so a row's arithmetic
-          // never depends on other rows' data.
-          const float m_new = need ? fmaxf(m_ref[u], mt) : m_ref[u];
-          const float alpha = (need && m_new != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref[u] - m_new) : 1.0f;
-          lsum[u] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[u][cb][r] *= alpha;
-          m_ref[u] = m_new;
-          // Masked keys get exactly 0, also when scale is 0 or no key is visible yet.
-          exponentiate(m_ref[u] == -INFINITY ? 0.0f : m_ref[u], true);
-        }
-        lsum[u] += ls;
-
+        // V^T operands of O^T += V^T P^T for the whole tile, read once and used
+        // by every query sub-block: step t4 supplies keys 16t4 + 4half + {0..3}
+        // and 16t4 + 8 + 4half + {0..3} of this lane's feature row.
+        u32x4_t vop[4][2];
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) o[u][cb] = Op::mma(vop[t4][cb], pb[t4], o[u][cb]);
-      }
-    }
+          for (int cb = 0; cb < 2; ++cb) {
+            const u32x2_t lo = vread(buf, 16 * t4 + tr_row, cb);
+            const u32x2_t hi = vread(buf, 16 * t4 + 8 + tr_row, cb);
+            vop[t4][cb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+        // The next tile's loads go out after this tile's last LDS reads.
+        issue_tile(t + 1, buf ^ 1);
 
-    wait_vmcnt<0>();
-    stage_barrier();
+        // Register (jb, r) of this lane holds key j0 + 32jb + 8(r/4) + 4half + r%4;
+        // invisible keys become -inf (only diagonal and tail tiles have any).
+        if (j0 + kBN > kmin_wave) {
+#pragma unroll
+          for (int u = 0; u < QS; ++u) {
+            const int lim = kend[u] - j0 - 4 * half;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (jb * 32 + (r >> 2) * 8 + (r & 3) >= lim) s[u][jb][r] = -INFINITY;
+          }
+        }
+
+        // Sub-blocks one after the other: softmax, then P V, with no branch
+        // between one sub-block's P V MFMAs and the next one's softmax
+        // arithmetic, so the two can be interleaved.
+#pragma unroll
+        for (int u = 0; u < QS; ++u) {
+          u32x4_t pb[4];
+
+          // P = exp2(s * c2 - m_ref), packed to the MFMA input type in the order
+          // the P^T operand needs (step t4 takes registers 8(t4%2) .. +7 of
+          // s[t4/2]); the row sum comes from the packed values with v_dot2.
+          float ls = 0.0f;
+          auto exponentiate = [&](float mu, bool select_masked) {
+            // Four partial sums (one per register pair of a step) keep the
+            // v_dot2 accumulation chains short.
+            float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const int jb = t4 >> 1, r = (t4 & 1) * 8 + 2 * w;
+                float p0 = __builtin_amdgcn_exp2f(fmaf(s[u][jb][r], c2, -mu));
+                float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][jb][r + 1], c2, -mu));
+                if (select_masked) {
+                  p0 = s[u][jb][r] == -INFINITY ? 0.0f : p0;
+                  p1 = s[u][jb][r + 1] == -INFINITY ? 0.0f : p1;
+                }
+                pb[t4][w] = Op::pack(p0, p1);
+                lp[w] = Op::sum2(pb[t4][w], lp[w]);
+              }
+            ls = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+          };
+          // Optimistic pass against the current reference.  It is kept unless
+          // this query's partial sum is not finite or exceeds kGuard (a new
+          // maximum far above the reference, or masked keys with no reference
+          // yet).  While no query of the wave has a reference (its first tile)
+          // the pass would always fail; the short-sequence configuration (QS = 1,
+          // mostly a single tile) skips it then, which halves its softmax work
+          // (7.95 vs 8.2 us on the base decoder workload).  Long sequences keep
+          // the branch-free loop (the check cost 3% there).
+          // The common path asks only whether any lane's partial sum failed the
+          // guard (one compare and a wave vote); which queries must rescale --
+          // lanes l and l + 32 hold one query and decide together -- is worked
+          // out only on the rare path.  The unguarded pass takes the rare path
+          // only until every query of the sub-block has a reference.
+          bool ran = false, any_need = true;
+          if (QS > 1 || !__all(m_ref[u] == -INFINITY)) {
+            exponentiate(m_ref[u], false);
+            ran = true;
+            if constexpr (FAST)
+              any_need = !refd[u];
+            else
+              any_need = __any(!(ls <= Op::kGuard));
+          }
+          if (any_need) {
+            const bool need = ran ? lanes_max(ls <= Op::kGuard ? 0.0f : 1.0f) > 0.0f : true;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][jb][r]);
+            mx = lanes_max(mx);
+            const float mt = (mx == -INFINITY) ? -INFINITY : mx * c2;
+            // Queries that passed keep their reference, so a row's arithmetic
+            // never depends on other rows' data.
+            const float m_new = need ? fmaxf(m_ref[u], mt) : m_ref[u];
+            const float alpha = (need && m_new != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref[u] - m_new) : 1.0f;
+            lsum[u] *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[u][cb][r] *= alpha;
+            m_ref[u] = m_new;
+            // Masked keys get exactly 0, also when scale is 0 or no key is visible yet.
+            exponentiate(m_ref[u] == -INFINITY ? 0.0f : m_ref[u], true);
+            if constexpr (FAST) refd[u] = __all(m_ref[u] != -INFINITY);
+          }
+          lsum[u] += ls;
+
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) o[u][cb] = Op::mma(vop[t4][cb], pb[t4], o[u][cb]);
+        }
+      }
+
+      wait_vmcnt<0>();
+      stage_barrier();
+    }
+  };
+  // P in bf16 has the exponent range of fp32, so a tile whose scores rise far
+  // above the reference still gives finite weights; the unguarded pass is
+  // kept if every partial row sum stays at most 2^100 and every accumulator
+  // is finite (the partial sums never decrease, so no intermediate exceeded
+  // them either).  Otherwise the whole workgroup redoes the pass with the
+  // guard.  fp16 weights overflow at 2^16, so that type always takes the
+  // guarded pass.
+  constexpr bool kWideP = Op::kGuard > 1.0e6f;
+  if constexpr (kWideP) {
+    key_pass(std::true_type{});
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < QS; ++u) {
+      ok = ok && lsum[u] <= 0x1p100f;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ok = ok && fabsf(o[u][cb][r]) <= 3.0e38f;
+    }
+    if (__syncthreads_or(!ok)) key_pass(std::false_type{});
+  } else {
+    key_pass(std::false_type{});
   }
 
   // Epilogue through LDS so the output rows leave as whole 128-byte segments:
