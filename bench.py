@@ -447,10 +447,11 @@ def measure(w, steps: int, warmup: int, sets: int = 0, plan: str = "auto"):
             if st != 0:
                 raise RuntimeError(lib.mha_last_error_message().decode())
         # Kernel -> (start, end) event indices of mha_proj_forward_timed.
-        fused = lib.mha_proj_fused(w.B, w.Nq, w.Nk, w.D, w.d, w.d, 0 if w.cross else 1)
-        if plan == "fused" and not fused:
-            raise SystemExit("--plan fused: the fused kernel does not take these sizes")
-        if fused and plan != "unfused":
+        # --plan fused on sizes the fused kernel does not take fails in the
+        # library with MHA_ERR_UNSUPPORTED.
+        fused = plan == "fused" or (plan == "auto" and lib.mha_proj_fused(w.B, w.Nq, w.Nk, w.D, w.d, w.d,
+                                                                          0 if w.cross else 1))
+        if fused:
             stage_events = {"qkv_attention": (0, 1), "out_projection": (4, 5)}
         else:
             stage_events = {"qkv_projection": (0, 1), "attention": (2, 3), "out_projection": (4, 5)}

@@ -176,7 +176,8 @@ int mha_proj_forward_gqa_timed(const void* x_q, const void* x_kv, const void* W_
  * events[4..5] the output projection, and events[2..3] are left untouched.
  * Its last argument selects the kernel plan: MHA_PLAN_AUTO (the plan
  * mha_proj_forward takes), MHA_PLAN_UNFUSED, or MHA_PLAN_FUSED (returns
- * MHA_ERR_UNSUPPORTED when mha_proj_fused is 0 for these sizes); an unknown
+ * MHA_ERR_UNSUPPORTED when the fused kernel does not take these sizes -- see
+ * mha_proj_fused); an unknown
  * value is MHA_ERR_INVALID_ARG.  Both plans compute the same function; they
  * agree bit for bit when every sequence has at most 64 keys.
  */
@@ -389,11 +390,13 @@ size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k,
  * kernels (the Q/K/V projections fused with attention, then the output
  * projection), 0 if it runs as three (projections, attention, output
  * projection).  self_attention: nonzero when x_kv is NULL or equal to x_q.
- * The fused form applies when D is a multiple of 64, d_k == d_v == 64
- * (bf16 or f16), and either self-attention with Nq == Nk <= 128 or
- * cross-attention with Nq <= 64 and Nk <= 128 -- sentence-length encoder,
- * decoder and encoder-decoder layers.  Pure function of its arguments; no
- * device access.
+ * The fused kernel takes D a multiple of 64, d_k == d_v == 64 (bf16 or
+ * f16), and either self-attention with Nq == Nk <= 128 or cross-attention
+ * with Nq <= 64 and Nk <= 128 -- sentence-length encoder, decoder and
+ * encoder-decoder layers.  mha_proj_forward uses it for all of these except
+ * cross-attention with D >= 768 over 65..96 keys, where the three-kernel plan
+ * measured faster (MHA_PLAN_FUSED still runs it there).  Pure function of its
+ * arguments; no device access.
  */
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention);
 

@@ -93,9 +93,24 @@ def test_base_encoder_proj_full():
 
 
 def test_big_cross_proj_full():
+    """The benchmark's big cross-attention workload, in the launch
+    configuration it times (the three-kernel plan at this shape)."""
     w = synth.WORKLOADS["big_cross_proj"]
+    assert mha.load().mha_proj_fused(w.B, w.Nq, w.Nk, w.D, 64, 64, 0) == 0
     inp = synth.workload_inputs(w)
     assert_close(run_proj(inp, w.H, w.dtype, w.mask), ref_proj(inp, w.H, w.mask), w.dtype, w.name)
+
+
+def test_big_cross_proj_full_fused_plan():
+    """The same workload forced through the fused projection+attention kernel,
+    which takes these sizes although mha_proj_forward does not choose it."""
+    w = synth.WORKLOADS["big_cross_proj"]
+    inp = synth.workload_inputs(w)
+    d = _proj_dev(inp, w.dtype)
+    out = mha.proj_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=w.H,
+                           mask_kind=w.mask, key_lens=lens_dev(inp["key_lens"]), plan=mha.PLAN_FUSED)
+    torch.cuda.synchronize()
+    assert_close(to_host(out), ref_proj(inp, w.H, w.mask), w.dtype, w.name + " fused plan")
 
 
 def test_long_causal_sampled_rows():

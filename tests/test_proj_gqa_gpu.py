@@ -1,14 +1,15 @@
 """GPU parity of the projection path with shared key/value projections
 (mha_proj_forward_gqa) against the fp64 oracle (oracle.mha_proj_gqa, pinned by
 a closed form and by per-head projections), through the C ABI.  Tolerance as
-for mha_proj_forward (bf16/f16: 2e-2 absolute on the output)."""
+for mha_proj_forward (bf16/f16: 2e-2 absolute on the output; outputs well
+above unit scale: 2e-2 + u |ref|, u the output type's rounding unit)."""
 import ctypes
 
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, lens_dev, to_dev, to_host
+from gpu_util import assert_close_scaled, assert_close, lens_dev, to_dev, to_host
 from transformer_head_scaled_softmax_amd import _binding as mb, synth
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +43,7 @@ def run(inp, H, Hkv, dtype, mask, biases=None):
     (3, 17, 33, 256, 4, 2, True, NONE),       # cross-attention, groups of two
     (2, 70, 70, 512, 8, 2, False, NONE),      # several key tiles, groups of four
     (1, 130, 130, 384, 6, 3, False, CAUSAL),  # causal, ragged tail
-    (4, 64, 80, 1024, 16, 4, True, NONE),     # the big cross shape with four key/value heads
+    (4, 64, 80, 1024, 16, 4, True, NONE),     # the big cross shape with four key/value heads (three kernels)
 ])
 def test_proj_gqa_matches_oracle(dtype, B, Nq, Nk, D, H, Hkv, cross, mask):
     inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed=B * 10 + Nq + H, cross=cross, Hkv=Hkv)
@@ -54,6 +55,29 @@ def test_proj_gqa_matches_oracle(dtype, B, Nq, Nk, D, H, Hkv, cross, mask):
     ref = oracle.mha_proj_gqa(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"], H=H,
                               H_kv=Hkv, mask_kind=mask, key_lens=inp["key_lens"], **biases)
     assert_close(got, ref, dtype, f"proj gqa B{B} Nq{Nq} Nk{Nk} D{D} H{H} Hkv{Hkv}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B,Nq,Nk,D,H,Hkv", [
+    (3, 64, 112, 1024, 16, 4),   # d_model 1024 over 112 keys: the fused kernel
+    (3, 64, 80, 512, 8, 2),      # d_model 512 over 80 keys: the fused kernel
+])
+def test_proj_gqa_fused_cross(dtype, B, Nq, Nk, D, H, Hkv):
+    """Cross-attention sublayers that mha_proj_forward runs through the fused
+    kernel, with shared key/value heads and biases.  With the biases the
+    outputs reach |out| ~ 5 (not the unit scale the flat 2e-2 bound is stated
+    for), and rounding such a value to bf16 alone costs up to 2^-8 |out|, so
+    these take the suite's bound for larger outputs, 2e-2 + u |ref|."""
+    assert mha.load().mha_proj_fused(B, Nq, Nk, D, 64, 64, 0) == 1
+    inp = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed=B * 10 + Nq + H, cross=True, Hkv=Hkv)
+    g = synth.generator(D + Nq + Hkv)
+    inp["key_lens"] = g.integers(1, Nk + 1, size=B).astype(np.int32)
+    biases = {n: synth.round_to(synth.normal(g, (size,), dtype) * np.float32(0.5), dtype)
+              for n, size in (("b_Q", H * 64), ("b_K", Hkv * 64), ("b_V", Hkv * 64), ("b_O", D))}
+    got = run(inp, H, Hkv, dtype, NONE, biases)
+    ref = oracle.mha_proj_gqa(inp["x_q"], inp["x_kv"], inp["W_Q"], inp["W_K"], inp["W_V"], inp["W_O"], H=H,
+                              H_kv=Hkv, mask_kind=NONE, key_lens=inp["key_lens"], **biases)
+    assert_close_scaled(got, ref, dtype, f"proj gqa fused cross B{B} Nq{Nq} Nk{Nk} D{D} H{H} Hkv{Hkv}")
 
 
 def test_base_encoder_proj_gqa_full():

@@ -261,11 +261,22 @@ size_t mha_proj_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k, in
 
 namespace {
 
-// Whether the projection path runs as the fused projection+attention kernel
-// plus the output projection (short sequences).
-bool use_fused(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
+// Whether the fused projection+attention kernel takes these sizes.
+bool fused_supported(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
   return mha::proj_attn_supported(self, Nq, Nk, D, d_k, d_v) && int64_t(B) * Nq * D * 2 < kMaxBufferBytes &&
          int64_t(B) * Nk * D * 2 < kMaxBufferBytes;
+}
+
+// Whether the projection path runs as the fused projection+attention kernel
+// plus the output projection (short sequences): wherever the fused kernel
+// applies, except cross-attention with d_model >= 768 over 65..96 keys, where
+// the three-kernel plan measured 2-19% faster.  (Both plans timed on one
+// MI355X over cross-attention with B 16-64, Nq 32-64, Nk 64-128, d_model
+// 512-1024: the fused plan wins by 8% at d_model 512, ties at 640 and at
+// 64 keys, and wins by 20% from 112 keys; self-attention fuses at every
+// measured size.)
+bool use_fused(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
+  return fused_supported(self, B, Nq, Nk, D, d_k, d_v) && (self || D < 768 || Nk <= 64 || Nk > 96);
 }
 
 // The residual connection and layer normalisation after the sublayer
@@ -376,12 +387,11 @@ int proj_forward_impl(const void* x_q, const void* x_kv, const void* W_Q, const 
 
   auto evt = [&](int i) -> hipEvent_t { return ev ? ev[i] : nullptr; };
 
-  // Short self-attention: projections and attention in one fused launch that
+  // Short sequences: projections and attention in one fused launch that
   // writes the head-major concatenation directly, then the output projection.
-  const bool fusable = use_fused(xkv == x_q, B, Nq, Nk, D, d_k, d_v);
-  if (plan == MHA_PLAN_FUSED && !fusable)
+  if (plan == MHA_PLAN_FUSED && !fused_supported(xkv == x_q, B, Nq, Nk, D, d_k, d_v))
     return fail(MHA_ERR_UNSUPPORTED, "these sizes have no fused projection+attention kernel");
-  if (fusable && plan != MHA_PLAN_UNFUSED) {
+  if (plan == MHA_PLAN_FUSED || (plan == MHA_PLAN_AUTO && use_fused(xkv == x_q, B, Nq, Nk, D, d_k, d_v))) {
     mha::ProjAttnArgs pa{};
     pa.xq = x_q;
     pa.xkv = xkv;
