@@ -401,6 +401,24 @@ size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k,
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention);
 
 /*
+ * mha_forward_block_queries -- queries per workgroup of the attention kernel
+ * that mha_forward (and the attention step of the other entry points) runs
+ * for B sequences of H query heads with Nq queries: 4 for MHA_F32 (vector
+ * ALUs); for MHA_BF16 / MHA_F16, 32 (one wave per workgroup, each wave
+ * reading its own key/value tiles) or 512 (eight waves sharing each key/value
+ * tile staged in LDS).  Both bf16/f16 kernels give the same results bit for
+ * bit; the 512-query one is chosen when its workgroups would be well used:
+ * u = (Nq / query slots) x (workgroups / workgroup slots of the rounds they
+ * take on the 256 compute units) at least 0.45 without a mask, 0.8 with the
+ * causal mask, and Nq > 64 ([TP] "The Trade-Off: Quadratic Cost": long
+ * sequences are where the quadratic term dominates).  The environment
+ * variable MHA_ATTENTION_BLOCK=32 or =512, read on every call, forces one of
+ * the two (for tests and measurement).  0 for invalid arguments.  Pure
+ * function of its arguments and that variable; no device access.
+ */
+int mha_forward_block_queries(int B, int H, int Nq, int mask_kind, int dtype);
+
+/*
  * Decoding against a key/value cache ([AD] "How predictions are generated, per
  * downstream task", "Translation and summarization (encoder-decoder)": during
  * generation the keys and values of the positions already produced are kept

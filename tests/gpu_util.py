@@ -21,6 +21,9 @@ Tolerances (stated for the whole suite):
 """
 from __future__ import annotations
 
+import contextlib
+import os
+
 import numpy as np
 
 TOL_F32_REL = 1e-5
@@ -113,3 +116,24 @@ def assert_close_grad(got: np.ndarray, ref: np.ndarray, A: np.ndarray, dtype: st
     ratio = float(np.max(np.abs(got - ref) / bound))
     assert ratio <= 1.0, f"{what}: error reaches {ratio:.3g} x the bound (max abs err {np.max(np.abs(got - ref)):.3g})"
     return ratio
+
+
+@contextlib.contextmanager
+def attention_block(block):
+    """Run the bf16/f16 attention calls inside the block with the kernel of
+    ``block`` queries per workgroup (32: one-wave workgroups, 512: eight-wave
+    workgroups) through the library's MHA_ATTENTION_BLOCK override; None keeps
+    the library's own choice (mha_forward_block_queries)."""
+    old = os.environ.get("MHA_ATTENTION_BLOCK")
+    if block is None:
+        os.environ.pop("MHA_ATTENTION_BLOCK", None)
+    else:
+        os.environ["MHA_ATTENTION_BLOCK"] = str(block)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("MHA_ATTENTION_BLOCK", None)
+        else:
+            os.environ["MHA_ATTENTION_BLOCK"] = old
+

@@ -174,6 +174,40 @@ def test_proj_fused_plan(lib, args, fused):
     assert lib.mha_proj_fused(*args) == fused
 
 
+@pytest.mark.parametrize("args,block", [
+    ((64, 8, 64, mb.MASK_CAUSAL, mb.BF16), 32),      # sentence length: one-wave workgroups
+    ((64, 8, 128, mb.MASK_CAUSAL, mb.BF16), 32),     # u = 0.25
+    ((128, 8, 192, mb.MASK_NONE, mb.F16), 32),       # u = 0.375
+    ((64, 16, 256, mb.MASK_NONE, mb.BF16), 512),     # u = 0.5 without a mask
+    ((64, 16, 256, mb.MASK_CAUSAL, mb.BF16), 32),    # u = 0.5 under the causal mask
+    ((32, 16, 384, mb.MASK_CAUSAL, mb.BF16), 32),    # u = 0.75 < 0.8 under the causal mask
+    ((32, 16, 384, mb.MASK_NONE, mb.BF16), 512),     # u = 0.75 without a mask
+    ((16, 16, 1024, mb.MASK_CAUSAL, mb.BF16), 512),  # u = 1
+    ((2, 8, 1024, mb.MASK_CAUSAL, mb.BF16), 32),     # 32 workgroups on 256 compute units
+    ((2, 16, 8192, mb.MASK_CAUSAL, mb.BF16), 512),   # the long causal workload
+    ((2, 16, 8192, mb.MASK_CAUSAL, mb.F32), 4),      # fp32: vector-ALU kernel
+    ((0, 16, 8192, mb.MASK_CAUSAL, mb.BF16), 0),     # invalid sizes
+    ((2, 16, 8192, 7, mb.BF16), 0),                  # unknown mask
+    ((2, 16, 8192, mb.MASK_CAUSAL, 9), 0),           # unknown dtype
+])
+def test_forward_block_queries(lib, args, block, monkeypatch):
+    monkeypatch.delenv("MHA_ATTENTION_BLOCK", raising=False)
+    assert lib.mha_forward_block_queries(*args) == block
+
+
+def test_forward_block_queries_override(lib, monkeypatch):
+    """MHA_ATTENTION_BLOCK forces either bf16/f16 kernel, read on every call;
+    other values leave the choice to the library."""
+    args = (2, 16, 8192, mb.MASK_CAUSAL, mb.BF16)
+    monkeypatch.setenv("MHA_ATTENTION_BLOCK", "32")
+    assert lib.mha_forward_block_queries(*args) == 32
+    monkeypatch.setenv("MHA_ATTENTION_BLOCK", "512")
+    assert lib.mha_forward_block_queries(64, 8, 64, mb.MASK_NONE, mb.BF16) == 512
+    monkeypatch.setenv("MHA_ATTENTION_BLOCK", "64")
+    assert lib.mha_forward_block_queries(*args) == 512
+    assert lib.mha_forward_block_queries(2, 16, 8192, mb.MASK_CAUSAL, mb.F32) == 4
+
+
 def test_proj_timed_rejects_unknown_plan(lib):
     import ctypes
     fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first

@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, assert_close_grad, grad_bounds, lens_dev, to_dev, to_host
+from gpu_util import assert_close, assert_close_grad, attention_block, grad_bounds, lens_dev, to_dev, to_host
 from transformer_head_scaled_softmax_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -108,19 +108,22 @@ def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override
 # ---------------------------------------------------------------------------
 # The row statistic.
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("dtype,block", [("bf16", 32), ("bf16", 512), ("f16", 32), ("f16", 512), ("f32", None)])
 @pytest.mark.parametrize("B,H,Nq,Nk,mask,lens", [
     (2, 3, 64, 64, NONE, None),
     (2, 2, 150, 150, CAUSAL, (20, 150)),
     (3, 2, 37, 101, NONE, (1, 101)),
     (1, 2, 300, 300, CAUSAL, None),
 ])
-def test_forward_lse_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
+def test_forward_lse_matches_oracle(dtype, block, B, H, Nq, Nk, mask, lens):
+    """The row statistic from both bf16/f16 attention kernels (32 and 512
+    queries per workgroup)."""
     inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, dtype, 11, lens)
     q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
     kl = lens_dev(inp["key_lens"])
-    out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=kl)
-    plain = mha.forward(q, k, v, mask_kind=mask, key_lens=kl)
+    with attention_block(block):
+        out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=kl)
+        plain = mha.forward(q, k, v, mask_kind=mask, key_lens=kl)
     torch.cuda.synchronize()
     # The statistic is an extra output: the attention output is unchanged.
     assert torch.equal(out, plain)

@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import (ROUNDING_UNIT, TOL_LOWP_ABS, assert_close, assert_close_grad, grad_bounds, lens_dev,
+from gpu_util import (ROUNDING_UNIT, TOL_LOWP_ABS, assert_close, assert_close_grad, attention_block, grad_bounds,
+                      lens_dev,
                       to_dev, to_host)
 from transformer_head_scaled_softmax_amd import _binding as mb, synth
 
@@ -37,11 +38,14 @@ def _device():
     torch.cuda.synchronize()
 
 
-def gpu_train(inp, dtype, mask):
+def gpu_train(inp, dtype, mask, block=None):
+    """Forward (through the attention kernel of ``block`` queries per
+    workgroup, or the library's choice for None), then backward."""
     q, k, v, dout = (to_dev(inp[n], dtype) for n in ("q", "k", "v", "dout"))
     lens = lens_dev(inp["key_lens"])
-    out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=lens)
-    plain = mha.forward(q, k, v, mask_kind=mask, key_lens=lens)
+    with attention_block(block):
+        out, lse = mha.forward_lse(q, k, v, mask_kind=mask, key_lens=lens)
+        plain = mha.forward(q, k, v, mask_kind=mask, key_lens=lens)
     dq, dk, dv = mha.backward(q, k, v, out, dout, lse, mask_kind=mask, key_lens=lens)
     torch.cuda.synchronize()
     assert torch.equal(out, plain), "forward with and without the row statistic differ"
@@ -50,12 +54,12 @@ def gpu_train(inp, dtype, mask):
             "dk": to_host(dk), "dv": to_host(dv)}
 
 
-def check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed, lens_override=None):
+def check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed, lens_override=None, block=None):
     inp = synth.train_inputs(B, H, Nq, Nk, 64, 64, dtype, seed, lens, Hkv=Hkv)
     if lens_override is not None:
         inp["key_lens"] = np.asarray(lens_override, np.int32)
-    what = f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} {dtype} mask{mask} lens{inp['key_lens']}"
-    got = gpu_train(inp, dtype, mask)
+    what = f"B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} {dtype} mask{mask} lens{inp['key_lens']} block{block}"
+    got = gpu_train(inp, dtype, mask, block)
     kw = dict(mask_kind=mask, key_lens=inp["key_lens"])
     G = H // Hkv
 
@@ -91,7 +95,7 @@ def check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed, lens_override=None):
     return got
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("dtype,block", [("bf16", 32), ("bf16", 512), ("f16", 32), ("f16", 512), ("f32", None)])
 @pytest.mark.parametrize("B,H,Hkv,Nq,Nk,mask,lens", [
     (2, 8, 2, 150, 150, CAUSAL, (20, 150)),  # groups of 4, several tiles, ragged tail, padding
     (2, 6, 1, 64, 200, NONE, (1, 200)),      # multi-query: one key/value head, cross-shaped
@@ -99,8 +103,8 @@ def check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed, lens_override=None):
     (1, 6, 3, 300, 300, CAUSAL, None),       # long query blocks, groups of 2
     (2, 2, 1, 1, 1, NONE, None),             # one query, one key
 ])
-def test_gqa_training_matches_oracle(dtype, B, H, Hkv, Nq, Nk, mask, lens):
-    check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed=41)
+def test_gqa_training_matches_oracle(dtype, block, B, H, Hkv, Nq, Nk, mask, lens):
+    check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed=41, block=block)
 
 
 def test_gqa_training_empty_sequences():

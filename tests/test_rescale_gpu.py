@@ -4,8 +4,8 @@ first visible key tile, and with negative scales, against the fp64 oracle.
 The kernels exponentiate each key tile against the row's current reference
 maximum and only take a new reference -- rescaling the running sum and the
 accumulators, then exponentiating the tile again -- when the partial sum
-passes a guard (2^64 for bf16 weights, 2^15 for f16).  The bf16 kernel for
-more than 64 queries first skips that guard after each row's first tile and
+passes a guard (2^64 for bf16 weights, 2^15 for f16).  The bf16 kernel of
+512-query workgroups first skips that guard after each row's first tile and
 checks the pass at the end (row sums at most 2^100, accumulators finite),
 redoing it with the guard otherwise; the inputs below take both outcomes.
 N(0,1) data at the pages' scale never gets there after the first tile, so these inputs plant
@@ -17,8 +17,9 @@ slots sit in the second, third and fifth key tile, so a row rescales up to
 three times, and the last two planted keys carry nearly equal scores, so
 the result mixes their values rather than selecting one.
 
-Shapes cover both attention configurations (more than 64 queries: eight
-waves of 64 queries each; at most 64: one wave of 32), causal and unmasked,
+Shapes run through both attention kernels (workgroups of 512 queries: eight
+waves of 64 queries each; of 32: one wave, forced through
+MHA_ATTENTION_BLOCK), causal and unmasked,
 padded sequences (planted slots past a key length must not count), the
 decoding kernel with caches cut between many waves (so the merging kernel
 combines partial states whose references are far apart), and the fused
@@ -31,7 +32,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, lens_dev, to_dev, to_host
+from gpu_util import assert_close, attention_block, lens_dev, to_dev, to_host
 from transformer_head_scaled_softmax_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -64,10 +65,15 @@ def _attention_case(B, H, Nq, Nk, lens, dtype, scale, jump, seed):
     return inp
 
 
-def _run_attention(inp, dtype, mask, scale):
+def _run_attention(inp, dtype, mask, scale, block):
+    """mha.forward with the attention kernel of ``block`` (32 or 512) queries
+    per workgroup."""
     q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
-    out = mha.forward(q, k, v, mask_kind=mask, key_lens=lens_dev(inp["key_lens"]), scale=scale)
-    torch.cuda.synchronize()
+    with attention_block(block):
+        B, H, Nq = q.shape[:3]
+        assert mha.load().mha_forward_block_queries(B, H, Nq, mask, mha._dtype_code(q)) == block
+        out = mha.forward(q, k, v, mask_kind=mask, key_lens=lens_dev(inp["key_lens"]), scale=scale)
+        torch.cuda.synchronize()
     return to_host(out)
 
 
@@ -76,27 +82,29 @@ def _ref_attention(inp, mask, scale):
 
 
 ATTN_SHAPES = {
-    # (B, H, Nq, Nk, key_lens, mask): eight-wave configuration (Nq > 64)
+    # (B, H, Nq, Nk, key_lens, mask): several query sub-blocks per wave and
+    # waves past the last query in the 512-query kernel
     "long_causal": (2, 2, 300, 300, [300, 157], CAUSAL),
     "long_cross": (2, 2, 200, 333, [333, 140], NONE),
-    # one-wave configuration (Nq <= 64) streaming several key tiles
+    # few queries streaming several key tiles
     "short_cross": (3, 2, 40, 300, [300, 129, 262], NONE),
 }
 
 
+@pytest.mark.parametrize("block", [32, 512])
 @pytest.mark.parametrize("shape", sorted(ATTN_SHAPES))
 @pytest.mark.parametrize("scale", [0.125, 1.0, -0.5])
 @pytest.mark.parametrize("jump", [60.0, 20.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_attention_late_maximum(shape, scale, jump, dtype):
+def test_attention_late_maximum(shape, scale, jump, dtype, block):
     B, H, Nq, Nk, lens, mask = ATTN_SHAPES[shape]
     inp = _attention_case(B, H, Nq, Nk, lens, dtype, scale, jump, seed=_seed(shape, dtype))
-    got = _run_attention(inp, dtype, mask, scale)
+    got = _run_attention(inp, dtype, mask, scale, block)
     ref = _ref_attention(inp, mask, scale)
     # the planted keys decide most rows: the outputs must be far from the
     # unplanted mean and the last two planted values must both carry weight
     assert np.max(np.abs(ref)) > 0.5
-    assert_close(got, ref, dtype, f"{shape} scale {scale} jump {jump} {dtype}")
+    assert_close(got, ref, dtype, f"{shape} scale {scale} jump {jump} {dtype} block {block}")
 
 
 @pytest.mark.parametrize("shape", ["long_causal", "long_cross"])
@@ -108,8 +116,8 @@ def test_attention_bf16_large_weights_without_rescale(shape, scale):
     Measured against each row's first-tile maximum, 13-20% of the rows get a
     weight above 2^64 (the guard of the streaming softmax) while every row
     sum stays below 2^90 (largest 2^89.2), so the bf16 kernel keeps its
-    unguarded first pass, with weights far above 2^64, and must still match
-    the oracle."""
+    unguarded first pass of the 512-query kernel, with weights far above
+    2^64, and must still match the oracle."""
     B, H, Nq, Nk, lens, mask = ATTN_SHAPES[shape]
     inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, "bf16", _seed(shape, "wide"))
     synth.plant_score_outliers(inp["q"], inp["k"], [70], 9.0, scale, "bf16", _seed(shape, "wide") + 1)
@@ -117,21 +125,22 @@ def test_attention_bf16_large_weights_without_rescale(shape, scale):
     ref = _ref_attention(inp, mask, scale)
     # the planted key dominates: rows far from the unplanted mean
     assert np.max(np.abs(ref)) > 0.5
-    assert_close(_run_attention(inp, "bf16", mask, scale), ref, "bf16", f"{shape} scale {scale}")
+    assert_close(_run_attention(inp, "bf16", mask, scale, 512), ref, "bf16", f"{shape} scale {scale}")
 
 
 @pytest.mark.parametrize("scale", [-0.5, -2.0])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [(2, 3, 200, 200, CAUSAL), (3, 2, 50, 50, CAUSAL), (2, 2, 37, 150, NONE),
                                    (2, 2, 130, 70, NONE)])
-def test_attention_negative_scale(shape, scale, dtype):
+@pytest.mark.parametrize("block", [32, 512])
+def test_attention_negative_scale(shape, scale, dtype, block):
     """N(0,1) data at negative scales: the row maximum of scale * q.k is its
     smallest q.k, which the kernels must take as the reference."""
     B, H, Nq, Nk, mask = shape
     inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, dtype, seed=Nq * 7 + Nk)
     inp["key_lens"] = np.asarray([Nk] + [max(1, Nk // (b + 2)) for b in range(1, B)], np.int32)
-    assert_close(_run_attention(inp, dtype, mask, scale), _ref_attention(inp, mask, scale), dtype,
-                 f"{shape} scale {scale} {dtype}")
+    assert_close(_run_attention(inp, dtype, mask, scale, block), _ref_attention(inp, mask, scale), dtype,
+                 f"{shape} scale {scale} {dtype} block {block}")
 
 
 # ---------------------------------------------------------------------------

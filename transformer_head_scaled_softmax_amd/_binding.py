@@ -25,7 +25,7 @@ ERR_HIP = -4
 
 # Every symbol include/mha.h declares.
 EXPORTS = ("mha_forward", "mha_forward_timed", "mha_proj_workspace_bytes", "mha_proj_forward",
-           "mha_proj_forward_timed", "mha_proj_fused", "mha_proj_ln_forward", "mha_proj_ln_forward_timed",
+           "mha_proj_forward_timed", "mha_proj_fused", "mha_forward_block_queries", "mha_proj_ln_forward", "mha_proj_ln_forward_timed",
            "mha_proj_ln_workspace_bytes", "mha_decode_workspace_bytes", "mha_decode_forward",
            "mha_decode_forward_timed", "mha_decode_forward_noalloc", "mha_decode_split", "mha_forward_lse", "mha_forward_strided",
            "mha_forward_gqa", "mha_backward_workspace_bytes", "mha_backward", "mha_backward_timed",
@@ -65,6 +65,8 @@ def load(path: pathlib.Path | str | None = None) -> ctypes.CDLL:
     lib.mha_proj_forward_timed.restype = i
     lib.mha_proj_fused.argtypes = [i] * 7
     lib.mha_proj_fused.restype = i
+    lib.mha_forward_block_queries.argtypes = [i] * 5
+    lib.mha_forward_block_queries.restype = i
     lib.mha_proj_ln_forward.argtypes = [vp] * 12 + [f, vp] + [i] * 8 + [vp, f, i, vp, ctypes.c_size_t, vp]
     lib.mha_proj_ln_forward.restype = i
     lib.mha_proj_ln_forward_timed.argtypes = lib.mha_proj_ln_forward.argtypes + [vp, i]

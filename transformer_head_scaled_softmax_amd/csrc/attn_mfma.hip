@@ -9,11 +9,13 @@
 // streamed through LDS in tiles of 64 and the row softmax is carried as a
 // running maximum and sum (an exact rearrangement of the same result).
 //
-// Two kernels.  attn_mfma_kernel (more than 64 queries) gives a workgroup 512
-// consecutive queries of one (b, h): eight waves of 64, each as two sub-blocks
-// of 32 that share every K operand read.  attn_short_kernel (at most 64
-// queries) gives one wave 32 queries and arranges its memory traffic so that
-// it waits for memory once.  In both, per key tile a wave computes the
+// Two kernels, with the same arithmetic step for step (same results bit for
+// bit).  attn_mfma_kernel gives a workgroup 512 consecutive queries of one
+// (b, h): eight waves of 64, each as two sub-blocks of 32 that share every K
+// operand read.  attn_short_kernel gives one wave 32 queries and arranges its
+// memory traffic so that it waits for memory once per tile.  The second runs
+// every query block of at most 64 rows and the longer ones where the first
+// would leave many waves or compute units idle (attention_block_queries).  In both, per key tile a wave computes the
 // TRANSPOSED scores S^T (64 keys x 32 queries) = K_tile * Q^T, so that each
 // lane ends up holding 32 scores of one query (lanes l and l+32 share a query
 // and split its keys).  That layout is exactly the B operand of the second
@@ -393,7 +395,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
 
 // One wave per workgroup: 32 queries of one (b, h), for query blocks of at
 // most 64 rows (sentence-length self-attention, cross-attention from short
-// query sequences).  The arithmetic is step for step that of attn_mfma_kernel
+// query sequences) and for longer ones whose 512-query workgroups would be
+// poorly used (a few hundred queries, or few heads).  The arithmetic is step for step that of attn_mfma_kernel
 // with one 32-query sub-block.  What differs is the memory traffic, which is
 // what bounds a wave that is alone on its SIMD for the whole of a short
 // launch: it is arranged so that a wave waits for memory once.
@@ -732,12 +735,7 @@ hipError_t launch_short(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hi
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  // Short query blocks (sentence-length sequences) use one wave (32 queries)
-  // per workgroup so the grid has many workgroups in flight; long ones use
-  // eight waves of 64 queries, so each staged K/V tile serves 512 queries and
-  // the tiles are read from L2 half as often as with four waves (measured:
-  // 282 vs 297 us on the long causal workload).
-  const bool longq = a.Nq > 64;
+  const bool longq = attention_block_queries(a.B, a.H, a.Nq, a.causal) == 512;
   if (dt == DType::BF16)
     return longq ? launch<BF16, 8, 2>(a, stream, t0, t1) : launch_short<BF16>(a, stream, t0, t1);
   return longq ? launch<F16, 8, 2>(a, stream, t0, t1) : launch_short<F16>(a, stream, t0, t1);

@@ -148,7 +148,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, int B, 
   if (key_lens && !aligned(key_lens, 4)) return fail(MHA_ERR_INVALID_ARG, "key_lens must be 4-byte aligned");
   if ((want_lse && !lse) || !aligned(lse, 4))
     return fail(MHA_ERR_INVALID_ARG, "lse must be %s4-byte aligned", want_lse ? "non-null and " : "");
-  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 512 : 32);
+  const int64_t rows_per_block =
+      dtype == MHA_F32 ? 4 : mha::attention_block_queries(B, H, Nq, mask_kind == MHA_MASK_CAUSAL);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
   // The matrix-core kernel addresses one (b, h) slice with 32-bit byte offsets
@@ -519,6 +520,13 @@ int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_atte
   return use_fused(self_attention != 0, B, Nq, Nk, D, d_k, d_v) ? 1 : 0;
 }
 
+int mha_forward_block_queries(int B, int H, int Nq, int mask_kind, int dtype) {
+  if (B < 1 || H < 1 || Nq < 1 || (mask_kind != MHA_MASK_NONE && mask_kind != MHA_MASK_CAUSAL)) return 0;
+  if (dtype == MHA_F32) return 4;
+  if (dtype != MHA_BF16 && dtype != MHA_F16) return 0;
+  return mha::attention_block_queries(B, H, Nq, mask_kind == MHA_MASK_CAUSAL);
+}
+
 size_t mha_proj_gqa_workspace_bytes(int B, int Nq, int Nk, int D, int H, int H_kv, int d_k, int d_v, int dtype) {
   ProjLayout L;
   if (D < 1 || H_kv < 1 || !proj_layout(B, Nq, Nk, H, d_k, d_v, dtype, &L, H_kv)) return 0;
@@ -809,7 +817,8 @@ int decode_forward_impl(const void* q, const void* k_cache, const void* v_cache,
     return MHA_OK;
   }
 
-  const int64_t rows_per_block = dtype == MHA_F32 ? 4 : (Nq > 64 ? 512 : 32);
+  const int64_t rows_per_block =
+      dtype == MHA_F32 ? 4 : mha::attention_block_queries(B, H, Nq, mask_kind == MHA_MASK_CAUSAL);
   if ((Nq + rows_per_block - 1) / rows_per_block * int64_t(H) * B > kMaxBlocks)
     return fail(MHA_ERR_UNSUPPORTED, "problem too large for one launch");
   mha::AttnArgs a{};

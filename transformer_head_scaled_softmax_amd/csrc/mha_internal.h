@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 namespace mha {
 
@@ -186,6 +188,36 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream, hipEvent_t t0 
                            hipEvent_t t1 = nullptr);
 hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
+// Queries per workgroup of the bf16/f16 attention launch: 32 (one-wave
+// workgroups) or 512 (eight waves).  The 512-query kernel shares each staged
+// K/V tile among eight waves and reads the tiles from L2 half as often as four
+// waves would (282 vs 297 us on the long causal workload), but a query length
+// that is not a multiple of 512 leaves some of its waves without queries, and
+// few workgroups leave compute units idle.  Its utilisation u = (queries /
+// query slots) x (workgroups / slots of the rounds they take on 256 compute
+// units) decides.  Measured on one MI355X over query lengths 96-4096 (outputs
+// identical bit for bit), the one-wave kernel takes about 1.9x the 512-query
+// kernel's time per unit of work without a mask and 1.2-1.3x under the causal
+// mask (whose workgroups end unevenly); it runs when u < 0.45 without a mask
+// (at u = 0.5 it won on one grid of 256 workgroups and lost by 40% on four
+// rounds of them) and when u < 0.8 with it.  Every query length of at most
+// 192 takes it, for example.  MHA_ATTENTION_BLOCK=32 or 512 in the
+// environment, read on every call, forces one of the two kernels.
+inline int attention_block_queries(int B, int H, int Nq, bool causal) {
+  if (const char* force = getenv("MHA_ATTENTION_BLOCK")) {
+    if (!strcmp(force, "32")) return 32;
+    if (!strcmp(force, "512")) return 512;
+  }
+  if (Nq <= 64) return 32;
+  constexpr int64_t kQueriesPerBlock = 512, kComputeUnits = 256;
+  const int64_t nqb = (Nq + kQueriesPerBlock - 1) / kQueriesPerBlock;
+  const int64_t wgs = nqb * B * H;
+  if (wgs <= 0) return 32;
+  const int64_t rounds = (wgs + kComputeUnits - 1) / kComputeUnits;
+  const double u = double(Nq) / double(nqb * kQueriesPerBlock) * double(wgs) / double(rounds * kComputeUnits);
+  return u < (causal ? 0.8 : 0.45) ? 32 : 512;
+}
+
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
 // Output projection followed by the residual connection and layer
