@@ -153,7 +153,7 @@ def test_forward_lse_rows_without_keys_are_minus_inf():
     (2, 2, 150, 150, CAUSAL, (20, 150)),     # several tiles, ragged tail, padding
     (3, 2, 37, 101, NONE, (1, 101)),         # cross-attention, padded, Nq < Nk
     (2, 2, 200, 64, NONE, (30, 64)),         # cross-attention, Nq > Nk
-    (1, 2, 300, 300, CAUSAL, None),          # long blocks (four waves) with a ragged tail
+    (1, 2, 300, 300, CAUSAL, None),          # four-wave dQ and dK/dV blocks with a ragged tail
     (1, 1, 1, 1, NONE, None),                # one query, one key
     (1, 1, 33, 33, CAUSAL, None),            # one row past a 32-row block
     (3, 2, 37, 50, NONE, (1, 50)),           # single launch: Nq < Nk, padded
@@ -161,6 +161,12 @@ def test_forward_lse_rows_without_keys_are_minus_inf():
 ])
 def test_backward_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
     check_train(B, H, Nq, Nk, dtype, mask, lens, seed=13)
+
+
+def test_backward_eight_wave_dq_blocks_with_ragged_tail():
+    """From 4096 queries the dQ kernel runs eight waves (256 queries) per
+    workgroup; 4100 queries leave a ragged last block."""
+    check_train(1, 1, 4100, 4100, "bf16", CAUSAL, None, seed=19)
 
 
 

@@ -626,10 +626,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t const* ev
     return hipGetLastError();
   }
   // The dQ kernel writes D, which the dK/dV kernel reads: stream order.
-  // Long sequences: eight waves per dQ workgroup (256 queries share each K/V
-  // tile; 397 vs 407 us at n = 8192), four per dK/dV workgroup (eight were 1%
-  // slower there).
-  hipError_t e = a.Nq > 64 ? launch_dq<Op, 8>(a, stream, evt(0), evt(1)) : launch_dq<Op, 2>(a, stream, evt(0), evt(1));
+  // dQ workgroups: two waves (64 queries) for at most 64 queries, four (128)
+  // up to 4096, eight (256 queries share each K/V tile) beyond.  Measured on
+  // one MI355X, whole backward pass, causal, bf16 (same results bit for bit):
+  // four waves against eight 23.1 vs 28.7 us at B 64, h 8, n 100; 25.4 vs
+  // 31.2 us at n 128; 91.8 vs 102.7 us at B 8, h 16, n 1024; 147.8 vs 159.4
+  // us at B 4, h 16, n 2048; at n = 8192 eight stay ahead (944 vs 953 us for
+  // the pass; the dQ kernel alone 397 vs 407 us).  dK/dV workgroups: four
+  // waves (128 keys) beyond 64 keys (eight were 1% slower at n = 8192).
+  hipError_t e = a.Nq <= 64     ? launch_dq<Op, 2>(a, stream, evt(0), evt(1))
+                 : a.Nq < 4096 ? launch_dq<Op, 4>(a, stream, evt(0), evt(1))
+                               : launch_dq<Op, 8>(a, stream, evt(0), evt(1));
   if (e != hipSuccess) return e;
   return bwd_dkdv_keys_per_block(a.Nk) == 128 ? launch_dkdv<Op, 4>(a, stream, evt(2), evt(3))
                                               : launch_dkdv<Op, 2>(a, stream, evt(2), evt(3));
