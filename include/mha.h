@@ -402,19 +402,21 @@ int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_atte
 
 /*
  * mha_forward_block_queries -- queries per workgroup of the attention kernel
- * that mha_forward (and the attention step of the other entry points) runs
- * for B sequences of H query heads with Nq queries: 4 for MHA_F32 (vector
- * ALUs); for MHA_BF16 / MHA_F16, 32 (one wave per workgroup, each wave
- * reading its own key/value tiles) or 512 (eight waves sharing each key/value
- * tile staged in LDS).  Both bf16/f16 kernels give the same results bit for
- * bit; the 512-query one is chosen when its workgroups would be well used:
- * u = (Nq / query slots) x (workgroups / workgroup slots of the rounds they
- * take on the 256 compute units) at least 0.45 without a mask, 0.8 with the
- * causal mask, and Nq > 64 ([TP] "The Trade-Off: Quadratic Cost": long
- * sequences are where the quadratic term dominates).  The environment
- * variable MHA_ATTENTION_BLOCK=32 or =512, read on every call, forces one of
- * the two (for tests and measurement).  0 for invalid arguments.  Pure
- * function of its arguments and that variable; no device access.
+ * that mha_forward (and the attention step of mha_forward_lse,
+ * mha_forward_gqa, mha_forward_strided, the three-kernel projection plan and
+ * decoding with more rows than the decoding kernel takes) runs for B
+ * sequences of H query heads with Nq queries: 4 for MHA_F32 (vector ALUs);
+ * for MHA_BF16 / MHA_F16, 32 (one wave per workgroup, each wave reading its
+ * own key/value tiles), 256 or 512 (four or eight waves sharing each
+ * key/value tile staged in LDS).  The three give the same results bit for
+ * bit; the choice follows how well each would use the chip ([TP] "The
+ * Trade-Off: Quadratic Cost": the longer the sequence, the more the shared
+ * tiles pay): at most 64 queries take 32; from 4096 queries with well-filled
+ * 512-query blocks, 512; where 256-query blocks are well filled, 256; else 32
+ * up to 2048 queries and 256 beyond.  The environment variable
+ * MHA_ATTENTION_BLOCK=32, =256 or =512, read on every call, forces one of
+ * them (for tests and measurement).  0 for invalid arguments.  Pure function
+ * of its arguments and that variable; no device access.
  */
 int mha_forward_block_queries(int B, int H, int Nq, int mask_kind, int dtype);
 

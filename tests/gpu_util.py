@@ -121,8 +121,9 @@ def assert_close_grad(got: np.ndarray, ref: np.ndarray, A: np.ndarray, dtype: st
 @contextlib.contextmanager
 def attention_block(block):
     """Run the bf16/f16 attention calls inside the block with the kernel of
-    ``block`` queries per workgroup (32: one-wave workgroups, 512: eight-wave
-    workgroups) through the library's MHA_ATTENTION_BLOCK override; None keeps
+    ``block`` queries per workgroup (32: one-wave workgroups, 256 / 512: four-
+    or eight-wave workgroups) through the library's MHA_ATTENTION_BLOCK
+    override; None keeps
     the library's own choice (mha_forward_block_queries)."""
     old = os.environ.get("MHA_ATTENTION_BLOCK")
     if block is None:

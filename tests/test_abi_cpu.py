@@ -176,14 +176,14 @@ def test_proj_fused_plan(lib, args, fused):
 
 @pytest.mark.parametrize("args,block", [
     ((64, 8, 64, mb.MASK_CAUSAL, mb.BF16), 32),      # sentence length: one-wave workgroups
-    ((64, 8, 128, mb.MASK_CAUSAL, mb.BF16), 32),     # u = 0.25
-    ((128, 8, 192, mb.MASK_NONE, mb.F16), 32),       # u = 0.375
-    ((64, 16, 256, mb.MASK_NONE, mb.BF16), 512),     # u = 0.5 without a mask
-    ((64, 16, 256, mb.MASK_CAUSAL, mb.BF16), 32),    # u = 0.5 under the causal mask
-    ((32, 16, 384, mb.MASK_CAUSAL, mb.BF16), 32),    # u = 0.75 < 0.8 under the causal mask
-    ((32, 16, 384, mb.MASK_NONE, mb.BF16), 512),     # u = 0.75 without a mask
-    ((16, 16, 1024, mb.MASK_CAUSAL, mb.BF16), 512),  # u = 1
-    ((2, 8, 1024, mb.MASK_CAUSAL, mb.BF16), 32),     # 32 workgroups on 256 compute units
+    ((64, 8, 128, mb.MASK_CAUSAL, mb.BF16), 32),     # u(256) = 0.5 < 0.7 under the causal mask
+    ((64, 8, 128, mb.MASK_NONE, mb.BF16), 256),      # u(256) = 0.5 >= 0.45 without it
+    ((128, 8, 192, mb.MASK_NONE, mb.F16), 256),      # u(256) = 0.75
+    ((64, 16, 256, mb.MASK_CAUSAL, mb.BF16), 256),   # u(256) = 1
+    ((32, 8, 256, mb.MASK_CAUSAL, mb.BF16), 32),     # 256 workgroups of 256 queries: half a round
+    ((16, 16, 1024, mb.MASK_CAUSAL, mb.BF16), 256),  # below 4096 queries
+    ((2, 8, 1024, mb.MASK_CAUSAL, mb.BF16), 32),     # few heads: one-wave workgroups fill the chip
+    ((1, 4, 8192, mb.MASK_CAUSAL, mb.BF16), 256),    # beyond 2048 queries, 512-query blocks under-used
     ((2, 16, 8192, mb.MASK_CAUSAL, mb.BF16), 512),   # the long causal workload
     ((2, 16, 8192, mb.MASK_CAUSAL, mb.F32), 4),      # fp32: vector-ALU kernel
     ((0, 16, 8192, mb.MASK_CAUSAL, mb.BF16), 0),     # invalid sizes
@@ -203,6 +203,8 @@ def test_forward_block_queries_override(lib, monkeypatch):
     assert lib.mha_forward_block_queries(*args) == 32
     monkeypatch.setenv("MHA_ATTENTION_BLOCK", "512")
     assert lib.mha_forward_block_queries(64, 8, 64, mb.MASK_NONE, mb.BF16) == 512
+    monkeypatch.setenv("MHA_ATTENTION_BLOCK", "256")
+    assert lib.mha_forward_block_queries(*args) == 256
     monkeypatch.setenv("MHA_ATTENTION_BLOCK", "64")
     assert lib.mha_forward_block_queries(*args) == 512
     assert lib.mha_forward_block_queries(2, 16, 8192, mb.MASK_CAUSAL, mb.F32) == 4

@@ -108,7 +108,7 @@ def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override
 # ---------------------------------------------------------------------------
 # The row statistic.
 
-@pytest.mark.parametrize("dtype,block", [("bf16", 32), ("bf16", 512), ("f16", 32), ("f16", 512), ("f32", None)])
+@pytest.mark.parametrize("dtype,block", [("bf16", 32), ("bf16", 256), ("bf16", 512), ("f16", 32), ("f16", 256), ("f16", 512), ("f32", None)])
 @pytest.mark.parametrize("B,H,Nq,Nk,mask,lens", [
     (2, 3, 64, 64, NONE, None),
     (2, 2, 150, 150, CAUSAL, (20, 150)),
@@ -116,7 +116,7 @@ def check_train(B, H, Nq, Nk, dtype, mask, lens, seed, scale=None, lens_override
     (1, 2, 300, 300, CAUSAL, None),
 ])
 def test_forward_lse_matches_oracle(dtype, block, B, H, Nq, Nk, mask, lens):
-    """The row statistic from both bf16/f16 attention kernels (32 and 512
+    """The row statistic from the three bf16/f16 attention kernels (32, 256 and 512
     queries per workgroup)."""
     inp = synth.core_inputs(B, H, Nq, Nk, 64, 64, dtype, 11, lens)
     q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))

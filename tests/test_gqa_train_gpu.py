@@ -95,7 +95,7 @@ def check_gqa(B, H, Hkv, Nq, Nk, dtype, mask, lens, seed, lens_override=None, bl
     return got
 
 
-@pytest.mark.parametrize("dtype,block", [("bf16", 32), ("bf16", 512), ("f16", 32), ("f16", 512), ("f32", None)])
+@pytest.mark.parametrize("dtype,block", [("bf16", 32), ("bf16", 256), ("bf16", 512), ("f16", 32), ("f16", 256), ("f16", 512), ("f32", None)])
 @pytest.mark.parametrize("B,H,Hkv,Nq,Nk,mask,lens", [
     (2, 8, 2, 150, 150, CAUSAL, (20, 150)),  # groups of 4, several tiles, ragged tail, padding
     (2, 6, 1, 64, 200, NONE, (1, 200)),      # multi-query: one key/value head, cross-shaped

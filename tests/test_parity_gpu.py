@@ -30,7 +30,7 @@ def _device():
 
 
 def run_core(inp, dtype, mask, scale=None, lens_override="keep", block=None):
-    """mha.forward on the inputs; ``block`` (32 or 512) forces the bf16/f16
+    """mha.forward on the inputs; ``block`` (32, 256 or 512) forces the bf16/f16
     attention kernel of that many queries per workgroup, None takes the
     library's choice."""
     q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
@@ -44,10 +44,10 @@ def run_core(inp, dtype, mask, scale=None, lens_override="keep", block=None):
     return to_host(out)
 
 
-# Both bf16/f16 attention kernels (32 and 512 queries per workgroup) for the
+# The three bf16/f16 attention kernels (32, 256 and 512 queries per workgroup) for the
 # low-precision types; fp32 has one kernel.
 def with_blocks(dtypes):
-    return [(d, b) for d in dtypes for b in ((None,) if d == "f32" else (32, 512))]
+    return [(d, b) for d in dtypes for b in ((None,) if d == "f32" else (32, 256, 512))]
 
 
 def ref_core(inp, mask, scale=None, lens_override="keep"):
@@ -144,7 +144,7 @@ def test_long_causal_sampled_rows():
 EDGE_N = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 80, 127, 128, 129, 200, 257]
 
 
-@pytest.mark.parametrize("block", [32, 512])
+@pytest.mark.parametrize("block", [32, 256, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("n", EDGE_N)
 def test_causal_square_edges(dtype, n, block):
@@ -153,7 +153,7 @@ def test_causal_square_edges(dtype, n, block):
     check_core(3, 2, n, n, 64, dtype, CAUSAL, lens, seed=n, block=block)
 
 
-@pytest.mark.parametrize("block", [32, 512])
+@pytest.mark.parametrize("block", [32, 256, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("nq,nk", [(1, 1), (1, 129), (7, 64), (64, 80), (65, 63), (130, 17),
                                    (33, 300), (17, 500), (64, 257), (200, 129), (128, 1)])
@@ -172,7 +172,7 @@ def test_f32_shapes(nq, nk, dk, dv, mask):
     check_core(2, 3, nq, nk, dk, "f32", mask, lens, seed=nq + 17 * nk, dv=dv)
 
 
-@pytest.mark.parametrize("block", [32, 512])
+@pytest.mark.parametrize("block", [32, 256, 512])
 def test_no_key_lens_and_single_head(block):
     check_core(1, 1, 100, 100, 64, "bf16", CAUSAL, None, seed=5, block=block)
     check_core(1, 1, 40, 90, 64, "bf16", NONE, None, seed=6, block=block)
@@ -223,7 +223,7 @@ def test_padded_slots_never_reach_the_output(dtype, block, nq, n, mask):
         assert np.array_equal(got, clean), f"poison {poison} changed the output"
 
 
-@pytest.mark.parametrize("block", [32, 512])
+@pytest.mark.parametrize("block", [32, 256, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("nq,nk,mask,lens", [(65, 63, NONE, (63, 1, 40)), (100, 100, CAUSAL, (100, 37, 70)),
                                              (130, 200, NONE, (200, 150, 129))])

@@ -66,7 +66,7 @@ def _attention_case(B, H, Nq, Nk, lens, dtype, scale, jump, seed):
 
 
 def _run_attention(inp, dtype, mask, scale, block):
-    """mha.forward with the attention kernel of ``block`` (32 or 512) queries
+    """mha.forward with the attention kernel of ``block`` (32, 256 or 512) queries
     per workgroup."""
     q, k, v = (to_dev(inp[n], dtype) for n in ("q", "k", "v"))
     with attention_block(block):
@@ -91,7 +91,7 @@ ATTN_SHAPES = {
 }
 
 
-@pytest.mark.parametrize("block", [32, 512])
+@pytest.mark.parametrize("block", [32, 256, 512])
 @pytest.mark.parametrize("shape", sorted(ATTN_SHAPES))
 @pytest.mark.parametrize("scale", [0.125, 1.0, -0.5])
 @pytest.mark.parametrize("jump", [60.0, 20.0])
@@ -132,7 +132,7 @@ def test_attention_bf16_large_weights_without_rescale(shape, scale):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [(2, 3, 200, 200, CAUSAL), (3, 2, 50, 50, CAUSAL), (2, 2, 37, 150, NONE),
                                    (2, 2, 130, 70, NONE)])
-@pytest.mark.parametrize("block", [32, 512])
+@pytest.mark.parametrize("block", [32, 256, 512])
 def test_attention_negative_scale(shape, scale, dtype, block):
     """N(0,1) data at negative scales: the row maximum of scale * q.k is its
     smallest q.k, which the kernels must take as the reference."""

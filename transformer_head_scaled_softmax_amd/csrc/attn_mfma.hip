@@ -59,7 +59,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
   constexpr int NT = NW * 64;
   constexpr int QW = 32 * QS;         // queries per wave: QS sub-blocks of 32
   constexpr int QB = NW * QW;         // queries per workgroup
-  static_assert(NW == 8, "one 1 KiB group of K and one of V per wave per tile");
+  static_assert(NW == 4 || NW == 8, "a tile is eight 1 KiB groups of K and eight of V");
+  constexpr int GPW = 8 / NW;  // 1 KiB groups of each tile that one wave moves
 
   // K and V tiles, double-buffered; after the key loop the same memory stages
   // the output rows (32 rows of kKS elements per wave).
@@ -130,15 +131,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
   // XOR-swizzled, so lane l fetches the global chunk that belongs in its
   // slot: for K the operand swizzle of the row (conflict-free 16-byte
   // operand reads), for V bit 1 of the row (conflict-free transposing reads).
+  // Wave w moves groups w, w + NW, ...: rows 8 NW apart.  NW is even, so the
+  // swizzle of a lane's row is the same in every group it moves.
   const int grow = 8 * wave + (lane >> 3), gslot = lane & 7;
   const int koff = (int)((grow * a.k_sn + ((gslot ^ operand_swizzle(grow)) << 3)) * 2);
   const int voff = (int)((grow * a.v_sn + ((gslot ^ (((grow >> 1) & 1) << 2)) << 3)) * 2);
+  const int kgrp = (int)(8 * NW * a.k_sn * 2), vgrp = (int)(8 * NW * a.v_sn * 2);
   const int ktile = (int)(kBN * a.k_sn * 2), vtile = (int)(kBN * a.v_sn * 2);
   // Tiles at or past the workgroup's key end fall outside the range check, so
   // the prefetch issued during the last tile reads nothing.
   auto issue_tile = [&](int t, int buf) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, MHA_LDS(&ks[buf][wave * 512]), 16, koff + t * ktile, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrc, MHA_LDS(&vs[buf][wave * 512]), 16, voff + t * vtile, 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+      const int grp = wave + NW * g;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, MHA_LDS(&ks[buf][grp * 512]), 16, koff + g * kgrp + t * ktile, 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrc, MHA_LDS(&vs[buf][grp * 512]), 16, voff + g * vgrp + t * vtile, 0,
+                                               0, 0);
+    }
   };
   const int kswz = operand_swizzle(col);  // = operand_swizzle(32jb + col)
 
@@ -732,13 +742,24 @@ hipError_t launch_short(const AttnArgs& a, hipStream_t stream, hipEvent_t t0, hi
   return hipGetLastError();
 }
 
+// Workgroups of qb queries: 32 (one wave), or 256 / 512 (four or eight waves
+// of 64 queries sharing each staged K/V tile).
+template <class Op>
+hipError_t launch_sized(const AttnArgs& a, int qb, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  switch (qb) {
+    case 512: return launch<Op, 8, 2>(a, stream, t0, t1);
+    case 256: return launch<Op, 4, 2>(a, stream, t0, t1);
+    default: return launch_short<Op>(a, stream, t0, t1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
-  const bool longq = attention_block_queries(a.B, a.H, a.Nq, a.causal) == 512;
+  const int qb = attention_block_queries(a.B, a.H, a.Nq, a.causal);
   if (dt == DType::BF16)
-    return longq ? launch<BF16, 8, 2>(a, stream, t0, t1) : launch_short<BF16>(a, stream, t0, t1);
-  return longq ? launch<F16, 8, 2>(a, stream, t0, t1) : launch_short<F16>(a, stream, t0, t1);
+    return launch_sized<BF16>(a, qb, stream, t0, t1);
+  return launch_sized<F16>(a, qb, stream, t0, t1);
 }
 
 }  // namespace mha

@@ -188,34 +188,40 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream, hipEvent_t t0 
                            hipEvent_t t1 = nullptr);
 hipError_t launch_attn_mfma(const AttnArgs& a, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
                             hipEvent_t t1 = nullptr);
-// Queries per workgroup of the bf16/f16 attention launch: 32 (one-wave
-// workgroups) or 512 (eight waves).  The 512-query kernel shares each staged
-// K/V tile among eight waves and reads the tiles from L2 half as often as four
-// waves would (282 vs 297 us on the long causal workload), but a query length
-// that is not a multiple of 512 leaves some of its waves without queries, and
-// few workgroups leave compute units idle.  Its utilisation u = (queries /
-// query slots) x (workgroups / slots of the rounds they take on 256 compute
-// units) decides.  Measured on one MI355X over query lengths 96-4096 (outputs
-// identical bit for bit), the one-wave kernel takes about 1.9x the 512-query
-// kernel's time per unit of work without a mask and 1.2-1.3x under the causal
-// mask (whose workgroups end unevenly); it runs when u < 0.45 without a mask
-// (at u = 0.5 it won on one grid of 256 workgroups and lost by 40% on four
-// rounds of them) and when u < 0.8 with it.  Every query length of at most
-// 192 takes it, for example.  MHA_ATTENTION_BLOCK=32 or 512 in the
-// environment, read on every call, forces one of the two kernels.
+// Queries per workgroup of the bf16/f16 attention launch: 32 (one wave per
+// workgroup, reading its own key/value tiles), 256 or 512 (four or eight waves
+// of 64 queries sharing each key/value tile staged in LDS).  All three give
+// the same results bit for bit.  Shared tiles serve more queries per byte
+// read, but a query length that is not a multiple of the workgroup's leaves
+// waves idle, and few workgroups leave compute units idle: the utilisation
+// u = (queries / query slots) x (workgroups / workgroup slots of the rounds
+// they take) -- one 512-query or two 256-query workgroups per compute unit,
+// 256 compute units -- decides, from measurements on one MI355X of the three
+// kernels over 38 shapes (96-8192 queries, cross-attention up to 4096 keys):
+//   * at most 64 queries: 32;
+//   * from 4096 queries with u(512) >= 0.9: 512 (2-3% ahead of 256 at 8192);
+//   * u(256) >= 0.7 under the causal mask, >= 0.45 without it: 256 (up to
+//     1.6x ahead of the others at a few hundred queries with many heads);
+//   * otherwise, up to 2048 queries: 32 (its small workgroups fill the chip
+//     when there are few heads or the 256-query blocks are mostly empty);
+//     beyond: 256.
+// MHA_ATTENTION_BLOCK=32, 256 or 512 in the environment, read on every call,
+// forces one of the kernels.
+inline double attention_block_use(int64_t B, int64_t H, int64_t Nq, int64_t qb, int64_t per_round) {
+  const int64_t nqb = (Nq + qb - 1) / qb, wgs = nqb * B * H;
+  if (wgs <= 0) return 0.0;
+  const int64_t rounds = (wgs + per_round - 1) / per_round;
+  return double(Nq) / double(nqb * qb) * double(wgs) / double(rounds * per_round);
+}
 inline int attention_block_queries(int B, int H, int Nq, bool causal) {
-  if (const char* force = getenv("MHA_ATTENTION_BLOCK")) {
-    if (!strcmp(force, "32")) return 32;
-    if (!strcmp(force, "512")) return 512;
-  }
+  if (const char* force = getenv("MHA_ATTENTION_BLOCK"))
+    for (int qb : {32, 256, 512})
+      if (atoi(force) == qb) return qb;
   if (Nq <= 64) return 32;
-  constexpr int64_t kQueriesPerBlock = 512, kComputeUnits = 256;
-  const int64_t nqb = (Nq + kQueriesPerBlock - 1) / kQueriesPerBlock;
-  const int64_t wgs = nqb * B * H;
-  if (wgs <= 0) return 32;
-  const int64_t rounds = (wgs + kComputeUnits - 1) / kComputeUnits;
-  const double u = double(Nq) / double(nqb * kQueriesPerBlock) * double(wgs) / double(rounds * kComputeUnits);
-  return u < (causal ? 0.8 : 0.45) ? 32 : 512;
+  constexpr int64_t kComputeUnits = 256;
+  if (Nq >= 4096 && attention_block_use(B, H, Nq, 512, kComputeUnits) >= 0.9) return 512;
+  if (attention_block_use(B, H, Nq, 256, 2 * kComputeUnits) >= (causal ? 0.7 : 0.45)) return 256;
+  return Nq <= 2048 ? 32 : 256;
 }
 
 hipError_t launch_gemm_mfma(const GemmBatch& g, DType dt, hipStream_t stream, hipEvent_t t0 = nullptr,
