@@ -81,6 +81,16 @@ def test_base_decoder_causal_full():
     assert_close(run_core(inp, w.dtype, w.mask), ref_core(inp, w.mask), w.dtype, w.name)
 
 
+@pytest.mark.parametrize("name,block", [("translation_decoder_causal", 32), ("mid_causal", 256)])
+def test_mid_length_workloads_full(name, block):
+    """The mid-length workloads in the launch configuration the benchmark times
+    (one-wave workgroups at 100 tokens, 256-query workgroups at 256 tokens)."""
+    w = synth.WORKLOADS[name]
+    assert mha.load().mha_forward_block_queries(w.B, w.H, w.Nq, w.mask, mha.BF16) == block
+    inp = synth.workload_inputs(w)
+    assert_close(run_core(inp, w.dtype, w.mask), ref_core(inp, w.mask), w.dtype, w.name)
+
+
 def _proj_dev(inp, dtype):
     return {n: to_dev(inp[n], dtype) for n in ("x_q", "x_kv", "W_Q", "W_K", "W_V", "W_O")}
 

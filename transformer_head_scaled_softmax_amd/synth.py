@@ -109,6 +109,11 @@ WORKLOADS = {
         Workload("base_encoder_proj_gqa", 64, 8, 64, 64, 64, "bf16", MASK_NONE, (10, 64), True, False, 8,
                  "Transformer-base encoder self-attention with grouped-query projections (B=64, n=64, "
                  "d_model=512, 8 query heads over 2 key/value heads, d=64, lengths U{10..64})", Hkv=2),
+        Workload("translation_decoder_causal", 64, 8, 100, 100, 64, "bf16", MASK_CAUSAL, (10, 100), False, False,
+                 13, "Transformer-base decoder masked self-attention at the translation length the pages give "
+                 "(B=64, n=100, h=8, d=64, lengths U{10..100})"),
+        Workload("mid_causal", 64, 16, 256, 256, 64, "bf16", MASK_CAUSAL, None, False, False, 14,
+                 "causal self-attention over a few hundred tokens with many heads (B=64, n=256, h=16, d=64)"),
         Workload("long_causal_gqa_bwd", 2, 16, 8192, 8192, 64, "bf16", MASK_CAUSAL, None, False, False, 6,
                  "backward pass of long-context causal self-attention with grouped-query attention "
                  "(B=2, n=8192, h=16 query heads over 4 key/value heads, d=64, output gradient N(0,1))",
