@@ -393,10 +393,13 @@ size_t mha_proj_ln_workspace_bytes(int B, int Nq, int Nk, int D, int H, int d_k,
  * The fused kernel takes D a multiple of 64, d_k == d_v == 64 (bf16 or
  * f16), and either self-attention with Nq == Nk <= 128 or cross-attention
  * with Nq <= 64 and Nk <= 128 -- sentence-length encoder, decoder and
- * encoder-decoder layers.  mha_proj_forward uses it for all of these except
- * cross-attention with D >= 768 over 65..96 keys, where the three-kernel plan
- * measured faster (MHA_PLAN_FUSED still runs it there).  Pure function of its
- * arguments; no device access.
+ * encoder-decoder layers.  mha_proj_forward uses it for these except where
+ * the three-kernel plan measured faster: cross-attention with D >= 768 over
+ * 65..96 keys, and small batches, whose fused grid -- one workgroup per head
+ * (taken as D / 64 heads) and per 128 token rows (self-attention) or two
+ * sequences (cross-attention) -- has fewer than D / 8 (self) or 256 (cross)
+ * workgroups.  MHA_PLAN_FUSED still runs the fused kernel there.  Pure
+ * function of its arguments; no device access.
  */
 int mha_proj_fused(int B, int Nq, int Nk, int D, int d_k, int d_v, int self_attention);
 

@@ -155,15 +155,19 @@ def test_proj_empty_is_ok(lib):
 
 @pytest.mark.parametrize("args,fused", [
     ((64, 64, 64, 512, 64, 64, 1), 1),     # sentence-length self-attention
-    ((3, 128, 128, 64, 64, 64, 1), 1),     # longest fused sequence
+    ((64, 128, 128, 64, 64, 64, 1), 1),    # longest fused sequence
     ((3, 129, 129, 64, 64, 64, 1), 0),     # too long for one tile
     ((64, 64, 80, 512, 64, 64, 0), 1),     # sentence-length cross-attention
     ((32, 64, 80, 1024, 64, 64, 0), 0),    # d_model >= 768 over 65..96 keys: three kernels measured faster
     ((32, 64, 96, 768, 64, 64, 0), 0),
-    ((32, 64, 80, 640, 64, 64, 0), 1),     # d_model below 768
+    ((64, 64, 80, 640, 64, 64, 0), 1),     # d_model below 768
     ((32, 64, 64, 1024, 64, 64, 0), 1),    # one key tile
     ((32, 64, 97, 1024, 64, 64, 0), 1),    # more than 96 keys
     ((32, 64, 64, 1024, 64, 64, 1), 1),    # self-attention at d_model 1024
+    ((8, 64, 64, 512, 64, 64, 1), 0),      # small batch: 32 fused workgroups < D / 8
+    ((16, 64, 64, 512, 64, 64, 1), 1),     # 64 fused workgroups
+    ((8, 64, 64, 1024, 64, 64, 1), 0),     # 64 < 1024 / 8
+    ((16, 64, 128, 512, 64, 64, 0), 0),    # cross-attention: 64 fused workgroups < 256
     ((32, 65, 80, 1024, 64, 64, 0), 0),    # cross-attention with more than 64 queries
     ((32, 64, 129, 1024, 64, 64, 0), 0),   # cross-attention with more than 128 keys
     ((2, 64, 64, 200, 64, 64, 1), 0),      # D not a multiple of 64

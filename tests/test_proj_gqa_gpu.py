@@ -59,8 +59,8 @@ def test_proj_gqa_matches_oracle(dtype, B, Nq, Nk, D, H, Hkv, cross, mask):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("B,Nq,Nk,D,H,Hkv", [
-    (3, 64, 112, 1024, 16, 4),   # d_model 1024 over 112 keys: the fused kernel
-    (3, 64, 80, 512, 8, 2),      # d_model 512 over 80 keys: the fused kernel
+    (32, 64, 112, 1024, 16, 4),  # d_model 1024 over 112 keys: the fused kernel (256 workgroups)
+    (64, 64, 80, 512, 8, 2),     # d_model 512 over 80 keys: the fused kernel (256 workgroups)
 ])
 def test_proj_gqa_fused_cross(dtype, B, Nq, Nk, D, H, Hkv):
     """Cross-attention sublayers that mha_proj_forward runs through the fused

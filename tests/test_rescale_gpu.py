@@ -212,10 +212,9 @@ def test_projection_negative_scale(scale, dtype, cross):
     checked at -1/8 and f16 at larger negative scales."""
     B, Nq, Nk, D, H = (8, 64, 80, 256, 4) if cross else (8, 64, 64, 256, 4)
     p = synth.proj_inputs(B, Nq, Nk, D, H, 64, 64, dtype, seed=91 + cross, cross=cross, lens=(5, Nk))
-    assert mha.load().mha_proj_fused(B, Nq, Nk, D, 64, 64, int(not cross)) == 1
     d = {n: to_dev(p[n], dtype) for n in ("x_q", "x_kv", "W_Q", "W_K", "W_V", "W_O")}
     out = mha.proj_forward(d["x_q"], d["x_kv"], d["W_Q"], d["W_K"], d["W_V"], d["W_O"], H=H,
-                           key_lens=lens_dev(p["key_lens"]), scale=scale)
+                           key_lens=lens_dev(p["key_lens"]), scale=scale, plan=mha.PLAN_FUSED)
     torch.cuda.synchronize()
     ref = oracle.mha_proj(p["x_q"], p["x_kv"], p["W_Q"], p["W_K"], p["W_V"], p["W_O"], H=H,
                           key_lens=p["key_lens"], scale=scale)

@@ -274,10 +274,24 @@ bool fused_supported(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) 
 // the three-kernel plan measured 2-19% faster.  (Both plans timed on one
 // MI355X over cross-attention with B 16-64, Nq 32-64, Nk 64-128, d_model
 // 512-1024: the fused plan wins by 8% at d_model 512, ties at 640 and at
-// 64 keys, and wins by 20% from 112 keys; self-attention fuses at every
-// measured size.)
+// 64 keys, and wins by 20% from 112 keys; self-attention fused at every
+// size of that sweep.)
+//
+// Small batches: the fused kernel's grid is one workgroup per head and 128
+// token rows (self-attention: 128 / NPQ sequences of NPQ = 32, 64 or 128
+// padded rows) or two sequences (cross-attention), which leaves most compute
+// units idle when there are few sequences, while the three-kernel plan spreads
+// over many more workgroups.  With D / 64 heads, the fused plan is taken from
+// D / 8 workgroups (self-attention) or 256 (cross-attention) on; measured on
+// one MI355X, the three kernels were 4-13% faster for self-attention below
+// that (B 1-8 at d_model 512, B 4-8 at 1024) and 10-34% for cross-attention
+// (B 4-16), the fused kernel 5-20% faster above it.
 bool use_fused(bool self, int B, int Nq, int Nk, int D, int d_k, int d_v) {
-  return fused_supported(self, B, Nq, Nk, D, d_k, d_v) && (self || D < 768 || Nk <= 64 || Nk > 96);
+  if (!fused_supported(self, B, Nq, Nk, D, d_k, d_v) || (!self && D >= 768 && Nk > 64 && Nk <= 96)) return false;
+  const int64_t heads = D / 64;
+  const int64_t per_wg = self ? 128 / (Nq <= 32 ? 32 : Nq <= 64 ? 64 : 128) : 2;
+  const int64_t wgs = (B + per_wg - 1) / per_wg * heads;
+  return wgs >= (self ? D / 8 : 256);
 }
 
 // The residual connection and layer normalisation after the sublayer
