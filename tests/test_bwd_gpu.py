@@ -163,10 +163,29 @@ def test_backward_matches_oracle(dtype, B, H, Nq, Nk, mask, lens):
     check_train(B, H, Nq, Nk, dtype, mask, lens, seed=13)
 
 
-def test_backward_eight_wave_dq_blocks_with_ragged_tail():
-    """From 4096 queries the dQ kernel runs eight waves (256 queries) per
-    workgroup; 4100 queries leave a ragged last block."""
+def test_backward_four_wave_dq_blocks_on_a_long_sequence():
+    """From 4096 queries on few heads the dQ kernel keeps four waves (128
+    queries) per workgroup; 4100 queries leave a ragged last block."""
     check_train(1, 1, 4100, 4100, "bf16", CAUSAL, None, seed=19)
+
+
+def test_backward_eight_wave_dq_blocks_with_ragged_tail():
+    """From 4096 queries with at least 512 workgroups the dQ kernel runs eight
+    waves (256 queries) per workgroup: 4100 queries over 32 heads (17 blocks
+    each) leave a ragged last block.  Two (b, h) slices against the oracle."""
+    B, H, N = 1, 32, 4100
+    inp = synth.train_inputs(B, H, N, N, 64, 64, "bf16", 23, (3000, N))
+    got = gpu_train(inp, "bf16", CAUSAL)
+    picks = (0, 31)
+    lens = inp["key_lens"]
+    sl = {n: np.ascontiguousarray(inp[n][:, list(picks)]) for n in ("q", "k", "v", "dout")}
+    kw = dict(mask_kind=CAUSAL, key_lens=lens)
+    ref = oracle.attention_backward(sl["q"], sl["k"], sl["v"], sl["dout"], **kw)
+    out, P = oracle.attention(sl["q"], sl["k"], sl["v"], return_weights=True, **kw)
+    A = grad_bounds(sl["q"], sl["k"], sl["v"], sl["dout"], P, out, 1.0 / np.sqrt(64))
+    del P
+    for i, n in enumerate(("dq", "dk", "dv")):
+        assert_close_grad(got[n][:, list(picks)], ref[i], A[i], "bf16", f"{n} eight-wave dQ blocks")
 
 
 

@@ -626,17 +626,21 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t const* ev
     return hipGetLastError();
   }
   // The dQ kernel writes D, which the dK/dV kernel reads: stream order.
-  // dQ workgroups: two waves (64 queries) for at most 64 queries, four (128)
-  // up to 4096, eight (256 queries share each K/V tile) beyond.  Measured on
-  // one MI355X, whole backward pass, causal, bf16 (same results bit for bit):
-  // four waves against eight 23.1 vs 28.7 us at B 64, h 8, n 100; 25.4 vs
-  // 31.2 us at n 128; 91.8 vs 102.7 us at B 8, h 16, n 1024; 147.8 vs 159.4
-  // us at B 4, h 16, n 2048; at n = 8192 eight stay ahead (944 vs 953 us for
-  // the pass; the dQ kernel alone 397 vs 407 us).  dK/dV workgroups: four
-  // waves (128 keys) beyond 64 keys (eight were 1% slower at n = 8192).
-  hipError_t e = a.Nq <= 64     ? launch_dq<Op, 2>(a, stream, evt(0), evt(1))
-                 : a.Nq < 4096 ? launch_dq<Op, 4>(a, stream, evt(0), evt(1))
-                               : launch_dq<Op, 8>(a, stream, evt(0), evt(1));
+  // dQ workgroups: two waves (64 queries) for at most 64 queries; eight (256
+  // queries share each K/V tile) from 4096 queries when that still gives at
+  // least 512 workgroups (two rounds of the chip); four (128) otherwise.
+  // Measured on one MI355X, whole backward pass, causal, bf16 (same results bit
+  // for bit), four waves against eight: 23.1 vs 28.7 us at B 64, h 8, n 100;
+  // 25.4 vs 31.2 us at n 128; 91.8 vs 102.7 us at B 8, h 16, n 1024; 147.8 vs
+  // 159.4 us at B 4, h 16, n 2048; 292 vs 337 us at B 1, h 4, n 8192 and 571
+  // vs 658 us at B 1, h 2, n 16384 (128 eight-wave workgroups); 953 vs 944 us
+  // at B 2, h 16, n 8192 (1024 of them; the dQ kernel alone 407 vs 397 us).
+  // dK/dV workgroups: four waves (128 keys) beyond 64 keys (eight were 1%
+  // slower at n = 8192).
+  const bool wide = a.Nq >= 4096 && (int64_t)((a.Nq + 255) / 256) * a.B * a.H >= 512;
+  hipError_t e = a.Nq <= 64 ? launch_dq<Op, 2>(a, stream, evt(0), evt(1))
+                 : wide     ? launch_dq<Op, 8>(a, stream, evt(0), evt(1))
+                            : launch_dq<Op, 4>(a, stream, evt(0), evt(1));
   if (e != hipSuccess) return e;
   return bwd_dkdv_keys_per_block(a.Nk) == 128 ? launch_dkdv<Op, 4>(a, stream, evt(2), evt(3))
                                               : launch_dkdv<Op, 2>(a, stream, evt(2), evt(3));
