@@ -292,15 +292,17 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_mfma_kernel(Att
           // yet).  While no query of the wave has a reference (its first tile)
           // the pass would always fail; the short-sequence configuration (QS = 1,
           // mostly a single tile) skips it then, which halves its softmax work
-          // (7.95 vs 8.2 us on the base decoder workload).  Long sequences keep
-          // the branch-free loop (the check cost 3% there).
+          // (7.95 vs 8.2 us on the base decoder workload), and so do four-wave
+          // workgroups, which serve sequences of a few key tiles.  Eight-wave
+          // workgroups (long sequences) keep the branch-free loop (the check
+          // cost 3% there).
           // The common path asks only whether any lane's partial sum failed the
           // guard (one compare and a wave vote); which queries must rescale --
           // lanes l and l + 32 hold one query and decide together -- is worked
           // out only on the rare path.  The unguarded pass takes the rare path
           // only until every query of the sub-block has a reference.
           bool ran = false, any_need = true;
-          if (QS > 1 || !__all(m_ref[u] == -INFINITY)) {
+          if ((QS > 1 && NW == 8) || !__all(m_ref[u] == -INFINITY)) {
             exponentiate(m_ref[u], false);
             ran = true;
             if constexpr (FAST)
