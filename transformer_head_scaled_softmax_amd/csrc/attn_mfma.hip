@@ -10,12 +10,14 @@
 // running maximum and sum (an exact rearrangement of the same result).
 //
 // Two kernels, with the same arithmetic step for step (same results bit for
-// bit).  attn_mfma_kernel gives a workgroup 512 consecutive queries of one
-// (b, h): eight waves of 64, each as two sub-blocks of 32 that share every K
-// operand read.  attn_short_kernel gives one wave 32 queries and arranges its
-// memory traffic so that it waits for memory once per tile.  The second runs
-// every query block of at most 64 rows and the longer ones where the first
-// would leave many waves or compute units idle (attention_block_queries).  In both, per key tile a wave computes the
+// bit).  attn_mfma_kernel gives a workgroup 512 (or 256) consecutive queries
+// of one (b, h): eight (four) waves of 64, each as two sub-blocks of 32 that
+// share every K operand read, and every wave sharing each key/value tile
+// staged in LDS.  attn_short_kernel gives one wave 32 queries and arranges its
+// memory traffic so that it waits for memory once per tile.  The launcher
+// picks the workgroup size from how well each would fill the chip
+// (attention_block_queries): one-wave workgroups for query blocks of at most
+// 64 rows and where the larger ones would leave waves or compute units idle.  In both, per key tile a wave computes the
 // TRANSPOSED scores S^T (64 keys x 32 queries) = K_tile * Q^T, so that each
 // lane ends up holding 32 scores of one query (lanes l and l+32 share a query
 // and split its keys).  That layout is exactly the B operand of the second
